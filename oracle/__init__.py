@@ -1,0 +1,11 @@
+"""Float64 CPU checker (test infrastructure only).
+
+Imported by the tests, the smoke check and the benchmark's CPU-baseline leg;
+never by the product path. See ``oracle.attention`` for what it computes.
+"""
+
+from .attention import (CAUSAL, CROSS, EMPTY_SENTINEL, FULL, attention_forward,
+                        decode_forward, window_length)
+
+__all__ = ["CAUSAL", "FULL", "CROSS", "EMPTY_SENTINEL", "attention_forward",
+           "decode_forward", "window_length"]

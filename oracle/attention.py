@@ -1,0 +1,160 @@
+"""Float64 CPU checker for the fused attention forward.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module; the product path never calls it and
+shares no code with it.
+
+What it computes is the plain definition that the pages' tiled online-softmax
+shaders reach up to rounding order:
+
+    s_ij = scale * <Q[i, h], K[j, kv_head(h)]>           for j < w_i
+    m_i  = max_j s_ij
+    Z_i  = sum_j exp(s_ij - m_i)
+    out[i, h] = sum_j exp(s_ij - m_i) / Z_i * V[j, kv_head(h)]
+    lse[i, h] = (m_i, log Z_i)
+
+Sources (pages' titles and the part of each shader):
+  * meganeura ``attention.wgsl`` -- header comment (the causal / full / cross
+    windows), ``main`` body (GQA head map, online update, normalisation with a
+    safe zero sum, and the (max, log of the running sum) pair written "for
+    backward");
+  * meganeura ``cached_attention.wgsl`` -- header and ``main`` (one query row,
+    window [0, kv_pos] with kv_pos read from a device buffer);
+  * cera ``attention_prefill.wgsl`` -- header "Constraints" and ``main`` (causal
+    window continued from ``start_pos`` and clamped to the cache length; a
+    zero-length window writes zeros).
+
+The scores are materialised block-of-rows by block-of-rows (rows are
+independent, so this changes no arithmetic of any row); everything is float64.
+Parity is pinned by the CPU tests (closed forms, brute force, torch's library
+attention, invariants); no function here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+CAUSAL, FULL, CROSS = 0, 1, 2
+
+# Initial running max and empty-window log-sum value of meganeura
+# attention.wgsl (``main``: ``max_score`` start value and the ``select`` on a
+# zero sum in the side-output write).
+EMPTY_SENTINEL = -1e30
+
+
+def window_length(mode: int, i: int, q_seq: int, kv_len: int, start_pos: int) -> int:
+    """Keys [0, w) that query row i attends to.
+
+    attention.wgsl header: causal uses pos+1, full uses q_seq, cross uses the
+    kv length. attention_prefill.wgsl ``main``: the causal position is
+    start_pos + i and the window is clamped to the cache length.
+    """
+    if mode == CAUSAL:
+        return max(0, min(start_pos + i + 1, kv_len))
+    if mode == FULL:
+        return q_seq
+    if mode == CROSS:
+        return kv_len
+    raise ValueError(f"unknown mode {mode}")
+
+
+def _check_shapes(q, k, v, num_heads, num_kv_heads, head_dim, kv_len):
+    if num_heads % num_kv_heads != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    if q.shape[1] != num_heads * head_dim:
+        raise ValueError("q must be [q_seq, num_heads*head_dim]")
+    if k.shape[1] != num_kv_heads * head_dim or v.shape[1] != num_kv_heads * head_dim:
+        raise ValueError("k, v must be [rows, num_kv_heads*head_dim]")
+    if k.shape[0] < kv_len or v.shape[0] < kv_len:
+        raise ValueError("k, v hold fewer than kv_len rows")
+
+
+def attention_forward(q, k, v, *, num_heads: int, num_kv_heads: int, head_dim: int,
+                      mode: int, kv_len: int, start_pos: int = 0, scale: float,
+                      rows=None, row_block: int = 256):
+    """Attention forward in float64 for the query rows ``rows`` (default: all).
+
+    q: [q_seq, num_heads*head_dim]; k, v: [>= kv_len, num_kv_heads*head_dim].
+    Returns (out [n_rows, num_heads*head_dim], lse [n_rows, num_heads, 2]),
+    both float64; lse[..., 0] is the row max and lse[..., 1] the log of the
+    sum of exp(score - max), the pair meganeura attention.wgsl stores.
+    """
+    _check_shapes(q, k, v, num_heads, num_kv_heads, head_dim, kv_len)
+    q_seq = q.shape[0]
+    if mode == FULL and kv_len != q_seq:
+        raise ValueError("full attention needs kv_len == q_seq")
+    if rows is None:
+        rows = np.arange(q_seq)
+    rows = np.asarray(rows, dtype=np.int64)
+    n = rows.shape[0]
+    group = num_heads // num_kv_heads
+    d = head_dim
+
+    out = np.zeros((n, num_heads * d), dtype=np.float64)
+    lse = np.full((n, num_heads, 2), EMPTY_SENTINEL, dtype=np.float64)
+    win = np.array([window_length(mode, int(i), q_seq, kv_len, start_pos) for i in rows],
+                   dtype=np.int64)
+
+    for h in range(num_heads):
+        kvh = h // group  # GQA: contiguous groups of query heads share a KV head
+        qh = q[:, h * d:(h + 1) * d]
+        kh = k[:, kvh * d:(kvh + 1) * d]
+        vh = v[:, kvh * d:(kvh + 1) * d]
+        for b0 in range(0, n, row_block):
+            sel = slice(b0, min(b0 + row_block, n))
+            r = rows[sel]
+            w = win[sel]
+            wmax = int(w.max()) if w.size else 0
+            if wmax == 0:
+                continue  # every row empty: out stays 0, lse stays the sentinel
+            qb = qh[r].astype(np.float64)
+            kb = kh[:wmax].astype(np.float64)
+            vb = vh[:wmax].astype(np.float64)
+            s = scale * (qb @ kb.T)  # [rows, wmax]
+            valid = np.arange(wmax)[None, :] < w[:, None]
+            s = np.where(valid, s, -np.inf)
+            m = s.max(axis=1)
+            nonempty = w > 0
+            m_safe = np.where(nonempty, m, 0.0)
+            e = np.where(valid, np.exp(s - m_safe[:, None]), 0.0)
+            z = e.sum(axis=1)
+            z_safe = np.where(nonempty, z, 1.0)
+            o = (e @ vb) / z_safe[:, None]
+            out[sel, h * d:(h + 1) * d] = np.where(nonempty[:, None], o, 0.0)
+            lse[sel, h, 0] = np.where(nonempty, m, EMPTY_SENTINEL)
+            lse[sel, h, 1] = np.where(nonempty, np.log(z_safe), EMPTY_SENTINEL)
+    return out, lse
+
+
+def decode_forward(q, k_cache, v_cache, *, kv_pos: int, num_heads: int,
+                   num_kv_heads: int, head_dim: int, max_seq: int, scale: float):
+    """One-token decode over a cache, in float64.
+
+    cached_attention.wgsl ``main``: the window is [0, kv_pos] (kv_len =
+    kv_pos + 1), one query row of num_heads heads; the length is clamped to the
+    cache's max_seq rows as attention_prefill.wgsl clamps its window.
+    q: [1, num_heads*head_dim]; caches: [max_seq, num_kv_heads*head_dim].
+    Returns (out [1, num_heads*head_dim], lse [1, num_heads, 2]).
+    """
+    if num_heads % num_kv_heads != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    kv_len = max(0, min(int(kv_pos) + 1, max_seq))
+    group = num_heads // num_kv_heads
+    d = head_dim
+    out = np.zeros((1, num_heads * d), dtype=np.float64)
+    lse = np.full((1, num_heads, 2), EMPTY_SENTINEL, dtype=np.float64)
+    if kv_len == 0:
+        return out, lse
+    for h in range(num_heads):
+        kvh = h // group
+        qv = q[0, h * d:(h + 1) * d].astype(np.float64)
+        kw = k_cache[:kv_len, kvh * d:(kvh + 1) * d].astype(np.float64)
+        vw = v_cache[:kv_len, kvh * d:(kvh + 1) * d].astype(np.float64)
+        s = scale * (kw @ qv)
+        m = s.max()
+        e = np.exp(s - m)
+        z = e.sum()
+        out[0, h * d:(h + 1) * d] = (e @ vw) / z
+        lse[0, h, 0] = m
+        lse[0, h, 1] = np.log(z)
+    return out, lse

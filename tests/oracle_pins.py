@@ -1,0 +1,360 @@
+"""Checks that pin the float64 checker (``oracle``) to facts that do not come
+from the checker itself: closed forms, brute-force scalar loops, the page's
+own sequential online-softmax update, torch's library attention, and
+invariants of softmax attention.
+
+Each ``pin_*`` takes the checker module as its argument and raises
+AssertionError on a mismatch, so the same pins run against the real checker
+(test_oracle.py) and against deliberately broken copies of it
+(test_oracle_mutants.py).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+CAUSAL, FULL, CROSS = 0, 1, 2
+SENT = -1e30
+
+
+def _rand(shape, seed, scale=1.0):
+    return (np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32)
+
+
+def _close(a, b, tol=1e-10, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def _fwd(orc, q, k, v, H, Hkv, d, mode, kv_len, start_pos=0, scale=None, rows=None):
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return orc.attention_forward(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d,
+                                 mode=mode, kv_len=kv_len, start_pos=start_pos,
+                                 scale=scale, rows=rows)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def pin_single_key_returns_that_v_row(orc):
+    """A window of one key: the weight is 1, so out is that V row, the max is
+    that key's score and log(sum) = log 1 = 0."""
+    H, Hkv, d = 4, 2, 8
+    q = _rand((3, H * d), 1)
+    k = _rand((1, Hkv * d), 2)
+    v = _rand((1, Hkv * d), 3)
+    scale = 0.37
+    out, lse = _fwd(orc, q, k, v, H, Hkv, d, CROSS, 1, scale=scale)
+    for i in range(3):
+        for h in range(H):
+            kvh = h // (H // Hkv)
+            _close(out[i, h * d:(h + 1) * d], v[0, kvh * d:(kvh + 1) * d], 1e-12, "out")
+            s = scale * math.fsum(float(q[i, h * d + t]) * float(k[0, kvh * d + t])
+                                  for t in range(d))
+            _close(lse[i, h, 0], s, 1e-12, "max")
+            _close(lse[i, h, 1], 0.0, 1e-12, "logsum")
+
+
+def pin_identical_keys_give_mean_of_v(orc):
+    """All keys equal: every weight is 1/w, out is the mean of V over the
+    window, the max is the common score and log(sum) = log w."""
+    H, Hkv, d, n = 2, 1, 4, 6
+    q = _rand((n, H * d), 4)
+    k = np.repeat(_rand((1, Hkv * d), 5), n, axis=0)
+    v = _rand((n, Hkv * d), 6)
+    out, lse = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, n)
+    scale = 1.0 / math.sqrt(d)
+    for i in range(n):
+        w = i + 1
+        for h in range(H):
+            _close(out[i, h * d:(h + 1) * d], v[:w, :d].astype(np.float64).mean(axis=0),
+                   1e-12, "mean")
+            s = scale * math.fsum(float(q[i, h * d + t]) * float(k[0, t]) for t in range(d))
+            _close(lse[i, h, 0], s, 1e-12, "max")
+            _close(lse[i, h, 1], math.log(w), 1e-12, "log w")
+
+
+def pin_zero_query_gives_mean(orc):
+    """Q = 0: all scores are 0, max 0, log(sum) = log w, out = mean of V."""
+    H, Hkv, d, n = 2, 2, 4, 5
+    q = np.zeros((n, H * d), np.float32)
+    k = _rand((n, Hkv * d), 7)
+    v = _rand((n, Hkv * d), 8)
+    out, lse = _fwd(orc, q, k, v, H, Hkv, d, FULL, n)
+    for h in range(H):
+        _close(out[:, h * d:(h + 1) * d],
+               np.broadcast_to(v[:, h * d:(h + 1) * d].astype(np.float64).mean(0), (n, d)),
+               1e-12, "mean")
+    _close(lse[..., 0], np.zeros((n, H)), 0.0, "max")
+    _close(lse[..., 1], np.full((n, H), math.log(n)), 1e-12, "log n")
+
+
+def pin_causal_row0_returns_v0(orc):
+    """Causal, start_pos 0: row 0 sees only key 0."""
+    H, Hkv, d, n = 4, 2, 8, 7
+    q, k, v = _rand((n, H * d), 9), _rand((n, Hkv * d), 10), _rand((n, Hkv * d), 11)
+    out, lse = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, n)
+    for h in range(H):
+        kvh = h // 2
+        _close(out[0, h * d:(h + 1) * d], v[0, kvh * d:(kvh + 1) * d], 1e-12, "row0")
+        _close(lse[0, h, 1], 0.0, 1e-12, "row0 logsum")
+
+
+def pin_two_keys_logistic(orc):
+    """Two keys, d=1: weights are logistic functions of the score gap, and
+    log(sum) = log(1 + exp(-|s0 - s1|))."""
+    q = np.array([[1.5], [-0.5]], np.float32)
+    k = np.array([[2.0], [-1.0]], np.float32)
+    v = np.array([[3.0], [-7.0]], np.float32)
+    scale = 0.75
+    out, lse = _fwd(orc, q, k, v, 1, 1, 1, CROSS, 2, scale=scale)
+    for i in range(2):
+        s0 = scale * float(q[i, 0]) * 2.0
+        s1 = scale * float(q[i, 0]) * -1.0
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        _close(out[i, 0], w0 * 3.0 + (1.0 - w0) * -7.0, 1e-12, "logistic out")
+        _close(lse[i, 0, 0], max(s0, s1), 1e-12, "max")
+        _close(lse[i, 0, 1], math.log1p(math.exp(-abs(s0 - s1))), 1e-12, "softplus")
+
+
+def pin_zero_scale_is_uniform(orc):
+    """scale = 0: uniform weights over each row's own window."""
+    H, Hkv, d, n, sp = 2, 1, 4, 4, 3
+    q = _rand((n, H * d), 12)
+    k, v = _rand((sp + n, Hkv * d), 13), _rand((sp + n, Hkv * d), 14)
+    out, lse = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, sp + n, start_pos=sp, scale=0.0)
+    for i in range(n):
+        w = sp + i + 1
+        for h in range(H):
+            _close(out[i, h * d:(h + 1) * d], v[:w].astype(np.float64).mean(0), 1e-12,
+                   "uniform")
+            _close(lse[i, h, 1], math.log(w), 1e-12, "log w")
+
+
+def pin_empty_window_sentinel(orc):
+    """Cross attention over zero keys: the shaders' safe sum gives out = 0, and
+    the side output keeps the -1e30 start max and writes -1e30 for log(0)."""
+    H, Hkv, d = 2, 1, 4
+    q = _rand((3, H * d), 15)
+    k = np.zeros((0, Hkv * d), np.float32)
+    v = np.zeros((0, Hkv * d), np.float32)
+    out, lse = _fwd(orc, q, k, v, H, Hkv, d, CROSS, 0)
+    _close(out, np.zeros((3, H * d)), 0.0, "empty out")
+    _close(lse, np.full((3, H, 2), SENT), 0.0, "empty lse")
+
+
+# ------------------------------------------------------------- brute force
+
+def _window(mode, i, q_seq, kv_len, start_pos):
+    if mode == CAUSAL:
+        return min(start_pos + i + 1, kv_len)
+    return q_seq if mode == FULL else kv_len
+
+
+def _brute(q, k, v, H, Hkv, d, mode, kv_len, start_pos, scale):
+    """Scalar loops with math.fsum: the definition, one number at a time."""
+    n = q.shape[0]
+    g = H // Hkv
+    out = [[0.0] * (H * d) for _ in range(n)]
+    lse = [[[SENT, SENT] for _ in range(H)] for _ in range(n)]
+    for i in range(n):
+        w = _window(mode, i, n, kv_len, start_pos)
+        for h in range(H):
+            c = h // g
+            if w == 0:
+                continue
+            s = [scale * math.fsum(float(q[i][h * d + t]) * float(k[j][c * d + t])
+                                   for t in range(d)) for j in range(w)]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = math.fsum(e)
+            for t in range(d):
+                out[i][h * d + t] = math.fsum(e[j] * float(v[j][c * d + t])
+                                              for j in range(w)) / z
+            lse[i][h] = [m, math.log(z)]
+    return np.array(out), np.array(lse)
+
+
+def pin_brute_force_tiny(orc):
+    """Every mode, start_pos in {0, 2}, GQA groups 1/2/4, d up to 4."""
+    seed = 100
+    for mode in (CAUSAL, FULL, CROSS):
+        for (H, Hkv) in ((1, 1), (2, 1), (4, 2), (4, 1)):
+            for d in (1, 3, 4):
+                for sp in ((0, 2) if mode == CAUSAL else (0,)):
+                    n = 5
+                    kv = n if mode == FULL else (sp + n if mode == CAUSAL else 7)
+                    seed += 1
+                    q = _rand((n, H * d), seed)
+                    k = _rand((kv, Hkv * d), seed + 1000)
+                    v = _rand((kv, Hkv * d), seed + 2000)
+                    scale = 0.6
+                    bo, bl = _brute(q, k, v, H, Hkv, d, mode, kv, sp, scale)
+                    oo, ol = _fwd(orc, q, k, v, H, Hkv, d, mode, kv, sp, scale)
+                    tag = f"mode={mode} H={H} Hkv={Hkv} d={d} sp={sp}"
+                    _close(oo, bo, 1e-12, "brute out " + tag)
+                    _close(ol, bl, 1e-12, "brute lse " + tag)
+
+
+def pin_page_online_update(orc):
+    """The pages' per-score online update (running max, running sum rescaled
+    by exp(old max - new max), accumulator rescaled the same way), run
+    sequentially in float64 with a -1e30 start max, reaches the checker's
+    (out, max, log sum) for every row, including heavy-tailed scores."""
+    H, Hkv, d, n, sp = 4, 2, 8, 6, 5
+    q = _rand((n, H * d), 20)
+    k = _rand((sp + n, Hkv * d), 21)
+    k[[1, 7]] *= 8.0  # a few heavy keys force rescaling
+    v = _rand((sp + n, Hkv * d), 22)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, sp + n, sp, scale)
+    for i in range(n):
+        w = sp + i + 1
+        for h in range(H):
+            c = h // (H // Hkv)
+            mx, sm = -1e30, 0.0
+            acc = np.zeros(d)
+            for t in range(w):
+                s = scale * float(np.dot(q[i, h * d:(h + 1) * d].astype(np.float64),
+                                         k[t, c * d:(c + 1) * d].astype(np.float64)))
+                nm = max(mx, s)
+                corr = math.exp(mx - nm)
+                wt = math.exp(s - nm)
+                sm = sm * corr + wt
+                acc = acc * corr + wt * v[t, c * d:(c + 1) * d].astype(np.float64)
+                mx = nm
+            _close(out[i, h * d:(h + 1) * d], acc / sm, 1e-12, "online out")
+            _close(lse[i, h, 0], mx, 1e-12, "online max")
+            _close(lse[i, h, 1], math.log(sm), 1e-12, "online log sum")
+
+
+# ---------------------------------------------------------- library routines
+
+def pin_matches_torch_sdpa(orc):
+    """torch's CPU scaled_dot_product_attention in float64 with GQA and an
+    explicit boolean window mask (causal with start_pos, full, cross)."""
+    import torch
+    import torch.nn.functional as F
+    cases = [(CAUSAL, 9, 9, 0), (CAUSAL, 7, 12, 5), (FULL, 10, 10, 0), (CROSS, 6, 13, 0)]
+    for idx, (mode, n, kv, sp) in enumerate(cases):
+        H, Hkv, d = 8, 2, 16
+        q = _rand((n, H * d), 30 + idx)
+        k = _rand((kv, Hkv * d), 40 + idx)
+        v = _rand((kv, Hkv * d), 50 + idx)
+        scale = 1.0 / math.sqrt(d)
+        out, lse = _fwd(orc, q, k, v, H, Hkv, d, mode, kv, sp, scale)
+        qt = torch.from_numpy(q.astype(np.float64)).view(n, H, d).transpose(0, 1)[None]
+        kt = torch.from_numpy(k.astype(np.float64)).view(kv, Hkv, d).transpose(0, 1)[None]
+        vt = torch.from_numpy(v.astype(np.float64)).view(kv, Hkv, d).transpose(0, 1)[None]
+        mask = torch.zeros(n, kv, dtype=torch.bool)
+        for i in range(n):
+            mask[i, :_window(mode, i, n, kv, sp)] = True
+        ref = F.scaled_dot_product_attention(qt.contiguous(), kt.contiguous(),
+                                             vt.contiguous(), attn_mask=mask,
+                                             scale=scale, enable_gqa=True)
+        ref = ref[0].transpose(0, 1).reshape(n, H * d).numpy()
+        _close(out, ref, 1e-12, f"sdpa mode={mode}")
+        # m + log sum is the full log-sum-exp of the window's scores
+        kr = torch.repeat_interleave(kt[0], H // Hkv, dim=0)
+        s = scale * torch.matmul(qt[0], kr.transpose(1, 2).contiguous())
+        s = s.masked_fill(~mask[None], float("-inf"))
+        ref_lse = torch.logsumexp(s, dim=-1).transpose(0, 1).numpy()
+        _close(lse[..., 0] + lse[..., 1], ref_lse, 1e-11, f"logsumexp mode={mode}")
+
+
+def pin_logsumexp_scipy(orc):
+    """m + log(sum) equals scipy's logsumexp over brute-force scores."""
+    from scipy.special import logsumexp
+    H, Hkv, d, n = 2, 2, 5, 4
+    q, k = _rand((n, H * d), 60, 3.0), _rand((9, Hkv * d), 61, 3.0)
+    v = _rand((9, Hkv * d), 62)
+    _, lse = _fwd(orc, q, k, v, H, Hkv, d, CROSS, 9, scale=0.9)
+    for i in range(n):
+        for h in range(H):
+            s = [0.9 * math.fsum(float(q[i, h * d + t]) * float(k[j, h * d + t])
+                                 for t in range(d)) for j in range(9)]
+            _close(lse[i, h, 0], max(s), 1e-12, "max")
+            _close(lse[i, h, 0] + lse[i, h, 1], logsumexp(s), 1e-11, "lse")
+
+
+# -------------------------------------------------------------- invariants
+
+def pin_gqa_equals_repeated_heads(orc):
+    """GQA with group g equals MHA on K/V whose heads are repeated g times."""
+    H, Hkv, d, n = 8, 2, 4, 6
+    q, k, v = _rand((n, H * d), 70), _rand((n, Hkv * d), 71), _rand((n, Hkv * d), 72)
+    g = H // Hkv
+    kr = np.repeat(k.reshape(n, Hkv, d), g, axis=1).reshape(n, H * d)
+    vr = np.repeat(v.reshape(n, Hkv, d), g, axis=1).reshape(n, H * d)
+    a = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, n)
+    b = _fwd(orc, q, kr, vr, H, H, d, CAUSAL, n)
+    _close(a[0], b[0], 1e-12, "gqa out")
+    _close(a[1], b[1], 1e-12, "gqa lse")
+
+
+def pin_linear_in_v(orc):
+    """Weights sum to one: out(alpha*V + beta) = alpha*out(V) + beta."""
+    H, Hkv, d, n = 2, 1, 4, 5
+    q, k, v = _rand((n, H * d), 73), _rand((n, Hkv * d), 74), _rand((n, Hkv * d), 75)
+    o1, _ = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, n)
+    o2, _ = _fwd(orc, q, k, (2.5 * v.astype(np.float64) - 1.25), H, Hkv, d, CAUSAL, n)
+    _close(o2, 2.5 * o1 - 1.25, 1e-12, "linearity")
+
+
+def pin_kv_permutation_invariance(orc):
+    """Full/cross attention is a set function of the (K, V) rows."""
+    H, Hkv, d, n, kv = 2, 1, 4, 4, 8
+    q, k, v = _rand((n, H * d), 76), _rand((kv, Hkv * d), 77), _rand((kv, Hkv * d), 78)
+    perm = np.random.default_rng(79).permutation(kv)
+    a = _fwd(orc, q, k, v, H, Hkv, d, CROSS, kv)
+    b = _fwd(orc, q, k[perm], v[perm], H, Hkv, d, CROSS, kv)
+    _close(a[0], b[0], 1e-12, "perm out")
+    _close(a[1], b[1], 1e-12, "perm lse")
+
+
+def pin_cache_continuation(orc):
+    """Rows [s, s+n) of a whole causal pass equal a pass that starts at s."""
+    H, Hkv, d, total, s = 4, 2, 4, 11, 6
+    q, k, v = _rand((total, H * d), 80), _rand((total, Hkv * d), 81), _rand((total, Hkv * d), 82)
+    a = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, total)
+    b = _fwd(orc, q[s:], k, v, H, Hkv, d, CAUSAL, total, start_pos=s)
+    _close(a[0][s:], b[0], 1e-12, "continuation out")
+    _close(a[1][s:], b[1], 1e-12, "continuation lse")
+
+
+def pin_decode_is_prefill_row(orc):
+    """Decode at kv_pos p equals one causal row at start_pos p; the window is
+    clamped to the cache length."""
+    H, Hkv, d, max_seq = 4, 2, 8, 10
+    q = _rand((1, H * d), 83)
+    k, v = _rand((max_seq, Hkv * d), 84), _rand((max_seq, Hkv * d), 85)
+    scale = 1.0 / math.sqrt(d)
+    for p in (0, 3, 9, 15):
+        kv_len = min(p + 1, max_seq)
+        a = orc.decode_forward(q, k, v, kv_pos=p, num_heads=H, num_kv_heads=Hkv,
+                               head_dim=d, max_seq=max_seq, scale=scale)
+        b = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, kv_len, start_pos=min(p, kv_len - 1))
+        _close(a[0], b[0], 1e-12, f"decode out p={p}")
+        _close(a[1], b[1], 1e-12, f"decode lse p={p}")
+        bo, bl = _brute(q, k, v, H, Hkv, d, CROSS, kv_len, 0, scale)
+        _close(a[0], bo, 1e-12, f"decode brute p={p}")
+        _close(a[1], bl, 1e-12, f"decode brute lse p={p}")
+
+
+def pin_row_subset(orc):
+    """Computing a subset of rows gives those rows of the whole pass."""
+    H, Hkv, d, n = 2, 1, 4, 9
+    q, k, v = _rand((n, H * d), 86), _rand((n, Hkv * d), 87), _rand((n, Hkv * d), 88)
+    a = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, n)
+    rows = np.array([8, 0, 3])
+    b = _fwd(orc, q, k, v, H, Hkv, d, CAUSAL, n, rows=rows)
+    _close(a[0][rows], b[0], 0.0, "subset out")
+    _close(a[1][rows], b[1], 0.0, "subset lse")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,52 @@
+"""Plausible mistakes planted in copies of the float64 checker (on the CPU)
+must each be caught by at least one pin; the real checker is untouched."""
+
+import os
+import types
+
+import pytest
+
+from tests.oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "attention.py")
+
+MUTANTS = {
+    "gqa_modulo_map": ("kvh = h // group", "kvh = h % num_kv_heads"),
+    "causal_off_by_one": ("min(start_pos + i + 1, kv_len)", "min(start_pos + i, kv_len)"),
+    "start_pos_ignored": ("min(start_pos + i + 1, kv_len)", "min(i + 1, kv_len)"),
+    "scale_dropped": ("s = scale * (qb @ kb.T)", "s = (qb @ kb.T)"),
+    "scale_inverted": ("s = scale * (qb @ kb.T)", "s = (qb @ kb.T) / scale if scale else qb @ kb.T"),
+    "wrong_value_operand": ("o = (e @ vb)", "o = (e @ kb)"),
+    "max_sign_flip": ("np.exp(s - m_safe[:, None])", "np.exp(s + m_safe[:, None])"),
+    "full_lse_not_pair": ("np.where(nonempty, np.log(z_safe), EMPTY_SENTINEL)",
+                          "np.where(nonempty, np.log(z_safe) + m_safe, EMPTY_SENTINEL)"),
+    "no_normalisation": ("o = (e @ vb) / z_safe[:, None]", "o = (e @ vb)"),
+    "mask_inclusive": ("np.arange(wmax)[None, :] < w[:, None]",
+                       "np.arange(wmax)[None, :] <= w[:, None] - 2"),
+    "empty_sentinel_zero": ("EMPTY_SENTINEL = -1e30", "EMPTY_SENTINEL = 0.0"),
+    "decode_window_short": ("min(int(kv_pos) + 1, max_seq)", "min(int(kv_pos), max_seq)"),
+    "decode_gqa_modulo": ("        kvh = h // group\n        qv", "        kvh = h % num_kv_heads\n        qv"),
+    "decode_no_scale": ("s = scale * (kw @ qv)", "s = (kw @ qv)"),
+    "q_head_offset": ("qh = q[:, h * d:(h + 1) * d]", "qh = q[:, kvh * d:(kvh + 1) * d]"),
+}
+
+
+def _load_mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    mod = _load_mutant(*MUTANTS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as exc:  # an assertion or a crash both count
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin catches mutant {name}"
