@@ -1,0 +1,139 @@
+/*
+ * ta03.h -- C ABI of the MI355X (gfx950) fused attention forward.
+ *
+ *   out = softmax(scale * Q * K^T + mask) * V      (one pass, online softmax)
+ *
+ * with the per-(row, head) side output (max score, log of the sum of
+ * exp(score - max)). The operation and its conventions are those of three
+ * WGSL shaders:
+ *   - meganeura "attention.wgsl": whole-sequence tiled attention. Header
+ *     comment: the causal (window pos+1), full (window q_seq) and cross
+ *     (window kv_seq) variants. main(): GQA map kv_head = head /
+ *     (num_heads / num_kv_heads); running max starts at -1e30; the result is
+ *     divided by a zero-safe sum; the side output stores (max, log(sum)) and
+ *     -1e30 for log(0) "for the backward pass".
+ *   - meganeura "cached_attention.wgsl": one query token over a KV cache; the
+ *     cache position kv_pos is read from a device buffer and the window is
+ *     [0, kv_pos].
+ *   - cera "attention_prefill.wgsl": a batch of queries continuing a cache
+ *     from start_pos; query i attends to [0, start_pos + i]; header
+ *     "Constraints": head_dim <= 128 and the cache must hold start_pos +
+ *     n_queries valid rows, with a defensive clamp of the window to the cache.
+ *
+ * Layouts (all f32, dense, row-major, device memory):
+ *   q, out : [q_seq, num_heads * head_dim]       head h at columns h*head_dim
+ *   k, v   : [rows,  num_kv_heads * head_dim]    rows >= the window's end
+ *   lse    : [q_seq, num_heads, 2]               (max, log sum exp(s - max))
+ * Every tensor pointer must be 16-byte aligned.
+ *
+ * Ownership: the caller owns every buffer, the workspace and the stream. The
+ * library allocates nothing, frees nothing and never synchronises: each call
+ * validates its arguments on the host, enqueues its kernels on `stream` and
+ * returns. Invalid arguments are rejected before any HIP call is made, so
+ * nothing is enqueued on an error return.
+ *
+ * Thread safety: calls are independent; two calls that write the same
+ * buffers (or share one decode workspace) must be ordered by the caller.
+ */
+#ifndef TA03_H
+#define TA03_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Masking variant (meganeura attention.wgsl, header comment). */
+typedef enum {
+    TA03_CAUSAL = 0, /* row i sees keys [0, min(start_pos + i + 1, kv_len)) */
+    TA03_FULL = 1,   /* every row sees [0, kv_len); requires kv_len == q_seq */
+    TA03_CROSS = 2   /* every row sees [0, kv_len); any kv_len >= 0 */
+} ta03_mode;
+
+typedef enum {
+    TA03_OK = 0,
+    TA03_ERR_NULL = -1,        /* a required pointer is NULL */
+    TA03_ERR_SHAPE = -2,       /* inconsistent sizes (see each entry point) */
+    TA03_ERR_UNSUPPORTED = -3, /* head_dim outside {64, 128}, or a size too large */
+    TA03_ERR_WORKSPACE = -4,   /* decode workspace smaller than required */
+    TA03_ERR_HIP = -5,         /* a kernel launch failed (hipGetLastError) */
+    TA03_ERR_ALIGN = -6        /* a pointer is not 16-byte aligned */
+} ta03_status;
+
+/*
+ * attn_fwd -- prefill: whole-sequence causal / full / cross attention
+ * (meganeura attention.wgsl, main) and batched causal prefill continuing a
+ * cache from start_pos (cera attention_prefill.wgsl, main).
+ *
+ *   q        [q_seq, num_heads*head_dim]
+ *   k, v     [>= kv_len, num_kv_heads*head_dim]; only rows [0, kv_len) that
+ *            some row's window covers are read (may be NULL if kv_len == 0)
+ *   out      [q_seq, num_heads*head_dim], written in full
+ *   lse      [q_seq, num_heads, 2] or NULL; lse[i,h] = (m, log Z) with
+ *            m = max_j s_ij and Z = sum_j exp(s_ij - m), both natural-log
+ *            units; an empty window writes out = 0 and lse = (-1e30, -1e30)
+ *   mode     ta03_mode
+ *   start_pos causal offset of row 0 (0 unless mode == TA03_CAUSAL)
+ *   scale    multiplies Q.K^T (the pages use 1/sqrt(head_dim))
+ *
+ * Errors: TA03_ERR_NULL for a NULL q/out (or k/v with kv_len > 0);
+ * TA03_ERR_SHAPE if num_heads, num_kv_heads < 1, num_heads % num_kv_heads,
+ * q_seq, kv_len or start_pos < 0, mode unknown, start_pos != 0 outside
+ * causal mode, causal start_pos + q_seq > kv_len (the pages' host assert), a
+ * full call with kv_len != q_seq, or a non-finite scale;
+ * TA03_ERR_UNSUPPORTED for head_dim not in {64, 128} or q/k/v/out larger
+ * than 2^31 elements; TA03_ERR_ALIGN; TA03_ERR_HIP. q_seq == 0 is a valid
+ * no-op.
+ */
+int attn_fwd(const float* q, const float* k, const float* v, float* out, float* lse,
+             int q_seq, int kv_len, int num_heads, int num_kv_heads, int head_dim,
+             int mode, int start_pos, float scale, hipStream_t stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
+ * for these sizes (split-KV partial results: per query head and split, an
+ * unnormalised output row plus its max and sum). Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int num_heads, int num_kv_heads, int head_dim,
+                                   int max_seq);
+
+/*
+ * attn_decode -- one query token over a KV cache (meganeura
+ * cached_attention.wgsl, main). The window is [0, min(*kv_pos + 1,
+ * max_seq)): kv_pos lives in device memory (a uint32 written by earlier
+ * device work), so a captured launch can be replayed as the cache grows;
+ * the clamp to max_seq is the defensive clamp of cera
+ * attention_prefill.wgsl. Equivalent to attn_fwd(TA03_CAUSAL, q_seq = 1,
+ * start_pos = window - 1, kv_len = window).
+ *
+ *   q          [1, num_heads*head_dim]
+ *   k_cache,
+ *   v_cache    [max_seq, num_kv_heads*head_dim]
+ *   kv_pos     device pointer to one uint32 (4-byte aligned)
+ *   out        [1, num_heads*head_dim]
+ *   lse        [1, num_heads, 2] or NULL (same convention as attn_fwd)
+ *   workspace  device scratch of at least attn_decode_workspace_bytes(...)
+ *              bytes, owned by the caller; contents need no initialisation
+ *              and are left undefined
+ *
+ * Errors: TA03_ERR_NULL, TA03_ERR_SHAPE (num_heads, num_kv_heads, max_seq
+ * < 1, num_heads % num_kv_heads, non-finite scale), TA03_ERR_UNSUPPORTED,
+ * TA03_ERR_WORKSPACE, TA03_ERR_ALIGN, TA03_ERR_HIP.
+ */
+int attn_decode(const float* q, const float* k_cache, const float* v_cache,
+                const uint32_t* kv_pos, float* out, float* lse,
+                int num_heads, int num_kv_heads, int head_dim, int max_seq, float scale,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* attn_strerror -- static description of a ta03_status value. */
+const char* attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TA03_H */

@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/ta03.h declares, and rejects every invalid argument on the host
+(before any HIP call) with the documented status code."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from tiled_attention_03_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ta03.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
+A = 0x10000   # fake 16-byte-aligned addresses: never dereferenced, every call
+B = 0x20000   # below fails validation (or is a no-op) before any HIP call
+C = 0x30000
+O = 0x40000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libta03.so not built")
+    return binding.lib()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["attn_decode", "attn_decode_workspace_bytes",
+                                    "attn_fwd", "attn_strerror"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def fwd(lib, q=A, k=B, v=C, out=O, lse=None, q_seq=4, kv_len=4, H=4, Hkv=2, d=64,
+        mode=0, sp=0, scale=0.125):
+    return lib.attn_fwd(q, k, v, out, lse, q_seq, kv_len, H, Hkv, d, mode, sp, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ERR_NULL),
+    (dict(out=None), ERR_NULL),
+    (dict(k=None), ERR_NULL),
+    (dict(v=None, mode=2, kv_len=3), ERR_NULL),
+    (dict(H=4, Hkv=3), ERR_SHAPE),
+    (dict(H=0), ERR_SHAPE),
+    (dict(Hkv=0), ERR_SHAPE),
+    (dict(q_seq=-1), ERR_SHAPE),
+    (dict(kv_len=-1, mode=2), ERR_SHAPE),
+    (dict(sp=-1), ERR_SHAPE),
+    (dict(mode=3), ERR_SHAPE),
+    (dict(mode=1, kv_len=5), ERR_SHAPE),                 # full needs kv_len == q_seq
+    (dict(mode=2, sp=1, kv_len=9), ERR_SHAPE),           # start_pos only for causal
+    (dict(mode=0, sp=1, kv_len=4), ERR_SHAPE),           # start_pos + q_seq > kv_len
+    (dict(mode=0, q_seq=5, kv_len=4), ERR_SHAPE),
+    (dict(scale=float("nan")), ERR_SHAPE),
+    (dict(scale=float("inf")), ERR_SHAPE),
+    (dict(d=96), ERR_UNSUP),
+    (dict(d=256), ERR_UNSUP),
+    (dict(q_seq=1 << 20, kv_len=1 << 20, H=32, Hkv=8, d=128), ERR_UNSUP),  # > 2^31 elems
+    (dict(q=A + 4), ERR_ALIGN),
+    (dict(lse=O + 8), ERR_ALIGN),
+    (dict(q_seq=0, kv_len=0, q=None, k=None, v=None, out=None), OK),  # empty: no-op
+])
+def test_attn_fwd_rejects_on_host(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def test_validation_order_sizes_before_pointers(lib):
+    # an invalid size is reported even when pointers are also missing
+    assert fwd(lib, q=None, d=96) == ERR_UNSUP
+    assert fwd(lib, q=None, H=3, Hkv=2) == ERR_SHAPE
+
+
+def dec(lib, q=A, k=B, v=C, kv_pos=O, out=O + 0x1000, lse=None, H=32, Hkv=8, d=128,
+        max_seq=8192, scale=0.088, ws=0x90000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_workspace_bytes(H, Hkv, d, max_seq)
+    return lib.attn_decode(q, k, v, kv_pos, out, lse, H, Hkv, d, max_seq, scale, ws,
+                           ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ERR_NULL),
+    (dict(k=None), ERR_NULL),
+    (dict(v=None), ERR_NULL),
+    (dict(kv_pos=None), ERR_NULL),
+    (dict(out=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL),
+    (dict(H=32, Hkv=7, ws_bytes=1 << 30), ERR_SHAPE),
+    (dict(max_seq=0, ws_bytes=1 << 30), ERR_SHAPE),
+    (dict(scale=math.nan), ERR_SHAPE),
+    (dict(d=80, ws_bytes=1 << 30), ERR_UNSUP),
+    (dict(ws_bytes=16), ERR_WS),
+    (dict(kv_pos=O + 2), ERR_ALIGN),  # not 16-byte aligned
+])
+def test_attn_decode_rejects_on_host(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_workspace_bytes(lib):
+    f = lib.attn_decode_workspace_bytes
+    n = f(32, 8, 128, 8192)
+    assert n > 0 and n % 16 == 0 or n % 4 == 0
+    # per head and split: a head_dim row plus (max, sum), in float32
+    assert n % (32 * (128 + 2) * 4) == 0
+    assert f(32, 8, 128, 1) == 32 * 130 * 4          # one split for a one-row cache
+    assert f(32, 7, 128, 8192) == 0
+    assert f(32, 8, 96, 8192) == 0
+    assert f(32, 8, 128, 0) == 0
+    assert dec(lib, ws_bytes=n - 4) == ERR_WS
+
+
+def test_strerror_covers_every_status(lib):
+    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_ALIGN):
+        msg = binding.attn_strerror(st)
+        assert msg and msg != "unknown status"
+    assert binding.attn_strerror(12345) == "unknown status"
+
+
+def test_binding_checks_buffer_sizes():
+    torch = pytest.importorskip("torch")
+    # CPU tensors are refused before the library is called
+    q = torch.zeros(4, 256)
+    with pytest.raises(ValueError):
+        binding.attn_fwd(q, q, q, q, None, 4, 4, 4, 2, 64, 0, 0, 0.125, stream=0)

@@ -1,0 +1,131 @@
+"""Decode parity: split-KV decode through the C ABI against the float64
+checker, at the cache shapes of the pages' workload and on ragged caches."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import check_lse, check_out, device, gpu_prefill, log, to_dev
+from tiled_attention_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_decode(q, k, v, kv_pos, *, num_heads, num_kv_heads, head_dim, max_seq, scale,
+               with_lse=True, k_dev=None, v_dev=None, poison_outputs=True):
+    import torch
+    import tiled_attention_03_amd as ta
+    dev = device()
+    kd = to_dev(k) if k_dev is None else k_dev
+    vd = to_dev(v) if v_dev is None else v_dev
+    fill = float("nan") if poison_outputs else 0.0
+    out = torch.full((1, num_heads * head_dim), fill, device=dev)
+    lse = torch.full((1, num_heads, 2), fill, device=dev) if with_lse else None
+    pos = torch.tensor([kv_pos], dtype=torch.int32, device=dev)
+    nbytes = ta.attn_decode_workspace_bytes(num_heads, num_kv_heads, head_dim, max_seq)
+    ws = torch.full((nbytes // 4,), float("nan"), device=dev)
+    ta.attn_decode(to_dev(q), kd, vd, pos, out, lse, num_heads, num_kv_heads, head_dim,
+                   max_seq, scale, ws, nbytes)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (lse.cpu().numpy() if lse is not None else None)
+
+
+def ref_decode(q, k, v, kv_pos, *, num_heads, num_kv_heads, head_dim, max_seq, scale):
+    return oracle.decode_forward(q, k, v, kv_pos=kv_pos, num_heads=num_heads,
+                                 num_kv_heads=num_kv_heads, head_dim=head_dim,
+                                 max_seq=max_seq, scale=scale)
+
+
+@pytest.fixture(scope="module")
+def decode_8k():
+    w = inputs.DECODE_8K
+    q, k, v = inputs.make_decode(w)
+    return w, q, k, v, to_dev(k), to_dev(v)
+
+
+@pytest.mark.parametrize("kv_pos", inputs.DECODE_8K.kv_pos_values)
+def test_decode_pages_workload(decode_8k, kv_pos):
+    w, q, k, v, kd, vd = decode_8k
+    log(f"decode parity {w.name} kv_pos={kv_pos}")
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              max_seq=w.max_seq, scale=w.scale)
+    go, gl = gpu_decode(q, k, v, kv_pos, k_dev=kd, v_dev=vd, **kw)
+    ro, rl = ref_decode(q, k, v, kv_pos, **kw)
+    e_o = check_out(go, ro, f"decode kv_pos={kv_pos}")
+    e_l = check_lse(gl, rl, f"decode lse kv_pos={kv_pos}")
+    log(f"  max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
+
+
+def test_decode_position_past_cache_is_clamped(decode_8k):
+    w, q, k, v, kd, vd = decode_8k
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              max_seq=w.max_seq, scale=w.scale)
+    go, gl = gpu_decode(q, k, v, 20000, k_dev=kd, v_dev=vd, **kw)
+    ro, rl = ref_decode(q, k, v, w.max_seq - 1, **kw)
+    check_out(go, ro, "clamped")
+    check_lse(gl, rl, "clamped lse")
+
+
+DEC_SWEEP = [
+    # H, Hkv, d, max_seq, kv_pos
+    (1, 1, 64, 1, 0),
+    (2, 1, 64, 70, 69),
+    (4, 4, 128, 100, 37),
+    (8, 2, 128, 513, 512),
+    (12, 4, 64, 1000, 999),
+    (16, 2, 128, 300, 64),      # group 8: two head blocks per KV head
+    (32, 8, 128, 4096, 1),
+    (6, 3, 128, 2049, 2000),
+    (8, 8, 64, 9000, 8999),
+]
+
+
+@pytest.mark.parametrize("case", DEC_SWEEP, ids=[f"h{c[0]}x{c[1]}_d{c[2]}_max{c[3]}_pos{c[4]}"
+                                                 for c in DEC_SWEEP])
+def test_decode_ragged_sweep(case):
+    H, Hkv, d, max_seq, pos = case
+    log(f"decode sweep {case}")
+    seed = 900 + DEC_SWEEP.index(case)
+    q = inputs.normal((1, H * d), seed * 10 + 1)
+    k = inputs.normal((max_seq, Hkv * d), seed * 10 + 2)
+    v = inputs.normal((max_seq, Hkv * d), seed * 10 + 3)
+    # rows past the window are poison: they must never be read
+    k[pos + 1:] = np.nan
+    v[pos + 1:] = np.nan
+    kw = dict(num_heads=H, num_kv_heads=Hkv, head_dim=d, max_seq=max_seq, scale=d ** -0.5)
+    go, gl = gpu_decode(q, k, v, pos, **kw)
+    ro, rl = ref_decode(q, k, v, pos, **kw)
+    check_out(go, ro, str(case))
+    check_lse(gl, rl, str(case))
+
+
+def test_decode_without_lse(decode_8k):
+    w, q, k, v, kd, vd = decode_8k
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              max_seq=w.max_seq, scale=w.scale)
+    go, gl = gpu_decode(q, k, v, 3000, k_dev=kd, v_dev=vd, with_lse=False, **kw)
+    assert gl is None
+    ro, _ = ref_decode(q, k, v, 3000, **kw)
+    check_out(go, ro, "no lse")
+
+
+def test_decode_equals_prefill_row(decode_8k):
+    """attn_decode at kv_pos p equals attn_fwd(causal, one row, start_pos p)."""
+    w, q, k, v, kd, vd = decode_8k
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim)
+    for p in (0, 511, 5000):
+        do, dl = gpu_decode(q, k, v, p, max_seq=w.max_seq, scale=w.scale, k_dev=kd,
+                            v_dev=vd, **kw)
+        po, pl = gpu_prefill(q, k, v, mode=inputs.CAUSAL, kv_len=p + 1, start_pos=p,
+                             scale=w.scale, k_dev=kd, v_dev=vd, **kw)
+        check_out(do, po.astype(np.float64), f"decode vs prefill p={p}")
+        check_lse(dl, pl.astype(np.float64), f"decode vs prefill lse p={p}")
+
+
+def test_decode_deterministic(decode_8k):
+    w, q, k, v, kd, vd = decode_8k
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              max_seq=w.max_seq, scale=w.scale, k_dev=kd, v_dev=vd)
+    a = gpu_decode(q, k, v, 8191, **kw)
+    b = gpu_decode(q, k, v, 8191, **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -1,0 +1,172 @@
+"""Prefill parity: the HIP path through the C ABI against the float64 checker
+on the same seeded inputs, element by element."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import (check_lse, check_out, device, gpu_prefill, log,
+                            oracle_prefill, to_dev)
+from tiled_attention_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+CAUSAL, FULL, CROSS = inputs.CAUSAL, inputs.FULL, inputs.CROSS
+
+
+def _run_both(w, q, k, v, rows=None, with_lse=True):
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              mode=w.mode, kv_len=w.kv_len, start_pos=w.start_pos, scale=w.scale)
+    got_o, got_l = gpu_prefill(q, k, v, with_lse=with_lse, **kw)
+    ref_o, ref_l = oracle_prefill(q, k, v, rows=rows, **kw)
+    if rows is not None:
+        got_o = got_o[rows]
+        got_l = got_l[rows] if got_l is not None else None
+    return got_o, got_l, ref_o, ref_l
+
+
+@pytest.mark.parametrize("w", [inputs.CAUSAL_SMALL, inputs.FULL_1K, inputs.CROSS_512x2K,
+                               inputs.CONTINUE_512], ids=lambda w: w.name)
+def test_pages_workloads_full_parity(w):
+    log(f"prefill parity {w.name}")
+    q, k, v = inputs.make_prefill(w)
+    go, gl, ro, rl = _run_both(w, q, k, v)
+    e_o = check_out(go, ro, w.name)
+    e_l = check_lse(gl, rl, w.name)
+    log(f"  max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
+
+
+def test_long_causal_sampled_rows():
+    """16384-row causal pass with heavy K rows: sampled rows against the
+    checker, in the launch configuration the benchmark times."""
+    w = inputs.CAUSAL_16K
+    log(f"prefill parity (sampled rows) {w.name}")
+    q, k, v = inputs.make_prefill(w)
+    rng = np.random.default_rng(5099)
+    rows = np.unique(np.concatenate([
+        [0, 1, 2, 31, 32, 33, 127, 128, 4095, 8191, 8192, 16351, 16352, 16383],
+        rng.choice(w.q_seq, 18, replace=False)]))
+    go, gl, ro, rl = _run_both(w, q, k, v, rows=rows)
+    e_o = check_out(go, ro, w.name)
+    e_l = check_lse(gl, rl, w.name)
+    log(f"  rows={len(rows)} max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
+
+
+def test_golden_small_causal():
+    """The stored checker values for the small causal GQA workload."""
+    from tests.test_golden import load_golden
+    doc, out_g, lse_g = load_golden()
+    w = inputs.CAUSAL_SMALL
+    q, k, v = inputs.make_prefill(w)
+    go, gl = gpu_prefill(q, k, v, num_heads=w.num_heads, num_kv_heads=w.num_kv_heads,
+                         head_dim=w.head_dim, mode=w.mode, kv_len=w.kv_len, scale=w.scale)
+    check_out(go[doc["out_rows"]], out_g, "golden out")
+    check_lse(gl, lse_g, "golden lse")
+
+
+SWEEP = [
+    # mode, q_seq, kv_len, H, Hkv, d, start_pos
+    (CAUSAL, 1, 1, 1, 1, 64, 0),
+    (CAUSAL, 5, 5, 2, 1, 64, 0),
+    (CAUSAL, 33, 33, 4, 4, 64, 0),
+    (CAUSAL, 70, 70, 8, 2, 128, 0),
+    (CAUSAL, 129, 129, 6, 3, 128, 0),
+    (CAUSAL, 31, 100, 4, 1, 128, 69),
+    (CAUSAL, 65, 300, 8, 1, 64, 200),
+    (CAUSAL, 40, 97, 16, 2, 128, 57),    # group 8: two head blocks per KV head
+    (CAUSAL, 3, 1000, 4, 2, 128, 997),
+    (FULL, 1, 1, 2, 2, 128, 0),
+    (FULL, 47, 47, 4, 2, 64, 0),
+    (FULL, 96, 96, 3, 1, 128, 0),
+    (CROSS, 7, 1, 4, 2, 64, 0),
+    (CROSS, 33, 31, 2, 2, 128, 0),
+    (CROSS, 64, 257, 4, 4, 128, 0),
+    (CROSS, 100, 45, 12, 4, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"m{c[0]}_q{c[1]}_kv{c[2]}_h{c[3]}x{c[4]}_d{c[5]}_sp{c[6]}"
+                                             for c in SWEEP])
+def test_ragged_sweep(case):
+    mode, n, kv, H, Hkv, d, sp = case
+    log(f"prefill sweep {case}")
+    w, q, k, v = inputs.random_case(700 + SWEEP.index(case), mode, n, kv, H, Hkv, d,
+                                    start_pos=sp)
+    go, gl, ro, rl = _run_both(w, q, k, v)
+    check_out(go, ro, str(case))
+    check_lse(gl, rl, str(case))
+
+
+def test_empty_query_batch_is_a_noop():
+    import torch
+    dev = device()
+    q = torch.zeros((0, 256), device=dev)
+    out = torch.full((4, 256), 7.0, device=dev)
+    import tiled_attention_03_amd as ta
+    ta.attn_fwd(q, None, None, out, None, 0, 0, 4, 2, 64, CROSS, 0, 0.125)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_cross_over_zero_keys_writes_zeros_and_sentinel():
+    import torch
+    import tiled_attention_03_amd as ta
+    dev = device()
+    n, H, d = 37, 4, 64
+    q = to_dev(inputs.normal((n, H * d), 42))
+    out = torch.full((n, H * d), float("nan"), device=dev)
+    lse = torch.full((n, H, 2), float("nan"), device=dev)
+    ta.attn_fwd(q, None, None, out, lse, n, 0, H, 2, d, CROSS, 0, 0.125)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0.0)
+    assert torch.all(lse == -1e30)
+
+
+def test_poisoned_cache_and_outputs():
+    """Cache rows outside every window hold NaN and must not be read; out and
+    lse start as NaN and must be fully overwritten."""
+    import torch
+    import tiled_attention_03_amd as ta
+    H, Hkv, d, n, sp, rows = 8, 2, 128, 77, 150, 400
+    w, q, k, v = inputs.random_case(801, CAUSAL, n, sp + n, H, Hkv, d, start_pos=sp,
+                                    kv_rows=rows)
+    k[sp + n:] = np.nan
+    v[sp + n:] = np.nan
+    dev = device()
+    out = torch.full((n, H * d), float("nan"), device=dev)
+    lse = torch.full((n, H, 2), float("nan"), device=dev)
+    ta.attn_fwd(to_dev(q), to_dev(k), to_dev(v), out, lse, n, sp + n, H, Hkv, d, CAUSAL, sp,
+                w.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle_prefill(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=CAUSAL,
+                            kv_len=sp + n, start_pos=sp, scale=w.scale)
+    check_out(out.cpu().numpy(), ro, "poison out")
+    check_lse(lse.cpu().numpy(), rl, "poison lse")
+
+
+def test_run_to_run_bitwise_deterministic():
+    w = inputs.CONTINUE_512
+    q, k, v = inputs.make_prefill(w)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              mode=w.mode, kv_len=w.kv_len, start_pos=w.start_pos, scale=w.scale,
+              q_dev=qd, k_dev=kd, v_dev=vd)
+    a = gpu_prefill(q, k, v, **kw)
+    b = gpu_prefill(q, k, v, **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_continuation_matches_whole_pass_rows():
+    """Rows [s, s+n) of a whole causal pass equal a pass starting at s (both
+    on the GPU, within tolerance: different tilings of the same rows)."""
+    H, Hkv, d, total, s = 8, 2, 128, 300, 173
+    w, q, k, v = inputs.random_case(802, CAUSAL, total, total, H, Hkv, d)
+    scale = w.scale
+    a_o, a_l = gpu_prefill(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=CAUSAL,
+                           kv_len=total, scale=scale)
+    b_o, b_l = gpu_prefill(q[s:], k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d,
+                           mode=CAUSAL, kv_len=total, start_pos=s, scale=scale)
+    check_out(b_o, a_o[s:].astype(np.float64), "continuation")
+    check_lse(b_l, a_l[s:].astype(np.float64), "continuation lse")

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) fused attention forward: prefill and single-token decode
+behind a C ABI (include/ta03.h, libta03.so), with a ctypes binding.
+
+The library is loaded lazily on the first call, so importing the package (or
+its input generators) needs no GPU and no built library.
+"""
+
+from .binding import (CAUSAL, CROSS, FULL, Ta03Error, attention, attn_decode,
+                      attn_decode_workspace_bytes, attn_fwd, attn_strerror, lib)
+
+__all__ = ["CAUSAL", "FULL", "CROSS", "Ta03Error", "attention", "attn_fwd",
+           "attn_decode", "attn_decode_workspace_bytes", "attn_strerror", "lib"]

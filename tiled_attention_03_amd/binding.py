@@ -1,0 +1,156 @@
+"""ctypes binding of libta03.so: the C-ABI entry points under the same names.
+
+Argument marshalling only. Tensors are torch CUDA (HIP) float32 tensors, read
+through ``data_ptr()``; the stream defaults to torch's current stream. The
+binding checks that each tensor is on the GPU, float32, contiguous and large
+enough for the sizes passed (the C ABI sees bare pointers and cannot), then
+calls the library, which validates the sizes themselves. There is no other
+implementation behind these names: if the library is missing, every call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libta03.so")
+
+CAUSAL, FULL, CROSS = 0, 1, 2
+STATUS_NAMES = {0: "TA03_OK", -1: "TA03_ERR_NULL", -2: "TA03_ERR_SHAPE",
+                -3: "TA03_ERR_UNSUPPORTED", -4: "TA03_ERR_WORKSPACE",
+                -5: "TA03_ERR_HIP", -6: "TA03_ERR_ALIGN"}
+
+_lib = None
+
+
+class Ta03Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libta03.so (built in-tree by tiled_attention_03_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run "
+                               "`python -m tiled_attention_03_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+        L.attn_fwd.restype = I
+        L.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
+        L.attn_decode_workspace_bytes.restype = S
+        L.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P, S, P]
+        L.attn_decode.restype = I
+        L.attn_strerror.argtypes = [I]
+        L.attn_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def attn_strerror(status: int) -> str:
+    return lib().attn_strerror(int(status)).decode()
+
+
+def _ptr(t, min_numel: int, name: str, *, dtype_name="float32"):
+    """Device pointer of tensor ``t`` (or None -> NULL), after checks."""
+    if t is None:
+        return None
+    if isinstance(t, int):  # a raw device address
+        return t
+    import torch
+    want = {"float32": torch.float32, "int32": torch.int32, "uint32": torch.uint32}[dtype_name]
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != want:
+        raise ValueError(f"{name} must be {dtype_name}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {min_numel}")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != 0:
+        raise Ta03Error(status, attn_strerror(status))
+
+
+def attn_fwd(q, k, v, out, lse, q_seq: int, kv_len: int, num_heads: int,
+             num_kv_heads: int, head_dim: int, mode: int, start_pos: int,
+             scale: float, stream=None) -> None:
+    """Enqueue the prefill attention forward (see include/ta03.h)."""
+    qd, kvd = num_heads * head_dim, num_kv_heads * head_dim
+    kv_rows_needed = kv_len if mode != CAUSAL else min(kv_len, start_pos + q_seq)
+    status = lib().attn_fwd(
+        _ptr(q, q_seq * qd, "q"), _ptr(k, kv_rows_needed * kvd, "k"),
+        _ptr(v, kv_rows_needed * kvd, "v"), _ptr(out, q_seq * qd, "out"),
+        _ptr(lse, q_seq * num_heads * 2, "lse"), q_seq, kv_len, num_heads, num_kv_heads,
+        head_dim, mode, start_pos, float(scale), _stream(stream))
+    _check(status)
+
+
+def attn_decode_workspace_bytes(num_heads: int, num_kv_heads: int, head_dim: int,
+                                max_seq: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(num_heads, num_kv_heads, head_dim, max_seq))
+
+
+def attn_decode(q, k_cache, v_cache, kv_pos, out, lse, num_heads: int, num_kv_heads: int,
+                head_dim: int, max_seq: int, scale: float, workspace,
+                workspace_bytes: int, stream=None) -> None:
+    """Enqueue the single-token decode (see include/ta03.h). ``kv_pos`` is a
+    one-element int32/uint32 GPU tensor; ``workspace`` a GPU tensor of at
+    least ``workspace_bytes`` bytes."""
+    import torch
+    qd, kvd = num_heads * head_dim, num_kv_heads * head_dim
+    if isinstance(kv_pos, torch.Tensor):
+        kvp = _ptr(kv_pos, 1, "kv_pos",
+                   dtype_name="int32" if kv_pos.dtype == torch.int32 else "uint32")
+    else:
+        kvp = kv_pos
+    if isinstance(workspace, torch.Tensor):
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        if workspace.numel() * workspace.element_size() < workspace_bytes:
+            raise ValueError("workspace tensor smaller than workspace_bytes")
+        wsp = workspace.data_ptr()
+    else:
+        wsp = workspace
+    status = lib().attn_decode(
+        _ptr(q, qd, "q"), _ptr(k_cache, max_seq * kvd, "k_cache"),
+        _ptr(v_cache, max_seq * kvd, "v_cache"), kvp, _ptr(out, qd, "out"),
+        _ptr(lse, num_heads * 2, "lse"), num_heads, num_kv_heads, head_dim, max_seq,
+        float(scale), wsp, int(workspace_bytes), _stream(stream))
+    _check(status)
+
+
+def attention(q, k, v, *, num_heads: int, num_kv_heads: int, head_dim: int, mode: int,
+              kv_len: Optional[int] = None, start_pos: int = 0, scale: Optional[float] = None,
+              with_lse: bool = True, stream=None):
+    """Allocate out (and lse) with torch and call attn_fwd; returns (out, lse)."""
+    import torch
+    q_seq = q.shape[0]
+    if kv_len is None:
+        kv_len = k.shape[0]
+    if scale is None:
+        scale = head_dim ** -0.5
+    out = torch.empty((q_seq, num_heads * head_dim), dtype=torch.float32, device=q.device)
+    lse = (torch.empty((q_seq, num_heads, 2), dtype=torch.float32, device=q.device)
+           if with_lse else None)
+    attn_fwd(q, k, v, out, lse, q_seq, kv_len, num_heads, num_kv_heads, head_dim, mode,
+             start_pos, scale, stream)
+    return out, lse

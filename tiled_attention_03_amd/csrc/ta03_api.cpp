@@ -1,0 +1,101 @@
+// C ABI of the attention forward: argument validation, then kernel launch.
+// Every check happens on the host before any HIP call, so an invalid call
+// enqueues nothing and needs no device.
+
+#include <cmath>
+#include <cstdint>
+
+#include "ta03.h"
+#include "ta03_internal.h"
+
+namespace {
+
+constexpr long long kMaxElems = 1ll << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_supported(int d) { return d == 64 || d == 128; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const float* q, const float* k, const float* v, float* out, float* lse,
+             int q_seq, int kv_len, int num_heads, int num_kv_heads, int head_dim,
+             int mode, int start_pos, float scale, hipStream_t stream) {
+    if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0) return TA03_ERR_SHAPE;
+    if (q_seq < 0 || kv_len < 0 || start_pos < 0) return TA03_ERR_SHAPE;
+    if (mode != TA03_CAUSAL && mode != TA03_FULL && mode != TA03_CROSS) return TA03_ERR_SHAPE;
+    if (mode != TA03_CAUSAL && start_pos != 0) return TA03_ERR_SHAPE;
+    if (mode == TA03_CAUSAL && (long long)start_pos + q_seq > kv_len) return TA03_ERR_SHAPE;
+    if (mode == TA03_FULL && kv_len != q_seq) return TA03_ERR_SHAPE;
+    if (!std::isfinite(scale)) return TA03_ERR_SHAPE;
+    if (!head_dim_supported(head_dim)) return TA03_ERR_UNSUPPORTED;
+    if ((long long)q_seq * num_heads * head_dim >= kMaxElems ||
+        (long long)kv_len * num_kv_heads * head_dim >= kMaxElems)
+        return TA03_ERR_UNSUPPORTED;
+    if (q_seq == 0) return TA03_OK;
+    if (q == nullptr || out == nullptr) return TA03_ERR_NULL;
+    if (kv_len > 0 && (k == nullptr || v == nullptr)) return TA03_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k) || !aligned16(v) || !aligned16(lse))
+        return TA03_ERR_ALIGN;
+
+    ta03::PrefillShape s;
+    s.q_seq = q_seq;
+    s.kv_len = kv_len;
+    s.num_heads = num_heads;
+    s.num_kv_heads = num_kv_heads;
+    s.head_dim = head_dim;
+    s.causal = mode == TA03_CAUSAL ? 1 : 0;
+    s.start_pos = start_pos;
+    s.scale = scale;
+    const hipError_t e = ta03::launch_prefill(q, k, v, out, lse, s, stream);
+    return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
+}
+
+size_t attn_decode_workspace_bytes(int num_heads, int num_kv_heads, int head_dim, int max_seq) {
+    if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 || max_seq < 1)
+        return 0;
+    if (!head_dim_supported(head_dim)) return 0;
+    ta03::DecodeShape s{num_heads, num_kv_heads, head_dim, max_seq, 1.0f};
+    return ta03::decode_plan(s).ws_floats * sizeof(float);
+}
+
+int attn_decode(const float* q, const float* k_cache, const float* v_cache,
+                const uint32_t* kv_pos, float* out, float* lse,
+                int num_heads, int num_kv_heads, int head_dim, int max_seq, float scale,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 || max_seq < 1)
+        return TA03_ERR_SHAPE;
+    if (!std::isfinite(scale)) return TA03_ERR_SHAPE;
+    if (!head_dim_supported(head_dim)) return TA03_ERR_UNSUPPORTED;
+    if ((long long)max_seq * num_kv_heads * head_dim >= kMaxElems) return TA03_ERR_UNSUPPORTED;
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || kv_pos == nullptr ||
+        out == nullptr || workspace == nullptr)
+        return TA03_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(lse) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(kv_pos) & 3u) != 0)
+        return TA03_ERR_ALIGN;
+    ta03::DecodeShape s{num_heads, num_kv_heads, head_dim, max_seq, scale};
+    const ta03::DecodePlan p = ta03::decode_plan(s);
+    if (workspace_bytes < p.ws_floats * sizeof(float)) return TA03_ERR_WORKSPACE;
+    const hipError_t e = ta03::launch_decode(q, k_cache, v_cache, kv_pos, out, lse, s, p,
+                                             static_cast<float*>(workspace), stream);
+    return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
+}
+
+const char* attn_strerror(int status) {
+    switch (status) {
+        case TA03_OK: return "ok";
+        case TA03_ERR_NULL: return "a required pointer is NULL";
+        case TA03_ERR_SHAPE: return "inconsistent or invalid sizes";
+        case TA03_ERR_UNSUPPORTED: return "unsupported head_dim or size";
+        case TA03_ERR_WORKSPACE: return "decode workspace too small";
+        case TA03_ERR_HIP: return "HIP kernel launch failed";
+        case TA03_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

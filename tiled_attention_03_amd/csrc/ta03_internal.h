@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI (ta03_api.cpp) and the HIP
+// kernels. Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ta03 {
+
+struct PrefillShape {
+    int q_seq, kv_len, num_heads, num_kv_heads, head_dim;
+    int causal, start_pos;
+    float scale;
+};
+
+struct DecodeShape {
+    int num_heads, num_kv_heads, head_dim, max_seq;
+    float scale;
+};
+
+// Split-KV plan of the decode path; a pure function of the sizes so that the
+// workspace query and the launch agree.
+struct DecodePlan {
+    int group;          // query heads per KV head
+    int heads_per_blk;  // query heads one block serves (<= 4)
+    int blks_per_kv;    // blocks per KV head along the head axis
+    int n_splits;       // splits of the cache axis
+    size_t ws_floats;   // workspace size in floats
+};
+
+DecodePlan decode_plan(const DecodeShape& s);
+
+hipError_t launch_prefill(const float* q, const float* k, const float* v, float* out,
+                          float* lse, const PrefillShape& s, hipStream_t stream);
+
+hipError_t launch_decode(const float* q, const float* k, const float* v,
+                         const uint32_t* kv_pos, float* out, float* lse,
+                         const DecodeShape& s, const DecodePlan& p, float* ws,
+                         hipStream_t stream);
+
+}  // namespace ta03
