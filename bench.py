@@ -1,0 +1,300 @@
+"""Benchmark of the attention forward on one MI355X.
+
+One step is one call of the prefill path on the long causal workload
+(q_seq = kv_len = 16384, 32 query heads over 8 KV heads, head_dim 128, f32,
+with the (max, log-sum) side output). The same JSON line also carries the
+decode path measured on its cache workload (32/8 heads, head_dim 128, cache
+8192 rows) with the KV cache rotated through 8 copies so the 256 MB
+Infinity Cache cannot serve it, and the other prefill workloads as reported
+figures.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--only prefill|decode] [--no-cpu-baseline]
+                    [--copy-calibration]
+
+Timed region: barrier-free at one GPU; torch.cuda.synchronize() on both
+sides, wall clock around exactly K steps. Kernel durations come from HIP
+events recorded on the stream the kernels run on (torch's current stream).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from tiled_attention_03_amd import inputs  # noqa: E402
+
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense f32 matrix peak
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E peak
+METRIC = "prefill attention TFLOP/s and decode KV-read GB/s on 1 MI355X (% roofline)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_causal16k_traffic.md")
+PREFILL_SRC = os.path.join(ROOT, "tiled_attention_03_amd", "csrc", "prefill.hip")
+
+
+# ------------------------------------------------------------ accounting
+
+def window(w, i):
+    if w.mode == inputs.CAUSAL:
+        return min(w.start_pos + i + 1, w.kv_len)
+    return w.kv_len
+
+
+def unmasked_pairs(w, rows=None):
+    rows = range(w.q_seq) if rows is None else rows
+    return sum(window(w, int(i)) for i in rows)
+
+
+def prefill_flops(w, rows=None, heads=None):
+    """Q.K^T plus P.V over unmasked (row, key) pairs only."""
+    heads = w.num_heads if heads is None else heads
+    return 4 * w.head_dim * heads * unmasked_pairs(w, rows)
+
+
+def decode_bytes(w, kv_pos, with_lse=False):
+    """K and V rows [0, kv_len) of one KV layout (each read once, shared by
+    the GQA group) plus Q in and out (and lse)."""
+    kv_len = min(kv_pos + 1, w.max_seq)
+    b = 2 * kv_len * w.num_kv_heads * w.head_dim * 4 + 2 * w.num_heads * w.head_dim * 4
+    if with_lse:
+        b += w.num_heads * 2 * 4
+    return b
+
+
+# ------------------------------------------------------------ GPU timing
+
+def time_calls(fn, n, torch):
+    """Average per-call duration (s) from events around each call, on the
+    current stream, plus the wall time of the n calls."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
+    return float(np.mean(durs)), float(np.min(durs)), wall
+
+
+def bench_prefill(w, steps, warmup, torch, ta):
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.make_prefill(w)
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    del q, k, v
+    qdim = w.num_heads * w.head_dim
+    out = torch.empty((w.q_seq, qdim), device=dev)
+    lse = torch.empty((w.q_seq, w.num_heads, 2), device=dev) if w.with_lse else None
+
+    def call(_i):
+        ta.attn_fwd(qd, kd, vd, out, lse, w.q_seq, w.kv_len, w.num_heads, w.num_kv_heads,
+                    w.head_dim, w.mode, w.start_pos, w.scale)
+
+    for i in range(warmup):
+        call(i)
+    mean_s, min_s, wall = time_calls(call, steps, torch)
+    flops = prefill_flops(w)
+    return {"flops": flops, "mean_s": mean_s, "min_s": min_s, "wall_s": wall,
+            "tflops_kernel": flops / mean_s / 1e12, "tflops_wall": flops * steps / wall / 1e12}
+
+
+def bench_decode(w, kv_pos_values, iters, warmup, torch, ta, copies=8):
+    """Decode timing with the cache rotated over `copies` independent
+    allocations (copies x 64 MiB > the 256 MB Infinity Cache)."""
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.make_decode(w)
+    qd = torch.from_numpy(q).to(dev)
+    k0, v0 = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    caches = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    out = torch.empty((1, w.num_heads * w.head_dim), device=dev)
+    nbytes = ta.attn_decode_workspace_bytes(w.num_heads, w.num_kv_heads, w.head_dim,
+                                            w.max_seq)
+    ws = torch.zeros(max(nbytes // 4, 1), device=dev)  # zero-filled before first use
+    res = {}
+    for kv_pos in kv_pos_values:
+        pos = torch.tensor([kv_pos], dtype=torch.int32, device=dev)
+
+        def call(i):
+            kc, vc = caches[i % copies]
+            ta.attn_decode(qd, kc, vc, pos, out, None, w.num_heads, w.num_kv_heads,
+                           w.head_dim, w.max_seq, w.scale, ws, nbytes)
+
+        for i in range(warmup):
+            call(i)
+        mean_s, min_s, _ = time_calls(call, iters, torch)
+        b = decode_bytes(w, kv_pos)
+        res[str(kv_pos)] = {"us": round(mean_s * 1e6, 2), "us_min": round(min_s * 1e6, 2),
+                            "GB/s": round(b / mean_s / 1e9, 1),
+                            "frac": round(b / mean_s / 1e9 / HBM_PEAK_GBPS, 4)}
+    return res
+
+
+def copy_calibration(torch, mib=1024, reps=3):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 4
+    a = torch.randn(n, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "reps": reps}), flush=True)
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(w, budget_s=10.0, block=256, max_blocks=8):
+    """The float64 checker on the host cores, on the heaviest row blocks of
+    the same workload (all heads), walked from the last row backwards until
+    `budget_s` of CPU work or `max_blocks` blocks."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q, k, v = inputs.make_prefill(w)
+    total_s, flops, done = 0.0, 0, 0
+    hi = w.q_seq
+    while done < max_blocks and hi > 0 and total_s < budget_s:
+        rows = np.arange(max(0, hi - block), hi)
+        t0 = time.perf_counter()
+        oracle.attention_forward(q, k, v, num_heads=w.num_heads, num_kv_heads=w.num_kv_heads,
+                                 head_dim=w.head_dim, mode=w.mode, kv_len=w.kv_len,
+                                 start_pos=w.start_pos, scale=w.scale, rows=rows)
+        total_s += time.perf_counter() - t0
+        flops += prefill_flops(w, rows)
+        hi -= block
+        done += 1
+    return {"value": flops / total_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"rows [{hi}, {w.q_seq}) x {w.num_heads} heads of {w.name}, "
+                      f"float64 numpy, {total_s:.1f} s, {flops / 1e9:.1f} GFLOP",
+            "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+# ------------------------------------------------------------ traffic
+
+def stored_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current prefill kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m_b or not m_h:
+        return None
+    cur = hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if m_h.group(1) == cur else None
+
+
+# ------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reported", action="store_true",
+                    help="skip the smaller prefill workloads")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); multi-GPU runs are not part of this build.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import tiled_attention_03_amd as ta
+    ta.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    w = inputs.CAUSAL_16K
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "f32", "data": "synthetic"}
+
+    if args.only != "decode":
+        print(f"[bench] prefill {w.name}: {args.warmup} warmup + {args.steps} timed",
+              flush=True)
+        p = bench_prefill(w, args.steps, args.warmup, torch, ta)
+        result.update({
+            "value": round(p["tflops_wall"], 3), "unit": "TFLOP/s",
+            "ms_per_step": round(p["wall_s"] / args.steps * 1e3, 3),
+            "config": {"workload": w.name, "mode": "causal", "q_seq": w.q_seq,
+                       "kv_len": w.kv_len, "num_heads": w.num_heads,
+                       "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                       "lse": True, "heavy_k_rows": "1% x8",
+                       "flops_per_step": p["flops"]},
+            "roofline": {"bound": "mfma", "achieved": round(p["tflops_kernel"], 3),
+                         "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(p["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
+                         "traffic": stored_traffic(),
+                         "kernel": "prefill_kernel<128>",
+                         "kernel_ms_mean": round(p["mean_s"] * 1e3, 3),
+                         "kernel_ms_min": round(p["min_s"] * 1e3, 3)},
+        })
+        print(f"[bench] prefill {p['tflops_kernel']:.2f} TFLOP/s "
+              f"({p['mean_s'] * 1e3:.2f} ms/launch)", flush=True)
+        if not args.no_reported:
+            rep = {}
+            for wr in (inputs.FULL_1K, inputs.CROSS_512x2K, inputs.CONTINUE_512):
+                r = bench_prefill(wr, 50, 10, torch, ta)
+                rep[wr.name] = {"us": round(r["mean_s"] * 1e6, 2),
+                                "TFLOP/s": round(r["tflops_kernel"], 3),
+                                "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4)}
+                print(f"[bench] {wr.name}: {rep[wr.name]}", flush=True)
+            result["prefill_reported"] = rep
+
+    if args.only != "prefill":
+        wd = inputs.DECODE_8K
+        print(f"[bench] decode {wd.name}", flush=True)
+        d = bench_decode(wd, wd.kv_pos_values, 200, 20, torch, ta)
+        head = d[str(wd.kv_pos_values[-1])]
+        result["decode"] = {
+            "workload": wd.name, "unit": "GB/s", "kv_pos": d,
+            "roofline": {"bound": "hbm", "achieved": head["GB/s"], "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": head["frac"], "traffic": None,
+                         "kernel": "decode_kernel<128>",
+                         "kv_pos": wd.kv_pos_values[-1]}}
+        print(f"[bench] decode {d}", flush=True)
+        if args.only == "decode":
+            result.update({"value": head["GB/s"], "unit": "GB/s",
+                           "ms_per_step": head["us"] / 1e3,
+                           "config": {"workload": wd.name,
+                                      "kv_pos": wd.kv_pos_values[-1]}})
+
+    if not args.no_cpu_baseline and args.only is None:
+        print("[bench] cpu baseline (float64 checker on host cores)", flush=True)
+        result["cpu_baseline"] = cpu_baseline(w)
+
+    props = torch.cuda.get_device_properties(0)
+    result["device"] = {"name": props.name, "cus": props.multi_processor_count}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -95,11 +95,23 @@ int attn_fwd(const float* q, const float* k, const float* v, float* out, float* 
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
- * for these sizes (split-KV partial results: per query head and split, an
- * unnormalised output row plus its max and sum). Returns 0 for invalid sizes.
+ * for these sizes: split-KV partial results (per query head and split, an
+ * unnormalised output row plus its max and sum) and one completion counter
+ * per (kv head, head block). Returns 0 for invalid sizes.
  */
 size_t attn_decode_workspace_bytes(int num_heads, int num_kv_heads, int head_dim,
                                    int max_seq);
+
+/*
+ * attn_decode_workspace_init -- enqueue on `stream` the zero fill of the
+ * completion counters of a decode workspace (one small kernel; no memset
+ * node, so it may be captured in a graph). Same size arguments as
+ * attn_decode_workspace_bytes. Errors: TA03_ERR_SHAPE, TA03_ERR_UNSUPPORTED,
+ * TA03_ERR_NULL, TA03_ERR_ALIGN, TA03_ERR_WORKSPACE, TA03_ERR_HIP.
+ */
+int attn_decode_workspace_init(void* workspace, size_t workspace_bytes, int num_heads,
+                               int num_kv_heads, int head_dim, int max_seq,
+                               hipStream_t stream);
 
 /*
  * attn_decode -- one query token over a KV cache (meganeura
@@ -117,8 +129,13 @@ size_t attn_decode_workspace_bytes(int num_heads, int num_kv_heads, int head_dim
  *   out        [1, num_heads*head_dim]
  *   lse        [1, num_heads, 2] or NULL (same convention as attn_fwd)
  *   workspace  device scratch of at least attn_decode_workspace_bytes(...)
- *              bytes, owned by the caller; contents need no initialisation
- *              and are left undefined
+ *              bytes, owned by the caller. It holds the split partials and
+ *              one completion counter per (kv head, head block); it must be
+ *              zero-filled before its first use (attn_decode_workspace_init,
+ *              or any zero fill). Every call leaves the counters at zero, so
+ *              a workspace is reused, or a captured call replayed, without
+ *              re-initialisation. Calls sharing a workspace must be ordered
+ *              on one stream.
  *
  * Errors: TA03_ERR_NULL, TA03_ERR_SHAPE (num_heads, num_kv_heads, max_seq
  * < 1, num_heads % num_kv_heads, non-finite scale), TA03_ERR_UNSUPPORTED,

@@ -37,7 +37,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_decode", "attn_decode_workspace_bytes",
-                                    "attn_fwd", "attn_strerror"]
+                                    "attn_decode_workspace_init", "attn_fwd",
+                                    "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -115,14 +116,26 @@ def test_attn_decode_rejects_on_host(lib, kw, status):
 def test_workspace_bytes(lib):
     f = lib.attn_decode_workspace_bytes
     n = f(32, 8, 128, 8192)
-    assert n > 0 and n % 16 == 0 or n % 4 == 0
-    # per head and split: a head_dim row plus (max, sum), in float32
-    assert n % (32 * (128 + 2) * 4) == 0
-    assert f(32, 8, 128, 1) == 32 * 130 * 4          # one split for a one-row cache
+    assert n > 0 and n % 16 == 0
+    # one split for a one-row cache: per head a head_dim row plus (max, sum),
+    # then one 4-byte counter per KV head, padded to 16 bytes
+    assert f(32, 8, 128, 1) == 32 * 130 * 4 + 32
     assert f(32, 7, 128, 8192) == 0
     assert f(32, 8, 96, 8192) == 0
     assert f(32, 8, 128, 0) == 0
     assert dec(lib, ws_bytes=n - 4) == ERR_WS
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1 << 20, 32, 8, 128, 8192), ERR_NULL),
+    ((A + 4, 1 << 20, 32, 8, 128, 8192), ERR_ALIGN),
+    ((A, 16, 32, 8, 128, 8192), ERR_WS),
+    ((A, 1 << 20, 32, 7, 128, 8192), ERR_SHAPE),
+    ((A, 1 << 20, 32, 8, 128, 0), ERR_SHAPE),
+    ((A, 1 << 20, 32, 8, 100, 8192), ERR_UNSUP),
+])
+def test_workspace_init_rejects_on_host(lib, args, status):
+    assert lib.attn_decode_workspace_init(*args, None) == status
 
 
 def test_strerror_covers_every_status(lib):

@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 
 
 def gpu_decode(q, k, v, kv_pos, *, num_heads, num_kv_heads, head_dim, max_seq, scale,
-               with_lse=True, k_dev=None, v_dev=None, poison_outputs=True):
+               with_lse=True, k_dev=None, v_dev=None, poison_outputs=True, ws=None):
     import torch
     import tiled_attention_03_amd as ta
     dev = device()
@@ -23,7 +23,10 @@ def gpu_decode(q, k, v, kv_pos, *, num_heads, num_kv_heads, head_dim, max_seq, s
     lse = torch.full((1, num_heads, 2), fill, device=dev) if with_lse else None
     pos = torch.tensor([kv_pos], dtype=torch.int32, device=dev)
     nbytes = ta.attn_decode_workspace_bytes(num_heads, num_kv_heads, head_dim, max_seq)
-    ws = torch.full((nbytes // 4,), float("nan"), device=dev)
+    if ws is None:
+        # garbage everywhere, then the documented initialisation of the counters
+        ws = torch.full((nbytes // 4,), float("nan"), device=dev)
+        ta.attn_decode_workspace_init(ws, nbytes, num_heads, num_kv_heads, head_dim, max_seq)
     ta.attn_decode(to_dev(q), kd, vd, pos, out, lse, num_heads, num_kv_heads, head_dim,
                    max_seq, scale, ws, nbytes)
     torch.cuda.synchronize()
@@ -129,3 +132,22 @@ def test_decode_deterministic(decode_8k):
     a = gpu_decode(q, k, v, 8191, **kw)
     b = gpu_decode(q, k, v, 8191, **kw)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_workspace_reused_across_calls(decode_8k):
+    """One workspace, many calls with changing kv_pos: the completion counters
+    return to zero after every call, so each result is complete."""
+    import torch
+    import tiled_attention_03_amd as ta
+    w, q, k, v, kd, vd = decode_8k
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              max_seq=w.max_seq, scale=w.scale)
+    nbytes = ta.attn_decode_workspace_bytes(w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq)
+    ws = torch.zeros(nbytes // 4, device=device())
+    for p in (8191, 5, 700, 8191, 64, 63, 4096):
+        go, gl = gpu_decode(q, k, v, p, k_dev=kd, v_dev=vd, ws=ws, **kw)
+        ro, rl = ref_decode(q, k, v, p, **kw)
+        check_out(go, ro, f"reuse p={p}")
+        check_lse(gl, rl, f"reuse lse p={p}")
+    counters = ws[-(w.num_kv_heads):].view(torch.int32).cpu().numpy()
+    assert np.all(counters == 0)

@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd.restype = I
         L.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
         L.attn_decode_workspace_bytes.restype = S
+        L.attn_decode_workspace_init.argtypes = [P, S, I, I, I, I, P]
+        L.attn_decode_workspace_init.restype = I
         L.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P, S, P]
         L.attn_decode.restype = I
         L.attn_strerror.argtypes = [I]
@@ -109,12 +111,32 @@ def attn_decode_workspace_bytes(num_heads: int, num_kv_heads: int, head_dim: int
     return int(lib().attn_decode_workspace_bytes(num_heads, num_kv_heads, head_dim, max_seq))
 
 
+def attn_decode_workspace_init(workspace, workspace_bytes: int, num_heads: int,
+                               num_kv_heads: int, head_dim: int, max_seq: int,
+                               stream=None) -> None:
+    """Enqueue the zero fill of a decode workspace's completion counters."""
+    wsp = _workspace_ptr(workspace, workspace_bytes)
+    _check(lib().attn_decode_workspace_init(wsp, int(workspace_bytes), num_heads,
+                                            num_kv_heads, head_dim, max_seq, _stream(stream)))
+
+
+def _workspace_ptr(workspace, workspace_bytes):
+    import torch
+    if isinstance(workspace, torch.Tensor):
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        if workspace.numel() * workspace.element_size() < workspace_bytes:
+            raise ValueError("workspace tensor smaller than workspace_bytes")
+        return workspace.data_ptr()
+    return workspace
+
+
 def attn_decode(q, k_cache, v_cache, kv_pos, out, lse, num_heads: int, num_kv_heads: int,
                 head_dim: int, max_seq: int, scale: float, workspace,
                 workspace_bytes: int, stream=None) -> None:
     """Enqueue the single-token decode (see include/ta03.h). ``kv_pos`` is a
     one-element int32/uint32 GPU tensor; ``workspace`` a GPU tensor of at
-    least ``workspace_bytes`` bytes."""
+    least ``workspace_bytes`` bytes, zero-filled before its first use."""
     import torch
     qd, kvd = num_heads * head_dim, num_kv_heads * head_dim
     if isinstance(kv_pos, torch.Tensor):
@@ -122,14 +144,7 @@ def attn_decode(q, k_cache, v_cache, kv_pos, out, lse, num_heads: int, num_kv_he
                    dtype_name="int32" if kv_pos.dtype == torch.int32 else "uint32")
     else:
         kvp = kv_pos
-    if isinstance(workspace, torch.Tensor):
-        if not workspace.is_cuda or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous GPU tensor")
-        if workspace.numel() * workspace.element_size() < workspace_bytes:
-            raise ValueError("workspace tensor smaller than workspace_bytes")
-        wsp = workspace.data_ptr()
-    else:
-        wsp = workspace
+    wsp = _workspace_ptr(workspace, workspace_bytes)
     status = lib().attn_decode(
         _ptr(q, qd, "q"), _ptr(k_cache, max_seq * kvd, "k_cache"),
         _ptr(v_cache, max_seq * kvd, "v_cache"), kvp, _ptr(out, qd, "out"),

@@ -1,4 +1,4 @@
-// Single-token decode over a KV cache, split along the cache axis.
+// Single-token decode over a KV cache, split along the cache axis, one launch.
 //
 // What it computes is meganeura cached_attention.wgsl (main): one query row
 // of num_heads heads attends to cache rows [0, kv_pos] with kv_pos read from
@@ -7,22 +7,30 @@
 // causal window.
 //
 // The page runs one workgroup per head over every cache row in sequence, and
-// every head of a GQA group reads the same K/V rows again. Here the path is
-// bandwidth-bound, so it is organised around reading each K/V byte once with
-// the whole chip busy:
-//   1. split kernel: grid (split, kv-head x head-block). A block reads kv_pos,
-//      derives the cache length and its chunk on the device (so a recorded
-//      launch stays valid as kv_pos grows), streams its chunk of K and V once
-//      in 64-row sub-tiles (128-bit coalesced loads, one sub-tile ahead in
-//      registers, staged through LDS), and serves up to 4 query heads of the
-//      group from each staged tile: wave w computes head w's scores (lane =
-//      key), its tile max / sum with in-wave shuffles, and its P.V partial
-//      (lane = two head-dim columns). It writes an unnormalised partial row
-//      and its (max, sum) per head and split to the workspace.
-//   2. merge kernel: per head, combine the active splits' partials with
-//      log-sum-exp weights: M = max m_s, L = sum l_s 2^(m_s - M),
-//      out = sum 2^(m_s - M) O_s / L -- the same rescale the online update
-//      applies when a tile raises the running max.
+// each head of a GQA group re-reads the same K/V rows. This path is bound by
+// HBM bandwidth, so it is built to read each K/V byte once with the chip
+// full of requests:
+//   * grid (split, kv head x head block); a block reads kv_pos, derives the
+//     cache length and its chunk on the device (a recorded launch stays valid
+//     as kv_pos grows) and serves up to 4 query heads of one GQA group;
+//   * inside a block the 4 waves are independent: wave w owns keys
+//     [16w, 16w+16) of every 64-key sub-tile, with its own online-softmax
+//     state per head, and prefetches its next sub-tile while it computes;
+//   * K rows go HBM -> registers -> a wave-private LDS slice (rows padded to
+//     D+16 floats: conflict-free 128-bit reads), then lane (key, quarter)
+//     forms 4-head dot products over interleaved 16-byte pieces and a quad
+//     shuffle finishes them; max and sum over the wave's 16 keys use
+//     shuffles;
+//   * V rows go HBM -> registers directly in the P.V layout (lane = 4
+//     head-dim columns of one key, 128-bit coalesced), never through LDS;
+//   * the 4 waves combine with log-sum-exp weights through LDS and the block
+//     writes one partial (unnormalised row, max, sum) per head;
+//   * the last block of each (kv head, head block) to finish -- an atomic
+//     ticket after a device-scope release -- merges all partials of its
+//     group: M = max m_s, L = sum l_s 2^(m_s - M), out = sum 2^(m_s - M) O_s
+//     / L, the rescale the online update applies when the running max grows.
+//     It then resets the ticket to zero for the next call.
+// Scores are in log2 units (log2(e) folded into the pre-scaled Q; exp2).
 
 #include <hip/hip_runtime.h>
 
@@ -32,20 +40,23 @@ namespace ta03 {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kT = 64;           // keys per sub-tile
-constexpr int kMaxHeads = 4;     // query heads per block
-constexpr int kTargetBlocks = 1024;
+constexpr int kWaves = 4;
+constexpr int kT = 64;            // keys per sub-tile (16 per wave)
+constexpr int kKW = kT / kWaves;  // keys per wave per sub-tile
+constexpr int kG = 4;             // query heads per block
+constexpr int kTargetBlocks = 512;
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct Args {
-    int num_heads, num_kv_heads, head_dim, max_seq;
+    int num_heads, num_kv_heads, max_seq;
     int group, heads_per_blk, blks_per_kv, n_splits;
     float qscale;  // scale * log2(e)
+    size_t cnt_offset;  // floats from ws to the ticket counters
 };
 
-// Cache length and chunking, derived identically by both kernels.
+// Cache length and chunking, derived identically by every block.
 __device__ __forceinline__ void chunking(const uint32_t* kv_pos, const Args& a,
                                          int* kv_len, int* chunk, int* n_active) {
     const unsigned long long len = (unsigned long long)(*kv_pos) + 1ull;
@@ -57,186 +68,278 @@ __device__ __forceinline__ void chunking(const uint32_t* kv_pos, const Args& a,
     *n_active = (L + c - 1) / c;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-    return x;
+// LDS written by this wave's lanes becomes readable by its other lanes: DS
+// instructions of one wave execute in order, so waiting for the wave's own
+// LDS operations (lgkmcnt = 0; vector memory counters untouched) suffices.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
 }
 
 template <int D>
 __global__ void __launch_bounds__(kBlock)
-decode_split_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                    const float* __restrict__ v, const uint32_t* __restrict__ kv_pos,
-                    float* __restrict__ ws, Args a) {
-    constexpr int KS = D + 4;
-    constexpr int F4_ROW = D / 4;
-    constexpr int F4_THR = kT * F4_ROW / kBlock;  // 8 (D=128) or 4 (D=64)
-    constexpr int DPL = D / 64;                   // head-dim columns per lane in P.V
+decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
+              const float* __restrict__ v, const uint32_t* __restrict__ kv_pos,
+              float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws,
+              Args a) {
+    constexpr int KS = D + 16;           // padded K row in LDS (floats)
+    constexpr int F4_ROW = D / 4;        // float4 per row
+    constexpr int KF4 = kKW * F4_ROW / 64;  // K float4 per lane per sub-tile
+    constexpr int LPR = D / 4;           // lanes per V row in P.V (one float4 each)
+    constexpr int KR = 64 / LPR;         // key groups per wave in P.V
+    constexpr int VK = kKW / KR;         // V rows per lane per sub-tile
+    constexpr int QI = D / 16;           // 16-float pieces per row in the score loop
 
-    __shared__ __attribute__((aligned(16))) float Ks[kT * KS];
-    __shared__ __attribute__((aligned(16))) float Vs[kT * D];
-    __shared__ __attribute__((aligned(16))) float Qs[kMaxHeads * D];
-    __shared__ float Ps[kMaxHeads * kT];
+    __shared__ __attribute__((aligned(16))) float Ks[kWaves][kKW * KS];
+    __shared__ __attribute__((aligned(16))) float Qs[kG * D];
+    __shared__ __attribute__((aligned(16))) float Ps[kWaves][kKW * kG];
+    __shared__ __attribute__((aligned(16))) float Ow[kWaves][kG * D];
+    __shared__ float Mw[kWaves][kG], Lw[kWaves][kG];
+    __shared__ int last_flag;
 
     int kv_len, chunk, n_active;
     chunking(kv_pos, a, &kv_len, &chunk, &n_active);
     const int split = blockIdx.x;
-    if (split >= n_active) return;  // whole block: nothing to read
+    if (split >= n_active) return;  // whole block: nothing of this cache to read
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kv_head = blockIdx.y / a.blks_per_kv;
-    const int hsub = blockIdx.y % a.blks_per_kv;
+    const int grp = blockIdx.y;  // kv_head * blks_per_kv + hsub
+    const int kv_head = grp / a.blks_per_kv;
+    const int hsub = grp % a.blks_per_kv;
     const int head0 = kv_head * a.group + hsub * a.heads_per_blk;
     const int nh = min(a.heads_per_blk, a.group - hsub * a.heads_per_blk);
     const int kvdim = a.num_kv_heads * D;
     const int c0 = split * chunk;
     const int c1 = min(c0 + chunk, kv_len);
 
-    for (int i = tid; i < nh * D; i += kBlock) Qs[i] = q[(size_t)head0 * D + i] * a.qscale;
-
     const float* kbase = k + kv_head * D;
     const float* vbase = v + kv_head * D;
-    float4 kp[F4_THR], vp[F4_THR];
+
+    // Per-lane roles.
+    const int kk = lane >> 2;   // score phase: key within the wave's 16
+    const int qq = lane & 3;    // score phase: quarter (interleaved 16-byte pieces)
+    const int dq = lane % LPR;  // P.V phase: head-dim float4 index
+    const int kr = lane / LPR;  // P.V phase: key group
+
+    float4 kp[KF4], vp[VK];
     auto gload = [&](int base) {
+        const int wbase = base + wave * kKW;
 #pragma unroll
-        for (int it = 0; it < F4_THR; ++it) {
-            const int idx = tid + it * kBlock;
-            const int r = idx / F4_ROW;
-            const int c4 = idx % F4_ROW;
-            const int key = base + r;
-            if (key < c1) {
-                const size_t off = (size_t)key * kvdim + 4 * c4;
-                kp[it] = *reinterpret_cast<const float4*>(kbase + off);
-                vp[it] = *reinterpret_cast<const float4*>(vbase + off);
-            } else {
-                kp[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-                vp[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+        for (int it = 0; it < KF4; ++it) {
+            const int idx = lane + it * 64;
+            const int r = idx / F4_ROW, c4 = idx % F4_ROW;
+            const int key = wbase + r;
+            kp[it] = key < c1 ? *reinterpret_cast<const float4*>(kbase + (size_t)key * kvdim + 4 * c4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < VK; ++i) {
+            const int key = wbase + kr * VK + i;
+            vp[i] = key < c1 ? *reinterpret_cast<const float4*>(vbase + (size_t)key * kvdim + 4 * dq)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
 
-    const bool active = wave < nh;
-    float m_run = kNegBig, l_run = 0.f;
-    float acc[DPL];
-#pragma unroll
-    for (int c = 0; c < DPL; ++c) acc[c] = 0.f;
+    gload(c0);  // first sub-tile in flight before Q arrives
 
-    gload(c0);
-    for (int base = c0; base < c1; base += kT) {
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < F4_THR; ++it) {
-            const int idx = tid + it * kBlock;
-            const int r = idx / F4_ROW;
-            const int c4 = idx % F4_ROW;
-            *reinterpret_cast<float4*>(&Ks[r * KS + 4 * c4]) = kp[it];
-            *reinterpret_cast<float4*>(&Vs[r * D + 4 * c4]) = vp[it];
-        }
-        __syncthreads();
-        if (base + kT < c1) gload(base + kT);
+    for (int i = tid; i < kG * D; i += kBlock) {
+        const int h = i / D;
+        Qs[i] = h < nh ? q[(size_t)(head0 + h) * D + (i % D)] * a.qscale : 0.f;
+    }
+    __syncthreads();
 
-        if (active) {
-            // Scores: lane = key of the sub-tile, wave = head.
-            const int key = base + lane;
-            const float* qh = Qs + wave * D;
-            const float* kr = Ks + lane * KS;
-            float s = 0.f;
+    float m_run[kG], l_run[kG];
+    float4 acc[kG];
 #pragma unroll
-            for (int d = 0; d < D; d += 4) {
-                const float4 kk = *reinterpret_cast<const float4*>(kr + d);
-                const float4 qq = *reinterpret_cast<const float4*>(qh + d);
-                s = fmaf(qq.x, kk.x, s);
-                s = fmaf(qq.y, kk.y, s);
-                s = fmaf(qq.z, kk.z, s);
-                s = fmaf(qq.w, kk.w, s);
-            }
-            if (key >= c1) s = -INFINITY;
-            const float m_new = fmaxf(m_run, wave_max(s));
-            const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-            const float p = __builtin_amdgcn_exp2f(s - m_new);
-            l_run = l_run * corr + wave_sum(p);
-            m_run = m_new;
-            Ps[wave * kT + lane] = p;
-#pragma unroll
-            for (int c = 0; c < DPL; ++c) acc[c] *= corr;
-        }
-        __syncthreads();
-        if (active) {
-            const float* pw = Ps + wave * kT;
-#pragma unroll 8
-            for (int r = 0; r < kT; ++r) {
-                const float p = pw[r];
-                if constexpr (DPL == 2) {
-                    const float2 vv = *reinterpret_cast<const float2*>(Vs + r * D + 2 * lane);
-                    acc[0] = fmaf(p, vv.x, acc[0]);
-                    acc[1] = fmaf(p, vv.y, acc[1]);
-                } else {
-                    acc[0] = fmaf(p, Vs[r * D + lane], acc[0]);
-                }
-            }
-        }
+    for (int h = 0; h < kG; ++h) {
+        m_run[h] = kNegBig;
+        l_run[h] = 0.f;
+        acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
-    if (!active) return;
-    const int head = head0 + wave;
-    float* part = ws + ((size_t)head * a.n_splits + split) * (D + 2);
-    if constexpr (DPL == 2) {
-        *reinterpret_cast<float2*>(part + 2 * lane) = make_float2(acc[0], acc[1]);
-    } else {
-        part[lane] = acc[0];
+    float* ks = Ks[wave];
+    float* ps = Ps[wave];
+    for (int base = c0; base < c1; base += kT) {
+        // Stage this sub-tile's K slice; keep its V in registers.
+#pragma unroll
+        for (int it = 0; it < KF4; ++it) {
+            const int idx = lane + it * 64;
+            const int r = idx / F4_ROW, c4 = idx % F4_ROW;
+            *reinterpret_cast<float4*>(ks + r * KS + 4 * c4) = kp[it];
+        }
+        float4 vc[VK];
+#pragma unroll
+        for (int i = 0; i < VK; ++i) vc[i] = vp[i];
+        wave_lds_sync();
+        if (base + kT < c1) gload(base + kT);  // next sub-tile in flight
+
+        // Scores for key kk of the wave's slice, 4 heads, over this lane's pieces.
+        float s[kG];
+#pragma unroll
+        for (int h = 0; h < kG; ++h) s[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < QI; ++i) {
+            const float4 kx = *reinterpret_cast<const float4*>(ks + kk * KS + 16 * i + 4 * qq);
+#pragma unroll
+            for (int h = 0; h < kG; ++h) {
+                const float4 qx = *reinterpret_cast<const float4*>(Qs + h * D + 16 * i + 4 * qq);
+                s[h] = fmaf(qx.x, kx.x, s[h]);
+                s[h] = fmaf(qx.y, kx.y, s[h]);
+                s[h] = fmaf(qx.z, kx.z, s[h]);
+                s[h] = fmaf(qx.w, kx.w, s[h]);
+            }
+        }
+        const bool valid = base + wave * kKW + kk < c1;
+        float p[kG], corr[kG];
+#pragma unroll
+        for (int h = 0; h < kG; ++h) {
+            s[h] += __shfl_xor(s[h], 1);
+            s[h] += __shfl_xor(s[h], 2);
+            float x = valid ? s[h] : -INFINITY;
+            float mx = x;
+            mx = fmaxf(mx, __shfl_xor(mx, 4));
+            mx = fmaxf(mx, __shfl_xor(mx, 8));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run[h], mx);
+            corr[h] = __builtin_amdgcn_exp2f(m_run[h] - m_new);
+            p[h] = __builtin_amdgcn_exp2f(x - m_new);
+            float sm = qq == 0 ? p[h] : 0.f;  // one lane per key
+            sm += __shfl_xor(sm, 4);
+            sm += __shfl_xor(sm, 8);
+            sm += __shfl_xor(sm, 16);
+            sm += __shfl_xor(sm, 32);
+            l_run[h] = l_run[h] * corr[h] + sm;
+            m_run[h] = m_new;
+        }
+        if (qq == 0)
+            *reinterpret_cast<float4*>(ps + kk * kG) = make_float4(p[0], p[1], p[2], p[3]);
+        wave_lds_sync();
+
+        // O += P V over the wave's keys kr*VK .. kr*VK+VK-1, 4 columns per lane.
+#pragma unroll
+        for (int h = 0; h < kG; ++h) {
+            acc[h].x *= corr[h];
+            acc[h].y *= corr[h];
+            acc[h].z *= corr[h];
+            acc[h].w *= corr[h];
+        }
+#pragma unroll
+        for (int i = 0; i < VK; ++i) {
+            const float4 pk = *reinterpret_cast<const float4*>(ps + (kr * VK + i) * kG);
+            const float pv[kG] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+            for (int h = 0; h < kG; ++h) {
+                acc[h].x = fmaf(pv[h], vc[i].x, acc[h].x);
+                acc[h].y = fmaf(pv[h], vc[i].y, acc[h].y);
+                acc[h].z = fmaf(pv[h], vc[i].z, acc[h].z);
+                acc[h].w = fmaf(pv[h], vc[i].w, acc[h].w);
+            }
+        }
+        wave_lds_sync();  // this sub-tile's LDS reads are done before the next writes
+    }
+
+    // Sum the key groups of the wave (same running max within a wave).
+#pragma unroll
+    for (int h = 0; h < kG; ++h) {
+#pragma unroll
+        for (int m = LPR; m < 64; m <<= 1) {
+            acc[h].x += __shfl_xor(acc[h].x, m);
+            acc[h].y += __shfl_xor(acc[h].y, m);
+            acc[h].z += __shfl_xor(acc[h].z, m);
+            acc[h].w += __shfl_xor(acc[h].w, m);
+        }
+    }
+    if (kr == 0) {
+#pragma unroll
+        for (int h = 0; h < kG; ++h)
+            *reinterpret_cast<float4*>(&Ow[wave][h * D + 4 * dq]) = acc[h];
     }
     if (lane == 0) {
-        part[D] = m_run;
-        part[D + 1] = l_run;
+#pragma unroll
+        for (int h = 0; h < kG; ++h) {
+            Mw[wave][h] = m_run[h];
+            Lw[wave][h] = l_run[h];
+        }
+    }
+    __syncthreads();
+
+    // Block partial per head: combine the 4 waves with log-sum-exp weights.
+    const size_t row = D + 2;
+    for (int i = tid; i < nh * D; i += kBlock) {
+        const int h = i / D, d = i % D;
+        float M = Mw[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, Mw[w][h]);
+        float o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) o = fmaf(Ow[w][h * D + d], __builtin_amdgcn_exp2f(Mw[w][h] - M), o);
+        float* part = ws + ((size_t)(head0 + h) * a.n_splits + split) * row;
+        part[d] = o;
+        if (d == 0) {
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) L = fmaf(Lw[w][h], __builtin_amdgcn_exp2f(Mw[w][h] - M), L);
+            part[D] = M;
+            part[D + 1] = L;
+        }
+    }
+
+    // Ticket: the last block of this group to finish merges the group.
+    __threadfence();  // device-scope release of this block's partial
+    __syncthreads();
+    unsigned int* cnt = reinterpret_cast<unsigned int*>(ws + a.cnt_offset) + grp;
+    if (tid == 0) {
+        const unsigned int t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (t == (unsigned int)(n_active - 1)) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();  // acquire: every partial of the group is visible
+
+    // Merge: wave h handles head head0 + h (nh <= 4 waves); lanes cover D.
+    if (wave < nh) {
+        const int head = head0 + wave;
+        const float* hb = ws + (size_t)head * a.n_splits * row;
+        float M = kNegBig;
+        for (int s = lane; s < n_active; s += 64) M = fmaxf(M, hb[(size_t)s * row + D]);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+        float L = 0.f;
+        for (int s = lane; s < n_active; s += 64)
+            L = fmaf(hb[(size_t)s * row + D + 1], __builtin_amdgcn_exp2f(hb[(size_t)s * row + D] - M), L);
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m);
+        constexpr int DPL = D / 64;  // columns per lane
+        float o[DPL];
+#pragma unroll
+        for (int c = 0; c < DPL; ++c) o[c] = 0.f;
+#pragma unroll 4
+        for (int s = 0; s < n_active; ++s) {
+            const float* ps2 = hb + (size_t)s * row;
+            const float wgt = __builtin_amdgcn_exp2f(ps2[D] - M);
+#pragma unroll
+            for (int c = 0; c < DPL; ++c) o[c] = fmaf(ps2[lane * DPL + c], wgt, o[c]);
+        }
+        const float inv = 1.0f / L;
+#pragma unroll
+        for (int c = 0; c < DPL; ++c) out[(size_t)head * D + lane * DPL + c] = o[c] * inv;
+        if (lse != nullptr && lane == 0) {
+            lse[2 * head] = M * kLn2;
+            lse[2 * head + 1] = __logf(L);
+        }
+    }
+    if (tid == 0) {
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-template <int D>
-__global__ void __launch_bounds__(D)
-decode_merge_kernel(const uint32_t* __restrict__ kv_pos, const float* __restrict__ ws,
-                    float* __restrict__ out, float* __restrict__ lse, Args a) {
-    int kv_len, chunk, n_active;
-    chunking(kv_pos, a, &kv_len, &chunk, &n_active);
-    const int head = blockIdx.x;
-    const int t = threadIdx.x;
-    const float* base = ws + (size_t)head * a.n_splits * (D + 2);
-
-    float M = kNegBig;
-    for (int s = 0; s < n_active; ++s) M = fmaxf(M, base[(size_t)s * (D + 2) + D]);
-    float L = 0.f, o = 0.f;
-    for (int s = 0; s < n_active; ++s) {
-        const float* p = base + (size_t)s * (D + 2);
-        const float w = __builtin_amdgcn_exp2f(p[D] - M);
-        L = fmaf(p[D + 1], w, L);
-        o = fmaf(p[t], w, o);
-    }
-    out[(size_t)head * D + t] = o / L;
-    if (lse != nullptr && t == 0) {
-        lse[2 * head] = M * kLn2;
-        lse[2 * head + 1] = __logf(L);
-    }
-}
-
-Args make_args(const DecodeShape& s, const DecodePlan& p) {
-    Args a;
-    a.num_heads = s.num_heads;
-    a.num_kv_heads = s.num_kv_heads;
-    a.head_dim = s.head_dim;
-    a.max_seq = s.max_seq;
-    a.group = p.group;
-    a.heads_per_blk = p.heads_per_blk;
-    a.blks_per_kv = p.blks_per_kv;
-    a.n_splits = p.n_splits;
-    a.qscale = s.scale * kLog2e;
-    return a;
+__global__ void zero_u32_kernel(unsigned int* p, size_t n) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
 }
 
 }  // namespace
@@ -244,7 +347,7 @@ Args make_args(const DecodeShape& s, const DecodePlan& p) {
 DecodePlan decode_plan(const DecodeShape& s) {
     DecodePlan p;
     p.group = s.num_heads / s.num_kv_heads;
-    p.heads_per_blk = p.group < kMaxHeads ? p.group : kMaxHeads;
+    p.heads_per_blk = p.group < kG ? p.group : kG;
     p.blks_per_kv = (p.group + p.heads_per_blk - 1) / p.heads_per_blk;
     const long long rows = (long long)s.num_kv_heads * p.blks_per_kv;
     long long n = (kTargetBlocks + rows - 1) / rows;
@@ -252,26 +355,41 @@ DecodePlan decode_plan(const DecodeShape& s) {
     if (n > max_useful) n = max_useful;
     if (n < 1) n = 1;
     p.n_splits = (int)n;
-    p.ws_floats = (size_t)s.num_heads * (size_t)p.n_splits * (size_t)(s.head_dim + 2);
+    const size_t part = (size_t)s.num_heads * (size_t)p.n_splits * (size_t)(s.head_dim + 2);
+    p.cnt_offset = (part + 3) / 4 * 4;  // counters start 16-byte aligned
+    p.n_counters = (size_t)rows;
+    p.ws_floats = p.cnt_offset + (p.n_counters + 3) / 4 * 4;
     return p;
+}
+
+hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t stream) {
+    unsigned int* c = reinterpret_cast<unsigned int*>(ws + p.cnt_offset);
+    const unsigned int blocks = (unsigned int)((p.n_counters + 255) / 256);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(blocks), dim3(256), 0, stream, c, p.n_counters);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const float* q, const float* k, const float* v,
                          const uint32_t* kv_pos, float* out, float* lse,
                          const DecodeShape& s, const DecodePlan& p, float* ws,
                          hipStream_t stream) {
-    const Args a = make_args(s, p);
-    const dim3 grid1((unsigned)p.n_splits, (unsigned)(s.num_kv_heads * p.blks_per_kv));
+    Args a;
+    a.num_heads = s.num_heads;
+    a.num_kv_heads = s.num_kv_heads;
+    a.max_seq = s.max_seq;
+    a.group = p.group;
+    a.heads_per_blk = p.heads_per_blk;
+    a.blks_per_kv = p.blks_per_kv;
+    a.n_splits = p.n_splits;
+    a.qscale = s.scale * kLog2e;
+    a.cnt_offset = p.cnt_offset;
+    const dim3 grid((unsigned)p.n_splits, (unsigned)(s.num_kv_heads * p.blks_per_kv));
     if (s.head_dim == 128) {
-        hipLaunchKernelGGL(decode_split_kernel<128>, grid1, dim3(kBlock), 0, stream,
-                           q, k, v, kv_pos, ws, a);
-        hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)s.num_heads), dim3(128), 0,
-                           stream, kv_pos, ws, out, lse, a);
+        hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kBlock), 0, stream, q, k, v, kv_pos,
+                           out, lse, ws, a);
     } else {
-        hipLaunchKernelGGL(decode_split_kernel<64>, grid1, dim3(kBlock), 0, stream,
-                           q, k, v, kv_pos, ws, a);
-        hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)s.num_heads), dim3(64), 0,
-                           stream, kv_pos, ws, out, lse, a);
+        hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kBlock), 0, stream, q, k, v, kv_pos,
+                           out, lse, ws, a);
     }
     return hipGetLastError();
 }

@@ -61,6 +61,20 @@ size_t attn_decode_workspace_bytes(int num_heads, int num_kv_heads, int head_dim
     return ta03::decode_plan(s).ws_floats * sizeof(float);
 }
 
+int attn_decode_workspace_init(void* workspace, size_t workspace_bytes, int num_heads,
+                               int num_kv_heads, int head_dim, int max_seq, hipStream_t stream) {
+    if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 || max_seq < 1)
+        return TA03_ERR_SHAPE;
+    if (!head_dim_supported(head_dim)) return TA03_ERR_UNSUPPORTED;
+    if (workspace == nullptr) return TA03_ERR_NULL;
+    if (!aligned16(workspace)) return TA03_ERR_ALIGN;
+    ta03::DecodeShape s{num_heads, num_kv_heads, head_dim, max_seq, 1.0f};
+    const ta03::DecodePlan p = ta03::decode_plan(s);
+    if (workspace_bytes < p.ws_floats * sizeof(float)) return TA03_ERR_WORKSPACE;
+    const hipError_t e = ta03::launch_decode_ws_init(static_cast<float*>(workspace), p, stream);
+    return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
+}
+
 int attn_decode(const float* q, const float* k_cache, const float* v_cache,
                 const uint32_t* kv_pos, float* out, float* lse,
                 int num_heads, int num_kv_heads, int head_dim, int max_seq, float scale,

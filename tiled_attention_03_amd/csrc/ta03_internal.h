@@ -25,6 +25,8 @@ struct DecodePlan {
     int heads_per_blk;  // query heads one block serves (<= 4)
     int blks_per_kv;    // blocks per KV head along the head axis
     int n_splits;       // splits of the cache axis
+    size_t cnt_offset;  // floats from the workspace start to the ticket counters
+    size_t n_counters;  // one ticket counter per (kv head, head block)
     size_t ws_floats;   // workspace size in floats
 };
 
@@ -32,6 +34,8 @@ DecodePlan decode_plan(const DecodeShape& s);
 
 hipError_t launch_prefill(const float* q, const float* k, const float* v, float* out,
                           float* lse, const PrefillShape& s, hipStream_t stream);
+
+hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t stream);
 
 hipError_t launch_decode(const float* q, const float* k, const float* v,
                          const uint32_t* kv_pos, float* out, float* lse,
