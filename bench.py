@@ -110,9 +110,12 @@ def bench_prefill(w, steps, warmup, torch, ta):
             "tflops_kernel": flops / mean_s / 1e12, "tflops_wall": flops * steps / wall / 1e12}
 
 
-def bench_decode(w, kv_pos_values, iters, warmup, torch, ta, copies=8):
-    """Decode timing with the cache rotated over `copies` independent
-    allocations (copies x 64 MiB > the 256 MB Infinity Cache)."""
+def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8):
+    """Decode device time. The cache is rotated over `copies` independent
+    allocations (copies x 64 MiB > the 256 MB Infinity Cache), and the
+    `copies` calls are captured once in a HIP graph and replayed, so the
+    GPU runs the calls back to back instead of waiting on Python launches.
+    kv_pos lives in device memory: the same graph serves every kv_pos."""
     dev = torch.device("cuda:0")
     q, k, v = inputs.make_decode(w)
     qd = torch.from_numpy(q).to(dev)
@@ -122,22 +125,42 @@ def bench_decode(w, kv_pos_values, iters, warmup, torch, ta, copies=8):
     nbytes = ta.attn_decode_workspace_bytes(w.num_heads, w.num_kv_heads, w.head_dim,
                                             w.max_seq)
     ws = torch.zeros(max(nbytes // 4, 1), device=dev)  # zero-filled before first use
+    pos = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def call(i):
+        kc, vc = caches[i % copies]
+        ta.attn_decode(qd, kc, vc, pos, out, None, w.num_heads, w.num_kv_heads,
+                       w.head_dim, w.max_seq, w.scale, ws, nbytes)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(copies):
+            call(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(copies):
+            call(i)
     res = {}
     for kv_pos in kv_pos_values:
-        pos = torch.tensor([kv_pos], dtype=torch.int32, device=dev)
-
-        def call(i):
-            kc, vc = caches[i % copies]
-            ta.attn_decode(qd, kc, vc, pos, out, None, w.num_heads, w.num_kv_heads,
-                           w.head_dim, w.max_seq, w.scale, ws, nbytes)
-
-        for i in range(warmup):
-            call(i)
-        mean_s, min_s, _ = time_calls(call, iters, torch)
+        pos.fill_(kv_pos)
+        for _ in range(3):
+            graph.replay()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(replays):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        per_call = start.elapsed_time(end) * 1e-3 / (replays * copies)
         b = decode_bytes(w, kv_pos)
-        res[str(kv_pos)] = {"us": round(mean_s * 1e6, 2), "us_min": round(min_s * 1e6, 2),
-                            "GB/s": round(b / mean_s / 1e9, 1),
-                            "frac": round(b / mean_s / 1e9 / HBM_PEAK_GBPS, 4)}
+        res[str(kv_pos)] = {"us": round(per_call * 1e6, 2),
+                            "GB/s": round(b / per_call / 1e9, 1),
+                            "frac": round(b / per_call / 1e9 / HBM_PEAK_GBPS, 4)}
     return res
 
 
@@ -272,7 +295,7 @@ def main():
     if args.only != "prefill":
         wd = inputs.DECODE_8K
         print(f"[bench] decode {wd.name}", flush=True)
-        d = bench_decode(wd, wd.kv_pos_values, 200, 20, torch, ta)
+        d = bench_decode(wd, wd.kv_pos_values, 25, torch, ta)
         head = d[str(wd.kv_pos_values[-1])]
         result["decode"] = {
             "workload": wd.name, "unit": "GB/s", "kv_pos": d,

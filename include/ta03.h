@@ -105,7 +105,7 @@ size_t attn_decode_workspace_bytes(int num_heads, int num_kv_heads, int head_dim
 /*
  * attn_decode_workspace_init -- enqueue on `stream` the zero fill of the
  * completion counters of a decode workspace (one small kernel; no memset
- * node, so it may be captured in a graph). Same size arguments as
+ * node, so it may also be captured in a graph). Same size arguments as
  * attn_decode_workspace_bytes. Errors: TA03_ERR_SHAPE, TA03_ERR_UNSUPPORTED,
  * TA03_ERR_NULL, TA03_ERR_ALIGN, TA03_ERR_WORKSPACE, TA03_ERR_HIP.
  */

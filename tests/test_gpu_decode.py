@@ -135,15 +135,17 @@ def test_decode_deterministic(decode_8k):
 
 
 def test_workspace_reused_across_calls(decode_8k):
-    """One workspace, many calls with changing kv_pos: the completion counters
-    return to zero after every call, so each result is complete."""
+    """One workspace, many calls with changing kv_pos: the completion
+    counters return to zero after every call and no stale partial of an
+    earlier call leaks into a later one."""
     import torch
     import tiled_attention_03_amd as ta
     w, q, k, v, kd, vd = decode_8k
     kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
               max_seq=w.max_seq, scale=w.scale)
     nbytes = ta.attn_decode_workspace_bytes(w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq)
-    ws = torch.zeros(nbytes // 4, device=device())
+    ws = torch.full((nbytes // 4,), float("nan"), device=device())
+    ta.attn_decode_workspace_init(ws, nbytes, w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq)
     for p in (8191, 5, 700, 8191, 64, 63, 4096):
         go, gl = gpu_decode(q, k, v, p, k_dev=kd, v_dev=vd, ws=ws, **kw)
         ro, rl = ref_decode(q, k, v, p, **kw)
@@ -151,3 +153,43 @@ def test_workspace_reused_across_calls(decode_8k):
         check_lse(gl, rl, f"reuse lse p={p}")
     counters = ws[-(w.num_kv_heads):].view(torch.int32).cpu().numpy()
     assert np.all(counters == 0)
+
+
+def test_graph_replay_follows_device_kv_pos(decode_8k):
+    """A decode captured once in a HIP graph, replayed after the device-side
+    kv_pos changes (with eager work and synchronisation between replays):
+    every replay matches the checker."""
+    import torch
+    import tiled_attention_03_amd as ta
+    w, q, k, v, kd, vd = decode_8k
+    dev = device()
+    nbytes = ta.attn_decode_workspace_bytes(w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq)
+    ws = torch.zeros(nbytes // 4, device=dev)
+    qd = to_dev(q)
+    out = torch.empty((1, w.num_heads * w.head_dim), device=dev)
+    lse = torch.empty((1, w.num_heads, 2), device=dev)
+    pos = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def call():
+        ta.attn_decode(qd, kd, vd, pos, out, lse, w.num_heads, w.num_kv_heads, w.head_dim,
+                       w.max_seq, w.scale, ws, nbytes)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              max_seq=w.max_seq, scale=w.scale)
+    for p in (100, 8191, 2047, 0, 5555):
+        pos.fill_(p)
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        ro, rl = ref_decode(q, k, v, p, **kw)
+        check_out(out.cpu().numpy(), ro, f"graph replay p={p}")
+        check_lse(lse.cpu().numpy(), rl, f"graph replay lse p={p}")

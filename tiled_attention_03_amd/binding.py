@@ -136,7 +136,8 @@ def attn_decode(q, k_cache, v_cache, kv_pos, out, lse, num_heads: int, num_kv_he
                 workspace_bytes: int, stream=None) -> None:
     """Enqueue the single-token decode (see include/ta03.h). ``kv_pos`` is a
     one-element int32/uint32 GPU tensor; ``workspace`` a GPU tensor of at
-    least ``workspace_bytes`` bytes, zero-filled before its first use."""
+    least ``workspace_bytes`` bytes, zero-filled before its first use
+    (``attn_decode_workspace_init``); calls leave it reusable."""
     import torch
     qd, kvd = num_heads * head_dim, num_kv_heads * head_dim
     if isinstance(kv_pos, torch.Tensor):

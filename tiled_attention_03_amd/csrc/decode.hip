@@ -1,4 +1,4 @@
-// Single-token decode over a KV cache, split along the cache axis, one launch.
+// Single-token decode over a KV cache, split along the cache axis.
 //
 // What it computes is meganeura cached_attention.wgsl (main): one query row
 // of num_heads heads attends to cache rows [0, kv_pos] with kv_pos read from
@@ -15,21 +15,29 @@
 //     as kv_pos grows) and serves up to 4 query heads of one GQA group;
 //   * inside a block the 4 waves are independent: wave w owns keys
 //     [16w, 16w+16) of every 64-key sub-tile, with its own online-softmax
-//     state per head, and prefetches its next sub-tile while it computes;
-//   * K rows go HBM -> registers -> a wave-private LDS slice (rows padded to
-//     D+16 floats: conflict-free 128-bit reads), then lane (key, quarter)
-//     forms 4-head dot products over interleaved 16-byte pieces and a quad
-//     shuffle finishes them; max and sum over the wave's 16 keys use
-//     shuffles;
+//     state per head;
+//   * K rows go HBM -> registers directly in the score layout: lane (key,
+//     quarter) holds interleaved 16-byte pieces of its key (each load
+//     instruction covers 64 contiguous bytes of 16 rows) and forms 4-head
+//     dot products against Q broadcast from LDS; a quad shuffle finishes
+//     them, and max and sum over the wave's 16 keys use shuffles. Staging K
+//     through LDS measured markedly slower here;
 //   * V rows go HBM -> registers directly in the P.V layout (lane = 4
-//     head-dim columns of one key, 128-bit coalesced), never through LDS;
+//     head-dim columns of one key, 128-bit coalesced);
+//   * two register sets per wave: the next sub-tile's loads are issued
+//     before the current one is consumed;
 //   * the 4 waves combine with log-sum-exp weights through LDS and the block
-//     writes one partial (unnormalised row, max, sum) per head;
-//   * the last block of each (kv head, head block) to finish -- an atomic
-//     ticket after a device-scope release -- merges all partials of its
-//     group: M = max m_s, L = sum l_s 2^(m_s - M), out = sum 2^(m_s - M) O_s
-//     / L, the rescale the online update applies when the running max grows.
-//     It then resets the ticket to zero for the next call.
+//     publishes one partial (unnormalised row, max, sum) per head with
+//     device-scope atomic stores;
+//   * the last block of each (kv head, head block) to finish -- found with an
+//     atomic ticket taken by one thread once the block's partial stores are
+//     complete --
+//     merges the group's partials: M = max m_s, L = sum l_s 2^(m_s - M),
+//     out = sum 2^(m_s - M) O_s / L, the rescale the online update applies
+//     when the running max grows; its loads over the splits are independent
+//     and issued together. It then resets the ticket for the next call. One
+//     launch per call: on this stack a kernel launch alone costs about as much
+//     as streaming 20 MB, and the ticket replaces a second launch.
 // Scores are in log2 units (log2(e) folded into the pre-scaled Q; exp2).
 
 #include <hip/hip_runtime.h>
@@ -44,7 +52,11 @@ constexpr int kWaves = 4;
 constexpr int kT = 64;            // keys per sub-tile (16 per wave)
 constexpr int kKW = kT / kWaves;  // keys per wave per sub-tile
 constexpr int kG = 4;             // query heads per block
-constexpr int kTargetBlocks = 512;
+#ifndef TA03_DECODE_TARGET_BLOCKS
+#define TA03_DECODE_TARGET_BLOCKS 256
+#endif
+constexpr int kTargetBlocks = TA03_DECODE_TARGET_BLOCKS;
+constexpr int kMinChunk = 2 * kT;  // keys per block at least
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -63,6 +75,7 @@ __device__ __forceinline__ void chunking(const uint32_t* kv_pos, const Args& a,
     const int L = (int)(len < (unsigned long long)a.max_seq ? len : (unsigned long long)a.max_seq);
     int c = (L + a.n_splits - 1) / a.n_splits;
     c = (c + kT - 1) / kT * kT;
+    c = c < kMinChunk ? kMinChunk : c;  // both ping-pong sub-tiles of a wave in flight
     *kv_len = L;
     *chunk = c;
     *n_active = (L + c - 1) / c;
@@ -82,15 +95,11 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
               const float* __restrict__ v, const uint32_t* __restrict__ kv_pos,
               float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws,
               Args a) {
-    constexpr int KS = D + 16;           // padded K row in LDS (floats)
-    constexpr int F4_ROW = D / 4;        // float4 per row
-    constexpr int KF4 = kKW * F4_ROW / 64;  // K float4 per lane per sub-tile
-    constexpr int LPR = D / 4;           // lanes per V row in P.V (one float4 each)
-    constexpr int KR = 64 / LPR;         // key groups per wave in P.V
-    constexpr int VK = kKW / KR;         // V rows per lane per sub-tile
-    constexpr int QI = D / 16;           // 16-float pieces per row in the score loop
+    constexpr int QI = D / 16;    // 16-float pieces per K row: K float4 per lane per sub-tile
+    constexpr int LPR = D / 4;    // lanes per V row in P.V (one float4 each)
+    constexpr int KR = 64 / LPR;  // key groups per wave in P.V
+    constexpr int VK = kKW / KR;  // V rows per lane per sub-tile
 
-    __shared__ __attribute__((aligned(16))) float Ks[kWaves][kKW * KS];
     __shared__ __attribute__((aligned(16))) float Qs[kG * D];
     __shared__ __attribute__((aligned(16))) float Ps[kWaves][kKW * kG];
     __shared__ __attribute__((aligned(16))) float Ow[kWaves][kG * D];
@@ -118,31 +127,31 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const float* vbase = v + kv_head * D;
 
     // Per-lane roles.
-    const int kk = lane >> 2;   // score phase: key within the wave's 16
-    const int qq = lane & 3;    // score phase: quarter (interleaved 16-byte pieces)
-    const int dq = lane % LPR;  // P.V phase: head-dim float4 index
-    const int kr = lane / LPR;  // P.V phase: key group
+    const int kk = lane >> 2;   // scores: key within the wave's 16
+    const int qq = lane & 3;    // scores: which 16-byte piece of each 64 bytes
+    const int dq = lane % LPR;  // P.V: head-dim float4 index
+    const int kr = lane / LPR;  // P.V: key group
 
-    float4 kp[KF4], vp[VK];
-    auto gload = [&](int base) {
+    // K arrives straight in the score layout: lane (kk, qq) holds the pieces
+    // [16 i + 4 qq, +4) of its key for i < QI (each load instruction covers
+    // 64 contiguous bytes of 16 rows). V arrives in the P.V layout. Rows past
+    // the chunk end are read as the chunk's last row (in bounds, no branch
+    // around the load); their scores are masked and their weight is 0.
+    auto gload = [&](float4 (&kx)[QI], float4 (&vx)[VK], int base) {
         const int wbase = base + wave * kKW;
+        const int key = min(wbase + kk, c1 - 1);
+        const float* kp = kbase + (size_t)key * kvdim + 4 * qq;
 #pragma unroll
-        for (int it = 0; it < KF4; ++it) {
-            const int idx = lane + it * 64;
-            const int r = idx / F4_ROW, c4 = idx % F4_ROW;
-            const int key = wbase + r;
-            kp[it] = key < c1 ? *reinterpret_cast<const float4*>(kbase + (size_t)key * kvdim + 4 * c4)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        for (int i = 0; i < QI; ++i) kx[i] = *reinterpret_cast<const float4*>(kp + 16 * i);
 #pragma unroll
         for (int i = 0; i < VK; ++i) {
-            const int key = wbase + kr * VK + i;
-            vp[i] = key < c1 ? *reinterpret_cast<const float4*>(vbase + (size_t)key * kvdim + 4 * dq)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int vkey = min(wbase + kr * VK + i, c1 - 1);
+            vx[i] = *reinterpret_cast<const float4*>(vbase + (size_t)vkey * kvdim + 4 * dq);
         }
     };
 
-    gload(c0);  // first sub-tile in flight before Q arrives
+    float4 ka[QI], va[VK], kb[QI], vb[VK];
+    gload(ka, va, c0);  // first sub-tile in flight before Q arrives
 
     for (int i = tid; i < kG * D; i += kBlock) {
         const int h = i / D;
@@ -158,37 +167,23 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
         l_run[h] = 0.f;
         acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-
-    float* ks = Ks[wave];
     float* ps = Ps[wave];
-    for (int base = c0; base < c1; base += kT) {
-        // Stage this sub-tile's K slice; keep its V in registers.
-#pragma unroll
-        for (int it = 0; it < KF4; ++it) {
-            const int idx = lane + it * 64;
-            const int r = idx / F4_ROW, c4 = idx % F4_ROW;
-            *reinterpret_cast<float4*>(ks + r * KS + 4 * c4) = kp[it];
-        }
-        float4 vc[VK];
-#pragma unroll
-        for (int i = 0; i < VK; ++i) vc[i] = vp[i];
-        wave_lds_sync();
-        if (base + kT < c1) gload(base + kT);  // next sub-tile in flight
 
-        // Scores for key kk of the wave's slice, 4 heads, over this lane's pieces.
+    auto process = [&](const float4 (&kx)[QI], const float4 (&vx)[VK], int base) {
+        // Scores for key kk, 4 heads, over this lane's pieces; a quad
+        // shuffle completes the dot products.
         float s[kG];
 #pragma unroll
         for (int h = 0; h < kG; ++h) s[h] = 0.f;
 #pragma unroll
         for (int i = 0; i < QI; ++i) {
-            const float4 kx = *reinterpret_cast<const float4*>(ks + kk * KS + 16 * i + 4 * qq);
 #pragma unroll
             for (int h = 0; h < kG; ++h) {
                 const float4 qx = *reinterpret_cast<const float4*>(Qs + h * D + 16 * i + 4 * qq);
-                s[h] = fmaf(qx.x, kx.x, s[h]);
-                s[h] = fmaf(qx.y, kx.y, s[h]);
-                s[h] = fmaf(qx.z, kx.z, s[h]);
-                s[h] = fmaf(qx.w, kx.w, s[h]);
+                s[h] = fmaf(qx.x, kx[i].x, s[h]);
+                s[h] = fmaf(qx.y, kx[i].y, s[h]);
+                s[h] = fmaf(qx.z, kx[i].z, s[h]);
+                s[h] = fmaf(qx.w, kx[i].w, s[h]);
             }
         }
         const bool valid = base + wave * kKW + kk < c1;
@@ -197,7 +192,7 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
         for (int h = 0; h < kG; ++h) {
             s[h] += __shfl_xor(s[h], 1);
             s[h] += __shfl_xor(s[h], 2);
-            float x = valid ? s[h] : -INFINITY;
+            const float x = valid ? s[h] : -INFINITY;
             float mx = x;
             mx = fmaxf(mx, __shfl_xor(mx, 4));
             mx = fmaxf(mx, __shfl_xor(mx, 8));
@@ -232,13 +227,24 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
             const float pv[kG] = {pk.x, pk.y, pk.z, pk.w};
 #pragma unroll
             for (int h = 0; h < kG; ++h) {
-                acc[h].x = fmaf(pv[h], vc[i].x, acc[h].x);
-                acc[h].y = fmaf(pv[h], vc[i].y, acc[h].y);
-                acc[h].z = fmaf(pv[h], vc[i].z, acc[h].z);
-                acc[h].w = fmaf(pv[h], vc[i].w, acc[h].w);
+                acc[h].x = fmaf(pv[h], vx[i].x, acc[h].x);
+                acc[h].y = fmaf(pv[h], vx[i].y, acc[h].y);
+                acc[h].z = fmaf(pv[h], vx[i].z, acc[h].z);
+                acc[h].w = fmaf(pv[h], vx[i].w, acc[h].w);
             }
         }
-        wave_lds_sync();  // this sub-tile's LDS reads are done before the next writes
+        wave_lds_sync();  // P reads done before the next sub-tile rewrites it
+    };
+
+    // Two register sets: the next sub-tile's loads are issued before the
+    // current one is consumed, so two sub-tiles per wave are in flight.
+    for (int base = c0; base < c1; base += 2 * kT) {
+        if (base + kT < c1) gload(kb, vb, base + kT);
+        process(ka, va, base);
+        if (base + kT < c1) {
+            if (base + 2 * kT < c1) gload(ka, va, base + 2 * kT);
+            process(kb, vb, base + kT);
+        }
     }
 
     // Sum the key groups of the wave (same running max within a wave).
@@ -268,6 +274,28 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
     // Block partial per head: combine the 4 waves with log-sum-exp weights.
     const size_t row = D + 2;
+    if (n_active == 1) {
+        // One split covers the cache: this block's partial is the result.
+        for (int i = tid; i < nh * D; i += kBlock) {
+            const int h = i / D, d = i % D;
+            float M = Mw[0][h];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, Mw[w][h]);
+            float o = 0.f, L = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float wt = __builtin_amdgcn_exp2f(Mw[w][h] - M);
+                o = fmaf(Ow[w][h * D + d], wt, o);
+                L = fmaf(Lw[w][h], wt, L);
+            }
+            out[(size_t)(head0 + h) * D + d] = o / L;
+            if (lse != nullptr && d == 0) {
+                lse[2 * (head0 + h)] = M * kLn2;
+                lse[2 * (head0 + h) + 1] = __logf(L);
+            }
+        }
+        return;
+    }
     for (int i = tid; i < nh * D; i += kBlock) {
         const int h = i / D, d = i % D;
         float M = Mw[0][h];
@@ -277,52 +305,75 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) o = fmaf(Ow[w][h * D + d], __builtin_amdgcn_exp2f(Mw[w][h] - M), o);
         float* part = ws + ((size_t)(head0 + h) * a.n_splits + split) * row;
-        part[d] = o;
+        __hip_atomic_store(part + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (d == 0) {
             float L = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) L = fmaf(Lw[w][h], __builtin_amdgcn_exp2f(Mw[w][h] - M), L);
-            part[D] = M;
-            part[D + 1] = L;
+            __hip_atomic_store(part + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + D + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
-    // Ticket: the last block of this group to finish merges the group.
-    __threadfence();  // device-scope release of this block's partial
+    // Ticket. The partial stores above are device-coherent (agent-scope
+    // atomic stores write through to the coherence point); each wave waits
+    // for their completion (vmcnt = 0) before the block barrier, so when
+    // thread 0's atomic increment is performed every partial of this block
+    // is visible to any agent-scope load. The last block reads the partials
+    // with agent-scope atomic loads, which are served from the coherence
+    // point. No L2-wide write-back or invalidate is needed (a release/acquire
+    // ticket would issue one per block, which costs more than the merge).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
     __syncthreads();
-    unsigned int* cnt = reinterpret_cast<unsigned int*>(ws + a.cnt_offset) + grp;
+    unsigned int* cnt = reinterpret_cast<unsigned int*>(ws + a.cnt_offset) + blockIdx.y;
     if (tid == 0) {
-        const unsigned int t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL,
+        const unsigned int t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (t == (unsigned int)(n_active - 1)) ? 1 : 0;
+        last_flag = t == (unsigned int)(n_active - 1);
     }
     __syncthreads();
     if (!last_flag) return;
-    __threadfence();  // acquire: every partial of the group is visible
 
-    // Merge: wave h handles head head0 + h (nh <= 4 waves); lanes cover D.
+    // Merge: wave h serves head head0 + h, each lane D/64 columns. Up to 32
+    // splits are loaded in one batch (one round trip for the pages'
+    // configurations), with a running rescale across batches. Indices past
+    // the last split are clamped to it (no load sits behind a branch) and
+    // their weight is zeroed.
     if (wave < nh) {
+        constexpr int DPL = D / 64;
+        constexpr int NB = 32;
         const int head = head0 + wave;
         const float* hb = ws + (size_t)head * a.n_splits * row;
-        float M = kNegBig;
-        for (int s = lane; s < n_active; s += 64) M = fmaxf(M, hb[(size_t)s * row + D]);
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
-        float L = 0.f;
-        for (int s = lane; s < n_active; s += 64)
-            L = fmaf(hb[(size_t)s * row + D + 1], __builtin_amdgcn_exp2f(hb[(size_t)s * row + D] - M), L);
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m);
-        constexpr int DPL = D / 64;  // columns per lane
-        float o[DPL];
+        float M = kNegBig, L = 0.f, o[DPL];
 #pragma unroll
         for (int c = 0; c < DPL; ++c) o[c] = 0.f;
-#pragma unroll 4
-        for (int s = 0; s < n_active; ++s) {
-            const float* ps2 = hb + (size_t)s * row;
-            const float wgt = __builtin_amdgcn_exp2f(ps2[D] - M);
+        for (int s0 = 0; s0 < n_active; s0 += NB) {
+            float mv[NB], lv[NB], ov[NB][DPL];
 #pragma unroll
-            for (int c = 0; c < DPL; ++c) o[c] = fmaf(ps2[lane * DPL + c], wgt, o[c]);
+            for (int j = 0; j < NB; ++j) {
+                const float* p = hb + (size_t)min(s0 + j, n_active - 1) * row;
+                mv[j] = __hip_atomic_load(p + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                lv[j] = __hip_atomic_load(p + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int c = 0; c < DPL; ++c)
+                    ov[j][c] = __hip_atomic_load(p + lane * DPL + c, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            }
+            float bm = M;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) bm = fmaxf(bm, mv[j]);  // clamped repeats change nothing
+            const float r = __builtin_amdgcn_exp2f(M - bm);
+            L *= r;
+#pragma unroll
+            for (int c = 0; c < DPL; ++c) o[c] *= r;
+            M = bm;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const float w = s0 + j < n_active ? __builtin_amdgcn_exp2f(mv[j] - M) : 0.f;
+                L = fmaf(lv[j], w, L);
+#pragma unroll
+                for (int c = 0; c < DPL; ++c) o[c] = fmaf(ov[j][c], w, o[c]);
+            }
         }
         const float inv = 1.0f / L;
 #pragma unroll
@@ -332,13 +383,11 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
             lse[2 * head + 1] = __logf(L);
         }
     }
-    if (tid == 0) {
-        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ void zero_u32_kernel(unsigned int* p, size_t n) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void zero_counters_kernel(unsigned int* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
 }
 
@@ -364,8 +413,9 @@ DecodePlan decode_plan(const DecodeShape& s) {
 
 hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t stream) {
     unsigned int* c = reinterpret_cast<unsigned int*>(ws + p.cnt_offset);
-    const unsigned int blocks = (unsigned int)((p.n_counters + 255) / 256);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(blocks), dim3(256), 0, stream, c, p.n_counters);
+    const int n = (int)p.n_counters;
+    hipLaunchKernelGGL(zero_counters_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, c, n);
     return hipGetLastError();
 }
 
