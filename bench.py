@@ -37,8 +37,10 @@ from tiled_attention_03_amd import inputs  # noqa: E402
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense f32 matrix peak
 HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E peak
 METRIC = "prefill attention TFLOP/s and decode KV-read GB/s on 1 MI355X (% roofline)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_causal16k_traffic.md")
-PREFILL_SRC = os.path.join(ROOT, "tiled_attention_03_amd", "csrc", "prefill.hip")
+PREFILL_TRAFFIC = (os.path.join(ROOT, "profiles", "prefill_causal16k_traffic.md"),
+                   os.path.join(ROOT, "tiled_attention_03_amd", "csrc", "prefill.hip"))
+DECODE_TRAFFIC = (os.path.join(ROOT, "profiles", "decode_cache8192_traffic.md"),
+                  os.path.join(ROOT, "tiled_attention_03_amd", "csrc", "decode.hip"))
 
 
 # ------------------------------------------------------------ accounting
@@ -211,18 +213,39 @@ def cpu_baseline(w, budget_s=10.0, block=256, max_blocks=8):
 
 # ------------------------------------------------------------ traffic
 
-def stored_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current prefill kernel source; otherwise None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def stored_traffic(files):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    summary, src = files
+    if not os.path.exists(summary):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(summary).read()
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     if not m_b or not m_h:
         return None
-    cur = hashlib.sha256(open(PREFILL_SRC, "rb").read()).hexdigest()
+    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
     return float(m_b.group(1)) if m_h.group(1) == cur else None
+
+
+def read_ceiling(torch, mib=64, copies=8, reps=48):
+    """Measured context for the decode roofline: torch's own full-read
+    reduction over `copies` rotated buffers of `mib` MiB (the decode cache
+    size), in GB/s. Not part of the library path."""
+    dev = torch.device("cuda:0")
+    bufs = [torch.ones(mib * (1 << 20) // 4, device=dev) for _ in range(copies)]
+    for i in range(copies):
+        bufs[i].sum()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(reps):
+        bufs[i % copies].sum()
+    end.record()
+    torch.cuda.synchronize()
+    per = start.elapsed_time(end) * 1e-3 / reps
+    return round(mib * (1 << 20) / per / 1e9, 1)
 
 
 # ------------------------------------------------------------ main
@@ -275,7 +298,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(p["tflops_kernel"], 3),
                          "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(p["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                         "traffic": stored_traffic(),
+                         "traffic": stored_traffic(PREFILL_TRAFFIC),
                          "kernel": "prefill_kernel<128>",
                          "kernel_ms_mean": round(p["mean_s"] * 1e3, 3),
                          "kernel_ms_min": round(p["min_s"] * 1e3, 3)},
@@ -300,9 +323,11 @@ def main():
         result["decode"] = {
             "workload": wd.name, "unit": "GB/s", "kv_pos": d,
             "roofline": {"bound": "hbm", "achieved": head["GB/s"], "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": head["frac"], "traffic": None,
+                         "unit": "GB/s", "frac": head["frac"],
+                         "traffic": stored_traffic(DECODE_TRAFFIC),
                          "kernel": "decode_kernel<128>",
-                         "kv_pos": wd.kv_pos_values[-1]}}
+                         "kv_pos": wd.kv_pos_values[-1],
+                         "measured_read_ceiling_GBps": read_ceiling(torch)}}
         print(f"[bench] decode {d}", flush=True)
         if args.only == "decode":
             result.update({"value": head["GB/s"], "unit": "GB/s",
