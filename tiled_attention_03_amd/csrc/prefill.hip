@@ -11,13 +11,19 @@
 // (attention.wgsl header; attention_prefill.wgsl main).
 //
 // Work decomposition (one 256-thread block = 4 waves of 64 lanes):
-//   * a wave owns 32 query rows of one head; the four waves of a block are
-//     the query heads of one GQA group on the same rows (or, for small
-//     groups, neighbouring 32-row strips of one head), so the block shares
-//     every K/V tile it stages;
-//   * K/V tiles of 32 keys go HBM -> registers (128-bit, coalesced, one tile
-//     ahead) -> LDS; K rows are padded by 4 floats so the transposed 128-bit
-//     reads are bank-conflict free;
+//   * a wave owns 32 query rows of one head and one share of the key range.
+//     The 4 waves of a block are, in some mix, query heads of one GQA group
+//     on the same rows (they share every staged K/V tile), neighbouring
+//     32-row strips of one head (they share the tiles too), and key-range
+//     splits of the same rows (used when the grid would otherwise leave CUs
+//     idle; their partial rows are merged through LDS at the end, so no
+//     workspace is needed);
+//   * K/V tiles of 32 keys go HBM -> LDS directly (global_load_lds, 16 bytes
+//     per lane, no staging registers), double-buffered with one barrier per
+//     tile. Rows past the block's window are loaded as its last row (always
+//     in bounds; their scores are masked and their weight is 0). Each K row's
+//     16-byte chunks are XOR-swizzled by the row index so that the transposed
+//     128-bit reads of the score product are bank-conflict free;
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x2_f32: each lane then holds one query column and 16
 //     of the tile's 32 keys, so the row max and row sum are in-lane plus one
@@ -39,10 +45,13 @@ namespace ta03 {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBlock = 256;  // 4 waves
+constexpr int kWaves = 4;
 constexpr int kBM = 32;      // query rows per wave
 constexpr int kBN = 32;      // keys per tile
+constexpr int kTargetWaves = 2048;  // two waves per SIMD on 256 CUs
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -57,12 +66,17 @@ __device__ __forceinline__ int acc_row(int r, int hh) {
     return 8 * (r >> 2) + 4 * hh + (r & 3);
 }
 
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed
+}
+
 struct Args {
     int q_seq, kv_len, num_heads, num_kv_heads, group;
     int causal, start_pos;
     float qscale;  // scale * log2(e)
     int hg;        // heads per block
     int rs;        // 32-row strips per block
+    int ks;        // key-range splits per block
     int n_head_blocks, n_row_blocks;
 };
 
@@ -71,14 +85,12 @@ __global__ void __launch_bounds__(kBlock, 2)
 prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                const float* __restrict__ v, float* __restrict__ out,
                float* __restrict__ lse, Args a) {
-    constexpr int KS = D + 4;               // padded K row (floats)
-    constexpr int NB = D / 32;              // 32-row blocks of O^T
-    constexpr int F4_ROW = D / 4;           // float4 per K/V row
-    constexpr int F4_THR = kBN * F4_ROW / kBlock;  // float4 per thread per tile
-    static_assert(F4_THR >= 1, "tile too small for the block");
-
-    __shared__ __attribute__((aligned(16))) float Ks[kBN * KS];
-    __shared__ __attribute__((aligned(16))) float Vs[kBN * D];
+    constexpr int NB = D / 32;                // 32-row blocks of O^T
+    constexpr int CPR = D / 4;                // 16-byte chunks per K/V row
+    constexpr int TILE_F = kBN * D;           // floats per K (or V) tile
+    constexpr int TILE_CHUNKS = TILE_F / 4;   // 16-byte chunks per tile
+    constexpr int LOADS = TILE_CHUNKS / 64;   // wave load instructions per tile
+    extern __shared__ __attribute__((aligned(16))) float smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -91,14 +103,19 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int seq = bid / a.n_head_blocks;
     const int rb = a.causal ? (a.n_row_blocks - 1 - seq) : seq;  // heaviest first
 
-    const int head = head_block * a.hg + wave % a.hg;
-    const int strip = wave / a.hg;
+    // wave -> (key split, head, strip); waves sharing a key split share tiles
+    const int kvs = wave % a.ks;
+    const int rest = wave / a.ks;
+    const int head = head_block * a.hg + rest % a.hg;
+    const int strip = rest / a.hg;
+    const int wg = wave / a.ks;              // index within its key split's group
+    const int gw = kWaves / a.ks;            // waves per key split
     const int row0 = (rb * a.rs + strip) * kBM;
     const int kv_head = head / a.group;
     const int qdim = a.num_heads * D;
     const int kvdim = a.num_kv_heads * D;
 
-    // Keys the block must stage: up to the last row's window.
+    // Keys the block needs: up to the last row's window.
     const int blk_rows_hi = min((rb + 1) * a.rs * kBM, a.q_seq);
     const int w_block = a.causal ? min(a.start_pos + blk_rows_hi, a.kv_len) : a.kv_len;
     const bool wave_live = row0 < a.q_seq;
@@ -107,6 +124,15 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int w_wave_min = a.causal ? min(a.start_pos + row0 + 1, a.kv_len) : a.kv_len;
     const int row = row0 + j;
     const int w_row = a.causal ? min(a.start_pos + row + 1, a.kv_len) : a.kv_len;
+
+    // Tiles of this wave's key split.
+    const int n_tiles_all = (w_block + kBN - 1) / kBN;
+    const int nt = (n_tiles_all + a.ks - 1) / a.ks;
+    const int t_begin = kvs * nt;
+    const int t_end = min(t_begin + nt, n_tiles_all);
+
+    // This key split's two LDS buffers: [buf][K tile | V tile].
+    float* my_lds = smem + (size_t)kvs * 2 * 2 * TILE_F;
 
     // Q^T operand: lane (j, hh) holds q[row][8*g + 4*hh + c] for k-step 4*g+c.
     float qr[D / 2];
@@ -132,56 +158,51 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     float m_run = kNegBig;  // log2 units
     float l_run = 0.f;
 
-    const int n_tiles = (w_block + kBN - 1) / kBN;
-    float4 kp[F4_THR], vp[F4_THR];
     const float* kbase = k + kv_head * D;
     const float* vbase = v + kv_head * D;
 
-    auto gload = [&](int t) {
+    // Issue this wave's share of tile t's K and V into buffer buf. LDS slot s
+    // (16 bytes) of a tile holds row s/CPR; for K its chunk position p holds
+    // logical chunk p ^ (row % 16), for V the natural chunk.
+    auto issue_tile = [&](int t, int buf) {
+        float* kd = my_lds + (size_t)buf * 2 * TILE_F;
+        float* vd = kd + TILE_F;
         const int kv0 = t * kBN;
-#pragma unroll
-        for (int it = 0; it < F4_THR; ++it) {
-            const int idx = tid + it * kBlock;
-            const int r = idx / F4_ROW;
-            const int c4 = idx % F4_ROW;
-            const int key = kv0 + r;
-            if (key < w_block) {
-                const size_t off = (size_t)key * kvdim + 4 * c4;
-                kp[it] = *reinterpret_cast<const float4*>(kbase + off);
-                vp[it] = *reinterpret_cast<const float4*>(vbase + off);
-            } else {
-                kp[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-                vp[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+#pragma unroll 1
+        for (int inst = wg; inst < LOADS; inst += gw) {
+            const int s = inst * 64 + lane;
+            const int r = s / CPR, p = s % CPR;
+            const int key = min(kv0 + r, w_block - 1);
+            const float* kg = kbase + (size_t)key * kvdim + 4 * (p ^ (r & 15));
+            const float* vg = vbase + (size_t)key * kvdim + 4 * p;
+            __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kd + inst * 256), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vg, (lds_void*)(vd + inst * 256), 16, 0, 0);
         }
     };
 
-    if (n_tiles > 0) gload(0);
+    if (t_begin < t_end) issue_tile(t_begin, 0);
 
-    for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();  // the previous tile's readers are done with LDS
-#pragma unroll
-        for (int it = 0; it < F4_THR; ++it) {
-            const int idx = tid + it * kBlock;
-            const int r = idx / F4_ROW;
-            const int c4 = idx % F4_ROW;
-            *reinterpret_cast<float4*>(&Ks[r * KS + 4 * c4]) = kp[it];
-            *reinterpret_cast<float4*>(&Vs[r * D + 4 * c4]) = vp[it];
-        }
-        __syncthreads();
-        if (t + 1 < n_tiles) gload(t + 1);  // in flight while this tile computes
-
+    for (int it = 0; it < nt; ++it) {
+        const int t = t_begin + it;
+        const bool have = t < t_end;
+        wait_vmem();
+        __syncthreads();  // tile t landed for every wave; buffer (it+1)&1 is free
+        if (have && t + 1 < t_end) issue_tile(t + 1, (it + 1) & 1);
         const int kv0 = t * kBN;
-        if (kv0 >= w_wave_max) continue;  // wave-uniform: past every row's window
+        if (!have || kv0 >= w_wave_max) continue;  // wave-uniform
+
+        const float* Ks = my_lds + (size_t)(it & 1) * 2 * TILE_F;
+        const float* Vs = Ks + TILE_F;
 
         // S^T = K Q^T for this tile (already in log2 units).
         f32x16 s;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
-        const float* kr = Ks + j * KS + 4 * hh;
+        const float* kr = Ks + j * D;
 #pragma unroll
         for (int g = 0; g < D / 8; ++g) {
-            const float4 kk = *reinterpret_cast<const float4*>(kr + 8 * g);
+            const int c = (2 * g + hh) ^ (j & 15);
+            const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * c);
             s = mfma32(kk.x, qr[4 * g + 0], s);
             s = mfma32(kk.y, qr[4 * g + 1], s);
             s = mfma32(kk.z, qr[4 * g + 2], s);
@@ -233,6 +254,38 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         }
     }
 
+    if (a.ks > 1) {
+        // Merge the key splits of the same (head, rows): splits 1.. publish
+        // (m, l, O) through LDS in register order, split 0 rescales and adds.
+        __syncthreads();  // every wave is done with the tile buffers
+        constexpr int PART = 2 + NB * 16;  // floats per lane
+        float* part = smem + (size_t)(wave * PART) * 64;
+        if (kvs > 0) {
+            part[lane] = m_run;
+            part[64 + lane] = l_run;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[(2 + b * 16 + r) * 64 + lane] = o[b][r];
+        }
+        __syncthreads();
+        if (kvs > 0) return;
+        for (int p = 1; p < a.ks; ++p) {
+            const float* pp = smem + (size_t)((wave + p) * PART) * 64;
+            const float mp = pp[lane], lp = pp[64 + lane];
+            const float M = fmaxf(m_run, mp);
+            const float f0 = __builtin_amdgcn_exp2f(m_run - M);
+            const float f1 = __builtin_amdgcn_exp2f(mp - M);
+            l_run = l_run * f0 + lp * f1;
+            m_run = M;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    o[b][r] = o[b][r] * f0 + pp[(2 + b * 16 + r) * 64 + lane] * f1;
+        }
+    }
+
     if (!wave_live || row >= a.q_seq) return;
 
     // Epilogue: O^T block b, register r holds head-dim NB*acc_row(r, hh) + b.
@@ -281,17 +334,39 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     a.causal = s.causal;
     a.start_pos = s.start_pos;
     a.qscale = s.scale * kLog2e;
-    a.hg = gcd_int(a.group, 4);
-    a.rs = 4 / a.hg;
+
+    // Block shape: heads of one GQA group x row strips x key splits = 4 waves.
+    // Key splits only when one wave per (32 rows, head) leaves the chip short
+    // of two waves per SIMD, and only over enough key tiles to share.
+    const int strips = (s.q_seq + kBM - 1) / kBM;
+    const long long base_waves = (long long)s.num_heads * strips;
+    const int max_w = s.causal ? min(s.start_pos + s.q_seq, s.kv_len) : s.kv_len;
+    const int key_tiles = (max_w + kBN - 1) / kBN;
+    const int max_ks = s.head_dim == 128 ? 2 : 4;  // 2 buffers x (K, V) per split in 160 KB
+    int ks = 1;
+    while (ks < max_ks && base_waves * ks < kTargetWaves && key_tiles >= 4 * ks * 2) ks *= 2;
+    a.ks = ks;
+    a.hg = gcd_int(a.group, kWaves / ks);
+    a.rs = kWaves / (ks * a.hg);
     a.n_head_blocks = s.num_heads / a.hg;
     a.n_row_blocks = (s.q_seq + a.rs * kBM - 1) / (a.rs * kBM);
     const long long grid = (long long)a.n_head_blocks * a.n_row_blocks;
     if (grid <= 0) return hipSuccess;
+    const size_t tile_bytes = (size_t)kBN * s.head_dim * sizeof(float);
+    const size_t lds = (size_t)ks * 2 * 2 * tile_bytes;  // per split: 2 buffers x (K, V)
     if (s.head_dim == 128) {
-        hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(prefill_kernel<128>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * 2 * 2 * kBN * 128 * (int)sizeof(float));
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)grid), dim3(kBlock), lds, stream,
                            q, k, v, out, lse, a);
     } else {
-        hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)grid), dim3(kBlock), 0, stream,
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(prefill_kernel<64>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 2 * 2 * kBN * 64 * (int)sizeof(float));
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)grid), dim3(kBlock), lds, stream,
                            q, k, v, out, lse, a);
     }
     return hipGetLastError();
