@@ -170,3 +170,43 @@ def test_continuation_matches_whole_pass_rows():
                            mode=CAUSAL, kv_len=total, start_pos=s, scale=scale)
     check_out(b_o, a_o[s:].astype(np.float64), "continuation")
     check_lse(b_l, a_l[s:].astype(np.float64), "continuation lse")
+
+
+def test_graph_replay_matches_checker():
+    """attn_fwd captured once in a HIP graph and replayed after the inputs
+    change in place (eager work and synchronisation between replays): every
+    replay matches the checker on that replay's inputs."""
+    import torch
+    import tiled_attention_03_amd as ta
+    w = inputs.FULL_1K
+    dev = device()
+    q0, k0, v0 = inputs.make_prefill(w)
+    qd, kd, vd = to_dev(q0), to_dev(k0), to_dev(v0)
+    out = torch.empty((w.q_seq, w.num_heads * w.head_dim), device=dev)
+    lse = torch.empty((w.q_seq, w.num_heads, 2), device=dev)
+
+    def call():
+        ta.attn_fwd(qd, kd, vd, out, lse, w.q_seq, w.kv_len, w.num_heads, w.num_kv_heads,
+                    w.head_dim, w.mode, 0, w.scale)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              mode=w.mode, kv_len=w.kv_len, scale=w.scale)
+    for rep in range(3):
+        q = inputs.normal(q0.shape, 6000 + rep)
+        qd.copy_(torch.from_numpy(q).to(dev))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ro, rl = oracle_prefill(q, k0, v0, **kw)
+        check_out(out.cpu().numpy(), ro, f"graph replay {rep}")
+        check_lse(lse.cpu().numpy(), rl, f"graph replay lse {rep}")

@@ -47,11 +47,15 @@
 namespace ta03 {
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kWaves = 4;
-constexpr int kT = 64;            // keys per sub-tile (16 per wave)
+#ifndef TA03_DECODE_WAVES
+#define TA03_DECODE_WAVES 4
+#endif
+constexpr int kWaves = TA03_DECODE_WAVES;
+constexpr int kBlock = 64 * kWaves;
+constexpr int kT = 16 * kWaves;   // keys per sub-tile (16 per wave)
 constexpr int kKW = kT / kWaves;  // keys per wave per sub-tile
 constexpr int kG = 4;             // query heads per block
+static_assert(kWaves >= kG, "the merge serves one head per wave");
 #ifndef TA03_DECODE_TARGET_BLOCKS
 #define TA03_DECODE_TARGET_BLOCKS 256
 #endif

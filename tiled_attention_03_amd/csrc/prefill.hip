@@ -194,6 +194,9 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const float* Ks = my_lds + (size_t)(it & 1) * 2 * TILE_F;
         const float* Vs = Ks + TILE_F;
 
+        // Matrix-core sections run at raised wave priority so the SIMD's
+        // other wave fills the gaps with its softmax work.
+        __builtin_amdgcn_s_setprio(1);
         // S^T = K Q^T for this tile (already in log2 units).
         f32x16 s;
 #pragma unroll
@@ -209,6 +212,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             s = mfma32(kk.w, qr[4 * g + 3], s);
         }
 
+        __builtin_amdgcn_s_setprio(0);
         if (kv0 + kBN > w_wave_min) {  // some key of the tile is outside some window
 #pragma unroll
             for (int r = 0; r < 16; ++r)
@@ -231,11 +235,16 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         ls += __shfl_xor(ls, 32);
         l_run = l_run * corr + ls;
         m_run = m_new;
+        // Rescale only if some row's max moved (after the first tiles it
+        // rarely does): one wave-wide vote instead of 16*NB multiplies.
+        if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0ull) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[b][r] *= corr;
+                for (int r = 0; r < 16; ++r) o[b][r] *= corr;
+        }
 
+        __builtin_amdgcn_s_setprio(1);
         // O^T += V^T P^T: k-step t pairs keys acc_row(t, 0) and acc_row(t, 1).
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) {
@@ -252,6 +261,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 o[1] = mfma32(vv.y, s[tt], o[1]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     if (a.ks > 1) {
