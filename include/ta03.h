@@ -85,13 +85,42 @@ typedef enum {
  * q_seq, kv_len or start_pos < 0, mode unknown, start_pos != 0 outside
  * causal mode, causal start_pos + q_seq > kv_len (the pages' host assert), a
  * full call with kv_len != q_seq, or a non-finite scale;
- * TA03_ERR_UNSUPPORTED for head_dim not in {64, 128} or q/k/v/out larger
- * than 2^31 elements; TA03_ERR_ALIGN; TA03_ERR_HIP. q_seq == 0 is a valid
- * no-op.
+ * TA03_ERR_UNSUPPORTED for head_dim not in {64, 128}; TA03_ERR_ALIGN;
+ * TA03_ERR_HIP. q_seq == 0 is a valid no-op. Same as attn_fwd_ex with dense
+ * row strides and q_base = 0.
  */
 int attn_fwd(const float* q, const float* k, const float* v, float* out, float* lse,
              int q_seq, int kv_len, int num_heads, int num_kv_heads, int head_dim,
              int mode, int start_pos, float scale, hipStream_t stream);
+
+/*
+ * attn_fwd_ex -- attn_fwd over strided rows and a sub-batch of the query
+ * batch: the parameter block of cera attention_prefill.wgsl (header and
+ * main: q_stride, out_stride, q_base; q_global = q_base + i addresses the
+ * rows and sets the causal position start_pos + q_global).
+ *
+ *   q_stride, out_stride  floats between consecutive rows of q / out
+ *                         (>= num_heads*head_dim), e.g. the row length of a
+ *                         fused QKV buffer
+ *   k_stride, v_stride    floats between consecutive cache rows
+ *                         (>= num_kv_heads*head_dim)
+ *   q_base                first row of q / out (and lse) this call handles;
+ *                         rows [q_base, q_base + q_seq) are read and written
+ *   lse                   [q_base + q_seq, num_heads, 2] rows, indexed by the
+ *                         global row, or NULL
+ *
+ * Causal rows see [0, min(start_pos + q_base + i + 1, kv_len)); full and
+ * cross rows see [0, kv_len) (full: q_base + q_seq <= kv_len). Strides must be
+ * multiples of 4 floats (TA03_ERR_ALIGN) and below 2^31
+ * (TA03_ERR_UNSUPPORTED). Otherwise as attn_fwd: TA03_ERR_SHAPE also for
+ * q_base < 0, a stride shorter than a row, or causal start_pos + q_base +
+ * q_seq > kv_len.
+ */
+int attn_fwd_ex(const float* q, long long q_stride, const float* k, long long k_stride,
+                const float* v, long long v_stride, float* out, long long out_stride,
+                float* lse, int q_base, int q_seq, int kv_len, int num_heads,
+                int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+                hipStream_t stream);
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs

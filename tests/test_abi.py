@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_decode", "attn_decode_workspace_bytes",
-                                    "attn_decode_workspace_init", "attn_fwd",
+                                    "attn_decode_workspace_init", "attn_fwd", "attn_fwd_ex",
                                     "attn_strerror"]
 
 
@@ -72,13 +72,44 @@ def fwd(lib, q=A, k=B, v=C, out=O, lse=None, q_seq=4, kv_len=4, H=4, Hkv=2, d=64
     (dict(scale=float("inf")), ERR_SHAPE),
     (dict(d=96), ERR_UNSUP),
     (dict(d=256), ERR_UNSUP),
-    (dict(q_seq=1 << 20, kv_len=1 << 20, H=32, Hkv=8, d=128), ERR_UNSUP),  # > 2^31 elems
     (dict(q=A + 4), ERR_ALIGN),
     (dict(lse=O + 8), ERR_ALIGN),
     (dict(q_seq=0, kv_len=0, q=None, k=None, v=None, out=None), OK),  # empty: no-op
 ])
 def test_attn_fwd_rejects_on_host(lib, kw, status):
     assert fwd(lib, **kw) == status
+
+
+def fwd_ex(lib, q=A, qs=None, k=B, ks=None, v=C, vs=None, out=O, os_=None, lse=None, q_base=0,
+           q_seq=4, kv_len=8, H=4, Hkv=2, d=64, mode=0, sp=0, scale=0.125):
+    qs = H * d if qs is None else qs
+    os_ = H * d if os_ is None else os_
+    ks = Hkv * d if ks is None else ks
+    vs = Hkv * d if vs is None else vs
+    return lib.attn_fwd_ex(q, qs, k, ks, v, vs, out, os_, lse, q_base, q_seq, kv_len, H, Hkv, d,
+                           mode, sp, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=255), ERR_SHAPE),                 # q row shorter than H*d
+    (dict(os_=128), ERR_SHAPE),
+    (dict(ks=127), ERR_SHAPE),
+    (dict(vs=64), ERR_SHAPE),
+    (dict(qs=258), ERR_ALIGN),                 # not a multiple of 4 floats
+    (dict(vs=130), ERR_ALIGN),
+    (dict(qs=1 << 31), ERR_UNSUP),
+    (dict(q_base=-1), ERR_SHAPE),
+    (dict(q_base=5, q_seq=4, kv_len=8), ERR_SHAPE),        # causal window past kv_len
+    (dict(q_base=2, q_seq=4, kv_len=8, sp=3), ERR_SHAPE),
+    (dict(mode=1, q_base=5, q_seq=4, kv_len=8), ERR_SHAPE),  # full sub-batch past the batch
+    (dict(mode=2, sp=1), ERR_SHAPE),
+    (dict(q=None), ERR_NULL),
+    (dict(q=A + 8), ERR_ALIGN),
+    (dict(d=96), ERR_UNSUP),
+    (dict(q_seq=0, q=None, out=None), OK),
+])
+def test_attn_fwd_ex_rejects_on_host(lib, kw, status):
+    assert fwd_ex(lib, **kw) == status
 
 
 def test_validation_order_sizes_before_pointers(lib):

@@ -210,3 +210,55 @@ def test_graph_replay_matches_checker():
         ro, rl = oracle_prefill(q, k0, v0, **kw)
         check_out(out.cpu().numpy(), ro, f"graph replay {rep}")
         check_lse(lse.cpu().numpy(), rl, f"graph replay lse {rep}")
+
+
+def test_strided_fused_qkv_and_padded_out():
+    """Q, K and V as column slices of one fused [n, (H+2Hkv)*d] buffer, out
+    with padded rows: matches the checker on dense copies, and the padding
+    columns are left untouched."""
+    import torch
+    import tiled_attention_03_amd as ta
+    H, Hkv, d, n, sp = 8, 2, 128, 300, 0
+    dev = device()
+    width = (H + 2 * Hkv) * d
+    qkv = inputs.normal((n, width), 811)
+    q = np.ascontiguousarray(qkv[:, :H * d])
+    k = np.ascontiguousarray(qkv[:, H * d:(H + Hkv) * d])
+    v = np.ascontiguousarray(qkv[:, (H + Hkv) * d:])
+    qkv_d = to_dev(qkv)
+    ostride = H * d + 64
+    out = torch.full((n, ostride), float("nan"), device=dev)
+    lse = torch.full((n, H, 2), float("nan"), device=dev)
+    scale = d ** -0.5
+    ta.attn_fwd_ex(qkv_d[:, :H * d], width, qkv_d[:, H * d:], width, qkv_d[:, (H + Hkv) * d:],
+                   width, out, ostride, lse, 0, n, n, H, Hkv, d, CAUSAL, sp, scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle_prefill(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=CAUSAL,
+                            kv_len=n, scale=scale)
+    got = out.cpu().numpy()
+    check_out(got[:, :H * d], ro, "strided out")
+    check_lse(lse.cpu().numpy(), rl, "strided lse")
+    assert np.all(np.isnan(got[:, H * d:])), "padding columns were written"
+
+
+@pytest.mark.parametrize("mode,sp", [(CAUSAL, 37), (CROSS, 0), (FULL, 0)])
+def test_sub_batches_with_q_base(mode, sp):
+    """Splitting the query batch into sub-batch calls with q_base (the
+    prefill page's sub-batched dispatch) reproduces the whole batch."""
+    import torch
+    import tiled_attention_03_amd as ta
+    H, Hkv, d, n = 4, 2, 64, 170
+    kv = n + sp if mode != CROSS else 211
+    w, q, k, v = inputs.random_case(820 + mode, mode, n, kv, H, Hkv, d, start_pos=sp)
+    dev = device()
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    out = torch.full((n, H * d), float("nan"), device=dev)
+    lse = torch.full((n, H, 2), float("nan"), device=dev)
+    for base, cnt in ((0, 61), (61, 64), (125, 45)):
+        ta.attn_fwd_ex(qd, H * d, kd, Hkv * d, vd, Hkv * d, out, H * d, lse, base, cnt, kv, H, Hkv,
+                       d, mode, sp, w.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle_prefill(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=mode,
+                            kv_len=kv, start_pos=sp, scale=w.scale)
+    check_out(out.cpu().numpy(), ro, f"sub-batches mode={mode}")
+    check_lse(lse.cpu().numpy(), rl, f"sub-batches lse mode={mode}")

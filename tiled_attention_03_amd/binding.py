@@ -41,8 +41,11 @@ def lib() -> ctypes.CDLL:
                                "`python -m tiled_attention_03_amd.build` first")
         L = ctypes.CDLL(LIB_PATH)
         P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        LL = ctypes.c_longlong
         L.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
         L.attn_fwd.restype = I
+        L.attn_fwd_ex.argtypes = [P, LL, P, LL, P, LL, P, LL, P, I, I, I, I, I, I, I, I, F, P]
+        L.attn_fwd_ex.restype = I
         L.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
         L.attn_decode_workspace_bytes.restype = S
         L.attn_decode_workspace_init.argtypes = [P, S, I, I, I, I, P]
@@ -103,6 +106,47 @@ def attn_fwd(q, k, v, out, lse, q_seq: int, kv_len: int, num_heads: int,
         _ptr(v, kv_rows_needed * kvd, "v"), _ptr(out, q_seq * qd, "out"),
         _ptr(lse, q_seq * num_heads * 2, "lse"), q_seq, kv_len, num_heads, num_kv_heads,
         head_dim, mode, start_pos, float(scale), _stream(stream))
+    _check(status)
+
+
+def _strided_ptr(t, extent: int, name: str):
+    """Device pointer of a (possibly strided) float32 view whose first
+    `extent` elements from its start must lie inside its storage."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if extent <= 0:
+        return t.data_ptr() if t.numel() > 0 else None
+    avail = t.untyped_storage().nbytes() // 4 - t.storage_offset()
+    if extent > avail:
+        raise ValueError(f"{name}: {extent} elements needed from its start, storage holds {avail}")
+    return t.data_ptr()
+
+
+def attn_fwd_ex(q, q_stride: int, k, k_stride: int, v, v_stride: int, out, out_stride: int,
+                lse, q_base: int, q_seq: int, kv_len: int, num_heads: int, num_kv_heads: int,
+                head_dim: int, mode: int, start_pos: int, scale: float, stream=None) -> None:
+    """Enqueue the prefill over strided rows and a sub-batch (see
+    include/ta03.h). Tensors may be strided views (e.g. column slices of a
+    fused QKV buffer); strides are in floats between rows."""
+    qd, kvd = num_heads * head_dim, num_kv_heads * head_dim
+    rows = q_base + q_seq
+    kv_rows = kv_len if mode != CAUSAL else min(kv_len, start_pos + rows)
+    def ext(n, stride, width):
+        return (n - 1) * stride + width if n > 0 else 0
+    status = lib().attn_fwd_ex(
+        _strided_ptr(q, ext(rows, q_stride, qd), "q"), int(q_stride),
+        _strided_ptr(k, ext(kv_rows, k_stride, kvd), "k"), int(k_stride),
+        _strided_ptr(v, ext(kv_rows, v_stride, kvd), "v"), int(v_stride),
+        _strided_ptr(out, ext(rows, out_stride, qd), "out"), int(out_stride),
+        _ptr(lse, rows * num_heads * 2, "lse"), q_base, q_seq, kv_len, num_heads,
+        num_kv_heads, head_dim, mode, start_pos, float(scale), _stream(stream))
     _check(status)
 
 

@@ -74,6 +74,7 @@ struct Args {
     int q_seq, kv_len, num_heads, num_kv_heads, group;
     int causal, start_pos;
     float qscale;  // scale * log2(e)
+    long long q_stride, k_stride, v_stride, out_stride;  // row strides (floats)
     int hg;        // heads per block
     int rs;        // 32-row strips per block
     int ks;        // key-range splits per block
@@ -112,8 +113,6 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int gw = kWaves / a.ks;            // waves per key split
     const int row0 = (rb * a.rs + strip) * kBM;
     const int kv_head = head / a.group;
-    const int qdim = a.num_heads * D;
-    const int kvdim = a.num_kv_heads * D;
 
     // Keys the block needs: up to the last row's window.
     const int blk_rows_hi = min((rb + 1) * a.rs * kBM, a.q_seq);
@@ -138,7 +137,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     float qr[D / 2];
     {
         const bool ok = row < a.q_seq;
-        const float* qp = q + (size_t)(ok ? row : 0) * qdim + head * D + 4 * hh;
+        const float* qp = q + (size_t)(ok ? row : 0) * a.q_stride + head * D + 4 * hh;
 #pragma unroll
         for (int g = 0; g < D / 8; ++g) {
             float4 x = ok ? *reinterpret_cast<const float4*>(qp + 8 * g)
@@ -173,8 +172,8 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             const int s = inst * 64 + lane;
             const int r = s / CPR, p = s % CPR;
             const int key = min(kv0 + r, w_block - 1);
-            const float* kg = kbase + (size_t)key * kvdim + 4 * (p ^ (r & 15));
-            const float* vg = vbase + (size_t)key * kvdim + 4 * p;
+            const float* kg = kbase + (size_t)key * a.k_stride + 4 * (p ^ (r & 15));
+            const float* vg = vbase + (size_t)key * a.v_stride + 4 * p;
             __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kd + inst * 256), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(vg, (lds_void*)(vd + inst * 256), 16, 0, 0);
         }
@@ -300,7 +299,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
     // Epilogue: O^T block b, register r holds head-dim NB*acc_row(r, hh) + b.
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    float* orow = out + (size_t)row * qdim + head * D;
+    float* orow = out + (size_t)row * a.out_stride + head * D;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int i = acc_row(r, hh);
@@ -344,6 +343,10 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     a.causal = s.causal;
     a.start_pos = s.start_pos;
     a.qscale = s.scale * kLog2e;
+    a.q_stride = s.q_stride;
+    a.k_stride = s.k_stride;
+    a.v_stride = s.v_stride;
+    a.out_stride = s.out_stride;
 
     // Block shape: heads of one GQA group x row strips x key splits = 4 waves.
     // Key splits only when one wave per (32 rows, head) leaves the chip short

@@ -20,24 +20,30 @@ bool head_dim_supported(int d) { return d == 64 || d == 128; }
 
 extern "C" {
 
-int attn_fwd(const float* q, const float* k, const float* v, float* out, float* lse,
-             int q_seq, int kv_len, int num_heads, int num_kv_heads, int head_dim,
-             int mode, int start_pos, float scale, hipStream_t stream) {
+int attn_fwd_ex(const float* q, long long q_stride, const float* k, long long k_stride,
+                const float* v, long long v_stride, float* out, long long out_stride,
+                float* lse, int q_base, int q_seq, int kv_len, int num_heads,
+                int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+                hipStream_t stream) {
     if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0) return TA03_ERR_SHAPE;
-    if (q_seq < 0 || kv_len < 0 || start_pos < 0) return TA03_ERR_SHAPE;
+    if (q_seq < 0 || kv_len < 0 || start_pos < 0 || q_base < 0) return TA03_ERR_SHAPE;
     if (mode != TA03_CAUSAL && mode != TA03_FULL && mode != TA03_CROSS) return TA03_ERR_SHAPE;
     if (mode != TA03_CAUSAL && start_pos != 0) return TA03_ERR_SHAPE;
-    if (mode == TA03_CAUSAL && (long long)start_pos + q_seq > kv_len) return TA03_ERR_SHAPE;
-    if (mode == TA03_FULL && kv_len != q_seq) return TA03_ERR_SHAPE;
+    if (mode == TA03_CAUSAL && (long long)start_pos + q_base + q_seq > kv_len) return TA03_ERR_SHAPE;
+    if (mode == TA03_FULL && (long long)q_base + q_seq > kv_len) return TA03_ERR_SHAPE;
     if (!std::isfinite(scale)) return TA03_ERR_SHAPE;
     if (!head_dim_supported(head_dim)) return TA03_ERR_UNSUPPORTED;
-    if ((long long)q_seq * num_heads * head_dim >= kMaxElems ||
-        (long long)kv_len * num_kv_heads * head_dim >= kMaxElems)
+    const long long qd = (long long)num_heads * head_dim;
+    const long long kvd = (long long)num_kv_heads * head_dim;
+    if (q_stride < qd || out_stride < qd || k_stride < kvd || v_stride < kvd) return TA03_ERR_SHAPE;
+    if (q_stride >= kMaxElems || out_stride >= kMaxElems || k_stride >= kMaxElems ||
+        v_stride >= kMaxElems)
         return TA03_ERR_UNSUPPORTED;
     if (q_seq == 0) return TA03_OK;
     if (q == nullptr || out == nullptr) return TA03_ERR_NULL;
     if (kv_len > 0 && (k == nullptr || v == nullptr)) return TA03_ERR_NULL;
-    if (!aligned16(q) || !aligned16(out) || !aligned16(k) || !aligned16(v) || !aligned16(lse))
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k) || !aligned16(v) || !aligned16(lse) ||
+        (q_stride | k_stride | v_stride | out_stride) % 4 != 0)
         return TA03_ERR_ALIGN;
 
     ta03::PrefillShape s;
@@ -47,10 +53,29 @@ int attn_fwd(const float* q, const float* k, const float* v, float* out, float* 
     s.num_kv_heads = num_kv_heads;
     s.head_dim = head_dim;
     s.causal = mode == TA03_CAUSAL ? 1 : 0;
-    s.start_pos = start_pos;
+    s.start_pos = start_pos + q_base;  // causal position of the first row handled
     s.scale = scale;
-    const hipError_t e = ta03::launch_prefill(q, k, v, out, lse, s, stream);
+    s.q_stride = q_stride;
+    s.k_stride = k_stride;
+    s.v_stride = v_stride;
+    s.out_stride = out_stride;
+    // Row q_base of the batch is row 0 of this launch.
+    const float* qb = q + (size_t)q_base * (size_t)q_stride;
+    float* ob = out + (size_t)q_base * (size_t)out_stride;
+    float* lb = lse != nullptr ? lse + (size_t)q_base * (size_t)num_heads * 2 : nullptr;
+    const hipError_t e = ta03::launch_prefill(qb, k, v, ob, lb, s, stream);
     return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
+}
+
+int attn_fwd(const float* q, const float* k, const float* v, float* out, float* lse,
+             int q_seq, int kv_len, int num_heads, int num_kv_heads, int head_dim,
+             int mode, int start_pos, float scale, hipStream_t stream) {
+    // Dense rows; full attention over the whole sequence.
+    if (mode == TA03_FULL && kv_len != q_seq) return TA03_ERR_SHAPE;
+    const long long qd = (long long)num_heads * head_dim;
+    const long long kvd = (long long)num_kv_heads * head_dim;
+    return attn_fwd_ex(q, qd, k, kvd, v, kvd, out, qd, lse, 0, q_seq, kv_len, num_heads,
+                       num_kv_heads, head_dim, mode, start_pos, scale, stream);
 }
 
 size_t attn_decode_workspace_bytes(int num_heads, int num_kv_heads, int head_dim, int max_seq) {

@@ -9,8 +9,9 @@ namespace ta03 {
 
 struct PrefillShape {
     int q_seq, kv_len, num_heads, num_kv_heads, head_dim;
-    int causal, start_pos;
+    int causal, start_pos;  // start_pos: causal position of row 0 of q/out
     float scale;
+    long long q_stride, k_stride, v_stride, out_stride;  // row strides in floats
 };
 
 struct DecodeShape {
