@@ -175,6 +175,34 @@ int attn_decode(const float* q, const float* k_cache, const float* v_cache,
                 int num_heads, int num_kv_heads, int head_dim, int max_seq, float scale,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * attn_decode_paged -- attn_decode over a paged KV cache. The pages call
+ * caches too long for one binding "future paged-KV work" (cera
+ * attention_prefill.wgsl, header) without giving a layout; this one is:
+ *
+ *   k_pool, v_pool  [num_pages, page_size, num_kv_heads*head_dim]: page p
+ *                   holds page_size consecutive token rows in the dense
+ *                   cache's row layout
+ *   block_table     device int32 [ceil(max_seq / page_size)]: token t lives
+ *                   in row t % page_size of page block_table[t / page_size];
+ *                   entries outside [0, num_pages) are clamped on the device
+ *                   (never an out-of-bounds read; the result is then
+ *                   meaningless)
+ *   page_size       a multiple of 16 tokens
+ *   max_seq         token capacity covered by the table
+ *
+ * kv_pos, window, q, out, lse and the workspace (same size and rules as
+ * attn_decode for the same num_heads, num_kv_heads, head_dim, max_seq) are
+ * as in attn_decode. Errors as attn_decode, plus TA03_ERR_SHAPE for
+ * num_pages or page_size < 1, TA03_ERR_UNSUPPORTED for a page_size that is
+ * not a multiple of 16 or a table slice too large for one block's LDS.
+ */
+int attn_decode_paged(const float* q, const float* k_pool, const float* v_pool, int num_pages,
+                      int page_size, const int32_t* block_table, const uint32_t* kv_pos,
+                      float* out, float* lse, int num_heads, int num_kv_heads, int head_dim,
+                      int max_seq, float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 /* attn_strerror -- static description of a ta03_status value. */
 const char* attn_strerror(int status);
 

@@ -36,7 +36,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_decode", "attn_decode_workspace_bytes",
+    assert declared_functions() == ["attn_decode", "attn_decode_paged",
+                                    "attn_decode_workspace_bytes",
                                     "attn_decode_workspace_init", "attn_fwd", "attn_fwd_ex",
                                     "attn_strerror"]
 
@@ -142,6 +143,33 @@ def dec(lib, q=A, k=B, v=C, kv_pos=O, out=O + 0x1000, lse=None, H=32, Hkv=8, d=1
 ])
 def test_attn_decode_rejects_on_host(lib, kw, status):
     assert dec(lib, **kw) == status
+
+
+def paged(lib, q=A, k=B, v=C, num_pages=600, page_size=16, table=O + 0x2000, kv_pos=O,
+          out=O + 0x1000, lse=None, H=32, Hkv=8, d=128, max_seq=8192, scale=0.088, ws=0x90000,
+          ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_workspace_bytes(H, Hkv, d, max_seq)
+    return lib.attn_decode_paged(q, k, v, num_pages, page_size, table, kv_pos, out, lse, H, Hkv,
+                                 d, max_seq, scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page_size=8), ERR_UNSUP),       # pages must hold a multiple of 16 tokens
+    (dict(page_size=40), ERR_UNSUP),
+    (dict(page_size=0), ERR_SHAPE),
+    (dict(num_pages=0), ERR_SHAPE),
+    (dict(H=32, Hkv=5, ws_bytes=1 << 30), ERR_SHAPE),
+    (dict(d=32, ws_bytes=1 << 30), ERR_UNSUP),
+    (dict(table=None), ERR_NULL),
+    (dict(k=None), ERR_NULL),
+    (dict(table=O + 0x2002), ERR_ALIGN),
+    (dict(v=C + 4), ERR_ALIGN),
+    (dict(ws_bytes=64), ERR_WS),
+    (dict(page_size=16, max_seq=1 << 30, ws_bytes=1 << 40), ERR_UNSUP),  # table slice > LDS
+])
+def test_attn_decode_paged_rejects_on_host(lib, kw, status):
+    assert paged(lib, **kw) == status
 
 
 def test_workspace_bytes(lib):

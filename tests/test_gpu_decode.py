@@ -193,3 +193,99 @@ def test_graph_replay_follows_device_kv_pos(decode_8k):
         ro, rl = ref_decode(q, k, v, p, **kw)
         check_out(out.cpu().numpy(), ro, f"graph replay p={p}")
         check_lse(lse.cpu().numpy(), rl, f"graph replay lse p={p}")
+
+
+def _paged_pool(k, v, page_size, extra_pages, seed):
+    """Scatter a dense cache into shuffled pages of a pool with unused pages
+    (NaN) mixed in; returns (k_pool, v_pool, table, num_pages)."""
+    max_seq, kvd = k.shape
+    nblk = -(-max_seq // page_size)
+    num_pages = nblk + extra_pages
+    rng = np.random.default_rng(seed)
+    pages = rng.permutation(num_pages)[:nblk].astype(np.int32)
+    kp = np.full((num_pages, page_size, kvd), np.nan, np.float32)
+    vp = np.full((num_pages, page_size, kvd), np.nan, np.float32)
+    for b in range(nblk):
+        rows = slice(b * page_size, min((b + 1) * page_size, max_seq))
+        n = rows.stop - rows.start
+        kp[pages[b], :n] = k[rows]
+        vp[pages[b], :n] = v[rows]
+    return kp, vp, pages, num_pages
+
+
+@pytest.mark.parametrize("page_size", [16, 64, 256])
+def test_paged_decode_matches_dense(decode_8k, page_size):
+    """Paged cache with shuffled pages and unused NaN pages: matches the
+    checker on the dense cache, and equals the dense decode bit for bit (same
+    arithmetic, only row addresses differ)."""
+    import torch
+    import tiled_attention_03_amd as ta
+    w, q, k, v, kd, vd = decode_8k
+    dev = device()
+    kp, vp, table, num_pages = _paged_pool(k, v, page_size, 37, 870 + page_size)
+    kpd, vpd, tbd = to_dev(kp), to_dev(vp), to_dev(table)
+    nbytes = ta.attn_decode_workspace_bytes(w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq)
+    ws = torch.zeros(nbytes // 4, device=dev)
+    qd = to_dev(q)
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              max_seq=w.max_seq, scale=w.scale)
+    for p in (0, 15, 16, 1000, 4095, 8191):
+        out = torch.full((1, w.num_heads * w.head_dim), float("nan"), device=dev)
+        lse = torch.full((1, w.num_heads, 2), float("nan"), device=dev)
+        pos = torch.tensor([p], dtype=torch.int32, device=dev)
+        ta.attn_decode_paged(qd, kpd, vpd, num_pages, page_size, tbd, pos, out, lse,
+                             w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq, w.scale, ws,
+                             nbytes)
+        torch.cuda.synchronize()
+        ro, rl = ref_decode(q, k, v, p, **kw)
+        go, gl = out.cpu().numpy(), lse.cpu().numpy()
+        check_out(go, ro, f"paged P={page_size} p={p}")
+        check_lse(gl, rl, f"paged lse P={page_size} p={p}")
+        do, dl = gpu_decode(q, k, v, p, k_dev=kd, v_dev=vd, **kw)
+        assert np.array_equal(go, do) and np.array_equal(gl, dl), f"paged != dense at p={p}"
+
+
+def test_paged_decode_ragged_small():
+    """A small cache whose last page is partly used, group 3, head_dim 64."""
+    import torch
+    import tiled_attention_03_amd as ta
+    H, Hkv, d, max_seq, P = 6, 2, 64, 200, 32
+    q = inputs.normal((1, H * d), 881)
+    k = inputs.normal((max_seq, Hkv * d), 882)
+    v = inputs.normal((max_seq, Hkv * d), 883)
+    kp, vp, table, num_pages = _paged_pool(k, v, P, 3, 884)
+    dev = device()
+    nbytes = ta.attn_decode_workspace_bytes(H, Hkv, d, max_seq)
+    ws = torch.zeros(nbytes // 4, device=dev)
+    for p in (0, 31, 32, 130, 199, 500):
+        out = torch.empty((1, H * d), device=dev)
+        lse = torch.empty((1, H, 2), device=dev)
+        pos = torch.tensor([p], dtype=torch.int32, device=dev)
+        ta.attn_decode_paged(to_dev(q), to_dev(kp), to_dev(vp), num_pages, P, to_dev(table), pos,
+                             out, lse, H, Hkv, d, max_seq, d ** -0.5, ws, nbytes)
+        torch.cuda.synchronize()
+        ro, rl = ref_decode(q, k, v, p, num_heads=H, num_kv_heads=Hkv, head_dim=d,
+                            max_seq=max_seq, scale=d ** -0.5)
+        check_out(out.cpu().numpy(), ro, f"paged small p={p}")
+        check_lse(lse.cpu().numpy(), rl, f"paged small lse p={p}")
+
+
+def test_paged_decode_clamps_bad_table_entries():
+    """Table entries outside [0, num_pages) are clamped on the device: the
+    call completes with finite output (the value itself is meaningless)."""
+    import torch
+    import tiled_attention_03_amd as ta
+    H, Hkv, d, max_seq, P, num_pages = 8, 2, 128, 256, 16, 16
+    dev = device()
+    q = to_dev(inputs.normal((1, H * d), 891))
+    kp = to_dev(inputs.normal((num_pages, P, Hkv * d), 892))
+    vp = to_dev(inputs.normal((num_pages, P, Hkv * d), 893))
+    table = torch.tensor([-5, 3, 10 ** 6, 2 ** 31 - 1] * 4, dtype=torch.int32, device=dev)
+    nbytes = ta.attn_decode_workspace_bytes(H, Hkv, d, max_seq)
+    ws = torch.zeros(nbytes // 4, device=dev)
+    out = torch.empty((1, H * d), device=dev)
+    pos = torch.tensor([max_seq - 1], dtype=torch.int32, device=dev)
+    ta.attn_decode_paged(q, kp, vp, num_pages, P, table, pos, out, None, H, Hkv, d, max_seq,
+                         d ** -0.5, ws, nbytes)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out))

@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_workspace_init.restype = I
         L.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P, S, P]
         L.attn_decode.restype = I
+        L.attn_decode_paged.argtypes = [P, P, P, I, I, P, P, P, P, I, I, I, I, F, P, S, P]
+        L.attn_decode_paged.restype = I
         L.attn_strerror.argtypes = [I]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -195,6 +197,29 @@ def attn_decode(q, k_cache, v_cache, kv_pos, out, lse, num_heads: int, num_kv_he
         _ptr(v_cache, max_seq * kvd, "v_cache"), kvp, _ptr(out, qd, "out"),
         _ptr(lse, num_heads * 2, "lse"), num_heads, num_kv_heads, head_dim, max_seq,
         float(scale), wsp, int(workspace_bytes), _stream(stream))
+    _check(status)
+
+
+def attn_decode_paged(q, k_pool, v_pool, num_pages: int, page_size: int, block_table, kv_pos,
+                      out, lse, num_heads: int, num_kv_heads: int, head_dim: int, max_seq: int,
+                      scale: float, workspace, workspace_bytes: int, stream=None) -> None:
+    """Enqueue the decode over a paged cache (see include/ta03.h).
+    ``block_table`` is an int32 GPU tensor of ceil(max_seq / page_size)
+    entries; the pools hold num_pages * page_size rows."""
+    import torch
+    qd, kvd = num_heads * head_dim, num_kv_heads * head_dim
+    kvp = _ptr(kv_pos, 1, "kv_pos",
+               dtype_name="int32" if kv_pos.dtype == torch.int32 else "uint32") \
+        if isinstance(kv_pos, torch.Tensor) else kv_pos
+    nblk = -(-max_seq // page_size) if page_size > 0 else 0
+    tbl = _ptr(block_table, nblk, "block_table", dtype_name="int32") \
+        if isinstance(block_table, torch.Tensor) else block_table
+    wsp = _workspace_ptr(workspace, workspace_bytes)
+    status = lib().attn_decode_paged(
+        _ptr(q, qd, "q"), _ptr(k_pool, num_pages * page_size * kvd, "k_pool"),
+        _ptr(v_pool, num_pages * page_size * kvd, "v_pool"), num_pages, page_size, tbl, kvp,
+        _ptr(out, qd, "out"), _ptr(lse, num_heads * 2, "lse"), num_heads, num_kv_heads,
+        head_dim, max_seq, float(scale), wsp, int(workspace_bytes), _stream(stream))
     _check(status)
 
 

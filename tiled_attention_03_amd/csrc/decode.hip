@@ -70,6 +70,11 @@ struct Args {
     int group, heads_per_blk, blks_per_kv, n_splits;
     float qscale;  // scale * log2(e)
     size_t cnt_offset;  // floats from ws to the ticket counters
+    // Paged cache (table == nullptr: one dense cache). Token t lives in row
+    // t % page_size of page table[t / page_size]; page_size is a multiple of
+    // 16, so a wave's 16-key slice never straddles two pages.
+    const int* table;
+    int page_size, num_pages;
 };
 
 // Cache length and chunking, derived identically by every block.
@@ -109,6 +114,7 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     __shared__ __attribute__((aligned(16))) float Ow[kWaves][kG * D];
     __shared__ float Mw[kWaves][kG], Lw[kWaves][kG];
     __shared__ int last_flag;
+    extern __shared__ int tbl[];  // this block's slice of the page table (paged cache)
 
     int kv_len, chunk, n_active;
     chunking(kv_pos, a, &kv_len, &chunk, &n_active);
@@ -136,20 +142,38 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int dq = lane % LPR;  // P.V: head-dim float4 index
     const int kr = lane / LPR;  // P.V: key group
 
+    // Paged cache: stage this chunk's table entries in LDS, each clamped to
+    // a valid page so that no table content can send a load out of bounds.
+    const bool paged = a.table != nullptr;
+    const int b0 = paged ? c0 / a.page_size : 0;
+    if (paged) {
+        const int nb = (c1 - 1) / a.page_size - b0 + 1;
+        for (int i = tid; i < nb; i += kBlock)
+            tbl[i] = min(max(a.table[b0 + i], 0), a.num_pages - 1);
+        __syncthreads();
+    }
+
     // K arrives straight in the score layout: lane (kk, qq) holds the pieces
     // [16 i + 4 qq, +4) of its key for i < QI (each load instruction covers
     // 64 contiguous bytes of 16 rows). V arrives in the P.V layout. Rows past
     // the chunk end are read as the chunk's last row (in bounds, no branch
-    // around the load); their scores are masked and their weight is 0.
+    // around the load); their scores are masked and their weight is 0. In a
+    // paged cache every key of the wave's slice (after that clamp) lies in the
+    // page of min(slice start, c1 - 1): one row offset per slice.
     auto gload = [&](float4 (&kx)[QI], float4 (&vx)[VK], int base) {
         const int wbase = base + wave * kKW;
-        const int key = min(wbase + kk, c1 - 1);
+        long long shift = 0;  // physical row - token index
+        if (paged) {
+            const int blk = min(wbase, c1 - 1) / a.page_size;
+            shift = (long long)(tbl[blk - b0] - blk) * a.page_size;
+        }
+        const long long key = min(wbase + kk, c1 - 1) + shift;
         const float* kp = kbase + (size_t)key * kvdim + 4 * qq;
 #pragma unroll
         for (int i = 0; i < QI; ++i) kx[i] = *reinterpret_cast<const float4*>(kp + 16 * i);
 #pragma unroll
         for (int i = 0; i < VK; ++i) {
-            const int vkey = min(wbase + kr * VK + i, c1 - 1);
+            const long long vkey = min(wbase + kr * VK + i, c1 - 1) + shift;
             vx[i] = *reinterpret_cast<const float4*>(vbase + (size_t)vkey * kvdim + 4 * dq);
         }
     };
@@ -423,10 +447,19 @@ hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t str
     return hipGetLastError();
 }
 
+size_t decode_table_lds_bytes(const DecodeShape& s, const DecodePlan& p, int page_size) {
+    // The largest chunk any kv_pos can give (the cache full), as chunking()
+    // computes it, and the table entries a chunk can touch.
+    long long c = ((long long)s.max_seq + p.n_splits - 1) / p.n_splits;
+    c = (c + kT - 1) / kT * kT;
+    if (c < kMinChunk) c = kMinChunk;
+    return (size_t)(c / page_size + 2) * sizeof(int);
+}
+
 hipError_t launch_decode(const float* q, const float* k, const float* v,
                          const uint32_t* kv_pos, float* out, float* lse,
                          const DecodeShape& s, const DecodePlan& p, float* ws,
-                         hipStream_t stream) {
+                         hipStream_t stream, const int* table, int page_size, int num_pages) {
     Args a;
     a.num_heads = s.num_heads;
     a.num_kv_heads = s.num_kv_heads;
@@ -437,12 +470,16 @@ hipError_t launch_decode(const float* q, const float* k, const float* v,
     a.n_splits = p.n_splits;
     a.qscale = s.scale * kLog2e;
     a.cnt_offset = p.cnt_offset;
+    a.table = table;
+    a.page_size = page_size;
+    a.num_pages = num_pages;
+    const size_t lds = table != nullptr ? decode_table_lds_bytes(s, p, page_size) : 0;
     const dim3 grid((unsigned)p.n_splits, (unsigned)(s.num_kv_heads * p.blks_per_kv));
     if (s.head_dim == 128) {
-        hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kBlock), 0, stream, q, k, v, kv_pos,
+        hipLaunchKernelGGL(decode_kernel<128>, grid, dim3(kBlock), lds, stream, q, k, v, kv_pos,
                            out, lse, ws, a);
     } else {
-        hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kBlock), 0, stream, q, k, v, kv_pos,
+        hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(kBlock), lds, stream, q, k, v, kv_pos,
                            out, lse, ws, a);
     }
     return hipGetLastError();

@@ -124,6 +124,36 @@ int attn_decode(const float* q, const float* k_cache, const float* v_cache,
     return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
 }
 
+int attn_decode_paged(const float* q, const float* k_pool, const float* v_pool, int num_pages,
+                      int page_size, const int32_t* block_table, const uint32_t* kv_pos,
+                      float* out, float* lse, int num_heads, int num_kv_heads, int head_dim,
+                      int max_seq, float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 || max_seq < 1 ||
+        num_pages < 1 || page_size < 1)
+        return TA03_ERR_SHAPE;
+    if (!std::isfinite(scale)) return TA03_ERR_SHAPE;
+    if (!head_dim_supported(head_dim) || page_size % 16 != 0) return TA03_ERR_UNSUPPORTED;
+    if ((long long)num_pages * page_size * num_kv_heads * head_dim >= (1ll << 40))
+        return TA03_ERR_UNSUPPORTED;
+    if (q == nullptr || k_pool == nullptr || v_pool == nullptr || block_table == nullptr ||
+        kv_pos == nullptr || out == nullptr || workspace == nullptr)
+        return TA03_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+        !aligned16(lse) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(kv_pos) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
+        return TA03_ERR_ALIGN;
+    ta03::DecodeShape s{num_heads, num_kv_heads, head_dim, max_seq, scale};
+    const ta03::DecodePlan p = ta03::decode_plan(s);
+    if (workspace_bytes < p.ws_floats * sizeof(float)) return TA03_ERR_WORKSPACE;
+    if (ta03::decode_table_lds_bytes(s, p, page_size) > 64 * 1024) return TA03_ERR_UNSUPPORTED;
+    const hipError_t e = ta03::launch_decode(q, k_pool, v_pool, kv_pos, out, lse, s, p,
+                                             static_cast<float*>(workspace), stream,
+                                             block_table, page_size, num_pages);
+    return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
+}
+
 const char* attn_strerror(int status) {
     switch (status) {
         case TA03_OK: return "ok";

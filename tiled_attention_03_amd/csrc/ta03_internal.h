@@ -38,9 +38,16 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
 
 hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t stream);
 
+// Dynamic LDS a paged decode launch needs for its page-table slice.
+size_t decode_table_lds_bytes(const DecodeShape& s, const DecodePlan& p, int page_size);
+
+// table == nullptr: one dense cache of max_seq rows; otherwise k/v are page
+// pools of num_pages pages of page_size rows and table maps token blocks to
+// pages.
 hipError_t launch_decode(const float* q, const float* k, const float* v,
                          const uint32_t* kv_pos, float* out, float* lse,
                          const DecodeShape& s, const DecodePlan& p, float* ws,
-                         hipStream_t stream);
+                         hipStream_t stream, const int* table = nullptr, int page_size = 0,
+                         int num_pages = 0);
 
 }  // namespace ta03
