@@ -24,8 +24,9 @@
 //     through LDS measured markedly slower here;
 //   * V rows go HBM -> registers directly in the P.V layout (lane = 4
 //     head-dim columns of one key, 128-bit coalesced);
-//   * two register sets per wave: the next sub-tile's loads are issued
-//     before the current one is consumed;
+//   * two register sets per wave, both in flight before the first wait and
+//     each refilled as soon as it has been consumed; Q is loaded ahead of
+//     them (vector loads complete in issue order);
 //   * the 4 waves combine with log-sum-exp weights through LDS and the block
 //     publishes one partial (unnormalised row, max, sum) per head with
 //     device-scope atomic stores;
@@ -60,7 +61,10 @@ static_assert(kWaves >= kG, "the merge serves one head per wave");
 #define TA03_DECODE_TARGET_BLOCKS 256
 #endif
 constexpr int kTargetBlocks = TA03_DECODE_TARGET_BLOCKS;
-constexpr int kMinChunk = 2 * kT;  // keys per block at least
+#ifndef TA03_DECODE_MIN_SUB
+#define TA03_DECODE_MIN_SUB 2
+#endif
+constexpr int kMinChunk = TA03_DECODE_MIN_SUB * kT;  // keys per block at least
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -116,19 +120,32 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     __shared__ int last_flag;
     extern __shared__ int tbl[];  // this block's slice of the page table (paged cache)
 
-    int kv_len, chunk, n_active;
-    chunking(kv_pos, a, &kv_len, &chunk, &n_active);
-    const int split = blockIdx.x;
-    if (split >= n_active) return;  // whole block: nothing of this cache to read
-
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = blockIdx.y;  // kv_head * blks_per_kv + hsub
     const int kv_head = grp / a.blks_per_kv;
     const int hsub = grp % a.blks_per_kv;
     const int head0 = kv_head * a.group + hsub * a.heads_per_blk;
     const int nh = min(a.heads_per_blk, a.group - hsub * a.heads_per_blk);
+
+    // Q is loaded first: it does not depend on kv_pos, and vector loads
+    // complete in issue order, so waiting for Q further down does not wait
+    // for the K/V loads issued after it.
+    constexpr int QPT = (kG * D + kBlock - 1) / kBlock;  // Q floats per thread
+    float qreg[QPT];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int i = tid + j * kBlock;
+        const int h = i / D;
+        qreg[j] = (i < kG * D && h < nh) ? q[(size_t)(head0 + h) * D + (i % D)] : 0.f;
+    }
+
+    int kv_len, chunk, n_active;
+    chunking(kv_pos, a, &kv_len, &chunk, &n_active);
+    const int split = blockIdx.x;
+    if (split >= n_active) return;  // whole block: nothing of this cache to read
+
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kvdim = a.num_kv_heads * D;
     const int c0 = split * chunk;
     const int c1 = min(c0 + chunk, kv_len);
@@ -178,12 +195,17 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
         }
     };
 
+    // Both register sets in flight before anything waits. Loads are never
+    // behind a branch (rows are clamped into the chunk), so the compiler's
+    // wait counts stay exact: waiting for one set never waits for the other.
     float4 ka[QI], va[VK], kb[QI], vb[VK];
-    gload(ka, va, c0);  // first sub-tile in flight before Q arrives
+    gload(ka, va, c0);
+    gload(kb, vb, c0 + kT);
 
-    for (int i = tid; i < kG * D; i += kBlock) {
-        const int h = i / D;
-        Qs[i] = h < nh ? q[(size_t)(head0 + h) * D + (i % D)] * a.qscale : 0.f;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int i = tid + j * kBlock;
+        if (i < kG * D) Qs[i] = qreg[j] * a.qscale;
     }
     __syncthreads();
 
@@ -264,16 +286,23 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
         wave_lds_sync();  // P reads done before the next sub-tile rewrites it
     };
 
-    // Two register sets: the next sub-tile's loads are issued before the
-    // current one is consumed, so two sub-tiles per wave are in flight.
-    for (int base = c0; base < c1; base += 2 * kT) {
-        if (base + kT < c1) gload(kb, vb, base + kT);
+    // Sub-tiles go in pairs, one per register set, each set refilled as soon
+    // as it has been consumed, so two sub-tiles per wave stay in flight. The
+    // last pair is peeled off (no refills): every iteration of the loop then
+    // has the same loads in flight, and nothing is requested that is not
+    // used. A sub-tile wholly past the chunk end (an odd count) reads the
+    // chunk's last row and contributes nothing: its scores are masked, so its
+    // weights are 0 and the running max is kept.
+    const int n_pairs = (c1 - c0 + 2 * kT - 1) / (2 * kT);
+    int base = c0;
+    for (int pr = 1; pr < n_pairs; ++pr, base += 2 * kT) {
         process(ka, va, base);
-        if (base + kT < c1) {
-            if (base + 2 * kT < c1) gload(ka, va, base + 2 * kT);
-            process(kb, vb, base + kT);
-        }
+        gload(ka, va, base + 2 * kT);
+        process(kb, vb, base + kT);
+        gload(kb, vb, base + 3 * kT);
     }
+    process(ka, va, base);
+    process(kb, vb, base + kT);
 
     // Sum the key groups of the wave (same running max within a wave).
 #pragma unroll
