@@ -24,6 +24,20 @@ Sources (pages' titles and the part of each shader):
     window continued from ``start_pos`` and clamped to the cache length; a
     zero-length window writes zeros).
 
+Rotary position embedding (optional, ``rope``): meganeura ``attention.wgsl``
+applies a rotation hook to each loaded query element and builds each key
+element through a hook expression, but the pages give no formula. The reading
+taken here is the common rotary embedding with "rotate-half" pairing: in each
+head, element e < d/2 pairs with element e + d/2, and the pair at position p is
+turned by the angle p * theta^(-2e/d):
+
+    x'[e]       = x[e] cos(a) - x[e + d/2] sin(a)
+    x'[e + d/2] = x[e + d/2] cos(a) + x[e] sin(a)
+
+with query row i at position start_pos + i and key row j at position j. The
+rotation takes its (cos, sin) values from a table [positions, d/2, 2], so a
+caller may pass any table; ``rope_table`` builds the standard one.
+
 The scores are materialised block-of-rows by block-of-rows (rows are
 independent, so this changes no arithmetic of any row); everything is float64.
 Parity is pinned by the CPU tests (closed forms, brute force, torch's library
@@ -58,6 +72,34 @@ def window_length(mode: int, i: int, q_seq: int, kv_len: int, start_pos: int) ->
     raise ValueError(f"unknown mode {mode}")
 
 
+def rope_table(rows: int, head_dim: int, theta: float):
+    """Standard rotary table [rows, head_dim/2, 2] in float64: entry (p, e) is
+    (cos, sin) of p * theta^(-2e/head_dim)."""
+    if head_dim % 2 != 0:
+        raise ValueError("head_dim must be even")
+    half = head_dim // 2
+    inv_freq = float(theta) ** (-(2.0 * np.arange(half, dtype=np.float64)) / head_dim)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1)
+
+
+def apply_rope(x, positions, table, num_heads: int, head_dim: int):
+    """Rotate every head of the rows x [n, num_heads*head_dim], row r at
+    position positions[r], with (cos, sin) from table [*, head_dim/2, 2]
+    (rotate-half pairing). Returns float64."""
+    positions = np.asarray(positions, dtype=np.int64)
+    n = positions.shape[0]
+    half = head_dim // 2
+    xh = np.asarray(x, dtype=np.float64).reshape(n, num_heads, head_dim)
+    t = np.asarray(table, dtype=np.float64)[positions]  # [n, half, 2]
+    c = t[:, None, :, 0]
+    s = t[:, None, :, 1]
+    lo = xh[..., :half]
+    hi = xh[..., half:]
+    out = np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+    return out.reshape(n, num_heads * head_dim)
+
+
 def _check_shapes(q, k, v, num_heads, num_kv_heads, head_dim, kv_len):
     if num_heads % num_kv_heads != 0:
         raise ValueError("num_heads must be a multiple of num_kv_heads")
@@ -71,13 +113,15 @@ def _check_shapes(q, k, v, num_heads, num_kv_heads, head_dim, kv_len):
 
 def attention_forward(q, k, v, *, num_heads: int, num_kv_heads: int, head_dim: int,
                       mode: int, kv_len: int, start_pos: int = 0, scale: float,
-                      rows=None, row_block: int = 256):
+                      rows=None, row_block: int = 256, rope=None):
     """Attention forward in float64 for the query rows ``rows`` (default: all).
 
     q: [q_seq, num_heads*head_dim]; k, v: [>= kv_len, num_kv_heads*head_dim].
     Returns (out [n_rows, num_heads*head_dim], lse [n_rows, num_heads, 2]),
     both float64; lse[..., 0] is the row max and lse[..., 1] the log of the
     sum of exp(score - max), the pair meganeura attention.wgsl stores.
+    rope: optional rotary table [positions, head_dim/2, 2]; query row i is
+    rotated at position start_pos + i, key row j at position j.
     """
     _check_shapes(q, k, v, num_heads, num_kv_heads, head_dim, kv_len)
     q_seq = q.shape[0]
@@ -95,6 +139,13 @@ def attention_forward(q, k, v, *, num_heads: int, num_kv_heads: int, head_dim: i
     win = np.array([window_length(mode, int(i), q_seq, kv_len, start_pos) for i in rows],
                    dtype=np.int64)
 
+    if rope is not None:
+        q = apply_rope(q[rows], start_pos + rows, rope, num_heads, d)
+        rows_in_q = np.arange(n)  # q now holds exactly the selected rows
+        k = apply_rope(k[:kv_len], np.arange(kv_len), rope, num_kv_heads, d)
+    else:
+        rows_in_q = rows
+
     for h in range(num_heads):
         kvh = h // group  # GQA: contiguous groups of query heads share a KV head
         qh = q[:, h * d:(h + 1) * d]
@@ -102,7 +153,7 @@ def attention_forward(q, k, v, *, num_heads: int, num_kv_heads: int, head_dim: i
         vh = v[:, kvh * d:(kvh + 1) * d]
         for b0 in range(0, n, row_block):
             sel = slice(b0, min(b0 + row_block, n))
-            r = rows[sel]
+            r = rows_in_q[sel]
             w = win[sel]
             wmax = int(w.max()) if w.size else 0
             if wmax == 0:

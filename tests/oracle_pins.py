@@ -357,4 +357,137 @@ def pin_row_subset(orc):
     _close(a[1][rows], b[1], 0.0, "subset lse")
 
 
+# ------------------------------------------------------ rotary embedding (RoPE)
+# The rotation the checker reads into the pages' rotary hooks: rotate-half
+# pairing (e with e + d/2), angle p * theta^(-2e/d). The pins below restate it
+# in other forms: complex multiplication, unit-vector probes, the 2-D rotation
+# matrix, scalar loops, and the relative-position property of rotary scores.
+
+def _complex_rotate(x, positions, H, d, theta):
+    """x [n, H*d] rotated as complex numbers z_e = x_e + i x_{e+d/2} times
+    exp(i p w_e), w_e = 1 / theta^(2e/d)."""
+    half = d // 2
+    w = 1.0 / np.power(float(theta), np.arange(0, d, 2, dtype=np.float64) / d)
+    xh = np.asarray(x, dtype=np.float64).reshape(len(positions), H, d)
+    z = xh[..., :half] + 1j * xh[..., half:]
+    z = z * np.exp(1j * np.asarray(positions, dtype=np.float64)[:, None, None] * w[None, None, :])
+    return np.concatenate([z.real, z.imag], axis=-1).reshape(len(positions), H * d)
+
+
+def pin_rope_complex_form(orc):
+    """The table-driven rotation equals multiplication by exp(i p w_e)."""
+    for theta, d in ((10000.0, 8), (500.0, 16), (1e6, 4)):
+        H, n = 3, 11
+        x = _rand((n, H * d), 301)
+        pos = np.random.default_rng(302).integers(0, 70, size=n)
+        got = orc.apply_rope(x, pos, orc.rope_table(70, d, theta), H, d)
+        _close(got, _complex_rotate(x, pos, H, d, theta), 1e-12, f"rope complex theta={theta}")
+
+
+def pin_rope_unit_vectors(orc):
+    """Basis vector e_k (k < d/2) at position p turns into cos(a) e_k +
+    sin(a) e_{k+d/2}; e_{k+d/2} into -sin(a) e_k + cos(a) e_{k+d/2};
+    a = p * theta^(-2k/d)."""
+    d, theta, p = 8, 10000.0, 37
+    table = orc.rope_table(p + 1, d, theta)
+    for k in range(d // 2):
+        a = p * math.pow(theta, -2.0 * k / d)
+        lo = np.zeros((1, d))
+        lo[0, k] = 1.0
+        want = np.zeros((1, d))
+        want[0, k], want[0, k + d // 2] = math.cos(a), math.sin(a)
+        _close(orc.apply_rope(lo, [p], table, 1, d), want, 1e-14, f"e_{k}")
+        hi = np.zeros((1, d))
+        hi[0, k + d // 2] = 1.0
+        want = np.zeros((1, d))
+        want[0, k], want[0, k + d // 2] = -math.sin(a), math.cos(a)
+        _close(orc.apply_rope(hi, [p], table, 1, d), want, 1e-14, f"e_{k + d // 2}")
+
+
+def pin_rope_position_zero_is_identity(orc):
+    x = _rand((4, 2 * 8), 303)
+    t = orc.rope_table(1, 8, 10000.0)
+    _close(t[0, :, 0], np.ones(4), 0.0, "cos at 0")
+    _close(t[0, :, 1], np.zeros(4), 0.0, "sin at 0")
+    _close(orc.apply_rope(x, [0, 0, 0, 0], t, 2, 8), x, 0.0, "rotation at 0")
+
+
+def pin_rope_head_dim_two_is_plane_rotation(orc):
+    """d = 2: one pair with frequency theta^0 = 1, i.e. the plane rotation by
+    p radians."""
+    x = _rand((5, 2), 304).astype(np.float64)
+    pos = np.array([0, 1, 2, 7, 100])
+    got = orc.apply_rope(x, pos, orc.rope_table(101, 2, 123.0), 1, 2)
+    for r, p in enumerate(pos):
+        c, s_ = math.cos(p), math.sin(p)
+        want = [c * x[r, 0] - s_ * x[r, 1], s_ * x[r, 0] + c * x[r, 1]]
+        _close(got[r], want, 1e-14, f"plane rotation p={p}")
+
+
+def pin_rope_relative_position(orc):
+    """Rotary scores depend on positions only through their difference, and
+    <R(m) q, R(n) k> = <q, R(n - m) k>; each pair keeps its norm."""
+    d, H, theta = 16, 2, 10000.0
+    table = orc.rope_table(200, d, theta)
+    q, k = _rand((1, H * d), 305), _rand((1, H * d), 306)
+    def dot(m, n, qq=q):
+        a = orc.apply_rope(qq, [m], table, H, d).reshape(H, d)
+        b = orc.apply_rope(k, [n], table, H, d).reshape(H, d)
+        return (a * b).sum(axis=1)
+    for m, n, c in ((3, 10, 50), (0, 0, 120), (40, 5, 7)):
+        _close(dot(m, n), dot(m + c, n + c), 1e-11, f"shift m={m} n={n}")
+    for m, n in ((3, 10), (20, 20), (2, 150)):
+        _close(dot(m, n), dot(0, n - m), 1e-11, f"difference m={m} n={n}")
+    r = orc.apply_rope(q, [77], table, H, d).reshape(H, 2, d // 2)
+    x = np.asarray(q, np.float64).reshape(H, 2, d // 2)
+    _close((r ** 2).sum(axis=1), (x ** 2).sum(axis=1), 1e-12, "pair norms")
+
+
+def pin_rope_attention_positions(orc):
+    """Attention with rotation equals plain attention on inputs turned by the
+    complex form: query row i at start_pos + i, key row j at j, every head
+    (GQA) rotated, for a causal continuation and a cross pass over a subset of
+    rows."""
+    H, Hkv, d, theta = 4, 2, 8, 10000.0
+    q_seq, kv_len, start = 5, 9, 4
+    q, k, v = _rand((q_seq, H * d), 307), _rand((kv_len + 2, Hkv * d), 308), _rand((kv_len + 2, Hkv * d), 309)
+    table = orc.rope_table(kv_len + 2, d, theta)
+    qr = _complex_rotate(q, start + np.arange(q_seq), H, d, theta)
+    kr = _complex_rotate(k, np.arange(kv_len + 2), Hkv, d, theta)
+    for mode, sp, rows in ((CAUSAL, start, None), (CROSS, 0, np.array([4, 1]))):
+        a = orc.attention_forward(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=mode,
+                                  kv_len=kv_len, start_pos=sp, scale=0.3, rows=rows, rope=table)
+        qq = qr if mode == CAUSAL else _complex_rotate(q, np.arange(q_seq), H, d, theta)
+        b = orc.attention_forward(qq, kr, v, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=mode,
+                                  kv_len=kv_len, start_pos=sp, scale=0.3, rows=rows)
+        _close(a[0], b[0], 1e-12, f"rope attention out mode={mode}")
+        _close(a[1], b[1], 1e-12, f"rope attention lse mode={mode}")
+
+
+def pin_rope_brute_force_tiny(orc):
+    """Scalar loops: rotate with math.cos / math.sin of p * theta^(-2e/d),
+    then the brute-force attention."""
+    H, Hkv, d, theta, q_seq, kv_len, start = 2, 1, 4, 50.0, 3, 5, 2
+    q, k, v = _rand((q_seq, H * d), 310), _rand((kv_len, Hkv * d), 311), _rand((kv_len, Hkv * d), 312)
+    def rot(x, nheads, pos_of):
+        y = np.array(x, dtype=np.float64)
+        for r in range(x.shape[0]):
+            p = pos_of(r)
+            for h in range(nheads):
+                for e in range(d // 2):
+                    a = p * math.pow(theta, -2.0 * e / d)
+                    x0, x1 = float(x[r, h * d + e]), float(x[r, h * d + e + d // 2])
+                    y[r, h * d + e] = x0 * math.cos(a) - x1 * math.sin(a)
+                    y[r, h * d + e + d // 2] = x1 * math.cos(a) + x0 * math.sin(a)
+        return y
+    qr = rot(q, H, lambda r: start + r)
+    kr = rot(k, Hkv, lambda r: r)
+    want = _brute(qr, kr, v, H, Hkv, d, CAUSAL, kv_len, start, 0.5)
+    got = orc.attention_forward(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=CAUSAL,
+                                kv_len=kv_len, start_pos=start, scale=0.5,
+                                rope=orc.rope_table(kv_len, d, theta))
+    _close(got[0], want[0], 1e-12, "rope brute out")
+    _close(got[1], want[1], 1e-12, "rope brute lse")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

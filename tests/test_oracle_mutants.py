@@ -29,6 +29,18 @@ MUTANTS = {
     "decode_gqa_modulo": ("        kvh = h // group\n        qv", "        kvh = h % num_kv_heads\n        qv"),
     "decode_no_scale": ("s = scale * (kw @ qv)", "s = (kw @ qv)"),
     "q_head_offset": ("qh = q[:, h * d:(h + 1) * d]", "qh = q[:, kvh * d:(kvh + 1) * d]"),
+    "rope_sign_flip": ("lo * c - hi * s, hi * c + lo * s", "lo * c + hi * s, hi * c - lo * s"),
+    "rope_interleaved_pairing": ("lo = xh[..., :half]\n    hi = xh[..., half:]",
+                                 "lo = xh[..., 0::2]\n    hi = xh[..., 1::2]"),
+    "rope_frequency_exponent": ("(-(2.0 * np.arange(half, dtype=np.float64)) / head_dim)",
+                                "(-(np.arange(half, dtype=np.float64)) / head_dim)"),
+    "rope_cos_sin_swapped": ("np.stack([np.cos(ang), np.sin(ang)], axis=-1)",
+                             "np.stack([np.sin(ang), np.cos(ang)], axis=-1)"),
+    "rope_query_position_no_start": ("apply_rope(q[rows], start_pos + rows,",
+                                     "apply_rope(q[rows], rows,"),
+    "rope_key_position_shift": ("np.arange(kv_len), rope, num_kv_heads",
+                                "np.arange(kv_len) // 2, rope, num_kv_heads"),
+    "rope_keys_unrotated": ("        k = apply_rope(k[:kv_len]", "        k = 1.0 * (k[:kv_len]"),
 }
 
 
