@@ -91,10 +91,12 @@ def time_calls(fn, n, torch):
     return float(np.mean(durs)), float(np.min(durs)), wall
 
 
-def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0):
+def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None):
     """Prefill timing. With graph_replays > 0 the call is captured once in a
     HIP graph and replayed back to back (for kernels shorter than a Python
-    launch); otherwise each call is launched eagerly between events."""
+    launch); otherwise each call is launched eagerly between events. With
+    rope_theta the rotary entry point runs (table built once, outside the
+    timed calls; the rotation is not counted in the FLOPs)."""
     dev = torch.device("cuda:0")
     q, k, v = inputs.make_prefill(w)
     qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
@@ -103,9 +105,20 @@ def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0):
     out = torch.empty((w.q_seq, qdim), device=dev)
     lse = torch.empty((w.q_seq, w.num_heads, 2), device=dev) if w.with_lse else None
 
-    def call(_i):
-        ta.attn_fwd(qd, kd, vd, out, lse, w.q_seq, w.kv_len, w.num_heads, w.num_kv_heads,
-                    w.head_dim, w.mode, w.start_pos, w.scale)
+    if rope_theta is None:
+        def call(_i):
+            ta.attn_fwd(qd, kd, vd, out, lse, w.q_seq, w.kv_len, w.num_heads, w.num_kv_heads,
+                        w.head_dim, w.mode, w.start_pos, w.scale)
+    else:
+        rows = max(w.start_pos + w.q_seq, w.kv_len)
+        table = torch.empty((rows, w.head_dim // 2, 2), device=dev)
+        ta.attn_rope_table(table, rows, w.head_dim, rope_theta)
+        kvdim = w.num_kv_heads * w.head_dim
+
+        def call(_i):
+            ta.attn_fwd_rope(qd, qdim, kd, kvdim, vd, kvdim, out, qdim, lse, 0, w.q_seq,
+                             w.kv_len, w.num_heads, w.num_kv_heads, w.head_dim, w.mode,
+                             w.start_pos, w.scale, table, rows)
 
     flops = prefill_flops(w)
     if graph_replays > 0:
@@ -329,7 +342,7 @@ def main():
                          "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(p["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
                          "traffic": stored_traffic(PREFILL_TRAFFIC),
-                         "kernel": "prefill_kernel<128>",
+                         "kernel": "prefill_kernel<128, false>",
                          "kernel_ms_mean": round(p["mean_s"] * 1e3, 3),
                          "kernel_ms_min": round(p["min_s"] * 1e3, 3)},
         })
@@ -344,6 +357,13 @@ def main():
                                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4)}
                 print(f"[bench] {wr.name}: {rep[wr.name]}", flush=True)
             result["prefill_reported"] = rep
+            r = bench_prefill(w, 3, 1, torch, ta, rope_theta=10000.0)
+            result["prefill_rope"] = {
+                "workload": w.name + "_rope_theta10000",
+                "ms": round(r["mean_s"] * 1e3, 3), "TFLOP/s": round(r["tflops_kernel"], 3),
+                "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
+                "kernel": "prefill_kernel<128, true>"}
+            print(f"[bench] rotary {result['prefill_rope']}", flush=True)
 
     if args.only != "prefill":
         wd = inputs.DECODE_8K

@@ -123,6 +123,51 @@ int attn_fwd_ex(const float* q, long long q_stride, const float* k, long long k_
                 hipStream_t stream);
 
 /*
+ * attn_fwd_rope -- attn_fwd_ex with a rotary position embedding applied to
+ * the queries and keys as the kernel loads them. meganeura attention.wgsl
+ * (main) routes each loaded query element through a rotation hook and builds
+ * each key element through a hook expression, but the page gives no formula;
+ * the rotation read into those hooks is the rotate-half form: in every head,
+ * element e < head_dim/2 pairs with element e + head_dim/2 and, at position p,
+ *     x'[e]       = x[e] * cos - x[e + head_dim/2] * sin
+ *     x'[e + d/2] = x[e + d/2] * cos + x[e] * sin
+ * with (cos, sin) = rope_cs[p][e]. The query of global row q_base + i sits at
+ * position start_pos + q_base + i (start_pos is 0 outside causal mode), key
+ * row j at position j. q and k are not modified.
+ *
+ *   rope_cs    device, [rope_rows, head_dim/2, 2] floats, 16-byte aligned:
+ *              the (cos, sin) pair of every (position, pair); attn_rope_table
+ *              fills the standard table, any other table is used as given
+ *   rope_rows  rows of rope_cs; must cover every position used:
+ *              >= max(start_pos + q_base + q_seq, kv_len)
+ *
+ * Errors as attn_fwd_ex, plus TA03_ERR_NULL for a NULL rope_cs,
+ * TA03_ERR_ALIGN for a misaligned one, TA03_ERR_SHAPE for too few rope_rows
+ * (q_seq > 0), TA03_ERR_UNSUPPORTED for rope_rows * head_dim >= 2^31.
+ */
+int attn_fwd_rope(const float* q, long long q_stride, const float* k, long long k_stride,
+                  const float* v, long long v_stride, float* out, long long out_stride,
+                  float* lse, int q_base, int q_seq, int kv_len, int num_heads,
+                  int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+                  const float* rope_cs, int rope_rows, hipStream_t stream);
+
+/*
+ * attn_rope_table -- fill the standard rotary table for attn_fwd_rope:
+ * cos_sin[p][e] = (cos(a), sin(a)), a = p * theta^(-2e/head_dim), for
+ * p < rows and e < head_dim/2 (the frequencies of the common rotary
+ * embedding; the pages name no base, theta is the caller's, e.g. 10000).
+ * Each angle and its cosine and sine are computed in double precision and
+ * rounded once to float.
+ *
+ *   cos_sin   device, rows * head_dim floats, 16-byte aligned, written in full
+ *
+ * Errors: TA03_ERR_SHAPE for rows < 0, head_dim < 2 or odd, theta not
+ * finite and positive; TA03_ERR_UNSUPPORTED for rows * head_dim >= 2^31;
+ * TA03_ERR_NULL; TA03_ERR_ALIGN; TA03_ERR_HIP. rows == 0 is a no-op.
+ */
+int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStream_t stream);
+
+/*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
  * for these sizes: split-KV partial results (per query head and split, an
  * unnormalised output row plus its max and sum) and one completion counter

@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_decode", "attn_decode_paged",
                                     "attn_decode_workspace_bytes",
                                     "attn_decode_workspace_init", "attn_fwd", "attn_fwd_ex",
-                                    "attn_strerror"]
+                                    "attn_fwd_rope", "attn_rope_table", "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -111,6 +111,45 @@ def fwd_ex(lib, q=A, qs=None, k=B, ks=None, v=C, vs=None, out=O, os_=None, lse=N
 ])
 def test_attn_fwd_ex_rejects_on_host(lib, kw, status):
     assert fwd_ex(lib, **kw) == status
+
+
+def fwd_rope(lib, cs=O + 0x8000, rope_rows=64, q_base=0, q_seq=4, kv_len=8, H=4, Hkv=2, d=64,
+             mode=0, sp=0, q=A, lse=None):
+    return lib.attn_fwd_rope(q, H * d, B, Hkv * d, C, Hkv * d, O, H * d, lse, q_base, q_seq,
+                             kv_len, H, Hkv, d, mode, sp, 0.125, cs, rope_rows, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cs=None), ERR_NULL),
+    (dict(cs=O + 0x8008), ERR_ALIGN),
+    (dict(rope_rows=7), ERR_SHAPE),                     # keys 0..7 need 8 positions
+    (dict(sp=2, q_seq=4, kv_len=8, rope_rows=7), ERR_SHAPE),
+    (dict(mode=2, q_base=10, q_seq=4, kv_len=3, rope_rows=13), ERR_SHAPE),  # rows up to 13
+    (dict(rope_rows=-1), ERR_SHAPE),
+    (dict(rope_rows=1 << 26, d=64), ERR_UNSUP),         # table of 2^32 floats
+    (dict(d=96), ERR_UNSUP),
+    (dict(H=3, Hkv=2), ERR_SHAPE),
+    (dict(q=None), ERR_NULL),
+    (dict(q_seq=0, cs=None), OK),                       # empty batch: nothing read
+])
+def test_attn_fwd_rope_rejects_on_host(lib, kw, status):
+    assert fwd_rope(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((O, -1, 64, 10000.0), ERR_SHAPE),
+    ((O, 8, 63, 10000.0), ERR_SHAPE),
+    ((O, 8, 0, 10000.0), ERR_SHAPE),
+    ((O, 8, 64, 0.0), ERR_SHAPE),
+    ((O, 8, 64, float("inf")), ERR_SHAPE),
+    ((O, 8, 64, float("nan")), ERR_SHAPE),
+    ((O, 1 << 25, 64, 10000.0), ERR_UNSUP),
+    ((None, 8, 64, 10000.0), ERR_NULL),
+    ((O + 8, 8, 64, 10000.0), ERR_ALIGN),
+    ((None, 0, 64, 10000.0), OK),
+])
+def test_attn_rope_table_rejects_on_host(lib, args, status):
+    assert lib.attn_rope_table(*args, None) == status
 
 
 def test_validation_order_sizes_before_pointers(lib):

@@ -1,0 +1,189 @@
+"""Rotary prefill parity: attn_fwd_rope and attn_rope_table through the C ABI
+against the float64 checker. Each side builds its own table from theta (the
+library on the device, the checker in float64) unless a test hands both the
+same arbitrary table."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import check_lse, check_out, device, log, to_dev
+from tiled_attention_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+CAUSAL, FULL, CROSS = inputs.CAUSAL, inputs.FULL, inputs.CROSS
+THETA = 10000.0
+
+
+def gpu_table(rows, head_dim, theta):
+    import torch
+    import tiled_attention_03_amd as ta
+    t = torch.full((rows, head_dim // 2, 2), float("nan"), dtype=torch.float32, device=device())
+    ta.attn_rope_table(t, rows, head_dim, theta)
+    torch.cuda.synchronize()
+    return t
+
+
+def gpu_rope(q, k, v, table, *, num_heads, num_kv_heads, head_dim, mode, kv_len, start_pos,
+             scale, with_lse=True):
+    """attn_fwd_rope over dense rows; table is a GPU tensor [rows, d/2, 2]."""
+    import torch
+    import tiled_attention_03_amd as ta
+    dev = device()
+    H, Hkv, d = num_heads, num_kv_heads, head_dim
+    n = q.shape[0]
+    out = torch.full((n, H * d), float("nan"), device=dev)
+    lse = torch.full((n, H, 2), float("nan"), device=dev) if with_lse else None
+    ta.attn_fwd_rope(to_dev(q), H * d, to_dev(k), Hkv * d, to_dev(v), Hkv * d, out, H * d, lse,
+                     0, n, kv_len, H, Hkv, d, mode, start_pos, scale, table, table.shape[0])
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (lse.cpu().numpy() if lse is not None else None)
+
+
+def oracle_rope(q, k, v, table, *, num_heads, num_kv_heads, head_dim, mode, kv_len, start_pos,
+                scale, rows=None):
+    return oracle.attention_forward(q, k, v, num_heads=num_heads, num_kv_heads=num_kv_heads,
+                                    head_dim=head_dim, mode=mode, kv_len=kv_len,
+                                    start_pos=start_pos, scale=scale, rows=rows, rope=table)
+
+
+def _kw(w):
+    return dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                mode=w.mode, kv_len=w.kv_len, start_pos=w.start_pos, scale=w.scale)
+
+
+def _table_rows(w):
+    return max(w.start_pos + w.q_seq, w.kv_len)
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("theta", [10000.0, 500.0, 1e6])
+def test_rope_table_matches_checker(head_dim, theta):
+    """Device table (double precision, rounded once) against the checker's
+    float64 table: within one float32 step of values in [-1, 1]."""
+    rows = 16384
+    got = gpu_table(rows, head_dim, theta).cpu().numpy().astype(np.float64)
+    ref = oracle.rope_table(rows, head_dim, theta)
+    err = np.abs(got - ref).max()
+    log(f"rope table d={head_dim} theta={theta}: max err {err:.2e}")
+    assert np.all(np.isfinite(got))
+    assert err <= 1.2e-7, err  # one float32 step at 1
+
+
+@pytest.mark.parametrize("w", [inputs.CAUSAL_SMALL, inputs.FULL_1K, inputs.CROSS_512x2K,
+                               inputs.CONTINUE_512], ids=lambda w: w.name)
+def test_rope_pages_workloads(w):
+    log(f"rope prefill parity {w.name}")
+    q, k, v = inputs.make_prefill(w)
+    rows = _table_rows(w)
+    go, gl = gpu_rope(q, k, v, gpu_table(rows, w.head_dim, THETA), **_kw(w))
+    ro, rl = oracle_rope(q, k, v, oracle.rope_table(rows, w.head_dim, THETA), **_kw(w))
+    e_o = check_out(go, ro, w.name)
+    e_l = check_lse(gl, rl, w.name)
+    log(f"  max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
+
+
+def test_rope_long_causal_sampled_rows():
+    """The 16384-row causal pass with heavy K rows and rotation: sampled rows
+    (angles up to 16383 radians in the first pair)."""
+    w = inputs.CAUSAL_16K
+    log(f"rope prefill parity (sampled rows) {w.name}")
+    q, k, v = inputs.make_prefill(w)
+    rng = np.random.default_rng(6099)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 4095, 8192, 16351, 16383],
+                                     rng.choice(w.q_seq, 12, replace=False)]))
+    go, gl = gpu_rope(q, k, v, gpu_table(w.kv_len, w.head_dim, THETA), **_kw(w))
+    ro, rl = oracle_rope(q, k, v, oracle.rope_table(w.kv_len, w.head_dim, THETA), rows=rows,
+                         **_kw(w))
+    e_o = check_out(go[rows], ro, w.name)
+    e_l = check_lse(gl[rows], rl, w.name)
+    log(f"  rows={len(rows)} max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
+
+
+RAGGED = [
+    # mode, q_seq, kv_len, H, Hkv, d, start_pos
+    (CAUSAL, 77, 77, 6, 2, 64, 0),
+    (CAUSAL, 33, 200, 4, 4, 64, 50),
+    (CAUSAL, 129, 129, 8, 2, 128, 0),
+    (CROSS, 40, 301, 8, 8, 128, 0),
+    (FULL, 130, 130, 4, 1, 128, 0),
+    (CROSS, 1, 5, 2, 1, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "m{}_q{}_kv{}_h{}kv{}_d{}_s{}".format(*c))
+def test_rope_arbitrary_table(case):
+    """Any (cos, sin) table is applied as given: a seeded table of arbitrary
+    values, the same on both sides, over ragged shapes (several tiles and a
+    tail). Arbitrary values make every index of the table count."""
+    mode, n, kv, H, Hkv, d, sp = case
+    w, q, k, v = inputs.random_case(900 + n + kv, mode, n, kv, H, Hkv, d, start_pos=sp)
+    rows = max(sp + n, kv) + 3
+    table = 0.7 * inputs.normal((rows, d // 2, 2), 901 + n)
+    go, gl = gpu_rope(q, k, v, to_dev(table), **_kw(w))
+    ro, rl = oracle_rope(q, k, v, table, **_kw(w))
+    check_out(go, ro, f"arbitrary table {case}")
+    check_lse(gl, rl, f"arbitrary table lse {case}")
+
+
+def test_rope_identity_table_is_plain_attention():
+    """cos = 1, sin = 0 everywhere: the plain attention."""
+    w, q, k, v = inputs.random_case(950, CAUSAL, 100, 100, 8, 2, 128)
+    table = np.zeros((100, 64, 2), np.float32)
+    table[..., 0] = 1.0
+    go, gl = gpu_rope(q, k, v, to_dev(table), **_kw(w))
+    ro, rl = oracle.attention_forward(q, k, v, **_kw(w))
+    check_out(go, ro, "identity table")
+    check_lse(gl, rl, "identity table lse")
+
+
+@pytest.mark.parametrize("mode,sp", [(CAUSAL, 37), (CROSS, 0)])
+def test_rope_strided_sub_batches(mode, sp):
+    """Fused QKV buffer (strided rows) split into q_base sub-batches: row
+    q_base + i is turned at position start_pos + q_base + i."""
+    import torch
+    import tiled_attention_03_amd as ta
+    H, Hkv, d, n = 4, 2, 64, 150
+    kv = n + sp if mode == CAUSAL else n
+    width = (H + 2 * Hkv) * d
+    qkv = inputs.normal((kv, width), 960 + mode)
+    q = np.ascontiguousarray(qkv[:n, :H * d])
+    k = np.ascontiguousarray(qkv[:, H * d:(H + Hkv) * d])
+    v = np.ascontiguousarray(qkv[:, (H + Hkv) * d:])
+    dev = device()
+    qkv_d = to_dev(qkv)
+    out = torch.full((n, H * d), float("nan"), device=dev)
+    lse = torch.full((n, H, 2), float("nan"), device=dev)
+    rows = max(sp + n, kv)
+    table = gpu_table(rows, d, THETA)
+    scale = d ** -0.5
+    for base, cnt in ((0, 50), (50, 64), (114, 36)):
+        ta.attn_fwd_rope(qkv_d[:, :H * d], width, qkv_d[:, H * d:], width,
+                         qkv_d[:, (H + Hkv) * d:], width, out, H * d, lse, base, cnt, kv, H, Hkv,
+                         d, mode, sp, scale, table, rows)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d,
+                                      mode=mode, kv_len=kv, start_pos=sp, scale=scale,
+                                      rope=oracle.rope_table(rows, d, THETA))
+    check_out(out.cpu().numpy(), ro, f"rope sub-batches mode={mode}")
+    check_lse(lse.cpu().numpy(), rl, f"rope sub-batches lse mode={mode}")
+
+
+def test_rope_empty_key_range():
+    """kv_len = 0 (cross): zero rows and the empty-window sentinel."""
+    H, Hkv, d, n = 4, 2, 64, 5
+    q = inputs.normal((n, H * d), 970)
+    k = np.zeros((1, Hkv * d), np.float32)
+    go, gl = gpu_rope(q, k, k, gpu_table(n, d, THETA), num_heads=H, num_kv_heads=Hkv,
+                      head_dim=d, mode=CROSS, kv_len=0, start_pos=0, scale=0.125)
+    assert np.array_equal(go, np.zeros_like(go))
+    assert np.all(gl == oracle.EMPTY_SENTINEL)
+
+
+def test_rope_deterministic():
+    w, q, k, v = inputs.random_case(980, CAUSAL, 300, 300, 8, 2, 128)
+    t = gpu_table(300, 128, THETA)
+    a = gpu_rope(q, k, v, t, **_kw(w))
+    b = gpu_rope(q, k, v, t, **_kw(w))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -6,11 +6,9 @@ its input generators) needs no GPU and no built library.
 """
 
 from .binding import (CAUSAL, CROSS, FULL, Ta03Error, attention, attn_decode,
-                      attn_decode_paged,
-                      attn_decode_workspace_bytes, attn_decode_workspace_init, attn_fwd,
-                      attn_fwd_ex,
-                      attn_strerror, lib)
+                      attn_decode_paged, attn_decode_workspace_bytes, attn_decode_workspace_init,
+                      attn_fwd, attn_fwd_ex, attn_fwd_rope, attn_rope_table, attn_strerror, lib)
 
 __all__ = ["CAUSAL", "FULL", "CROSS", "Ta03Error", "attention", "attn_fwd", "attn_fwd_ex",
-           "attn_decode", "attn_decode_paged", "attn_decode_workspace_bytes", "attn_decode_workspace_init", "attn_strerror",
-           "lib"]
+           "attn_fwd_rope", "attn_rope_table", "attn_decode", "attn_decode_paged",
+           "attn_decode_workspace_bytes", "attn_decode_workspace_init", "attn_strerror", "lib"]

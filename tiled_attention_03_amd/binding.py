@@ -46,6 +46,11 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd.restype = I
         L.attn_fwd_ex.argtypes = [P, LL, P, LL, P, LL, P, LL, P, I, I, I, I, I, I, I, I, F, P]
         L.attn_fwd_ex.restype = I
+        L.attn_fwd_rope.argtypes = [P, LL, P, LL, P, LL, P, LL, P, I, I, I, I, I, I, I, I, F,
+                                    P, I, P]
+        L.attn_fwd_rope.restype = I
+        L.attn_rope_table.argtypes = [P, I, I, ctypes.c_double, P]
+        L.attn_rope_table.restype = I
         L.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
         L.attn_decode_workspace_bytes.restype = S
         L.attn_decode_workspace_init.argtypes = [P, S, I, I, I, I, P]
@@ -150,6 +155,35 @@ def attn_fwd_ex(q, q_stride: int, k, k_stride: int, v, v_stride: int, out, out_s
         _ptr(lse, rows * num_heads * 2, "lse"), q_base, q_seq, kv_len, num_heads,
         num_kv_heads, head_dim, mode, start_pos, float(scale), _stream(stream))
     _check(status)
+
+
+def attn_fwd_rope(q, q_stride: int, k, k_stride: int, v, v_stride: int, out, out_stride: int,
+                  lse, q_base: int, q_seq: int, kv_len: int, num_heads: int, num_kv_heads: int,
+                  head_dim: int, mode: int, start_pos: int, scale: float, rope_cs,
+                  rope_rows: int, stream=None) -> None:
+    """Enqueue attn_fwd_ex with the rotary embedding turned into q and k at
+    load time (see include/ta03.h); rope_cs is a [rope_rows, head_dim/2, 2]
+    float32 GPU tensor of (cos, sin) pairs."""
+    qd, kvd = num_heads * head_dim, num_kv_heads * head_dim
+    rows = q_base + q_seq
+    kv_rows = kv_len if mode != CAUSAL else min(kv_len, start_pos + rows)
+    def ext(n, stride, width):
+        return (n - 1) * stride + width if n > 0 else 0
+    status = lib().attn_fwd_rope(
+        _strided_ptr(q, ext(rows, q_stride, qd), "q"), int(q_stride),
+        _strided_ptr(k, ext(kv_rows, k_stride, kvd), "k"), int(k_stride),
+        _strided_ptr(v, ext(kv_rows, v_stride, kvd), "v"), int(v_stride),
+        _strided_ptr(out, ext(rows, out_stride, qd), "out"), int(out_stride),
+        _ptr(lse, rows * num_heads * 2, "lse"), q_base, q_seq, kv_len, num_heads,
+        num_kv_heads, head_dim, mode, start_pos, float(scale),
+        _ptr(rope_cs, max(rope_rows, 0) * head_dim, "rope_cs"), int(rope_rows), _stream(stream))
+    _check(status)
+
+
+def attn_rope_table(cos_sin, rows: int, head_dim: int, theta: float, stream=None) -> None:
+    """Enqueue the fill of a standard rotary table [rows, head_dim/2, 2]."""
+    _check(lib().attn_rope_table(_ptr(cos_sin, max(rows, 0) * head_dim, "cos_sin"), int(rows),
+                                 int(head_dim), float(theta), _stream(stream)))
 
 
 def attn_decode_workspace_bytes(num_heads: int, num_kv_heads: int, head_dim: int,

@@ -35,7 +35,15 @@
 //   * exp is exp2 with log2(e) folded into the pre-scaled Q;
 //   * causal: key tiles past a block's last window are never loaded, tiles
 //     inside every row's window skip the mask, and blocks are issued
-//     heaviest-first.
+//     heaviest-first;
+//   * rotary embedding (a separate template instance): meganeura
+//     attention.wgsl turns each query and key element through hooks as it
+//     loads them, without giving the rotation. Here it is the rotate-half
+//     form, angle p * theta^(-2e/d) from a (cos, sin) table: the query is
+//     turned in registers right after loading (element e and its partner
+//     e + d/2 sit in the same lane of the operand layout); keys go HBM ->
+//     registers -> turned -> LDS, one tile ahead of their use, while V keeps
+//     the direct path.
 
 #include <hip/hip_runtime.h>
 
@@ -71,6 +79,7 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 struct Args {
+    const float* rope_cs;  // rotary (cos, sin) table [positions][D/2][2] (rotary instance)
     int q_seq, kv_len, num_heads, num_kv_heads, group;
     int causal, start_pos;
     float qscale;  // scale * log2(e)
@@ -81,7 +90,12 @@ struct Args {
     int n_head_blocks, n_row_blocks;
 };
 
+// Rotary instance: most chunk-pair load instructions one wave issues per key
+// tile (the host keeps the key splits low enough for this).
 template <int D>
+constexpr int rope_rmax() { return D == 128 ? 2 : 4; }
+
+template <int D, bool ROPE>
 __global__ void __launch_bounds__(kBlock, 2)
 prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                const float* __restrict__ v, float* __restrict__ out,
@@ -91,6 +105,9 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     constexpr int TILE_F = kBN * D;           // floats per K (or V) tile
     constexpr int TILE_CHUNKS = TILE_F / 4;   // 16-byte chunks per tile
     constexpr int LOADS = TILE_CHUNKS / 64;   // wave load instructions per tile
+    constexpr int HC = CPR / 2;               // 16-byte chunks per half row
+    constexpr int RP_INST = kBN * HC / 64;    // rotary: chunk-pair instructions per K tile
+    constexpr int RMAX = rope_rmax<D>();
     extern __shared__ __attribute__((aligned(16))) float smem[];
 
     const int tid = threadIdx.x;
@@ -147,6 +164,26 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             qr[4 * g + 2] = x.z * a.qscale;
             qr[4 * g + 3] = x.w * a.qscale;
         }
+        if constexpr (ROPE) {
+            // Element e = 8g + 4hh + c (register 4g + c) pairs with e + D/2
+            // (register 4(g + D/16) + c); the row sits at start_pos + row.
+            if (ok) {
+                const float* cs = a.rope_cs + (size_t)(a.start_pos + row) * D + 8 * hh;
+#pragma unroll
+                for (int g = 0; g < D / 16; ++g) {
+                    const float4 c0 = *reinterpret_cast<const float4*>(cs + 16 * g);
+                    const float4 c1 = *reinterpret_cast<const float4*>(cs + 16 * g + 4);
+                    const float cw[4] = {c0.x, c0.z, c1.x, c1.z};
+                    const float sw[4] = {c0.y, c0.w, c1.y, c1.w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float x = qr[4 * g + c], y = qr[4 * (g + D / 16) + c];
+                        qr[4 * g + c] = x * cw[c] - y * sw[c];
+                        qr[4 * (g + D / 16) + c] = y * cw[c] + x * sw[c];
+                    }
+                }
+            }
+        }
     }
 
     f32x16 o[NB];
@@ -172,95 +209,163 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             const int s = inst * 64 + lane;
             const int r = s / CPR, p = s % CPR;
             const int key = min(kv0 + r, w_block - 1);
-            const float* kg = kbase + (size_t)key * a.k_stride + 4 * (p ^ (r & 15));
+            if constexpr (!ROPE) {
+                const float* kg = kbase + (size_t)key * a.k_stride + 4 * (p ^ (r & 15));
+                __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kd + inst * 256), 16, 0, 0);
+            }
             const float* vg = vbase + (size_t)key * a.v_stride + 4 * p;
-            __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kd + inst * 256), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(vg, (lds_void*)(vd + inst * 256), 16, 0, 0);
         }
     };
 
-    if (t_begin < t_end) issue_tile(t_begin, 0);
+    // Rotary keys: lane work item s of a tile is (row s / HC, chunk pair
+    // (c, c + HC), c = s % HC), i.e. elements 4c..4c+3 and their partners
+    // D/2 further on, with the (cos, sin) of pairs 4c..4c+3 at the row's
+    // position. Rows past the block's window are the last row, as above.
+    float4 rk[ROPE ? RMAX : 1][2], rc[ROPE ? RMAX : 1][2];
+    auto load_k_rot = [&](int t) {
+        const int kv0 = t * kBN;
+#pragma unroll
+        for (int u = 0; u < RMAX; ++u) {
+            const int inst = wg + u * gw;
+            if (inst < RP_INST) {
+                const int s = inst * 64 + lane;
+                const int r = s / HC, c = s % HC;
+                const int key = min(kv0 + r, w_block - 1);
+                const float* kg = kbase + (size_t)key * a.k_stride + 4 * c;
+                rk[u][0] = *reinterpret_cast<const float4*>(kg);
+                rk[u][1] = *reinterpret_cast<const float4*>(kg + D / 2);
+                const float* cg = a.rope_cs + (size_t)key * D + 8 * c;
+                rc[u][0] = *reinterpret_cast<const float4*>(cg);
+                rc[u][1] = *reinterpret_cast<const float4*>(cg + 4);
+            }
+        }
+    };
+    auto store_k_rot = [&](int buf) {
+        float* kd = my_lds + (size_t)buf * 2 * TILE_F;
+#pragma unroll
+        for (int u = 0; u < RMAX; ++u) {
+            const int inst = wg + u * gw;
+            if (inst < RP_INST) {
+                const int s = inst * 64 + lane;
+                const int r = s / HC, c = s % HC;
+                const float4 lo = rk[u][0], hi = rk[u][1];
+                const float4 c0 = rc[u][0], c1 = rc[u][1];
+                float4 nlo, nhi;
+                nlo.x = lo.x * c0.x - hi.x * c0.y;
+                nhi.x = hi.x * c0.x + lo.x * c0.y;
+                nlo.y = lo.y * c0.z - hi.y * c0.w;
+                nhi.y = hi.y * c0.z + lo.y * c0.w;
+                nlo.z = lo.z * c1.x - hi.z * c1.y;
+                nhi.z = hi.z * c1.x + lo.z * c1.y;
+                nlo.w = lo.w * c1.z - hi.w * c1.w;
+                nhi.w = hi.w * c1.z + lo.w * c1.w;
+                // Logical chunk c of row r lives at position c ^ (r % 16).
+                *reinterpret_cast<float4*>(kd + r * D + 4 * (c ^ (r & 15))) = nlo;
+                *reinterpret_cast<float4*>(kd + r * D + 4 * ((c + HC) ^ (r & 15))) = nhi;
+            }
+        }
+    };
+
+    if (t_begin < t_end) {
+        issue_tile(t_begin, 0);
+        if constexpr (ROPE) {
+            load_k_rot(t_begin);
+            wait_vmem();
+            store_k_rot(0);
+        }
+    }
 
     for (int it = 0; it < nt; ++it) {
         const int t = t_begin + it;
         const bool have = t < t_end;
         wait_vmem();
         __syncthreads();  // tile t landed for every wave; buffer (it+1)&1 is free
-        if (have && t + 1 < t_end) issue_tile(t + 1, (it + 1) & 1);
+        const bool next = have && t + 1 < t_end;
+        if (next) {
+            issue_tile(t + 1, (it + 1) & 1);
+            if constexpr (ROPE) load_k_rot(t + 1);
+        }
         const int kv0 = t * kBN;
-        if (!have || kv0 >= w_wave_max) continue;  // wave-uniform
+        if (have && kv0 < w_wave_max) {  // wave-uniform
+            const float* Ks = my_lds + (size_t)(it & 1) * 2 * TILE_F;
+            const float* Vs = Ks + TILE_F;
 
-        const float* Ks = my_lds + (size_t)(it & 1) * 2 * TILE_F;
-        const float* Vs = Ks + TILE_F;
+            // Matrix-core sections run at raised wave priority so the SIMD's
+            // other wave fills the gaps with its softmax work.
+            __builtin_amdgcn_s_setprio(1);
+            // S^T = K Q^T for this tile (already in log2 units).
+            f32x16 s;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = 0.f;
+            const float* kr = Ks + j * D;
+#pragma unroll
+            for (int g = 0; g < D / 8; ++g) {
+                const int c = (2 * g + hh) ^ (j & 15);
+                const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * c);
+                s = mfma32(kk.x, qr[4 * g + 0], s);
+                s = mfma32(kk.y, qr[4 * g + 1], s);
+                s = mfma32(kk.z, qr[4 * g + 2], s);
+                s = mfma32(kk.w, qr[4 * g + 3], s);
+            }
 
-        // Matrix-core sections run at raised wave priority so the SIMD's
-        // other wave fills the gaps with its softmax work.
-        __builtin_amdgcn_s_setprio(1);
-        // S^T = K Q^T for this tile (already in log2 units).
-        f32x16 s;
+            __builtin_amdgcn_s_setprio(0);
+            if (kv0 + kBN > w_wave_min) {  // some key of the tile is outside some window
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-        const float* kr = Ks + j * D;
+                for (int r = 0; r < 16; ++r)
+                    if (kv0 + acc_row(r, hh) >= w_row) s[r] = -INFINITY;
+            }
+
+            // Online softmax for query column j.
+            float mx = s[0];
 #pragma unroll
-        for (int g = 0; g < D / 8; ++g) {
-            const int c = (2 * g + hh) ^ (j & 15);
-            const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * c);
-            s = mfma32(kk.x, qr[4 * g + 0], s);
-            s = mfma32(kk.y, qr[4 * g + 1], s);
-            s = mfma32(kk.z, qr[4 * g + 2], s);
-            s = mfma32(kk.w, qr[4 * g + 3], s);
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+            float ls = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
+                ls += s[r];
+            }
+            ls += __shfl_xor(ls, 32);
+            l_run = l_run * corr + ls;
+            m_run = m_new;
+            // Rescale only if some row's max moved (after the first tiles it
+            // rarely does): one wave-wide vote instead of 16*NB multiplies.
+            if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0ull) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[b][r] *= corr;
+            }
+
+            __builtin_amdgcn_s_setprio(1);
+            // O^T += V^T P^T: k-step t pairs keys acc_row(t, 0) and acc_row(t, 1).
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) {
+                const float* vr = Vs + acc_row(tt, hh) * D + NB * j;
+                if constexpr (NB == 4) {
+                    const float4 vv = *reinterpret_cast<const float4*>(vr);
+                    o[0] = mfma32(vv.x, s[tt], o[0]);
+                    o[1] = mfma32(vv.y, s[tt], o[1]);
+                    o[2] = mfma32(vv.z, s[tt], o[2]);
+                    o[3] = mfma32(vv.w, s[tt], o[3]);
+                } else {
+                    const float2 vv = *reinterpret_cast<const float2*>(vr);
+                    o[0] = mfma32(vv.x, s[tt], o[0]);
+                    o[1] = mfma32(vv.y, s[tt], o[1]);
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
         }
-
-        __builtin_amdgcn_s_setprio(0);
-        if (kv0 + kBN > w_wave_min) {  // some key of the tile is outside some window
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (kv0 + acc_row(r, hh) >= w_row) s[r] = -INFINITY;
-        }
-
-        // Online softmax for query column j.
-        float mx = s[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-        float ls = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
-            ls += s[r];
-        }
-        ls += __shfl_xor(ls, 32);
-        l_run = l_run * corr + ls;
-        m_run = m_new;
-        // Rescale only if some row's max moved (after the first tiles it
-        // rarely does): one wave-wide vote instead of 16*NB multiplies.
-        if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0ull) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[b][r] *= corr;
-        }
-
-        __builtin_amdgcn_s_setprio(1);
-        // O^T += V^T P^T: k-step t pairs keys acc_row(t, 0) and acc_row(t, 1).
-#pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-            const float* vr = Vs + acc_row(tt, hh) * D + NB * j;
-            if constexpr (NB == 4) {
-                const float4 vv = *reinterpret_cast<const float4*>(vr);
-                o[0] = mfma32(vv.x, s[tt], o[0]);
-                o[1] = mfma32(vv.y, s[tt], o[1]);
-                o[2] = mfma32(vv.z, s[tt], o[2]);
-                o[3] = mfma32(vv.w, s[tt], o[3]);
-            } else {
-                const float2 vv = *reinterpret_cast<const float2*>(vr);
-                o[0] = mfma32(vv.x, s[tt], o[0]);
-                o[1] = mfma32(vv.y, s[tt], o[1]);
+        if constexpr (ROPE) {
+            if (next) {  // next tile's keys: turned and written after this tile's math
+                wait_vmem();
+                store_k_rot((it + 1) & 1);
             }
         }
-        __builtin_amdgcn_s_setprio(0);
     }
 
     if (a.ks > 1) {
@@ -321,6 +426,23 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 }
 
+// Largest dynamic LDS an instance is launched with: the most key splits its
+// head_dim allows, 2 buffers x (K, V) each.
+template <int D, bool ROPE>
+hipError_t launch_instance(long long grid, size_t lds, hipStream_t stream, const float* q,
+                           const float* k, const float* v, float* out, float* lse,
+                           const Args& a) {
+    constexpr int max_splits = D == 128 ? 2 : 4;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(prefill_kernel<D, ROPE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        max_splits * 2 * 2 * kBN * D * (int)sizeof(float));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((prefill_kernel<D, ROPE>), dim3((unsigned)grid), dim3(kBlock), lds, stream,
+                       q, k, v, out, lse, a);
+    return hipSuccess;
+}
+
 int gcd_int(int x, int y) {
     while (y) {
         const int t = x % y;
@@ -335,6 +457,7 @@ int gcd_int(int x, int y) {
 hipError_t launch_prefill(const float* q, const float* k, const float* v, float* out,
                           float* lse, const PrefillShape& s, hipStream_t stream) {
     Args a;
+    a.rope_cs = s.rope_cs;
     a.q_seq = s.q_seq;
     a.kv_len = s.kv_len;
     a.num_heads = s.num_heads;
@@ -355,7 +478,10 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     const long long base_waves = (long long)s.num_heads * strips;
     const int max_w = s.causal ? min(s.start_pos + s.q_seq, s.kv_len) : s.kv_len;
     const int key_tiles = (max_w + kBN - 1) / kBN;
-    const int max_ks = s.head_dim == 128 ? 2 : 4;  // 2 buffers x (K, V) per split in 160 KB
+    // 2 buffers x (K, V) per split in 160 KB; the rotary instance also holds
+    // the next key tile in registers, at most rope_rmax instructions a wave.
+    const bool rope = s.rope_cs != nullptr;
+    const int max_ks = s.head_dim == 128 ? (rope ? 1 : 2) : 4;
     int ks = 1;
     while (ks < max_ks && base_waves * ks < kTargetWaves && key_tiles >= 4 * ks * 2) ks *= 2;
     a.ks = ks;
@@ -367,21 +493,15 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     if (grid <= 0) return hipSuccess;
     const size_t tile_bytes = (size_t)kBN * s.head_dim * sizeof(float);
     const size_t lds = (size_t)ks * 2 * 2 * tile_bytes;  // per split: 2 buffers x (K, V)
+    hipError_t e;
     if (s.head_dim == 128) {
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(prefill_kernel<128>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * 2 * 2 * kBN * 128 * (int)sizeof(float));
-        if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)grid), dim3(kBlock), lds, stream,
-                           q, k, v, out, lse, a);
+        e = rope ? launch_instance<128, true>(grid, lds, stream, q, k, v, out, lse, a)
+                 : launch_instance<128, false>(grid, lds, stream, q, k, v, out, lse, a);
     } else {
-        static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(prefill_kernel<64>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 2 * 2 * kBN * 64 * (int)sizeof(float));
-        if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)grid), dim3(kBlock), lds, stream,
-                           q, k, v, out, lse, a);
+        e = rope ? launch_instance<64, true>(grid, lds, stream, q, k, v, out, lse, a)
+                 : launch_instance<64, false>(grid, lds, stream, q, k, v, out, lse, a);
     }
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

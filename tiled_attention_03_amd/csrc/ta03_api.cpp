@@ -2,6 +2,7 @@
 // Every check happens on the host before any HIP call, so an invalid call
 // enqueues nothing and needs no device.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -16,15 +17,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool head_dim_supported(int d) { return d == 64 || d == 128; }
 
-}  // namespace
-
-extern "C" {
-
-int attn_fwd_ex(const float* q, long long q_stride, const float* k, long long k_stride,
-                const float* v, long long v_stride, float* out, long long out_stride,
-                float* lse, int q_base, int q_seq, int kv_len, int num_heads,
-                int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
-                hipStream_t stream) {
+// Shared validation and launch of attn_fwd_ex and attn_fwd_rope (rope_cs ==
+// nullptr: no rotation).
+int fwd_common(const float* q, long long q_stride, const float* k, long long k_stride,
+               const float* v, long long v_stride, float* out, long long out_stride,
+               float* lse, int q_base, int q_seq, int kv_len, int num_heads,
+               int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+               bool rope, const float* rope_cs, int rope_rows, hipStream_t stream) {
     if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0) return TA03_ERR_SHAPE;
     if (q_seq < 0 || kv_len < 0 || start_pos < 0 || q_base < 0) return TA03_ERR_SHAPE;
     if (mode != TA03_CAUSAL && mode != TA03_FULL && mode != TA03_CROSS) return TA03_ERR_SHAPE;
@@ -39,11 +38,18 @@ int attn_fwd_ex(const float* q, long long q_stride, const float* k, long long k_
     if (q_stride >= kMaxElems || out_stride >= kMaxElems || k_stride >= kMaxElems ||
         v_stride >= kMaxElems)
         return TA03_ERR_UNSUPPORTED;
+    if (rope) {
+        // Positions used: query rows start_pos + q_base .. + q_seq - 1, keys 0 .. kv_len - 1.
+        const long long need = std::max((long long)start_pos + q_base + q_seq, (long long)kv_len);
+        if (rope_rows < 0 || (q_seq > 0 && rope_rows < need)) return TA03_ERR_SHAPE;
+        if ((long long)rope_rows * head_dim >= kMaxElems) return TA03_ERR_UNSUPPORTED;
+    }
     if (q_seq == 0) return TA03_OK;
     if (q == nullptr || out == nullptr) return TA03_ERR_NULL;
     if (kv_len > 0 && (k == nullptr || v == nullptr)) return TA03_ERR_NULL;
+    if (rope && rope_cs == nullptr) return TA03_ERR_NULL;
     if (!aligned16(q) || !aligned16(out) || !aligned16(k) || !aligned16(v) || !aligned16(lse) ||
-        (q_stride | k_stride | v_stride | out_stride) % 4 != 0)
+        !aligned16(rope_cs) || (q_stride | k_stride | v_stride | out_stride) % 4 != 0)
         return TA03_ERR_ALIGN;
 
     ta03::PrefillShape s;
@@ -53,17 +59,53 @@ int attn_fwd_ex(const float* q, long long q_stride, const float* k, long long k_
     s.num_kv_heads = num_kv_heads;
     s.head_dim = head_dim;
     s.causal = mode == TA03_CAUSAL ? 1 : 0;
-    s.start_pos = start_pos + q_base;  // causal position of the first row handled
+    s.start_pos = start_pos + q_base;  // position of the first row handled
     s.scale = scale;
     s.q_stride = q_stride;
     s.k_stride = k_stride;
     s.v_stride = v_stride;
     s.out_stride = out_stride;
+    s.rope_cs = rope ? rope_cs : nullptr;
     // Row q_base of the batch is row 0 of this launch.
     const float* qb = q + (size_t)q_base * (size_t)q_stride;
     float* ob = out + (size_t)q_base * (size_t)out_stride;
     float* lb = lse != nullptr ? lse + (size_t)q_base * (size_t)num_heads * 2 : nullptr;
     const hipError_t e = ta03::launch_prefill(qb, k, v, ob, lb, s, stream);
+    return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_ex(const float* q, long long q_stride, const float* k, long long k_stride,
+                const float* v, long long v_stride, float* out, long long out_stride,
+                float* lse, int q_base, int q_seq, int kv_len, int num_heads,
+                int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+                hipStream_t stream) {
+    return fwd_common(q, q_stride, k, k_stride, v, v_stride, out, out_stride, lse, q_base,
+                      q_seq, kv_len, num_heads, num_kv_heads, head_dim, mode, start_pos, scale,
+                      false, nullptr, 0, stream);
+}
+
+int attn_fwd_rope(const float* q, long long q_stride, const float* k, long long k_stride,
+                  const float* v, long long v_stride, float* out, long long out_stride,
+                  float* lse, int q_base, int q_seq, int kv_len, int num_heads,
+                  int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+                  const float* rope_cs, int rope_rows, hipStream_t stream) {
+    return fwd_common(q, q_stride, k, k_stride, v, v_stride, out, out_stride, lse, q_base,
+                      q_seq, kv_len, num_heads, num_kv_heads, head_dim, mode, start_pos, scale,
+                      true, rope_cs, rope_rows, stream);
+}
+
+int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStream_t stream) {
+    if (rows < 0 || head_dim < 2 || head_dim % 2 != 0) return TA03_ERR_SHAPE;
+    if (!(theta > 0.0) || !std::isfinite(theta)) return TA03_ERR_SHAPE;
+    if ((long long)rows * head_dim >= kMaxElems) return TA03_ERR_UNSUPPORTED;
+    if (rows == 0) return TA03_OK;
+    if (cos_sin == nullptr) return TA03_ERR_NULL;
+    if (!aligned16(cos_sin)) return TA03_ERR_ALIGN;
+    const hipError_t e = ta03::launch_rope_table(cos_sin, rows, head_dim, theta, stream);
     return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
 }
 

@@ -12,6 +12,8 @@ struct PrefillShape {
     int causal, start_pos;  // start_pos: causal position of row 0 of q/out
     float scale;
     long long q_stride, k_stride, v_stride, out_stride;  // row strides in floats
+    // Rotary (cos, sin) table [positions][head_dim/2][2]; nullptr: no rotation.
+    const float* rope_cs = nullptr;
 };
 
 struct DecodeShape {
@@ -35,6 +37,9 @@ DecodePlan decode_plan(const DecodeShape& s);
 
 hipError_t launch_prefill(const float* q, const float* k, const float* v, float* out,
                           float* lse, const PrefillShape& s, hipStream_t stream);
+
+// Rotary table: entry (p, e) = (cos, sin) of p * theta^(-2e/head_dim).
+hipError_t launch_rope_table(float* cs, int rows, int head_dim, double theta, hipStream_t stream);
 
 hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t stream);
 
