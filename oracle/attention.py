@@ -24,6 +24,10 @@ Sources (pages' titles and the part of each shader):
     window continued from ``start_pos`` and clamped to the cache length; a
     zero-length window writes zeros).
 
+Backward (``attention_backward``): the pages store the (max, log-sum) pair
+for a backward pass they do not give; the checker returns the exact gradients
+of the definition above for the loss sum(dout * out).
+
 Rotary position embedding (optional, ``rope``): meganeura ``attention.wgsl``
 applies a rotation hook to each loaded query element and builds each key
 element through a hook expression, but the pages give no formula. The reading
@@ -175,6 +179,73 @@ def attention_forward(q, k, v, *, num_heads: int, num_kv_heads: int, head_dim: i
             lse[sel, h, 0] = np.where(nonempty, m, EMPTY_SENTINEL)
             lse[sel, h, 1] = np.where(nonempty, np.log(z_safe), EMPTY_SENTINEL)
     return out, lse
+
+
+def attention_backward(q, k, v, dout, *, num_heads: int, num_kv_heads: int, head_dim: int,
+                       mode: int, kv_len: int, start_pos: int = 0, scale: float,
+                       rows=None, keys=None, kv_heads=None, row_block: int = 256):
+    """Gradients of the forward above, in float64: for the loss
+    L = sum(dout * out), returns (dq, dk, dv).
+
+    The pages keep the (max, log-sum) pair "for backward" but give no
+    backward algorithm; this is the derivative of the plain definition.
+    Per head h (kv head c = h // group), over the rows' windows:
+        P   = softmax_j(s_ij)            (0 for an empty window)
+        dP  = dout_h V_c^T
+        D_i = sum_j P_ij dP_ij           (= <dout_i, out_i>)
+        dS  = P * (dP - D)
+        dq_h  = scale * dS K_c
+        dk_c += scale * dS^T Q_h
+        dv_c += P^T dout_h
+    q, dout: [q_seq, num_heads*head_dim]; k, v: [>= kv_len, num_kv_heads*head_dim].
+    rows / keys select the query rows of dq and the key rows of dk, dv that
+    are returned (default: all rows, keys [0, kv_len)); kv_heads restricts
+    the computation to the query heads of those KV heads (the other columns
+    are returned as 0). Returns dq [n_rows, H*d], dk, dv [n_keys, Hkv*d].
+    """
+    _check_shapes(q, k, v, num_heads, num_kv_heads, head_dim, kv_len)
+    q_seq = q.shape[0]
+    if mode == FULL and kv_len != q_seq:
+        raise ValueError("full attention needs kv_len == q_seq")
+    rows = np.arange(q_seq) if rows is None else np.asarray(rows, dtype=np.int64)
+    keys = np.arange(kv_len) if keys is None else np.asarray(keys, dtype=np.int64)
+    kv_heads = range(num_kv_heads) if kv_heads is None else kv_heads
+    group = num_heads // num_kv_heads
+    d = head_dim
+    row_pos = {int(r): n for n, r in enumerate(rows)}
+    dq = np.zeros((rows.shape[0], num_heads * d), dtype=np.float64)
+    dk = np.zeros((keys.shape[0], num_kv_heads * d), dtype=np.float64)
+    dv = np.zeros((keys.shape[0], num_kv_heads * d), dtype=np.float64)
+    win = np.array([window_length(mode, i, q_seq, kv_len, start_pos) for i in range(q_seq)],
+                   dtype=np.int64)
+    for c in kv_heads:
+        kc = k[:kv_len, c * d:(c + 1) * d].astype(np.float64)
+        vc = v[:kv_len, c * d:(c + 1) * d].astype(np.float64)
+        for h in range(c * group, (c + 1) * group):
+            for b0 in range(0, q_seq, row_block):
+                r = np.arange(b0, min(b0 + row_block, q_seq))
+                w = win[r]
+                if w.max() == 0:
+                    continue
+                qb = q[r, h * d:(h + 1) * d].astype(np.float64)
+                gb = dout[r, h * d:(h + 1) * d].astype(np.float64)
+                s = scale * (qb @ kc.T)
+                valid = np.arange(kv_len)[None, :] < w[:, None]
+                s = np.where(valid, s, -np.inf)
+                m = np.where(w > 0, s.max(axis=1), 0.0)
+                e = np.where(valid, np.exp(s - m[:, None]), 0.0)
+                z = e.sum(axis=1)
+                p = e / np.where(w > 0, z, 1.0)[:, None]
+                dp = gb @ vc.T
+                dd = (p * dp).sum(axis=1)
+                ds = p * (dp - dd[:, None])
+                dk[:, c * d:(c + 1) * d] += scale * (ds[:, keys].T @ qb)
+                dv[:, c * d:(c + 1) * d] += p[:, keys].T @ gb
+                sel = [n for n, i in enumerate(r) if int(i) in row_pos]
+                if sel:
+                    dq[[row_pos[int(r[n])] for n in sel], h * d:(h + 1) * d] = \
+                        scale * (ds[sel] @ kc)
+    return dq, dk, dv
 
 
 def decode_forward(q, k_cache, v_cache, *, kv_pos: int, num_heads: int,

@@ -490,4 +490,124 @@ def pin_rope_brute_force_tiny(orc):
     _close(got[1], want[1], 1e-12, "rope brute lse")
 
 
+# --------------------------------------------------------------- backward
+# The checker's gradients are pinned to the forward itself (central finite
+# differences of L = sum(dout * out)), to torch's autograd through a plain
+# masked-softmax attention, and to identities of the softmax Jacobian.
+
+def _bwd(orc, q, k, v, g, H, Hkv, d, mode, kv_len, start_pos=0, scale=0.4, **kw):
+    return orc.attention_backward(q, k, v, g, num_heads=H, num_kv_heads=Hkv, head_dim=d,
+                                  mode=mode, kv_len=kv_len, start_pos=start_pos, scale=scale,
+                                  **kw)
+
+
+def pin_backward_finite_differences(orc):
+    """Each gradient entry against (L(x + h) - L(x - h)) / 2h of the
+    checker's own forward, L = sum(dout * out)."""
+    H, Hkv, d, hstep = 2, 1, 3, 1e-6
+    for mode, n, kv_len, sp in ((CAUSAL, 4, 5, 1), (CROSS, 3, 4, 0), (FULL, 3, 3, 0)):
+        rng = np.random.default_rng(400 + mode)
+        q = rng.standard_normal((n, H * d))
+        k = rng.standard_normal((kv_len, Hkv * d))
+        v = rng.standard_normal((kv_len, Hkv * d))
+        g = rng.standard_normal((n, H * d))
+        def loss(qq, kk, vv):
+            o, _ = orc.attention_forward(qq, kk, vv, num_heads=H, num_kv_heads=Hkv, head_dim=d,
+                                         mode=mode, kv_len=kv_len, start_pos=sp, scale=0.4)
+            return float((o * g).sum())
+        dq, dk, dv = _bwd(orc, q, k, v, g, H, Hkv, d, mode, kv_len, sp)
+        for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += hstep
+                xm[idx] -= hstep
+                args = {"q": (q, k, v), "k": (q, k, v), "v": (q, k, v)}[name]
+                ap = [xp if a is x else a for a in args]
+                am = [xm if a is x else a for a in args]
+                num[idx] = (loss(*ap) - loss(*am)) / (2 * hstep)
+            _close(grad, num, 2e-7, f"finite differences d{name} mode={mode}")
+
+
+def pin_backward_torch_autograd(orc):
+    """torch autograd (float64, CPU) through a masked softmax attention."""
+    import torch
+    H, Hkv, d = 4, 2, 8
+    for mode, n, kv_len, sp in ((CAUSAL, 7, 9, 2), (FULL, 6, 6, 0), (CROSS, 5, 11, 0)):
+        q, k, v = _rand((n, H * d), 410), _rand((kv_len, Hkv * d), 411), _rand((kv_len, Hkv * d), 412)
+        g = _rand((n, H * d), 413)
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        g_ = H // Hkv
+        qh = tq.view(n, H, d).transpose(0, 1)
+        kh = tk.view(kv_len, Hkv, d).transpose(0, 1).repeat_interleave(g_, dim=0)
+        vh = tv.view(kv_len, Hkv, d).transpose(0, 1).repeat_interleave(g_, dim=0)
+        s = 0.4 * qh @ kh.transpose(1, 2)
+        w = torch.tensor([_window(mode, i, n, kv_len, sp) for i in range(n)])
+        mask = torch.arange(kv_len)[None, :] < w[:, None]
+        p = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1)
+        out = (p @ vh).transpose(0, 1).reshape(n, H * d)
+        (out * torch.tensor(g, dtype=torch.float64)).sum().backward()
+        dq, dk, dv = _bwd(orc, q, k, v, g, H, Hkv, d, mode, kv_len, sp)
+        _close(dq, tq.grad.numpy(), 1e-12, f"autograd dq mode={mode}")
+        _close(dk, tk.grad.numpy(), 1e-12, f"autograd dk mode={mode}")
+        _close(dv, tv.grad.numpy(), 1e-12, f"autograd dv mode={mode}")
+
+
+def pin_backward_single_key(orc):
+    """One key in every window: softmax is the constant 1, so dq = dk = 0 and
+    dv is the sum of dout over the rows and the group's heads."""
+    H, Hkv, d, n = 4, 2, 5, 6
+    q, k, v, g = _rand((n, H * d), 420), _rand((1, Hkv * d), 421), _rand((1, Hkv * d), 422), \
+        _rand((n, H * d), 423)
+    dq, dk, dv = _bwd(orc, q, k, v, g, H, Hkv, d, CROSS, 1)
+    _close(dq, np.zeros_like(dq), 0.0, "single key dq")
+    _close(dk, np.zeros_like(dk), 0.0, "single key dk")
+    gs = g.astype(np.float64).reshape(n, Hkv, H // Hkv, d).sum(axis=(0, 2)).reshape(1, Hkv * d)
+    _close(dv, gs, 1e-12, "single key dv")
+
+
+def pin_backward_sums(orc):
+    """Every row's dS sums to 0 over its window, so the keys' dk sum to 0;
+    every non-empty row's weights sum to 1, so the keys' dv sum to the
+    rows' dout (per KV head, over its group)."""
+    H, Hkv, d = 6, 2, 4
+    for mode, n, kv_len, sp in ((CAUSAL, 9, 12, 3), (CROSS, 5, 0, 0), (CROSS, 7, 10, 0)):
+        q, k, v, g = (_rand((n, H * d), 430), _rand((max(kv_len, 1), Hkv * d), 431),
+                      _rand((max(kv_len, 1), Hkv * d), 432), _rand((n, H * d), 433))
+        dq, dk, dv = _bwd(orc, q, k, v, g, H, Hkv, d, mode, kv_len, sp)
+        _close(dk.sum(axis=0), np.zeros(Hkv * d), 1e-12, f"sum dk mode={mode}")
+        live = np.array([_window(mode, i, n, kv_len, sp) > 0 for i in range(n)])
+        gs = g.astype(np.float64)[live].reshape(-1, Hkv, H // Hkv, d).sum(axis=(0, 2)).reshape(-1)
+        _close(dv.sum(axis=0), gs, 1e-12, f"sum dv mode={mode}")
+        if kv_len == 0:
+            _close(dq, np.zeros_like(dq), 0.0, "empty windows dq")
+
+
+def pin_backward_linear_in_dout(orc):
+    H, Hkv, d, n = 2, 1, 4, 6
+    q, k, v = _rand((n, H * d), 440), _rand((n, Hkv * d), 441), _rand((n, Hkv * d), 442)
+    g1, g2 = _rand((n, H * d), 443), _rand((n, H * d), 444)
+    a = _bwd(orc, q, k, v, g1, H, Hkv, d, CAUSAL, n)
+    b = _bwd(orc, q, k, v, g2, H, Hkv, d, CAUSAL, n)
+    c = _bwd(orc, q, k, v, 2.0 * g1.astype(np.float64) - 3.0 * g2.astype(np.float64), H, Hkv, d,
+             CAUSAL, n)
+    for x, y, z, nm in zip(a, b, c, ("dq", "dk", "dv")):
+        _close(z, 2.0 * x - 3.0 * y, 1e-12, f"linear {nm}")
+
+
+def pin_backward_selection(orc):
+    """rows / keys / kv_heads return exactly those parts of the whole."""
+    H, Hkv, d, n = 4, 2, 4, 11
+    q, k, v, g = (_rand((n, H * d), 450), _rand((n, Hkv * d), 451), _rand((n, Hkv * d), 452),
+                  _rand((n, H * d), 453))
+    dq, dk, dv = _bwd(orc, q, k, v, g, H, Hkv, d, CAUSAL, n, row_block=4)
+    rows, keys = np.array([10, 2, 5]), np.array([0, 7, 3])
+    sq, sk, sv = _bwd(orc, q, k, v, g, H, Hkv, d, CAUSAL, n, rows=rows, keys=keys, kv_heads=[1])
+    cols = slice(1 * 2 * d, 2 * 2 * d)
+    _close(sq[:, cols], dq[rows][:, cols], 1e-13, "selected dq")
+    _close(sq[:, :2 * d], np.zeros((3, 2 * d)), 0.0, "unselected heads dq")
+    _close(sk[:, d:], dk[keys][:, d:], 1e-13, "selected dk")
+    _close(sv[:, d:], dv[keys][:, d:], 1e-13, "selected dv")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

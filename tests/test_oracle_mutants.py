@@ -40,6 +40,13 @@ MUTANTS = {
                                      "apply_rope(q[rows], rows,"),
     "rope_key_position_shift": ("np.arange(kv_len), rope, num_kv_heads",
                                 "np.arange(kv_len) // 2, rope, num_kv_heads"),
+    "bwd_delta_sign": ("ds = p * (dp - dd[:, None])", "ds = p * (dp + dd[:, None])"),
+    "bwd_delta_unweighted": ("dd = (p * dp).sum(axis=1)", "dd = dp.sum(axis=1)"),
+    "bwd_dk_unscaled": ("+= scale * (ds[:, keys].T @ qb)", "+= (ds[:, keys].T @ qb)"),
+    "bwd_dv_from_ds": ("+= p[:, keys].T @ gb", "+= ds[:, keys].T @ gb"),
+    "bwd_dq_from_v": ("scale * (ds[sel] @ kc)", "scale * (ds[sel] @ vc)"),
+    "bwd_dk_overwritten": ("dk[:, c * d:(c + 1) * d] += scale", "dk[:, c * d:(c + 1) * d] = scale"),
+    "bwd_dv_not_summed_over_group": ("dv[:, c * d:(c + 1) * d] += p", "dv[:, c * d:(c + 1) * d] = p"),
     "rope_keys_unrotated": ("        k = apply_rope(k[:kv_len]", "        k = 1.0 * (k[:kv_len]"),
 }
 
