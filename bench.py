@@ -152,6 +152,37 @@ def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None)
             "tflops_kernel": flops / mean_s / 1e12, "tflops_wall": flops * steps / wall / 1e12}
 
 
+def bench_backward(w, steps, warmup, torch, ta):
+    """attn_bwd (both kernels) on the workload, fed by one forward pass;
+    FLOPs are the algorithmic five products per unmasked pair (recomputed
+    scores, dP, dV, dK, dQ): 2.5x the forward's."""
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.make_prefill(w)
+    g = inputs.normal(q.shape, w.seed_base + 7)
+    qd, kd, vd, gd = (torch.from_numpy(x).to(dev) for x in (q, k, v, g))
+    del q, k, v, g
+    H, Hkv, d = w.num_heads, w.num_kv_heads, w.head_dim
+    out = torch.empty((w.q_seq, H * d), device=dev)
+    lse = torch.empty((w.q_seq, H, 2), device=dev)
+    ta.attn_fwd(qd, kd, vd, out, lse, w.q_seq, w.kv_len, H, Hkv, d, w.mode, w.start_pos, w.scale)
+    dq = torch.empty_like(out)
+    dk = torch.empty((w.kv_len, Hkv * d), device=dev)
+    dv = torch.empty_like(dk)
+    nbytes = ta.attn_bwd_workspace_bytes(w.q_seq, H)
+    ws = torch.empty((nbytes // 4,), device=dev)
+
+    def call(_i):
+        ta.attn_bwd(qd, kd, vd, out, gd, lse, dq, dk, dv, w.q_seq, w.kv_len, H, Hkv, d, w.mode,
+                    w.start_pos, w.scale, ws, nbytes)
+
+    for i in range(warmup):
+        call(i)
+    mean_s, min_s, wall = time_calls(call, steps, torch)
+    flops = 2.5 * prefill_flops(w)
+    return {"flops": flops, "mean_s": mean_s, "min_s": min_s,
+            "tflops_kernel": flops / mean_s / 1e12}
+
+
 def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8):
     """Decode device time. The cache is rotated over `copies` independent
     allocations (copies x 64 MiB > the 256 MB Infinity Cache), and the
@@ -364,6 +395,13 @@ def main():
                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
                 "kernel": "prefill_kernel<128, true>"}
             print(f"[bench] rotary {result['prefill_rope']}", flush=True)
+            r = bench_backward(w, 3, 1, torch, ta)
+            result["backward"] = {
+                "workload": w.name, "ms": round(r["mean_s"] * 1e3, 3),
+                "flops_per_call": r["flops"], "TFLOP/s": round(r["tflops_kernel"], 3),
+                "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
+                "kernels": "bwd_dq_kernel<128> + bwd_dkdv_kernel<128>"}
+            print(f"[bench] backward {result['backward']}", flush=True)
 
     if args.only != "prefill":
         wd = inputs.DECODE_8K

@@ -168,6 +168,43 @@ int attn_fwd_rope(const float* q, long long q_stride, const float* k, long long 
 int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStream_t stream);
 
 /*
+ * attn_bwd -- gradients of attn_fwd (dense rows, no rotation) for a loss
+ * whose gradient with respect to out is dout. meganeura attention.wgsl keeps
+ * the pair lse = (m, log l) "for backward" without giving one; this is the
+ * exact derivative of the forward's definition, built on that pair:
+ *   P_ij = exp(s_ij - m_i - log l_i),  s_ij = scale <q_i, k_j>, j in row i's window
+ *   D_i = <dout_i, out_i>,  dS_ij = P_ij (<dout_i, v_j> - D_i)
+ *   dq_i = scale sum_j dS_ij k_j
+ *   dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i
+ * with dk and dv summed over the query heads of each KV head.
+ *
+ *   q, out, dout  [q_seq, num_heads*head_dim]: the forward's inputs and
+ *                 output, and the loss gradient
+ *   k, v          [>= kv_len, num_kv_heads*head_dim]; rows [0, kv_len) read
+ *   lse           [q_seq, num_heads, 2] as the forward with these inputs
+ *                 wrote it (required)
+ *   dq            [q_seq, num_heads*head_dim], written in full
+ *   dk, dv        [kv_len, num_kv_heads*head_dim], written in full (0 for
+ *                 keys no row sees)
+ *   mode, start_pos, scale  as the forward
+ *   workspace     device scratch of attn_bwd_workspace_bytes(q_seq,
+ *                 num_heads) bytes, 16-byte aligned; overwritten
+ *
+ * Two kernel launches on stream, no allocation, no atomics (results are
+ * run-to-run identical). Errors: as attn_fwd for the sizes and mode;
+ * TA03_ERR_NULL for a NULL q, out, dout, lse, dq or workspace (q_seq > 0) or
+ * k, v, dk, dv (kv_len > 0); TA03_ERR_WORKSPACE for a short workspace;
+ * TA03_ERR_UNSUPPORTED for q_seq*num_heads*head_dim or
+ * kv_len*num_kv_heads*head_dim >= 2^31; TA03_ERR_ALIGN; TA03_ERR_HIP.
+ * q_seq == 0 and kv_len == 0 is a no-op; q_seq == 0 alone writes zero dk, dv.
+ */
+size_t attn_bwd_workspace_bytes(int q_seq, int num_heads);
+int attn_bwd(const float* q, const float* k, const float* v, const float* out, const float* dout,
+             const float* lse, float* dq, float* dk, float* dv, int q_seq, int kv_len,
+             int num_heads, int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
  * for these sizes: split-KV partial results (per query head and split, an
  * unnormalised output row plus its max and sum) and one completion counter

@@ -183,7 +183,8 @@ def attention_forward(q, k, v, *, num_heads: int, num_kv_heads: int, head_dim: i
 
 def attention_backward(q, k, v, dout, *, num_heads: int, num_kv_heads: int, head_dim: int,
                        mode: int, kv_len: int, start_pos: int = 0, scale: float,
-                       rows=None, keys=None, kv_heads=None, row_block: int = 256):
+                       rows=None, keys=None, kv_heads=None, row_block: int = 256,
+                       magnitudes: bool = False):
     """Gradients of the forward above, in float64: for the loss
     L = sum(dout * out), returns (dq, dk, dv).
 
@@ -202,6 +203,11 @@ def attention_backward(q, k, v, dout, *, num_heads: int, num_kv_heads: int, head
     are returned (default: all rows, keys [0, kv_len)); kv_heads restricts
     the computation to the query heads of those KV heads (the other columns
     are returned as 0). Returns dq [n_rows, H*d], dk, dv [n_keys, Hkv*d].
+
+    magnitudes=True also returns, for a rounding-error bound of a float32
+    evaluation, the same sums over magnitudes (dq_m, dk_m, dv_m): with
+    E_ij = |dS_ij| + P_ij (|dP_ij| + |D_i|) (dS and the rounding of its two
+    terms), dq_m = scale E|K|, dk_m = scale E^T|Q|, dv_m = P^T|dout|.
     """
     _check_shapes(q, k, v, num_heads, num_kv_heads, head_dim, kv_len)
     q_seq = q.shape[0]
@@ -216,6 +222,8 @@ def attention_backward(q, k, v, dout, *, num_heads: int, num_kv_heads: int, head
     dq = np.zeros((rows.shape[0], num_heads * d), dtype=np.float64)
     dk = np.zeros((keys.shape[0], num_kv_heads * d), dtype=np.float64)
     dv = np.zeros((keys.shape[0], num_kv_heads * d), dtype=np.float64)
+    if magnitudes:
+        dq_m, dk_m, dv_m = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
     win = np.array([window_length(mode, i, q_seq, kv_len, start_pos) for i in range(q_seq)],
                    dtype=np.int64)
     for c in kv_heads:
@@ -245,6 +253,15 @@ def attention_backward(q, k, v, dout, *, num_heads: int, num_kv_heads: int, head
                 if sel:
                     dq[[row_pos[int(r[n])] for n in sel], h * d:(h + 1) * d] = \
                         scale * (ds[sel] @ kc)
+                if magnitudes:
+                    em = np.abs(ds) + p * (np.abs(dp) + np.abs(dd)[:, None])
+                    dk_m[:, c * d:(c + 1) * d] += scale * (em[:, keys].T @ np.abs(qb))
+                    dv_m[:, c * d:(c + 1) * d] += p[:, keys].T @ np.abs(gb)
+                    if sel:
+                        dq_m[[row_pos[int(r[n])] for n in sel], h * d:(h + 1) * d] = \
+                            scale * (em[sel] @ np.abs(kc))
+    if magnitudes:
+        return dq, dk, dv, dq_m, dk_m, dv_m
     return dq, dk, dv
 
 

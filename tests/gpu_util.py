@@ -3,6 +3,10 @@ C ABI (via the ctypes binding) and the tolerance checks.
 
 Tolerances: out elementwise |gpu - ref| <= 1e-4 + 1e-4*|ref|; each lse
 component |gpu - ref| <= 1e-4; the empty-window sentinel -1e30 exactly.
+Gradients (check_grad) add the rounding of a float32 sum of N terms to the
+out bound: 4 sqrt(N) u M, u = 2^-24, with M the sum of the terms' magnitudes
+(the checker's ``magnitudes``; a probabilistic form of the |error| <= N u M
+bound of recursive summation).
 """
 
 from __future__ import annotations
@@ -64,6 +68,21 @@ def check_out(got, ref, what=""):
     bound = OUT_ATOL + OUT_RTOL * np.abs(ref)
     bad = err > bound
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} out elements off; "
+                           f"worst {float((err - bound).max()):.3e} over bound, "
+                           f"max abs err {float(err.max()):.3e}")
+    return float(err.max()) if err.size else 0.0
+
+
+def check_grad(got, ref, mag, n_terms, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    err = np.abs(got - ref)
+    bound = (OUT_ATOL + OUT_RTOL * np.abs(ref)
+             + 4.0 * np.sqrt(max(n_terms, 1)) * 2.0 ** -24 * np.asarray(mag, dtype=np.float64))
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} gradient elements off; "
                            f"worst {float((err - bound).max()):.3e} over bound, "
                            f"max abs err {float(err.max()):.3e}")
     return float(err.max()) if err.size else 0.0

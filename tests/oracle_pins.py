@@ -610,4 +610,17 @@ def pin_backward_selection(orc):
     _close(sv[:, d:], dv[keys][:, d:], 1e-13, "selected dv")
 
 
+def pin_backward_magnitudes_bound_results(orc):
+    """The magnitude sums bound the gradients (triangle inequality) and are
+    returned beside the unchanged gradients."""
+    H, Hkv, d, n = 4, 2, 4, 10
+    q, k, v, g = (_rand((n, H * d), 460), _rand((n, Hkv * d), 461), _rand((n, Hkv * d), 462),
+                  _rand((n, H * d), 463))
+    plain = _bwd(orc, q, k, v, g, H, Hkv, d, CAUSAL, n)
+    full = _bwd(orc, q, k, v, g, H, Hkv, d, CAUSAL, n, magnitudes=True)
+    for a, b, m, nm in zip(plain, full[:3], full[3:], ("dq", "dk", "dv")):
+        _close(a, b, 0.0, f"{nm} unchanged")
+        assert np.all(m >= np.abs(b) - 1e-12), f"{nm} magnitudes below |gradient|"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

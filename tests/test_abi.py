@@ -36,7 +36,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_decode", "attn_decode_paged",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_bytes",
+                                    "attn_decode", "attn_decode_paged",
                                     "attn_decode_workspace_bytes",
                                     "attn_decode_workspace_init", "attn_fwd", "attn_fwd_ex",
                                     "attn_fwd_rope", "attn_rope_table", "attn_strerror"]
@@ -150,6 +151,47 @@ def test_attn_fwd_rope_rejects_on_host(lib, kw, status):
 ])
 def test_attn_rope_table_rejects_on_host(lib, args, status):
     assert lib.attn_rope_table(*args, None) == status
+
+
+def bwd(lib, q=A, k=B, v=C, out=O, dout=O + 0x1000, lse=O + 0x2000, dq=O + 0x3000,
+        dk=O + 0x4000, dv=O + 0x5000, q_seq=4, kv_len=8, H=4, Hkv=2, d=64, mode=0, sp=0,
+        scale=0.125, ws=O + 0x6000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.attn_bwd_workspace_bytes(q_seq, H)
+    return lib.attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, q_seq, kv_len, H, Hkv, d, mode, sp,
+                        scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=3, Hkv=2), ERR_SHAPE),
+    (dict(q_seq=-1), ERR_SHAPE),
+    (dict(mode=7), ERR_SHAPE),
+    (dict(mode=1, sp=1), ERR_SHAPE),
+    (dict(sp=5, q_seq=4, kv_len=8), ERR_SHAPE),       # causal start_pos + q_seq > kv_len
+    (dict(mode=1, q_seq=4, kv_len=5), ERR_SHAPE),      # full needs kv_len == q_seq
+    (dict(scale=float("nan")), ERR_SHAPE),
+    (dict(d=80), ERR_UNSUP),
+    (dict(q_seq=1 << 20, kv_len=1 << 20, H=64, Hkv=64, d=64, ws_bytes=1 << 40), ERR_UNSUP),
+    (dict(ws_bytes=8), ERR_WS),
+    (dict(lse=None), ERR_NULL),
+    (dict(dout=None), ERR_NULL),
+    (dict(dq=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL),
+    (dict(dk=None), ERR_NULL),
+    (dict(dv=O + 0x5004), ERR_ALIGN),
+    (dict(ws=O + 0x6008), ERR_ALIGN),
+    (dict(q_seq=0, kv_len=0, q=None, k=None, dk=None), OK),
+])
+def test_attn_bwd_rejects_on_host(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.attn_bwd_workspace_bytes(16384, 32) == 16384 * 32 * 4
+    assert lib.attn_bwd_workspace_bytes(3, 5) == 256  # rounded up to 256 bytes
+    assert lib.attn_bwd_workspace_bytes(0, 4) == 0
+    assert lib.attn_bwd_workspace_bytes(-1, 4) == 0
+    assert lib.attn_bwd_workspace_bytes(4, 0) == 0
 
 
 def test_validation_order_sizes_before_pointers(lib):

@@ -1,0 +1,218 @@
+"""Backward parity: attn_bwd through the C ABI (fed by the GPU forward's out
+and lse) against the float64 checker's exact gradients on the same seeded
+inputs, element by element. The bound is the forward's out tolerance plus
+the rounding of a float32 sum of the gradient's terms (check_grad): dq sums
+over a row's keys, dk and dv over the rows of every head of a group."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import check_grad, check_out, device, log, to_dev
+from tiled_attention_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+CAUSAL, FULL, CROSS = inputs.CAUSAL, inputs.FULL, inputs.CROSS
+
+
+def gpu_fwd_bwd(q, k, v, g, *, num_heads, num_kv_heads, head_dim, mode, kv_len, start_pos,
+                scale, poison=True):
+    """GPU forward (out, lse), then attn_bwd; outputs pre-filled with NaN so
+    that an element the kernels skip shows."""
+    import torch
+    import tiled_attention_03_amd as ta
+    dev = device()
+    H, Hkv, d = num_heads, num_kv_heads, head_dim
+    n = q.shape[0]
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    out, lse = ta.attention(qd, kd, vd, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=mode,
+                            kv_len=kv_len, start_pos=start_pos, scale=scale)
+    fill = float("nan") if poison else 0.0
+    dq = torch.full((n, H * d), fill, device=dev)
+    dk = torch.full((kv_len, Hkv * d), fill, device=dev)
+    dv = torch.full((kv_len, Hkv * d), fill, device=dev)
+    nbytes = ta.attn_bwd_workspace_bytes(n, H)
+    ws = torch.full((max(nbytes, 4) // 4,), fill, device=dev)
+    ta.attn_bwd(qd, kd, vd, out, gd, lse, dq, dk, dv, n, kv_len, H, Hkv, d, mode, start_pos,
+                scale, ws, nbytes)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def _kw(w):
+    return dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                mode=w.mode, kv_len=w.kv_len, start_pos=w.start_pos, scale=w.scale)
+
+
+def _check_all(got, ref, w, what):
+    """ref: the checker's (dq, dk, dv, dq_m, dk_m, dv_m)."""
+    terms = (w.kv_len, w.q_seq * w.group, w.q_seq * w.group)
+    return [check_grad(a, b, m, n, f"{what} {name}")
+            for name, a, b, m, n in zip(("dq", "dk", "dv"), got, ref[:3], ref[3:], terms)]
+
+
+@pytest.mark.parametrize("w", [inputs.CAUSAL_SMALL, inputs.FULL_1K, inputs.CROSS_512x2K,
+                               inputs.CONTINUE_512], ids=lambda w: w.name)
+def test_backward_pages_workloads(w):
+    log(f"backward parity {w.name}")
+    q, k, v = inputs.make_prefill(w)
+    g = inputs.normal(q.shape, w.seed_base + 7)
+    got = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    ref = oracle.attention_backward(q, k, v, g, magnitudes=True, **_kw(w))
+    e = _check_all(got, ref, w, w.name)
+    log("  max|d| dq={:.2e} dk={:.2e} dv={:.2e}".format(*e))
+
+
+def test_backward_long_causal_sampled():
+    """The 16384-row causal pass with heavy K rows: dq on sampled rows and
+    dk, dv on sampled keys of KV head 0 (the checker computes the query heads
+    of that KV head in full, the rest is left out)."""
+    w = inputs.CAUSAL_16K
+    log(f"backward parity (sampled) {w.name}")
+    q, k, v = inputs.make_prefill(w)
+    g = inputs.normal(q.shape, w.seed_base + 7)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    rng = np.random.default_rng(7099)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 8191, 16383],
+                                     rng.choice(w.q_seq, 10, replace=False)]))
+    heavy = inputs.heavy_rows(w.kv_len, w.heavy_frac, w.seed_base + 4)
+    keys = np.unique(np.concatenate([[0, 1, 127, 128, 8192, 16352, 16383], heavy[:3],
+                                     rng.choice(w.kv_len, 8, replace=False)]))
+    rq, rk, rv, mq, mk, mv = oracle.attention_backward(q, k, v, g, rows=rows, keys=keys,
+                                                       kv_heads=[0], magnitudes=True, **_kw(w))
+    group, d = w.group, w.head_dim
+    cq = slice(0, group * d)      # query heads of KV head 0
+    ck = slice(0, d)
+    n_rows = w.q_seq * group
+    e_q = check_grad(dq[rows][:, cq], rq[:, cq], mq[:, cq], w.kv_len, "dq sampled")
+    e_k = check_grad(dk[keys][:, ck], rk[:, ck], mk[:, ck], n_rows, "dk sampled")
+    e_v = check_grad(dv[keys][:, ck], rv[:, ck], mv[:, ck], n_rows, "dv sampled")
+    log(f"  rows={len(rows)} keys={len(keys)} max|d| dq={e_q:.2e} dk={e_k:.2e} dv={e_v:.2e}")
+    assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+
+
+BWD_SWEEP = [
+    # mode, q_seq, kv_len, H, Hkv, d, start_pos
+    (CAUSAL, 1, 1, 1, 1, 64, 0),
+    (CAUSAL, 5, 5, 2, 1, 64, 0),
+    (CAUSAL, 70, 70, 8, 2, 128, 0),
+    (CAUSAL, 129, 129, 6, 3, 128, 0),
+    (CAUSAL, 31, 100, 4, 1, 128, 69),
+    (CAUSAL, 65, 300, 8, 1, 64, 200),
+    (CAUSAL, 3, 1000, 4, 2, 128, 997),
+    (CAUSAL, 200, 330, 16, 2, 64, 130),
+    (FULL, 47, 47, 4, 2, 64, 0),
+    (FULL, 96, 96, 3, 1, 128, 0),
+    (CROSS, 7, 1, 4, 2, 64, 0),
+    (CROSS, 33, 31, 2, 2, 128, 0),
+    (CROSS, 64, 257, 4, 4, 128, 0),
+    (CROSS, 100, 45, 12, 4, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", BWD_SWEEP, ids=lambda c: "m{}_q{}_kv{}_h{}x{}_d{}_sp{}".format(*c))
+def test_backward_ragged_sweep(case):
+    """Ragged shapes: partial query and key tiles, GQA groups of 1 to 8,
+    continuation windows, single-key windows."""
+    mode, n, kv, H, Hkv, d, sp = case
+    w, q, k, v = inputs.random_case(1100 + n * 7 + kv, mode, n, kv, H, Hkv, d, start_pos=sp,
+                                    kv_rows=kv + 5)
+    k[kv:] = np.nan  # rows past kv_len must never be read into a result
+    v[kv:] = np.nan
+    g = inputs.normal(q.shape, 1101 + n)
+    got = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    ref = oracle.attention_backward(q, k, v, g, magnitudes=True, **_kw(w))
+    _check_all(got, ref, w, str(case))
+
+
+def test_backward_single_key_windows():
+    """CROSS over one key: dq = dk = 0 and dv is the sum of dout over rows and
+    the group's heads."""
+    H, Hkv, d, n = 8, 2, 128, 40
+    w, q, k, v = inputs.random_case(1150, CROSS, n, 1, H, Hkv, d)
+    g = inputs.normal(q.shape, 1151)
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    assert np.abs(dq).max() <= 1e-5 and np.abs(dk).max() <= 1e-5
+    want = g.astype(np.float64).reshape(n, Hkv, H // Hkv, d).sum(axis=(0, 2)).reshape(1, -1)
+    check_out(dv, want, "single key dv")
+
+
+def test_backward_empty_query_batch_zeroes_key_gradients():
+    import torch
+    import tiled_attention_03_amd as ta
+    H, Hkv, d, kv = 4, 2, 64, 50
+    dev = device()
+    k = to_dev(inputs.normal((kv, Hkv * d), 1160))
+    dk = torch.full((kv, Hkv * d), float("nan"), device=dev)
+    dv = torch.full((kv, Hkv * d), float("nan"), device=dev)
+    empty = torch.empty((0, H * d), device=dev)
+    lse = torch.empty((0, H, 2), device=dev)
+    ws = torch.empty((4,), device=dev)
+    ta.attn_bwd(empty, k, k, empty, empty, lse, empty, dk, dv, 0, kv, H, Hkv, d, CROSS, 0,
+                0.125, ws, 0)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_backward_zero_keys():
+    """CROSS with kv_len = 0: every window empty, dq = 0."""
+    H, Hkv, d, n = 4, 2, 64, 9
+    q = inputs.normal((n, H * d), 1170)
+    k = np.zeros((1, Hkv * d), np.float32)
+    g = inputs.normal((n, H * d), 1171)
+    dq, dk, dv = gpu_fwd_bwd(q, k, k, g, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=CROSS,
+                             kv_len=0, start_pos=0, scale=0.125)
+    assert np.array_equal(dq, np.zeros_like(dq)) and dk.size == 0 and dv.size == 0
+
+
+def test_backward_deterministic():
+    w, q, k, v = inputs.random_case(1180, CAUSAL, 300, 300, 8, 2, 128)
+    g = inputs.normal(q.shape, 1181)
+    a = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    b = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_backward_graph_replay():
+    """Forward and backward captured in one graph, replayed with the
+    program's own work in between: every replay matches the eager result."""
+    import torch
+    import tiled_attention_03_amd as ta
+    H, Hkv, d, n = 8, 2, 64, 160
+    w, q, k, v = inputs.random_case(1190, CAUSAL, n, n, H, Hkv, d)
+    g = inputs.normal(q.shape, 1191)
+    dev = device()
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    out = torch.empty((n, H * d), device=dev)
+    lse = torch.empty((n, H, 2), device=dev)
+    dq = torch.empty((n, H * d), device=dev)
+    dk = torch.empty((n, Hkv * d), device=dev)
+    dv = torch.empty((n, Hkv * d), device=dev)
+    nbytes = ta.attn_bwd_workspace_bytes(n, H)
+    ws = torch.empty((nbytes // 4,), device=dev)
+
+    def step():
+        ta.attn_fwd(qd, kd, vd, out, lse, n, n, H, Hkv, d, CAUSAL, 0, w.scale)
+        ta.attn_bwd(qd, kd, vd, out, gd, lse, dq, dk, dv, n, n, H, Hkv, d, CAUSAL, 0, w.scale,
+                    ws, nbytes)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in (dq, dk, dv)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for x in (dq, dk, dv):
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip((dq, dk, dv), eager):
+            assert torch.equal(x, y), f"replay {rep} differs"

@@ -51,6 +51,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_rope.restype = I
         L.attn_rope_table.argtypes = [P, I, I, ctypes.c_double, P]
         L.attn_rope_table.restype = I
+        L.attn_bwd_workspace_bytes.argtypes = [I, I]
+        L.attn_bwd_workspace_bytes.restype = S
+        L.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, S, P]
+        L.attn_bwd.restype = I
         L.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
         L.attn_decode_workspace_bytes.restype = S
         L.attn_decode_workspace_init.argtypes = [P, S, I, I, I, I, P]
@@ -184,6 +188,47 @@ def attn_rope_table(cos_sin, rows: int, head_dim: int, theta: float, stream=None
     """Enqueue the fill of a standard rotary table [rows, head_dim/2, 2]."""
     _check(lib().attn_rope_table(_ptr(cos_sin, max(rows, 0) * head_dim, "cos_sin"), int(rows),
                                  int(head_dim), float(theta), _stream(stream)))
+
+
+def attn_bwd_workspace_bytes(q_seq: int, num_heads: int) -> int:
+    return int(lib().attn_bwd_workspace_bytes(q_seq, num_heads))
+
+
+def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, q_seq: int, kv_len: int, num_heads: int,
+             num_kv_heads: int, head_dim: int, mode: int, start_pos: int, scale: float,
+             workspace, workspace_bytes: int, stream=None) -> None:
+    """Enqueue the attention backward (see include/ta03.h): dq, dk, dv from
+    the forward's inputs, its out and lse, and dout."""
+    qn = q_seq * num_heads * head_dim
+    kn = kv_len * num_kv_heads * head_dim
+    wsp = _workspace_ptr(workspace, workspace_bytes)
+    _check(lib().attn_bwd(
+        _ptr(q, qn, "q"), _ptr(k, kn, "k"), _ptr(v, kn, "v"), _ptr(out, qn, "out"),
+        _ptr(dout, qn, "dout"), _ptr(lse, q_seq * num_heads * 2, "lse"), _ptr(dq, qn, "dq"),
+        _ptr(dk, kn, "dk"), _ptr(dv, kn, "dv"), q_seq, kv_len, num_heads, num_kv_heads,
+        head_dim, mode, start_pos, float(scale), wsp, int(workspace_bytes), _stream(stream)))
+
+
+def attention_backward(q, k, v, out, dout, lse, *, num_heads: int, num_kv_heads: int,
+                       head_dim: int, mode: int, kv_len: Optional[int] = None,
+                       start_pos: int = 0, scale: Optional[float] = None, stream=None):
+    """Allocate dq, dk, dv and the scratch with torch and call attn_bwd;
+    returns (dq, dk, dv) with dk, dv of kv_len rows."""
+    import torch
+    q_seq = q.shape[0]
+    if kv_len is None:
+        kv_len = k.shape[0]
+    if scale is None:
+        scale = head_dim ** -0.5
+    dev = q.device
+    dq = torch.empty((q_seq, num_heads * head_dim), dtype=torch.float32, device=dev)
+    dk = torch.empty((kv_len, num_kv_heads * head_dim), dtype=torch.float32, device=dev)
+    dv = torch.empty((kv_len, num_kv_heads * head_dim), dtype=torch.float32, device=dev)
+    nbytes = attn_bwd_workspace_bytes(q_seq, num_heads)
+    ws = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=dev)
+    attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, q_seq, kv_len, num_heads, num_kv_heads,
+             head_dim, mode, start_pos, scale, ws, nbytes, stream)
+    return dq, dk, dv
 
 
 def attn_decode_workspace_bytes(num_heads: int, num_kv_heads: int, head_dim: int,

@@ -1,0 +1,522 @@
+// Attention backward on gfx950 f32 matrix cores.
+//
+// meganeura attention.wgsl writes, beside the output, the pair (row max m,
+// log of the running sum l) "for backward"; the pages give no backward. This
+// is the gradient of the forward's definition for a loss with dL/dout =
+// dout, built on that pair: with s = scale <q_i, k_j> and the forward's
+// (m_i, log l_i),
+//   P_ij  = exp(s_ij - m_i - log l_i)      (the softmax, recomputed exactly)
+//   dP_ij = <dout_i, v_j>,   D_i = <dout_i, out_i>
+//   dS_ij = P_ij (dP_ij - D_i)
+//   dq_i  = scale sum_j dS_ij k_j
+//   dk_j  = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i
+// summed over the query heads of each KV head for dk, dv (GQA).
+//
+// Two kernels, no atomics (run-to-run bitwise deterministic):
+//   * dq kernel (query-parallel, the forward's decomposition): a wave owns 32
+//     query rows of one head, holds Q^T (pre-scaled to log2 units) and dout^T
+//     as MFMA B operands in registers, and streams K/V tiles of 32 keys
+//     through LDS (HBM -> LDS directly, double-buffered, both XOR-swizzled).
+//     Per tile: S^T = K Q^T and dP^T = V dout^T (keys x rows), P^T and dS^T
+//     elementwise in the accumulator registers, dq^T += K^T dS^T with dS^T
+//     reused in place as the B operand (the forward's P.V pairing). It also
+//     computes D_i from out and dout and stores it for the second kernel;
+//   * dk/dv kernel (key-parallel): a wave owns 32 keys of one KV head, holds
+//     K and V as B operands in registers, and walks the query row tiles of
+//     every head of its group that can see its keys (causal: rows from
+//     key - start_pos on), Q and dout tiles streamed through LDS with their
+//     (m, log l) and D. Per tile: S = Q K^T and dP = dout V^T (rows x keys),
+//     then dv^T += dout^T P and dk^T += Q^T dS with P and dS in place.
+// Both run at one wave per SIMD: the accumulators (dq^T; dk^T and dv^T) live
+// in the accumulation registers beside the operands held in registers.
+
+#include <hip/hip_runtime.h>
+
+#include "ta03_internal.h"
+
+namespace ta03 {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kBlock = 256;  // 4 waves
+constexpr int kWaves = 4;
+constexpr int kBM = 32;      // query rows per wave (dq) / per tile (dk, dv)
+constexpr int kBN = 32;      // keys per tile (dq) / per wave (dk, dv)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Row index held by accumulator register r in half-wave hh of a 32x32 MFMA
+// result: 8*(r/4) + 4*hh + r%4.
+__device__ __forceinline__ int acc_row(int r, int hh) {
+    return 8 * (r >> 2) + 4 * hh + (r & 3);
+}
+
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+}
+
+// Offset (floats) in a swizzled LDS row of the NB floats starting at logical
+// column NB*j: 16-byte chunk c of row r is stored at position c ^ (r % 16).
+template <int NB>
+__device__ __forceinline__ int swz_cols(int j, int r) {
+    if constexpr (NB == 4) {
+        return 4 * (j ^ (r & 15));
+    } else {
+        return 4 * ((j >> 1) ^ (r & 15)) + 2 * (j & 1);
+    }
+}
+
+struct BwdArgs {
+    int q_seq, kv_len, num_heads, num_kv_heads, group;
+    int causal, start_pos;
+    float qscale;  // scale * log2(e)
+    float scale;
+    int hg, rs, n_head_blocks, n_row_blocks;  // dq kernel block shape
+    int n_key_blocks;                         // dk/dv kernel: 128-key blocks per KV head
+};
+
+// Issue this wave's share (inst = wave, wave + 4, ...) of a 32-row, D-wide
+// tile starting at row row0 of a matrix with row stride ld into LDS,
+// XOR-swizzled; row indices are clamped to row_hi - 1.
+template <int D>
+__device__ __forceinline__ void issue_rows(const float* base, long long ld, int row0, int row_hi,
+                                           float* dst, int wave, int lane) {
+    constexpr int CPR = D / 4;
+    constexpr int LOADS = kBN * D / 4 / 64;
+#pragma unroll 1
+    for (int inst = wave; inst < LOADS; inst += kWaves) {
+        const int s = inst * 64 + lane;
+        const int r = s / CPR, p = s % CPR;
+        const int row = min(row0 + r, row_hi - 1);
+        const float* g = base + (size_t)row * ld + 4 * (p ^ (r & 15));
+        __builtin_amdgcn_global_load_lds(g, (lds_void*)(dst + inst * 256), 16, 0, 0);
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kBlock, 1)
+bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
+              const float* __restrict__ v, const float* __restrict__ o,
+              const float* __restrict__ dout, const float* __restrict__ lse,
+              float* __restrict__ dq, float* __restrict__ delta, BwdArgs a) {
+    constexpr int NB = D / 32;
+    constexpr int TILE_F = kBN * D;
+    extern __shared__ __attribute__((aligned(16))) float smem[];  // [2][K tile | V tile]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31;
+    const int hh = lane >> 5;
+
+    const int bid = blockIdx.x;
+    const int head_block = bid % a.n_head_blocks;
+    const int seq = bid / a.n_head_blocks;
+    const int rb = a.causal ? (a.n_row_blocks - 1 - seq) : seq;  // heaviest first
+    const int head = head_block * a.hg + wave % a.hg;
+    const int strip = wave / a.hg;
+    const int row0 = (rb * a.rs + strip) * kBM;
+    const int kv_head = head / a.group;
+    const int qd = a.num_heads * D;
+    const int kvd = a.num_kv_heads * D;
+
+    const int blk_rows_hi = min((rb + 1) * a.rs * kBM, a.q_seq);
+    const int w_block = a.causal ? min(a.start_pos + blk_rows_hi, a.kv_len) : a.kv_len;
+    const bool wave_live = row0 < a.q_seq;
+    const int w_wave_max = !wave_live ? 0
+        : (a.causal ? min(a.start_pos + min(row0 + kBM, a.q_seq), a.kv_len) : a.kv_len);
+    const int w_wave_min = a.causal ? min(a.start_pos + row0 + 1, a.kv_len) : a.kv_len;
+    const int row = row0 + j;
+    const bool ok = row < a.q_seq;
+    const int w_row = a.causal ? min(a.start_pos + row + 1, a.kv_len) : a.kv_len;
+    const int n_tiles = (w_block + kBN - 1) / kBN;
+
+    // Q^T (log2 units) and dout^T operands: lane (j, hh) holds element
+    // 8g + 4hh + c of row j in register 4g + c. D_j = <dout_j, out_j>.
+    float qr[D / 2], gr[D / 2];
+    float dlt, lse2;
+    {
+        const size_t off = (size_t)(ok ? row : 0) * qd + head * D + 4 * hh;
+        float part = 0.f;
+#pragma unroll
+        for (int g = 0; g < D / 8; ++g) {
+            const float4 x = ok ? *reinterpret_cast<const float4*>(q + off + 8 * g)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 y = ok ? *reinterpret_cast<const float4*>(dout + off + 8 * g)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 z = ok ? *reinterpret_cast<const float4*>(o + off + 8 * g)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            qr[4 * g + 0] = x.x * a.qscale;
+            qr[4 * g + 1] = x.y * a.qscale;
+            qr[4 * g + 2] = x.z * a.qscale;
+            qr[4 * g + 3] = x.w * a.qscale;
+            gr[4 * g + 0] = y.x;
+            gr[4 * g + 1] = y.y;
+            gr[4 * g + 2] = y.z;
+            gr[4 * g + 3] = y.w;
+            part = fmaf(y.x, z.x, part);
+            part = fmaf(y.y, z.y, part);
+            part = fmaf(y.z, z.z, part);
+            part = fmaf(y.w, z.w, part);
+        }
+        dlt = part + __shfl_xor(part, 32);
+        lse2 = 0.f;
+        if (ok) {
+            const float2 ml = *reinterpret_cast<const float2*>(lse + ((size_t)row * a.num_heads + head) * 2);
+            lse2 = (ml.x + ml.y) * kLog2e;
+            if (hh == 0) delta[(size_t)row * a.num_heads + head] = dlt;
+        }
+    }
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+
+    const float* kbase = k + kv_head * D;
+    const float* vbase = v + kv_head * D;
+    auto issue_tile = [&](int t, int buf) {
+        float* kd = smem + (size_t)buf * 2 * TILE_F;
+        issue_rows<D>(kbase, kvd, t * kBN, w_block, kd, wave, lane);
+        issue_rows<D>(vbase, kvd, t * kBN, w_block, kd + TILE_F, wave, lane);
+    };
+
+    if (n_tiles > 0) issue_tile(0, 0);
+    for (int it = 0; it < n_tiles; ++it) {
+        wait_vmem();
+        __syncthreads();  // tile it landed for every wave; buffer (it+1)&1 is free
+        if (it + 1 < n_tiles) issue_tile(it + 1, (it + 1) & 1);
+        const int kv0 = it * kBN;
+        if (wave_live && kv0 < w_wave_max) {  // wave-uniform
+            const float* Ks = smem + (size_t)(it & 1) * 2 * TILE_F;
+            const float* Vs = Ks + TILE_F;
+            // S^T = K Q^T and dP^T = V dout^T (row: key, column: query j).
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = 0.f;
+                dp[r] = 0.f;
+            }
+            const float* kr = Ks + j * D;
+            const float* vr = Vs + j * D;
+#pragma unroll
+            for (int g = 0; g < D / 8; ++g) {
+                const int c = (2 * g + hh) ^ (j & 15);
+                const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * c);
+                const float4 vv = *reinterpret_cast<const float4*>(vr + 4 * c);
+                s = mfma32(kk.x, qr[4 * g + 0], s);
+                dp = mfma32(vv.x, gr[4 * g + 0], dp);
+                s = mfma32(kk.y, qr[4 * g + 1], s);
+                dp = mfma32(vv.y, gr[4 * g + 1], dp);
+                s = mfma32(kk.z, qr[4 * g + 2], s);
+                dp = mfma32(vv.z, gr[4 * g + 2], dp);
+                s = mfma32(kk.w, qr[4 * g + 3], s);
+                dp = mfma32(vv.w, gr[4 * g + 3], dp);
+            }
+            // dS^T in place of S^T; keys outside the row's window weigh 0.
+            const bool need_mask = kv0 + kBN > w_wave_min;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const bool valid = !need_mask || kv0 + acc_row(r, hh) < w_row;
+                const float p = valid ? __builtin_amdgcn_exp2f(s[r] - lse2) : 0.f;
+                s[r] = p * (dp[r] - dlt);
+            }
+            // dq^T += K^T dS^T: k-step t pairs keys acc_row(t, 0) and
+            // acc_row(t, 1); block b row m is head-dim NB*m + b.
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) {
+                const int kr2 = acc_row(tt, hh);
+                const float* kp = Ks + kr2 * D + swz_cols<NB>(j, kr2);
+                if constexpr (NB == 4) {
+                    const float4 kv = *reinterpret_cast<const float4*>(kp);
+                    acc[0] = mfma32(kv.x, s[tt], acc[0]);
+                    acc[1] = mfma32(kv.y, s[tt], acc[1]);
+                    acc[2] = mfma32(kv.z, s[tt], acc[2]);
+                    acc[3] = mfma32(kv.w, s[tt], acc[3]);
+                } else {
+                    const float2 kv = *reinterpret_cast<const float2*>(kp);
+                    acc[0] = mfma32(kv.x, s[tt], acc[0]);
+                    acc[1] = mfma32(kv.y, s[tt], acc[1]);
+                }
+            }
+        }
+    }
+
+    if (!ok) return;
+    float* drow = dq + (size_t)row * qd + head * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int i = acc_row(r, hh);
+        if constexpr (NB == 4) {
+            *reinterpret_cast<float4*>(drow + 4 * i) =
+                make_float4(acc[0][r] * a.scale, acc[1][r] * a.scale, acc[2][r] * a.scale,
+                            acc[3][r] * a.scale);
+        } else {
+            *reinterpret_cast<float2*>(drow + 2 * i) =
+                make_float2(acc[0][r] * a.scale, acc[1][r] * a.scale);
+        }
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kBlock, 1)
+bwd_dkdv_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                const float* __restrict__ v, const float* __restrict__ dout,
+                const float* __restrict__ lse, const float* __restrict__ delta,
+                float* __restrict__ dk, float* __restrict__ dv, BwdArgs a) {
+    constexpr int NB = D / 32;
+    constexpr int TILE_F = kBM * D;
+    // [2][Q tile | dout tile], then [2][64 floats: (m, log l) x 32 rows][64: D x 32, twice]
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    float* vecs = smem + 4 * TILE_F;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31;
+    const int hh = lane >> 5;
+
+    const int bid = blockIdx.x;
+    const int kv_head = bid % a.num_kv_heads;
+    const int kb = bid / a.num_kv_heads;  // low keys first: the most rows see them
+    const int blk_key0 = kb * kWaves * kBN;
+    const int key0 = blk_key0 + wave * kBN;
+    const bool strip_live = key0 < a.kv_len;
+    const int key = key0 + j;
+    const int qd = a.num_heads * D;
+    const int kvd = a.num_kv_heads * D;
+
+    // K (log2 units) and V of key j as B operands: element 8g + 4hh + c in
+    // register 4g + c. Keys past kv_len read the last key (masked below).
+    float kr[D / 2], vr[D / 2];
+    {
+        const size_t off = (size_t)min(key, a.kv_len - 1) * kvd + kv_head * D + 4 * hh;
+#pragma unroll
+        for (int g = 0; g < D / 8; ++g) {
+            const float4 x = *reinterpret_cast<const float4*>(k + off + 8 * g);
+            const float4 y = *reinterpret_cast<const float4*>(v + off + 8 * g);
+            kr[4 * g + 0] = x.x * a.qscale;
+            kr[4 * g + 1] = x.y * a.qscale;
+            kr[4 * g + 2] = x.z * a.qscale;
+            kr[4 * g + 3] = x.w * a.qscale;
+            vr[4 * g + 0] = y.x;
+            vr[4 * g + 1] = y.y;
+            vr[4 * g + 2] = y.z;
+            vr[4 * g + 3] = y.w;
+        }
+    }
+
+    f32x16 dka[NB], dva[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dka[b][r] = 0.f;
+            dva[b][r] = 0.f;
+        }
+
+    // Query rows that see some key of the block: causal rows from
+    // blk_key0 - start_pos on (window start_pos + i + 1 > blk_key0).
+    const int i_lo = a.causal ? max(0, blk_key0 - a.start_pos) : 0;
+    const int qt0 = i_lo / kBM;
+    const int n_qt = i_lo < a.q_seq ? (a.q_seq + kBM - 1) / kBM - qt0 : 0;
+    const int total = a.group * n_qt;
+
+    auto issue = [&](int it, int buf) {
+        const int h = kv_head * a.group + it / n_qt;
+        const int row0 = (qt0 + it % n_qt) * kBM;
+        float* qdst = smem + (size_t)buf * 2 * TILE_F;
+        issue_rows<D>(q + h * D, qd, row0, a.q_seq, qdst, wave, lane);
+        issue_rows<D>(dout + h * D, qd, row0, a.q_seq, qdst + TILE_F, wave, lane);
+        if (wave == 0) {
+            // lane l: (m, log l) component l % 2 of row l / 2; D of row l % 32
+            const int rl = min(row0 + (lane >> 1), a.q_seq - 1);
+            const int rd = min(row0 + (lane & 31), a.q_seq - 1);
+            float* vd = vecs + buf * 128;
+            __builtin_amdgcn_global_load_lds(lse + ((size_t)rl * a.num_heads + h) * 2 + (lane & 1),
+                                             (lds_void*)vd, 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(delta + (size_t)rd * a.num_heads + h,
+                                             (lds_void*)(vd + 64), 4, 0, 0);
+        }
+    };
+
+    if (total > 0) issue(0, 0);
+    for (int it = 0; it < total; ++it) {
+        wait_vmem();
+        __syncthreads();  // tile it landed for every wave; buffer (it+1)&1 is free
+        if (it + 1 < total) issue(it + 1, (it + 1) & 1);
+        const int row0 = (qt0 + it % n_qt) * kBM;
+        const int rows_hi = min(row0 + kBM, a.q_seq);
+        // Largest and smallest window over the tile's rows.
+        const int w_max = a.causal ? min(a.start_pos + rows_hi, a.kv_len) : a.kv_len;
+        const int w_min = a.causal ? min(a.start_pos + row0 + 1, a.kv_len) : a.kv_len;
+        if (strip_live && key0 < w_max) {  // wave-uniform
+            const float* Qs = smem + (size_t)(it & 1) * 2 * TILE_F;
+            const float* Gs = Qs + TILE_F;
+            const float* vd = vecs + (it & 1) * 128;
+            // S = Q K^T and dP = dout V^T (row: query, column: key j).
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = 0.f;
+                dp[r] = 0.f;
+            }
+            const float* qrow = Qs + j * D;
+            const float* grow = Gs + j * D;
+#pragma unroll
+            for (int g = 0; g < D / 8; ++g) {
+                const int c = (2 * g + hh) ^ (j & 15);
+                const float4 qq = *reinterpret_cast<const float4*>(qrow + 4 * c);
+                const float4 gg = *reinterpret_cast<const float4*>(grow + 4 * c);
+                s = mfma32(qq.x, kr[4 * g + 0], s);
+                dp = mfma32(gg.x, vr[4 * g + 0], dp);
+                s = mfma32(qq.y, kr[4 * g + 1], s);
+                dp = mfma32(gg.y, vr[4 * g + 1], dp);
+                s = mfma32(qq.z, kr[4 * g + 2], s);
+                dp = mfma32(gg.z, vr[4 * g + 2], dp);
+                s = mfma32(qq.w, kr[4 * g + 3], s);
+                dp = mfma32(gg.w, vr[4 * g + 3], dp);
+            }
+            // P in place of S, dS in place of dP; rows past q_seq and keys
+            // outside a row's window weigh 0.
+            const bool need_mask = key0 + kBN > w_min || rows_hi - row0 < kBM;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ir = acc_row(r, hh);
+                const int i = row0 + ir;
+                const float lse2 = (vd[2 * ir] + vd[2 * ir + 1]) * kLog2e;
+                const float dl = vd[64 + ir];
+                bool valid = true;
+                if (need_mask) {
+                    const int w = a.causal ? min(a.start_pos + i + 1, a.kv_len) : a.kv_len;
+                    valid = i < a.q_seq && key < w;
+                }
+                const float p = valid ? __builtin_amdgcn_exp2f(s[r] - lse2) : 0.f;
+                s[r] = p;
+                dp[r] = p * (dp[r] - dl);
+            }
+            // dv^T += dout^T P and dk^T += Q^T dS: k-step t pairs rows
+            // acc_row(t, 0) and acc_row(t, 1); block b row m is head-dim
+            // NB*m + b.
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) {
+                const int ir = acc_row(tt, hh);
+                const int cofs = ir * D + swz_cols<NB>(j, ir);
+                if constexpr (NB == 4) {
+                    const float4 gg = *reinterpret_cast<const float4*>(Gs + cofs);
+                    const float4 qq = *reinterpret_cast<const float4*>(Qs + cofs);
+                    dva[0] = mfma32(gg.x, s[tt], dva[0]);
+                    dka[0] = mfma32(qq.x, dp[tt], dka[0]);
+                    dva[1] = mfma32(gg.y, s[tt], dva[1]);
+                    dka[1] = mfma32(qq.y, dp[tt], dka[1]);
+                    dva[2] = mfma32(gg.z, s[tt], dva[2]);
+                    dka[2] = mfma32(qq.z, dp[tt], dka[2]);
+                    dva[3] = mfma32(gg.w, s[tt], dva[3]);
+                    dka[3] = mfma32(qq.w, dp[tt], dka[3]);
+                } else {
+                    const float2 gg = *reinterpret_cast<const float2*>(Gs + cofs);
+                    const float2 qq = *reinterpret_cast<const float2*>(Qs + cofs);
+                    dva[0] = mfma32(gg.x, s[tt], dva[0]);
+                    dka[0] = mfma32(qq.x, dp[tt], dka[0]);
+                    dva[1] = mfma32(gg.y, s[tt], dva[1]);
+                    dka[1] = mfma32(qq.y, dp[tt], dka[1]);
+                }
+            }
+        }
+    }
+
+    if (!strip_live || key >= a.kv_len) return;
+    float* krow = dk + (size_t)key * kvd + kv_head * D;
+    float* vrow = dv + (size_t)key * kvd + kv_head * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int i = acc_row(r, hh);
+        if constexpr (NB == 4) {
+            *reinterpret_cast<float4*>(krow + 4 * i) =
+                make_float4(dka[0][r] * a.scale, dka[1][r] * a.scale, dka[2][r] * a.scale,
+                            dka[3][r] * a.scale);
+            *reinterpret_cast<float4*>(vrow + 4 * i) =
+                make_float4(dva[0][r], dva[1][r], dva[2][r], dva[3][r]);
+        } else {
+            *reinterpret_cast<float2*>(krow + 2 * i) =
+                make_float2(dka[0][r] * a.scale, dka[1][r] * a.scale);
+            *reinterpret_cast<float2*>(vrow + 2 * i) = make_float2(dva[0][r], dva[1][r]);
+        }
+    }
+}
+
+int gcd_int(int x, int y) {
+    while (y) {
+        const int t = x % y;
+        x = y;
+        y = t;
+    }
+    return x;
+}
+
+template <int D>
+hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, const float* o,
+                               const float* dout, const float* lse, float* dq, float* dk,
+                               float* dv, float* delta, const BwdArgs& a, hipStream_t stream) {
+    const size_t tile_bytes = (size_t)kBN * D * sizeof(float);
+    const size_t lds_dq = 2 * 2 * tile_bytes;
+    const size_t lds_dkdv = 2 * 2 * tile_bytes + 2 * 128 * sizeof(float);
+    static const hipError_t attr1 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(bwd_dq_kernel<D>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dq);
+    static const hipError_t attr2 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(bwd_dkdv_kernel<D>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dkdv);
+    if (attr1 != hipSuccess) return attr1;
+    if (attr2 != hipSuccess) return attr2;
+    const long long g1 = (long long)a.n_head_blocks * a.n_row_blocks;
+    if (g1 > 0) {
+        hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)g1), dim3(kBlock), lds_dq, stream,
+                           q, k, v, o, dout, lse, dq, delta, a);
+    }
+    // With no query rows the dk/dv blocks walk no tiles and write zeros.
+    const long long g2 = (long long)a.num_kv_heads * a.n_key_blocks;
+    if (g2 > 0) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)g2), dim3(kBlock), lds_dkdv,
+                           stream, q, k, v, dout, lse, delta, dk, dv, a);
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const float* q, const float* k, const float* v, const float* o,
+                           const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                           float* delta, const PrefillShape& s, hipStream_t stream) {
+    BwdArgs a;
+    a.q_seq = s.q_seq;
+    a.kv_len = s.kv_len;
+    a.num_heads = s.num_heads;
+    a.num_kv_heads = s.num_kv_heads;
+    a.group = s.num_heads / s.num_kv_heads;
+    a.causal = s.causal;
+    a.start_pos = s.start_pos;
+    a.qscale = s.scale * kLog2e;
+    a.scale = s.scale;
+    a.hg = gcd_int(a.group, kWaves);
+    a.rs = kWaves / a.hg;
+    a.n_head_blocks = s.num_heads / a.hg;
+    a.n_row_blocks = (s.q_seq + a.rs * kBM - 1) / (a.rs * kBM);
+    a.n_key_blocks = (s.kv_len + kWaves * kBN - 1) / (kWaves * kBN);
+    hipError_t e;
+    if (s.head_dim == 128) {
+        e = launch_bwd_instance<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, a, stream);
+    } else {
+        e = launch_bwd_instance<64>(q, k, v, o, dout, lse, dq, dk, dv, delta, a, stream);
+    }
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+}  // namespace ta03

@@ -98,6 +98,54 @@ int attn_fwd_rope(const float* q, long long q_stride, const float* k, long long 
                       true, rope_cs, rope_rows, stream);
 }
 
+size_t attn_bwd_workspace_bytes(int q_seq, int num_heads) {
+    if (q_seq < 0 || num_heads < 1) return 0;
+    const size_t n = (size_t)q_seq * (size_t)num_heads * sizeof(float);
+    return (n + 255) / 256 * 256;
+}
+
+int attn_bwd(const float* q, const float* k, const float* v, const float* out, const float* dout,
+             const float* lse, float* dq, float* dk, float* dv, int q_seq, int kv_len,
+             int num_heads, int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0) return TA03_ERR_SHAPE;
+    if (q_seq < 0 || kv_len < 0 || start_pos < 0) return TA03_ERR_SHAPE;
+    if (mode != TA03_CAUSAL && mode != TA03_FULL && mode != TA03_CROSS) return TA03_ERR_SHAPE;
+    if (mode != TA03_CAUSAL && start_pos != 0) return TA03_ERR_SHAPE;
+    if (mode == TA03_CAUSAL && (long long)start_pos + q_seq > kv_len) return TA03_ERR_SHAPE;
+    if (mode == TA03_FULL && kv_len != q_seq) return TA03_ERR_SHAPE;
+    if (!std::isfinite(scale)) return TA03_ERR_SHAPE;
+    if (!head_dim_supported(head_dim)) return TA03_ERR_UNSUPPORTED;
+    if ((long long)q_seq * num_heads * head_dim >= kMaxElems ||
+        (long long)kv_len * num_kv_heads * head_dim >= kMaxElems)
+        return TA03_ERR_UNSUPPORTED;
+    if (q_seq == 0 && kv_len == 0) return TA03_OK;
+    if (workspace_bytes < attn_bwd_workspace_bytes(q_seq, num_heads)) return TA03_ERR_WORKSPACE;
+    if (q_seq > 0 && (q == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
+                      dq == nullptr || workspace == nullptr))
+        return TA03_ERR_NULL;
+    if (kv_len > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+        return TA03_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+        !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        !aligned16(workspace))
+        return TA03_ERR_ALIGN;
+    ta03::PrefillShape s;
+    s.q_seq = q_seq;
+    s.kv_len = kv_len;
+    s.num_heads = num_heads;
+    s.num_kv_heads = num_kv_heads;
+    s.head_dim = head_dim;
+    s.causal = mode == TA03_CAUSAL ? 1 : 0;
+    s.start_pos = start_pos;
+    s.scale = scale;
+    s.q_stride = s.out_stride = (long long)num_heads * head_dim;
+    s.k_stride = s.v_stride = (long long)num_kv_heads * head_dim;
+    const hipError_t e = ta03::launch_backward(q, k, v, out, dout, lse, dq, dk, dv,
+                                               static_cast<float*>(workspace), s, stream);
+    return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
+}
+
 int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStream_t stream) {
     if (rows < 0 || head_dim < 2 || head_dim % 2 != 0) return TA03_ERR_SHAPE;
     if (!(theta > 0.0) || !std::isfinite(theta)) return TA03_ERR_SHAPE;

@@ -38,6 +38,12 @@ DecodePlan decode_plan(const DecodeShape& s);
 hipError_t launch_prefill(const float* q, const float* k, const float* v, float* out,
                           float* lse, const PrefillShape& s, hipStream_t stream);
 
+// Attention backward (dense rows): dq [q_seq, H*d]; dk, dv [kv_len, Hkv*d];
+// delta: q_seq*H floats of scratch (D_i = <dout_i, out_i> per row and head).
+hipError_t launch_backward(const float* q, const float* k, const float* v, const float* o,
+                           const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                           float* delta, const PrefillShape& s, hipStream_t stream);
+
 // Rotary table: entry (p, e) = (cos, sin) of p * theta^(-2e/head_dim).
 hipError_t launch_rope_table(float* cs, int rows, int head_dim, double theta, hipStream_t stream);
 
