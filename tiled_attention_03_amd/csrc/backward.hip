@@ -27,8 +27,10 @@
 //     key - start_pos on), Q and dout tiles streamed through LDS with their
 //     (m, log l) and D. Per tile: S = Q K^T and dP = dout V^T (rows x keys),
 //     then dv^T += dout^T P and dk^T += Q^T dS with P and dS in place.
-// Both run at one wave per SIMD: the accumulators (dq^T; dk^T and dv^T) live
-// in the accumulation registers beside the operands held in registers.
+// The dq kernel runs two waves per SIMD (two 64 KiB blocks per CU; at d 128
+// the compiler spills a few registers, which measured cheaper than one wave
+// per SIMD); the dk/dv kernel two at d 64 and one at d 128, where dk^T and
+// dv^T sit in the accumulation registers beside K and V.
 
 #include <hip/hip_runtime.h>
 
@@ -99,7 +101,7 @@ __device__ __forceinline__ void issue_rows(const float* base, long long ld, int 
 }
 
 template <int D>
-__global__ void __launch_bounds__(kBlock, 1)
+__global__ void __launch_bounds__(kBlock, 2)
 bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
               const float* __restrict__ v, const float* __restrict__ o,
               const float* __restrict__ dout, const float* __restrict__ lse,
@@ -265,7 +267,7 @@ bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
 }
 
 template <int D>
-__global__ void __launch_bounds__(kBlock, 1)
+__global__ void __launch_bounds__(kBlock, D == 64 ? 2 : 1)
 bwd_dkdv_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 const float* __restrict__ v, const float* __restrict__ dout,
                 const float* __restrict__ lse, const float* __restrict__ delta,
