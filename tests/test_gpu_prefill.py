@@ -27,10 +27,13 @@ def _run_both(w, q, k, v, rows=None, with_lse=True):
     return got_o, got_l, ref_o, ref_l
 
 
+@pytest.mark.parametrize("rows", ["auto", "16", "32"])
 @pytest.mark.parametrize("w", [inputs.CAUSAL_SMALL, inputs.FULL_1K, inputs.CROSS_512x2K,
                                inputs.CONTINUE_512], ids=lambda w: w.name)
-def test_pages_workloads_full_parity(w):
-    log(f"prefill parity {w.name}")
+def test_pages_workloads_full_parity(w, rows, monkeypatch):
+    if rows != "auto":
+        monkeypatch.setenv("TA03_PREFILL_ROWS", rows)
+    log(f"prefill parity {w.name} rows={rows}")
     q, k, v = inputs.make_prefill(w)
     go, gl, ro, rl = _run_both(w, q, k, v)
     e_o = check_out(go, ro, w.name)
@@ -38,9 +41,13 @@ def test_pages_workloads_full_parity(w):
     log(f"  max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
 
 
-def test_long_causal_sampled_rows():
+@pytest.mark.parametrize("rows", ["auto", "16"])
+def test_long_causal_sampled_rows(rows, monkeypatch):
     """16384-row causal pass with heavy K rows: sampled rows against the
-    checker, in the launch configuration the benchmark times."""
+    checker, in the launch configuration the benchmark times (auto), and
+    through the 16-row kernel at this size."""
+    if rows != "auto":
+        monkeypatch.setenv("TA03_PREFILL_ROWS", rows)
     w = inputs.CAUSAL_16K
     log(f"prefill parity (sampled rows) {w.name}")
     q, k, v = inputs.make_prefill(w)
@@ -87,11 +94,17 @@ SWEEP = [
 ]
 
 
+@pytest.mark.parametrize("rows", ["auto", "16", "32"])
 @pytest.mark.parametrize("case", SWEEP, ids=[f"m{c[0]}_q{c[1]}_kv{c[2]}_h{c[3]}x{c[4]}_d{c[5]}_sp{c[6]}"
                                              for c in SWEEP])
-def test_ragged_sweep(case):
+def test_ragged_sweep(case, rows, monkeypatch):
+    """Every shape through the launch's own choice and through each of the
+    two prefill kernels (16-row and 32-row waves), forced by the library's
+    TA03_PREFILL_ROWS override."""
+    if rows != "auto":
+        monkeypatch.setenv("TA03_PREFILL_ROWS", rows)
     mode, n, kv, H, Hkv, d, sp = case
-    log(f"prefill sweep {case}")
+    log(f"prefill sweep {case} rows={rows}")
     w, q, k, v = inputs.random_case(700 + SWEEP.index(case), mode, n, kv, H, Hkv, d,
                                     start_pos=sp)
     go, gl, ro, rl = _run_both(w, q, k, v)

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libta03.so")
 
-SOURCES = ["ta03_api.cpp", "prefill.hip", "decode.hip", "rope.hip", "backward.hip"]
+SOURCES = ["ta03_api.cpp", "prefill.hip", "prefill16.hip", "decode.hip", "rope.hip",
+           "backward.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

@@ -47,6 +47,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "ta03_internal.h"
 
 namespace ta03 {
@@ -60,6 +63,7 @@ constexpr int kWaves = 4;
 constexpr int kBM = 32;      // query rows per wave
 constexpr int kBN = 32;      // keys per tile
 constexpr int kTargetWaves = 2048;  // two waves per SIMD on 256 CUs
+constexpr int kNumCUs = 256;
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -491,6 +495,15 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     a.n_row_blocks = (s.q_seq + a.rs * kBM - 1) / (a.rs * kBM);
     const long long grid = (long long)a.n_head_blocks * a.n_row_blocks;
     if (grid <= 0) return hipSuccess;
+    if (!rope) {
+        // Fewer blocks than compute units: the 16-row kernel, which needs no
+        // shared tiles, spreads the work over more waves. The environment
+        // variable TA03_PREFILL_ROWS (16 or 32) overrides the choice, for
+        // testing both kernels on the same shapes.
+        const char* force = std::getenv("TA03_PREFILL_ROWS");
+        const bool use16 = force != nullptr ? std::strcmp(force, "16") == 0 : grid < kNumCUs;
+        if (use16) return launch_prefill16(q, k, v, out, lse, s, stream);
+    }
     const size_t tile_bytes = (size_t)kBN * s.head_dim * sizeof(float);
     const size_t lds = (size_t)ks * 2 * 2 * tile_bytes;  // per split: 2 buffers x (K, V)
     hipError_t e;

@@ -38,6 +38,13 @@ DecodePlan decode_plan(const DecodeShape& s);
 hipError_t launch_prefill(const float* q, const float* k, const float* v, float* out,
                           float* lse, const PrefillShape& s, hipStream_t stream);
 
+// 16-row variant for launches with few query rows (no rotation); chosen by
+// launch_prefill when the 32-row kernel would launch fewer blocks than there
+// are compute units, or forced by the environment variable
+// TA03_PREFILL_ROWS = 16 | 32.
+hipError_t launch_prefill16(const float* q, const float* k, const float* v, float* out,
+                            float* lse, const PrefillShape& s, hipStream_t stream);
+
 // Attention backward (dense rows): dq [q_seq, H*d]; dk, dv [kv_len, Hkv*d];
 // delta: q_seq*H floats of scratch (D_i = <dout_i, out_i> per row and head).
 hipError_t launch_backward(const float* q, const float* k, const float* v, const float* o,
