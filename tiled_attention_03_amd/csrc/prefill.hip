@@ -78,6 +78,21 @@ __device__ __forceinline__ int acc_row(int r, int hh) {
     return 8 * (r >> 2) + 4 * hh + (r & 3);
 }
 
+// All-reduce over the two half-waves with one vector instruction (no LDS
+// round trip): v_permlane32_swap with both operands x hands each lane the
+// pair {x[l % 32], x[l % 32 + 32]} (lower lane first, so both partners
+// combine them in the same order).
+__device__ __forceinline__ float pair_max32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile loads have landed
 }
@@ -324,7 +339,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             float mx = s[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = pair_max32(mx);
             const float m_new = fmaxf(m_run, mx);
             const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
             float ls = 0.f;
@@ -333,7 +348,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
                 ls += s[r];
             }
-            ls += __shfl_xor(ls, 32);
+            ls = pair_sum32(ls);
             l_run = l_run * corr + ls;
             m_run = m_new;
             // Rescale only if some row's max moved (after the first tiles it

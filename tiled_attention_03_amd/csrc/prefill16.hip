@@ -21,8 +21,9 @@
 //     exactly register t of the score result in that lane, so P never leaves
 //     registers; O^T block b row m is head-dim (D/16)*m + b, so a lane reads
 //     D/16 contiguous floats of one V row per k-step;
-//   * row max and sum: in-lane over 4 keys plus two exchanges across the
-//     16-lane groups; exp is exp2 with log2(e) folded into the scaled Q.
+//   * row max and sum: in-lane over 4 keys plus two lane-pair exchanges
+//     (v_permlane16_swap, v_permlane32_swap); exp is exp2 with log2(e)
+//     folded into the scaled Q.
 
 #include <hip/hip_runtime.h>
 
@@ -44,6 +45,31 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// All-reduce over lane pairs with one vector instruction (no LDS round trip):
+// v_permlane16_swap / v_permlane32_swap with both operands x hand each lane
+// the pair {x[l], x[l ^ 16]} resp. {x[l % 32], x[l % 32 + 32]} (lower lane
+// first, so both partners combine them in the same order).
+__device__ __forceinline__ float pair_max16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float pair_max32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 __device__ __forceinline__ float comp(const float4& x, int i) {
@@ -157,9 +183,7 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         // result needs was found missing in the generated code.
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[r] = kv0 + 4 * g + r < w_row ? s[r] : -INFINITY;
-        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mx = pair_max32(pair_max16(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))));
         const float m_new = fmaxf(m_run, mx);
         const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
         float ls = 0.f;
@@ -168,8 +192,7 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
             s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
             ls += s[r];
         }
-        ls += __shfl_xor(ls, 16);
-        ls += __shfl_xor(ls, 32);
+        ls = pair_sum32(pair_sum16(ls));
         l_run = l_run * corr + ls;
         m_run = m_new;
         if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0ull) {
