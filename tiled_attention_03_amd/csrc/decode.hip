@@ -19,8 +19,9 @@
 //   * K rows go HBM -> registers directly in the score layout: lane (key,
 //     quarter) holds interleaved 16-byte pieces of its key (each load
 //     instruction covers 64 contiguous bytes of 16 rows) and forms 4-head
-//     dot products against Q broadcast from LDS; a quad shuffle finishes
-//     them, and max and sum over the wave's 16 keys use shuffles. Staging K
+//     dot products against Q broadcast from LDS; two DPP quad steps finish
+//     them, and max and sum over the wave's 16 keys use DPP mirrors and the
+//     row / half-wave swaps (no LDS permutes on the path). Staging K
 //     through LDS measured markedly slower here;
 //   * V rows go HBM -> registers directly in the P.V layout (lane = 4
 //     head-dim columns of one key, 128-bit coalesced);
@@ -92,6 +93,42 @@ __device__ __forceinline__ void chunking(const uint32_t* kv_pos, const Args& a,
     *kv_len = L;
     *chunk = c;
     *n_active = (L + c - 1) / c;
+}
+
+// Cross-lane steps that do not go through the LDS permute unit: DPP moves
+// inside a row of 16 lanes, and the gfx950 row / half-wave swaps
+// (v_permlane16_swap, v_permlane32_swap with both operands x hand each lane
+// the pair {x[l], x[l ^ 16]} resp. {x[l % 32], x[l % 32 + 32]}, lower lane
+// first, so both partners combine them in the same order).
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kRowMirror = 0x140;     // lane i <- 15 - i within a row of 16
+constexpr int kRowHalfMirror = 0x141; // lane i <- 7 - i within each half-row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL,
+                                                      0xF, 0xF, false));
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float pair_max16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float pair_max32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
 // LDS written by this wave's lanes becomes readable by its other lanes: DS
@@ -240,22 +277,22 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
         float p[kG], corr[kG];
 #pragma unroll
         for (int h = 0; h < kG; ++h) {
-            s[h] += __shfl_xor(s[h], 1);
-            s[h] += __shfl_xor(s[h], 2);
+            s[h] += dpp<kQuadXor1>(s[h]);
+            s[h] += dpp<kQuadXor2>(s[h]);
+            // From here each value is the same on the 4 lanes of its key's
+            // quad: the half-row mirror pairs neighbouring keys, the row
+            // mirror pairs key pairs, the swaps pair rows and half-waves, so
+            // each key enters the max and the sum once.
             const float x = valid ? s[h] : -INFINITY;
-            float mx = x;
-            mx = fmaxf(mx, __shfl_xor(mx, 4));
-            mx = fmaxf(mx, __shfl_xor(mx, 8));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            float mx = fmaxf(x, dpp<kRowHalfMirror>(x));
+            mx = fmaxf(mx, dpp<kRowMirror>(mx));
+            mx = pair_max32(pair_max16(mx));
             const float m_new = fmaxf(m_run[h], mx);
             corr[h] = __builtin_amdgcn_exp2f(m_run[h] - m_new);
             p[h] = __builtin_amdgcn_exp2f(x - m_new);
-            float sm = qq == 0 ? p[h] : 0.f;  // one lane per key
-            sm += __shfl_xor(sm, 4);
-            sm += __shfl_xor(sm, 8);
-            sm += __shfl_xor(sm, 16);
-            sm += __shfl_xor(sm, 32);
+            float sm = p[h] + dpp<kRowHalfMirror>(p[h]);
+            sm += dpp<kRowMirror>(sm);
+            sm = pair_sum32(pair_sum16(sm));
             l_run[h] = l_run[h] * corr[h] + sm;
             m_run[h] = m_new;
         }
@@ -307,13 +344,17 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // Sum the key groups of the wave (same running max within a wave).
 #pragma unroll
     for (int h = 0; h < kG; ++h) {
-#pragma unroll
-        for (int m = LPR; m < 64; m <<= 1) {
-            acc[h].x += __shfl_xor(acc[h].x, m);
-            acc[h].y += __shfl_xor(acc[h].y, m);
-            acc[h].z += __shfl_xor(acc[h].z, m);
-            acc[h].w += __shfl_xor(acc[h].w, m);
+        if constexpr (LPR == 16) {  // key groups in lane bits 4 and 5
+            acc[h].x = pair_sum16(acc[h].x);
+            acc[h].y = pair_sum16(acc[h].y);
+            acc[h].z = pair_sum16(acc[h].z);
+            acc[h].w = pair_sum16(acc[h].w);
         }
+        static_assert(LPR == 16 || LPR == 32, "head_dim 64 or 128");
+        acc[h].x = pair_sum32(acc[h].x);
+        acc[h].y = pair_sum32(acc[h].y);
+        acc[h].z = pair_sum32(acc[h].z);
+        acc[h].w = pair_sum32(acc[h].w);
     }
     if (kr == 0) {
 #pragma unroll
