@@ -412,7 +412,7 @@ def main():
                 "workload": w.name, "ms": round(r["mean_s"] * 1e3, 3),
                 "flops_per_call": r["flops"], "TFLOP/s": round(r["tflops_kernel"], 3),
                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                "kernels": "bwd_dq_kernel<128> + bwd_dkdv_kernel<128>"}
+                "kernels": "bwd_dq_kernel<128> + bwd_dkdv16_kernel<128>"}
             print(f"[bench] backward {result['backward']}", flush=True)
 
     if args.only != "prefill":

@@ -52,10 +52,15 @@ def _check_all(got, ref, w, what):
             for name, a, b, m, n in zip(("dq", "dk", "dv"), got, ref[:3], ref[3:], terms)]
 
 
+@pytest.mark.parametrize("keys", ["auto", "16", "32"])
 @pytest.mark.parametrize("w", [inputs.CAUSAL_SMALL, inputs.FULL_1K, inputs.CROSS_512x2K,
                                inputs.CONTINUE_512], ids=lambda w: w.name)
-def test_backward_pages_workloads(w):
-    log(f"backward parity {w.name}")
+def test_backward_pages_workloads(w, keys, monkeypatch):
+    """The pages' prefill workloads; keys: the dk/dv kernel the launch picks,
+    or the 16-key / 32-key one forced by the library's TA03_BWD_KEYS."""
+    if keys != "auto":
+        monkeypatch.setenv("TA03_BWD_KEYS", keys)
+    log(f"backward parity {w.name} keys={keys}")
     q, k, v = inputs.make_prefill(w)
     g = inputs.normal(q.shape, w.seed_base + 7)
     got = gpu_fwd_bwd(q, k, v, g, **_kw(w))
@@ -64,10 +69,13 @@ def test_backward_pages_workloads(w):
     log("  max|d| dq={:.2e} dk={:.2e} dv={:.2e}".format(*e))
 
 
-def test_backward_long_causal_sampled():
+@pytest.mark.parametrize("keys", ["auto", "32"])
+def test_backward_long_causal_sampled(keys, monkeypatch):
     """The 16384-row causal pass with heavy K rows: dq on sampled rows and
     dk, dv on sampled keys of KV head 0 (the checker computes the query heads
     of that KV head in full, the rest is left out)."""
+    if keys != "auto":
+        monkeypatch.setenv("TA03_BWD_KEYS", keys)
     w = inputs.CAUSAL_16K
     log(f"backward parity (sampled) {w.name}")
     q, k, v = inputs.make_prefill(w)
@@ -111,10 +119,13 @@ BWD_SWEEP = [
 ]
 
 
+@pytest.mark.parametrize("keys", ["auto", "16", "32"])
 @pytest.mark.parametrize("case", BWD_SWEEP, ids=lambda c: "m{}_q{}_kv{}_h{}x{}_d{}_sp{}".format(*c))
-def test_backward_ragged_sweep(case):
+def test_backward_ragged_sweep(case, keys, monkeypatch):
     """Ragged shapes: partial query and key tiles, GQA groups of 1 to 8,
-    continuation windows, single-key windows."""
+    continuation windows, single-key windows; through both dk/dv kernels."""
+    if keys != "auto":
+        monkeypatch.setenv("TA03_BWD_KEYS", keys)
     mode, n, kv, H, Hkv, d, sp = case
     w, q, k, v = inputs.random_case(1100 + n * 7 + kv, mode, n, kv, H, Hkv, d, start_pos=sp,
                                     kv_rows=kv + 5)

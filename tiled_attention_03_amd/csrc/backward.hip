@@ -34,6 +34,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "ta03_internal.h"
 
 namespace ta03 {
@@ -453,6 +456,197 @@ bwd_dkdv_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 }
 
+// dk/dv with 16-key waves on v_mfma_f32_16x16x4_f32: per wave K, V (B
+// operands) and the dk^T, dv^T accumulators take 32 registers each at
+// head_dim 128 (half of the 32-key kernel), so two waves share a SIMD.
+// Block: 8 waves x 16 keys of one KV head; query tiles of 16 rows (and their
+// dout rows, (m, log l) and D) are staged in XOR-swizzled LDS, double-
+// buffered. S = Q K^T: k-step s of lane group g carries head-dim g*D/4 + s
+// (each lane reads d/4 contiguous floats of its query row); the result's
+// register r of lane (j, g) is query 4g + r, key j, so in dv^T += dout^T P
+// and dk^T += Q^T dS the k-step t of lane group g pairs query 4g + t with
+// register t -- P and dS stay in registers. dk^T / dv^T block b row m is
+// head-dim (d/16)*m + b.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float comp4(const float4& x, int i) {
+    return i == 0 ? x.x : (i == 1 ? x.y : (i == 2 ? x.z : x.w));
+}
+
+constexpr int k16Waves = 8;
+constexpr int k16Block = 64 * k16Waves;
+constexpr int k16Keys = 16;  // keys per wave
+constexpr int k16Rows = 16;  // query rows per tile
+
+template <int D>
+__global__ void __launch_bounds__(k16Block, 1)
+bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                  const float* __restrict__ v, const float* __restrict__ dout,
+                  const float* __restrict__ lse, const float* __restrict__ delta,
+                  float* __restrict__ dk, float* __restrict__ dv, BwdArgs a) {
+    constexpr int KS = D / 4;   // k-steps of the score products
+    constexpr int NB = D / 16;  // 16-row blocks of dk^T, dv^T
+    constexpr int CPR = D / 4;  // 16-byte chunks per row
+    constexpr int TILE_F = k16Rows * D;
+    constexpr int LOADS = TILE_F / 4 / 64;  // wave instructions per tile (<= 8)
+    // [2][Q tile | dout tile], then [2][64 floats: (m, log l) x 16 rows, D x 16 rows, D again]
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    float* vecs = smem + 4 * TILE_F;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;
+    const int g = lane >> 4;
+
+    const int bid = blockIdx.x;
+    const int kv_head = bid % a.num_kv_heads;
+    const int kb = bid / a.num_kv_heads;  // low keys first: the most rows see them
+    const int blk_key0 = kb * k16Waves * k16Keys;
+    const int key0 = blk_key0 + wave * k16Keys;
+    const bool strip_live = key0 < a.kv_len;
+    const int key = key0 + j;
+    const int qd = a.num_heads * D;
+    const int kvd = a.num_kv_heads * D;
+
+    // K (log2 units) and V of key j: element g*KS + s in register s.
+    float kr[KS], vr[KS];
+    {
+        const size_t off = (size_t)min(key, a.kv_len - 1) * kvd + kv_head * D + g * KS;
+#pragma unroll
+        for (int c = 0; c < KS / 4; ++c) {
+            const float4 x = *reinterpret_cast<const float4*>(k + off + 4 * c);
+            const float4 y = *reinterpret_cast<const float4*>(v + off + 4 * c);
+            kr[4 * c + 0] = x.x * a.qscale;
+            kr[4 * c + 1] = x.y * a.qscale;
+            kr[4 * c + 2] = x.z * a.qscale;
+            kr[4 * c + 3] = x.w * a.qscale;
+            vr[4 * c + 0] = y.x;
+            vr[4 * c + 1] = y.y;
+            vr[4 * c + 2] = y.z;
+            vr[4 * c + 3] = y.w;
+        }
+    }
+
+    f32x4 dka[NB], dva[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        dka[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dva[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int i_lo = a.causal ? max(0, blk_key0 - a.start_pos) : 0;
+    const int qt0 = i_lo / k16Rows;
+    const int n_qt = i_lo < a.q_seq ? (a.q_seq + k16Rows - 1) / k16Rows - qt0 : 0;
+    const int total = a.group * n_qt;
+
+    auto issue = [&](int it, int buf) {
+        const int h = kv_head * a.group + it / n_qt;
+        const int row0 = (qt0 + it % n_qt) * k16Rows;
+        float* qdst = smem + (size_t)buf * 2 * TILE_F;
+        if (wave < LOADS) {
+            // slot s holds row s / CPR, position s % CPR = logical chunk ^ (row % 16)
+            const int s_ = wave * 64 + lane;
+            const int r = s_ / CPR, p = s_ % CPR;
+            const int row = min(row0 + r, a.q_seq - 1);
+            const size_t src = (size_t)row * qd + h * D + 4 * (p ^ (r & 15));
+            __builtin_amdgcn_global_load_lds(q + src, (lds_void*)(qdst + wave * 256), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(dout + src, (lds_void*)(qdst + TILE_F + wave * 256),
+                                             16, 0, 0);
+        }
+        if (wave == k16Waves - 1) {
+            // lanes 0..31: (m, log l) component l % 2 of row l / 2; 32..63: D of row l % 16
+            const float* src = lane < 32
+                ? lse + ((size_t)min(row0 + (lane >> 1), a.q_seq - 1) * a.num_heads + h) * 2 + (lane & 1)
+                : delta + (size_t)min(row0 + (lane & 15), a.q_seq - 1) * a.num_heads + h;
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(vecs + buf * 64), 4, 0, 0);
+        }
+    };
+
+    if (total > 0) issue(0, 0);
+    for (int it = 0; it < total; ++it) {
+        wait_vmem();
+        __syncthreads();  // tile it landed for every wave; buffer (it+1)&1 is free
+        if (it + 1 < total) issue(it + 1, (it + 1) & 1);
+        const int row0 = (qt0 + it % n_qt) * k16Rows;
+        const int rows_hi = min(row0 + k16Rows, a.q_seq);
+        const int w_max = a.causal ? min(a.start_pos + rows_hi, a.kv_len) : a.kv_len;
+        if (strip_live && key0 < w_max) {  // wave-uniform
+            const float* Qs = smem + (size_t)(it & 1) * 2 * TILE_F;
+            const float* Gs = Qs + TILE_F;
+            const float* vd = vecs + (it & 1) * 64;
+            // S = Q K^T, dP = dout V^T: register r of lane (j, g) is query
+            // row0 + 4g + r, key key0 + j.
+            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < KS / 4; ++c) {
+                const int pos = ((g * KS / 4 + c) ^ (j & 15)) * 4;
+                const float4 qq = *reinterpret_cast<const float4*>(Qs + j * D + pos);
+                const float4 gg = *reinterpret_cast<const float4*>(Gs + j * D + pos);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s = mfma16(comp4(qq, e), kr[4 * c + e], s);
+                    dp = mfma16(comp4(gg, e), vr[4 * c + e], dp);
+                }
+            }
+            // P in s, dS in dp. The window test is a select (no branch between
+            // the products and the first vector reads of their results).
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ir = 4 * g + r;
+                const int i = row0 + ir;
+                const float lse2 = (vd[2 * ir] + vd[2 * ir + 1]) * kLog2e;
+                const float dl = vd[32 + ir];
+                const int w = a.causal ? min(a.start_pos + i + 1, a.kv_len) : a.kv_len;
+                const bool valid = i < a.q_seq && key < w;
+                const float p = valid ? __builtin_amdgcn_exp2f(s[r] - lse2) : 0.f;
+                s[r] = p;
+                dp[r] = p * (dp[r] - dl);
+            }
+            // dv^T += dout^T P, dk^T += Q^T dS: k-step t of lane group g is
+            // query row 4g + t; lane (m, g) reads head-dims NB*m .. NB*m + NB.
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int ir = 4 * g + t;
+#pragma unroll
+                for (int c = 0; c < NB / 4; ++c) {
+                    const int pos = (((NB * j) / 4 + c) ^ (ir & 15)) * 4;
+                    const float4 gg = *reinterpret_cast<const float4*>(Gs + ir * D + pos);
+                    const float4 qq = *reinterpret_cast<const float4*>(Qs + ir * D + pos);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dva[4 * c + e] = mfma16(comp4(gg, e), s[t], dva[4 * c + e]);
+                        dka[4 * c + e] = mfma16(comp4(qq, e), dp[t], dka[4 * c + e]);
+                    }
+                }
+            }
+        }
+    }
+
+    if (!strip_live || key >= a.kv_len) return;
+    // dk^T / dv^T block b, register r of lane (j, g): head-dim NB*(4g + r) + b.
+    float* krow = dk + (size_t)key * kvd + kv_head * D;
+    float* vrow = dv + (size_t)key * kvd + kv_head * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int c = 0; c < NB / 4; ++c) {
+            const int d0 = NB * (4 * g + r) + 4 * c;
+            *reinterpret_cast<float4*>(krow + d0) =
+                make_float4(dka[4 * c + 0][r] * a.scale, dka[4 * c + 1][r] * a.scale,
+                            dka[4 * c + 2][r] * a.scale, dka[4 * c + 3][r] * a.scale);
+            *reinterpret_cast<float4*>(vrow + d0) =
+                make_float4(dva[4 * c + 0][r], dva[4 * c + 1][r], dva[4 * c + 2][r],
+                            dva[4 * c + 3][r]);
+        }
+    }
+}
+
 int gcd_int(int x, int y) {
     while (y) {
         const int t = x % y;
@@ -483,6 +677,22 @@ hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, c
                            q, k, v, o, dout, lse, dq, delta, a);
     }
     // With no query rows the dk/dv blocks walk no tiles and write zeros.
+    const char* force = std::getenv("TA03_BWD_KEYS");
+    const bool keys16 = force != nullptr ? std::strcmp(force, "16") == 0 : D == 128;
+    if (keys16) {
+        const size_t lds16 = 2 * 2 * (size_t)k16Rows * D * sizeof(float) + 2 * 64 * sizeof(float);
+        static const hipError_t attr3 = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(bwd_dkdv16_kernel<D>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds16);
+        if (attr3 != hipSuccess) return attr3;
+        const long long nkb = (a.kv_len + k16Waves * k16Keys - 1) / (k16Waves * k16Keys);
+        const long long g3 = (long long)a.num_kv_heads * nkb;
+        if (g3 > 0) {
+            hipLaunchKernelGGL((bwd_dkdv16_kernel<D>), dim3((unsigned)g3), dim3(k16Block), lds16,
+                               stream, q, k, v, dout, lse, delta, dk, dv, a);
+        }
+        return hipSuccess;
+    }
     const long long g2 = (long long)a.num_kv_heads * a.n_key_blocks;
     if (g2 > 0) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)g2), dim3(kBlock), lds_dkdv,
