@@ -50,6 +50,8 @@ constexpr int kWaves = 4;
 constexpr int kBM = 32;      // query rows per wave (dq) / per tile (dk, dv)
 constexpr int kBN = 32;      // keys per tile (dq) / per wave (dk, dv)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kNumCUs = 256;
+constexpr int kTargetWaves = 2048;  // two waves per SIMD
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -81,20 +83,20 @@ struct BwdArgs {
     int causal, start_pos;
     float qscale;  // scale * log2(e)
     float scale;
-    int hg, rs, n_head_blocks, n_row_blocks;  // dq kernel block shape
+    int hg, rs, ks, n_head_blocks, n_row_blocks;  // dq kernel block shape (ks: key splits)
     int n_key_blocks;                         // dk/dv kernel: 128-key blocks per KV head
 };
 
-// Issue this wave's share (inst = wave, wave + 4, ...) of a 32-row, D-wide
+// Issue this wave's share (inst = first, first + step, ...) of a 32-row, D-wide
 // tile starting at row row0 of a matrix with row stride ld into LDS,
 // XOR-swizzled; row indices are clamped to row_hi - 1.
 template <int D>
 __device__ __forceinline__ void issue_rows(const float* base, long long ld, int row0, int row_hi,
-                                           float* dst, int wave, int lane) {
+                                           float* dst, int first, int step, int lane) {
     constexpr int CPR = D / 4;
     constexpr int LOADS = kBN * D / 4 / 64;
 #pragma unroll 1
-    for (int inst = wave; inst < LOADS; inst += kWaves) {
+    for (int inst = first; inst < LOADS; inst += step) {
         const int s = inst * 64 + lane;
         const int r = s / CPR, p = s % CPR;
         const int row = min(row0 + r, row_hi - 1);
@@ -123,8 +125,13 @@ bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int head_block = bid % a.n_head_blocks;
     const int seq = bid / a.n_head_blocks;
     const int rb = a.causal ? (a.n_row_blocks - 1 - seq) : seq;  // heaviest first
-    const int head = head_block * a.hg + wave % a.hg;
-    const int strip = wave / a.hg;
+    // wave -> (key split, head, strip); waves of one key split share its tiles
+    const int kvs = wave % a.ks;
+    const int rest = wave / a.ks;
+    const int head = head_block * a.hg + rest % a.hg;
+    const int strip = rest / a.hg;
+    const int wg = wave / a.ks;       // index within its key split's group
+    const int gw = kWaves / a.ks;     // waves per key split
     const int row0 = (rb * a.rs + strip) * kBM;
     const int kv_head = head / a.group;
     const int qd = a.num_heads * D;
@@ -139,7 +146,11 @@ bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int row = row0 + j;
     const bool ok = row < a.q_seq;
     const int w_row = a.causal ? min(a.start_pos + row + 1, a.kv_len) : a.kv_len;
-    const int n_tiles = (w_block + kBN - 1) / kBN;
+    const int n_tiles_all = (w_block + kBN - 1) / kBN;
+    const int nt = (n_tiles_all + a.ks - 1) / a.ks;
+    const int t_begin = kvs * nt;
+    const int t_end = min(t_begin + nt, n_tiles_all);
+    float* my_lds = smem + (size_t)kvs * 2 * 2 * TILE_F;  // this split's [2][K | V]
 
     // Q^T (log2 units) and dout^T operands: lane (j, hh) holds element
     // 8g + 4hh + c of row j in register 4g + c. D_j = <dout_j, out_j>.
@@ -174,7 +185,7 @@ bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
         if (ok) {
             const float2 ml = *reinterpret_cast<const float2*>(lse + ((size_t)row * a.num_heads + head) * 2);
             lse2 = (ml.x + ml.y) * kLog2e;
-            if (hh == 0) delta[(size_t)row * a.num_heads + head] = dlt;
+            if (hh == 0 && kvs == 0) delta[(size_t)row * a.num_heads + head] = dlt;
         }
     }
 
@@ -187,19 +198,21 @@ bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const float* kbase = k + kv_head * D;
     const float* vbase = v + kv_head * D;
     auto issue_tile = [&](int t, int buf) {
-        float* kd = smem + (size_t)buf * 2 * TILE_F;
-        issue_rows<D>(kbase, kvd, t * kBN, w_block, kd, wave, lane);
-        issue_rows<D>(vbase, kvd, t * kBN, w_block, kd + TILE_F, wave, lane);
+        float* kd = my_lds + (size_t)buf * 2 * TILE_F;
+        issue_rows<D>(kbase, kvd, t * kBN, w_block, kd, wg, gw, lane);
+        issue_rows<D>(vbase, kvd, t * kBN, w_block, kd + TILE_F, wg, gw, lane);
     };
 
-    if (n_tiles > 0) issue_tile(0, 0);
-    for (int it = 0; it < n_tiles; ++it) {
+    if (t_begin < t_end) issue_tile(t_begin, 0);
+    for (int it = 0; it < nt; ++it) {
+        const int t = t_begin + it;
+        const bool have = t < t_end;
         wait_vmem();
-        __syncthreads();  // tile it landed for every wave; buffer (it+1)&1 is free
-        if (it + 1 < n_tiles) issue_tile(it + 1, (it + 1) & 1);
-        const int kv0 = it * kBN;
-        if (wave_live && kv0 < w_wave_max) {  // wave-uniform
-            const float* Ks = smem + (size_t)(it & 1) * 2 * TILE_F;
+        __syncthreads();  // tile t landed for every wave; buffer (it+1)&1 is free
+        if (have && t + 1 < t_end) issue_tile(t + 1, (it + 1) & 1);
+        const int kv0 = t * kBN;
+        if (have && wave_live && kv0 < w_wave_max) {  // wave-uniform
+            const float* Ks = my_lds + (size_t)(it & 1) * 2 * TILE_F;
             const float* Vs = Ks + TILE_F;
             // S^T = K Q^T and dP^T = V dout^T (row: key, column: query j).
             f32x16 s, dp;
@@ -250,6 +263,30 @@ bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
                     acc[1] = mfma32(kv.y, s[tt], acc[1]);
                 }
             }
+        }
+    }
+
+    if (a.ks > 1) {
+        // Key splits 1.. publish their dq^T partial sums through LDS (the
+        // tile buffers, free once every wave is past its last tile); split 0
+        // adds them in split order.
+        __syncthreads();
+        constexpr int PART = NB * 16;  // floats per lane
+        float* part = smem + (size_t)(wave * PART) * 64;
+        if (kvs > 0) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) part[(b * 16 + r) * 64 + lane] = acc[b][r];
+        }
+        __syncthreads();
+        if (kvs > 0) return;
+        for (int p = 1; p < a.ks; ++p) {
+            const float* pp = smem + (size_t)((wave + p) * PART) * 64;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[b][r] += pp[(b * 16 + r) * 64 + lane];
         }
     }
 
@@ -337,8 +374,8 @@ bwd_dkdv_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const int h = kv_head * a.group + it / n_qt;
         const int row0 = (qt0 + it % n_qt) * kBM;
         float* qdst = smem + (size_t)buf * 2 * TILE_F;
-        issue_rows<D>(q + h * D, qd, row0, a.q_seq, qdst, wave, lane);
-        issue_rows<D>(dout + h * D, qd, row0, a.q_seq, qdst + TILE_F, wave, lane);
+        issue_rows<D>(q + h * D, qd, row0, a.q_seq, qdst, wave, kWaves, lane);
+        issue_rows<D>(dout + h * D, qd, row0, a.q_seq, qdst + TILE_F, wave, kWaves, lane);
         if (wave == 0) {
             // lane l: (m, log l) component l % 2 of row l / 2; D of row l % 32
             const int rl = min(row0 + (lane >> 1), a.q_seq - 1);
@@ -459,7 +496,8 @@ bwd_dkdv_kernel(const float* __restrict__ q, const float* __restrict__ k,
 // dk/dv with 16-key waves on v_mfma_f32_16x16x4_f32: per wave K, V (B
 // operands) and the dk^T, dv^T accumulators take 32 registers each at
 // head_dim 128 (half of the 32-key kernel), so two waves share a SIMD.
-// Block: 8 waves x 16 keys of one KV head; query tiles of 16 rows (and their
+// Block: W waves x 16 keys of one KV head (W = 8, or 4 to give short key
+// ranges more blocks); query tiles of 16 rows (and their
 // dout rows, (m, log l) and D) are staged in XOR-swizzled LDS, double-
 // buffered. S = Q K^T: k-step s of lane group g carries head-dim g*D/4 + s
 // (each lane reads d/4 contiguous floats of its query row); the result's
@@ -477,13 +515,11 @@ __device__ __forceinline__ float comp4(const float4& x, int i) {
     return i == 0 ? x.x : (i == 1 ? x.y : (i == 2 ? x.z : x.w));
 }
 
-constexpr int k16Waves = 8;
-constexpr int k16Block = 64 * k16Waves;
 constexpr int k16Keys = 16;  // keys per wave
 constexpr int k16Rows = 16;  // query rows per tile
 
-template <int D>
-__global__ void __launch_bounds__(k16Block, 1)
+template <int D, int W>
+__global__ void __launch_bounds__(64 * W, 8 / W)  // 8 waves per CU: two per SIMD
 bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                   const float* __restrict__ v, const float* __restrict__ dout,
                   const float* __restrict__ lse, const float* __restrict__ delta,
@@ -506,7 +542,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int bid = blockIdx.x;
     const int kv_head = bid % a.num_kv_heads;
     const int kb = bid / a.num_kv_heads;  // low keys first: the most rows see them
-    const int blk_key0 = kb * k16Waves * k16Keys;
+    const int blk_key0 = kb * W * k16Keys;
     const int key0 = blk_key0 + wave * k16Keys;
     const bool strip_live = key0 < a.kv_len;
     const int key = key0 + j;
@@ -548,17 +584,18 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const int h = kv_head * a.group + it / n_qt;
         const int row0 = (qt0 + it % n_qt) * k16Rows;
         float* qdst = smem + (size_t)buf * 2 * TILE_F;
-        if (wave < LOADS) {
+#pragma unroll 1
+        for (int inst = wave; inst < LOADS; inst += W) {
             // slot s holds row s / CPR, position s % CPR = logical chunk ^ (row % 16)
-            const int s_ = wave * 64 + lane;
+            const int s_ = inst * 64 + lane;
             const int r = s_ / CPR, p = s_ % CPR;
             const int row = min(row0 + r, a.q_seq - 1);
             const size_t src = (size_t)row * qd + h * D + 4 * (p ^ (r & 15));
-            __builtin_amdgcn_global_load_lds(q + src, (lds_void*)(qdst + wave * 256), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(dout + src, (lds_void*)(qdst + TILE_F + wave * 256),
+            __builtin_amdgcn_global_load_lds(q + src, (lds_void*)(qdst + inst * 256), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(dout + src, (lds_void*)(qdst + TILE_F + inst * 256),
                                              16, 0, 0);
         }
-        if (wave == k16Waves - 1) {
+        if (wave == W - 1) {
             // lanes 0..31: (m, log l) component l % 2 of row l / 2; 32..63: D of row l % 16
             const float* src = lane < 32
                 ? lse + ((size_t)min(row0 + (lane >> 1), a.q_seq - 1) * a.num_heads + h) * 2 + (lane & 1)
@@ -656,16 +693,31 @@ int gcd_int(int x, int y) {
     return x;
 }
 
+template <int D, int W>
+hipError_t launch_dkdv16(long long grid, size_t lds, hipStream_t stream, const float* q,
+                         const float* k, const float* v, const float* dout, const float* lse,
+                         const float* delta, float* dk, float* dv, const BwdArgs& a) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(bwd_dkdv16_kernel<D, W>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    if (grid > 0) {
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<D, W>), dim3((unsigned)grid), dim3(64 * W), lds,
+                           stream, q, k, v, dout, lse, delta, dk, dv, a);
+    }
+    return hipSuccess;
+}
+
 template <int D>
 hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, const float* o,
                                const float* dout, const float* lse, float* dq, float* dk,
                                float* dv, float* delta, const BwdArgs& a, hipStream_t stream) {
     const size_t tile_bytes = (size_t)kBN * D * sizeof(float);
-    const size_t lds_dq = 2 * 2 * tile_bytes;
+    const size_t lds_dq = (size_t)a.ks * 2 * 2 * tile_bytes;  // per key split: 2 x (K, V)
     const size_t lds_dkdv = 2 * 2 * tile_bytes + 2 * 128 * sizeof(float);
     static const hipError_t attr1 = hipFuncSetAttribute(
         reinterpret_cast<const void*>(bwd_dq_kernel<D>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dq);
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)((D == 128 ? 2 : 4) * 2 * 2 * tile_bytes));
     static const hipError_t attr2 = hipFuncSetAttribute(
         reinterpret_cast<const void*>(bwd_dkdv_kernel<D>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dkdv);
@@ -678,20 +730,17 @@ hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, c
     }
     // With no query rows the dk/dv blocks walk no tiles and write zeros.
     const char* force = std::getenv("TA03_BWD_KEYS");
-    const bool keys16 = force != nullptr ? std::strcmp(force, "16") == 0 : D == 128;
+    const bool keys16 = force == nullptr || std::strcmp(force, "32") != 0;
     if (keys16) {
+        // 8 waves of 16 keys per block, or 4 when that leaves compute units
+        // without a block.
         const size_t lds16 = 2 * 2 * (size_t)k16Rows * D * sizeof(float) + 2 * 64 * sizeof(float);
-        static const hipError_t attr3 = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(bwd_dkdv16_kernel<D>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds16);
-        if (attr3 != hipSuccess) return attr3;
-        const long long nkb = (a.kv_len + k16Waves * k16Keys - 1) / (k16Waves * k16Keys);
-        const long long g3 = (long long)a.num_kv_heads * nkb;
-        if (g3 > 0) {
-            hipLaunchKernelGGL((bwd_dkdv16_kernel<D>), dim3((unsigned)g3), dim3(k16Block), lds16,
-                               stream, q, k, v, dout, lse, delta, dk, dv, a);
-        }
-        return hipSuccess;
+        const auto blocks = [&](int w) {
+            return (long long)a.num_kv_heads * ((a.kv_len + w * k16Keys - 1) / (w * k16Keys));
+        };
+        if (blocks(8) >= kNumCUs)
+            return launch_dkdv16<D, 8>(blocks(8), lds16, stream, q, k, v, dout, lse, delta, dk, dv, a);
+        return launch_dkdv16<D, 4>(blocks(4), lds16, stream, q, k, v, dout, lse, delta, dk, dv, a);
     }
     const long long g2 = (long long)a.num_kv_heads * a.n_key_blocks;
     if (g2 > 0) {
@@ -716,8 +765,18 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
     a.start_pos = s.start_pos;
     a.qscale = s.scale * kLog2e;
     a.scale = s.scale;
-    a.hg = gcd_int(a.group, kWaves);
-    a.rs = kWaves / a.hg;
+    // dq block: heads of a GQA group x row strips x key splits = 4 waves; key
+    // splits (as the forward's) only while the launch is short of two waves
+    // per SIMD and each split keeps several key tiles.
+    const long long base_waves = (long long)s.num_heads * ((s.q_seq + kBM - 1) / kBM);
+    const int max_w = s.causal ? min(s.start_pos + s.q_seq, s.kv_len) : s.kv_len;
+    const int key_tiles = (max_w + kBN - 1) / kBN;
+    const int max_ks = s.head_dim == 128 ? 2 : 4;  // 2 buffers x (K, V) per split in 160 KB
+    int ks = 1;
+    while (ks < max_ks && base_waves * ks < kTargetWaves && key_tiles >= 4 * ks * 2) ks *= 2;
+    a.ks = ks;
+    a.hg = gcd_int(a.group, kWaves / ks);
+    a.rs = kWaves / (ks * a.hg);
     a.n_head_blocks = s.num_heads / a.hg;
     a.n_row_blocks = (s.q_seq + a.rs * kBM - 1) / (a.rs * kBM);
     a.n_key_blocks = (s.kv_len + kWaves * kBN - 1) / (kWaves * kBN);
