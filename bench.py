@@ -5,8 +5,10 @@ One step is one call of the prefill path on the long causal workload
 with the (max, log-sum) side output). The same JSON line also carries the
 decode path measured on its cache workload (32/8 heads, head_dim 128, cache
 8192 rows) with the KV cache rotated through 8 copies so the 256 MB
-Infinity Cache cannot serve it, and the other prefill workloads as reported
-figures.
+Infinity Cache cannot serve it. Reported beside them: the smaller prefill
+workloads; the long causal workload read from a fused QKV buffer with row
+strides, with the rotary embedding fused in, and through the backward pass;
+and the decode over a paged cache (16- and 256-row pages).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--only prefill|decode] [--no-cpu-baseline]
@@ -91,21 +93,40 @@ def time_calls(fn, n, torch):
     return float(np.mean(durs)), float(np.min(durs)), wall
 
 
-def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None):
+def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None,
+                  fused_qkv=False):
     """Prefill timing. With graph_replays > 0 the call is captured once in a
     HIP graph and replayed back to back (for kernels shorter than a Python
     launch); otherwise each call is launched eagerly between events. With
     rope_theta the rotary entry point runs (table built once, outside the
-    timed calls; the rotation is not counted in the FLOPs)."""
+    timed calls; the rotation is not counted in the FLOPs). With fused_qkv,
+    q, k and v are column slices of one [rows, (H + 2 Hkv) d] buffer and out
+    is written into a buffer with 64 floats of padding per row
+    (attn_fwd_ex with row strides)."""
     dev = torch.device("cuda:0")
     q, k, v = inputs.make_prefill(w)
-    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
-    del q, k, v
     qdim = w.num_heads * w.head_dim
-    out = torch.empty((w.q_seq, qdim), device=dev)
+    kvdim = w.num_kv_heads * w.head_dim
+    if fused_qkv:
+        assert w.q_seq == w.rows and w.start_pos == 0
+        fused = torch.empty((w.q_seq, qdim + 2 * kvdim), device=dev)
+        for lo, x in ((0, q), (qdim, k), (qdim + kvdim, v)):
+            fused[:, lo:lo + x.shape[1]].copy_(torch.from_numpy(x))
+        qd, kd, vd = fused[:, :qdim], fused[:, qdim:qdim + kvdim], fused[:, qdim + kvdim:]
+        out_wide = torch.empty((w.q_seq, qdim + 64), device=dev)
+        out = out_wide[:, :qdim]
+    else:
+        qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+        out = torch.empty((w.q_seq, qdim), device=dev)
+    del q, k, v
     lse = torch.empty((w.q_seq, w.num_heads, 2), device=dev) if w.with_lse else None
 
-    if rope_theta is None:
+    if fused_qkv:
+        def call(_i):
+            ta.attn_fwd_ex(qd, qd.stride(0), kd, kd.stride(0), vd, vd.stride(0), out,
+                           out.stride(0), lse, 0, w.q_seq, w.kv_len, w.num_heads,
+                           w.num_kv_heads, w.head_dim, w.mode, w.start_pos, w.scale)
+    elif rope_theta is None:
         def call(_i):
             ta.attn_fwd(qd, kd, vd, out, lse, w.q_seq, w.kv_len, w.num_heads, w.num_kv_heads,
                         w.head_dim, w.mode, w.start_pos, w.scale)
@@ -113,7 +134,6 @@ def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None)
         rows = max(w.start_pos + w.q_seq, w.kv_len)
         table = torch.empty((rows, w.head_dim // 2, 2), device=dev)
         ta.attn_rope_table(table, rows, w.head_dim, rope_theta)
-        kvdim = w.num_kv_heads * w.head_dim
 
         def call(_i):
             ta.attn_fwd_rope(qd, qdim, kd, kvdim, vd, kvdim, out, qdim, lse, 0, w.q_seq,
@@ -183,16 +203,27 @@ def bench_backward(w, steps, warmup, torch, ta):
             "tflops_kernel": flops / mean_s / 1e12}
 
 
-def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8):
+def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8, page_size=None):
     """Decode device time. The cache is rotated over `copies` independent
     allocations (copies x 64 MiB > the 256 MB Infinity Cache), and the
     `copies` calls are captured once in a HIP graph and replayed, so the
     GPU runs the calls back to back instead of waiting on Python launches.
-    kv_pos lives in device memory: the same graph serves every kv_pos."""
+    kv_pos lives in device memory: the same graph serves every kv_pos.
+    With page_size, the cache is a pool of shuffled pages (64 unused pages
+    mixed in) read through a page table (attn_decode_paged)."""
     dev = torch.device("cuda:0")
     q, k, v = inputs.make_decode(w)
     qd = torch.from_numpy(q).to(dev)
-    k0, v0 = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    if page_size is None:
+        k0, v0 = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+        table, num_pages = None, 0
+    else:
+        kp, vp, tbl, num_pages = inputs.paged_pool(k, v, page_size, 64, w.seed_base + 9,
+                                                   fill=0.0)
+        k0, v0 = torch.from_numpy(kp).to(dev), torch.from_numpy(vp).to(dev)
+        table = torch.from_numpy(tbl).to(dev)
+        del kp, vp
+    del k, v
     caches = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
     out = torch.empty((1, w.num_heads * w.head_dim), device=dev)
     nbytes = ta.attn_decode_workspace_bytes(w.num_heads, w.num_kv_heads, w.head_dim,
@@ -202,8 +233,13 @@ def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8):
 
     def call(i):
         kc, vc = caches[i % copies]
-        ta.attn_decode(qd, kc, vc, pos, out, None, w.num_heads, w.num_kv_heads,
-                       w.head_dim, w.max_seq, w.scale, ws, nbytes)
+        if page_size is None:
+            ta.attn_decode(qd, kc, vc, pos, out, None, w.num_heads, w.num_kv_heads,
+                           w.head_dim, w.max_seq, w.scale, ws, nbytes)
+        else:
+            ta.attn_decode_paged(qd, kc, vc, num_pages, page_size, table, pos, out, None,
+                                 w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq, w.scale,
+                                 ws, nbytes)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -400,6 +436,14 @@ def main():
                                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4)}
                 print(f"[bench] {wr.name}: {rep[wr.name]}", flush=True)
             result["prefill_reported"] = rep
+            r = bench_prefill(w, 3, 1, torch, ta, fused_qkv=True)
+            result["prefill_strided"] = {
+                "workload": w.name + "_fused_qkv",
+                "layout": "q, k, v column slices of one [16384, 6144] buffer; out row stride 4160",
+                "ms": round(r["mean_s"] * 1e3, 3), "TFLOP/s": round(r["tflops_kernel"], 3),
+                "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
+                "kernel": "prefill_kernel<128, false>"}
+            print(f"[bench] strided {result['prefill_strided']}", flush=True)
             r = bench_prefill(w, 3, 1, torch, ta, rope_theta=10000.0)
             result["prefill_rope"] = {
                 "workload": w.name + "_rope_theta10000",
@@ -429,6 +473,14 @@ def main():
                          "kv_pos": wd.kv_pos_values[-1],
                          "measured_copy_GBps": copy_ceiling(torch)}}
         print(f"[bench] decode {d}", flush=True)
+        if not args.no_reported:
+            paged = {}
+            for P in (16, 256):
+                paged[str(P)] = bench_decode(wd, wd.kv_pos_values, 25, torch, ta, page_size=P)
+                print(f"[bench] decode paged {P}: {paged[str(P)]}", flush=True)
+            result["decode_paged"] = {"workload": wd.name + "_paged", "extra_pages": 64,
+                                      "unit": "GB/s", "page_size": paged,
+                                      "kernel": "decode_kernel<128>"}
         if args.only == "decode":
             result.update({"value": head["GB/s"], "unit": "GB/s",
                            "ms_per_step": head["us"] / 1e3,

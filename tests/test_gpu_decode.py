@@ -195,24 +195,6 @@ def test_graph_replay_follows_device_kv_pos(decode_8k):
         check_lse(lse.cpu().numpy(), rl, f"graph replay lse p={p}")
 
 
-def _paged_pool(k, v, page_size, extra_pages, seed):
-    """Scatter a dense cache into shuffled pages of a pool with unused pages
-    (NaN) mixed in; returns (k_pool, v_pool, table, num_pages)."""
-    max_seq, kvd = k.shape
-    nblk = -(-max_seq // page_size)
-    num_pages = nblk + extra_pages
-    rng = np.random.default_rng(seed)
-    pages = rng.permutation(num_pages)[:nblk].astype(np.int32)
-    kp = np.full((num_pages, page_size, kvd), np.nan, np.float32)
-    vp = np.full((num_pages, page_size, kvd), np.nan, np.float32)
-    for b in range(nblk):
-        rows = slice(b * page_size, min((b + 1) * page_size, max_seq))
-        n = rows.stop - rows.start
-        kp[pages[b], :n] = k[rows]
-        vp[pages[b], :n] = v[rows]
-    return kp, vp, pages, num_pages
-
-
 @pytest.mark.parametrize("page_size", [16, 64, 256])
 def test_paged_decode_matches_dense(decode_8k, page_size):
     """Paged cache with shuffled pages and unused NaN pages: matches the
@@ -222,7 +204,7 @@ def test_paged_decode_matches_dense(decode_8k, page_size):
     import tiled_attention_03_amd as ta
     w, q, k, v, kd, vd = decode_8k
     dev = device()
-    kp, vp, table, num_pages = _paged_pool(k, v, page_size, 37, 870 + page_size)
+    kp, vp, table, num_pages = inputs.paged_pool(k, v, page_size, 37, 870 + page_size)
     kpd, vpd, tbd = to_dev(kp), to_dev(vp), to_dev(table)
     nbytes = ta.attn_decode_workspace_bytes(w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq)
     ws = torch.zeros(nbytes // 4, device=dev)
@@ -253,7 +235,7 @@ def test_paged_decode_ragged_small():
     q = inputs.normal((1, H * d), 881)
     k = inputs.normal((max_seq, Hkv * d), 882)
     v = inputs.normal((max_seq, Hkv * d), 883)
-    kp, vp, table, num_pages = _paged_pool(k, v, P, 3, 884)
+    kp, vp, table, num_pages = inputs.paged_pool(k, v, P, 3, 884)
     dev = device()
     nbytes = ta.attn_decode_workspace_bytes(H, Hkv, d, max_seq)
     ws = torch.zeros(nbytes // 4, device=dev)

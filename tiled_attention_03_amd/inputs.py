@@ -147,3 +147,24 @@ def random_case(seed: int, mode: int, q_seq: int, kv_len: int, num_heads: int,
                  seed_base=seed * 10)
     q, k, v = make_prefill(w)
     return w, q, k, v
+
+
+def paged_pool(k: np.ndarray, v: np.ndarray, page_size: int, extra_pages: int, seed: int,
+               fill=np.nan):
+    """Lay a dense cache [max_seq, Hkv*d] out as a paged pool: the row block
+    b (page_size rows) goes to page table[b] of a pool of nblk + extra_pages
+    pages, with the table a seeded permutation; unused pages and the tail of
+    the last page hold `fill`. Returns (k_pool, v_pool [pages, page_size,
+    Hkv*d], table int32 [nblk], num_pages)."""
+    max_seq, kvd = k.shape
+    nblk = -(-max_seq // page_size)
+    num_pages = nblk + extra_pages
+    table = _rng(seed).permutation(num_pages)[:nblk].astype(np.int32)
+    kp = np.full((num_pages, page_size, kvd), fill, np.float32)
+    vp = np.full((num_pages, page_size, kvd), fill, np.float32)
+    for b in range(nblk):
+        lo = b * page_size
+        n = min(page_size, max_seq - lo)
+        kp[table[b], :n] = k[lo:lo + n]
+        vp[table[b], :n] = v[lo:lo + n]
+    return kp, vp, table, num_pages
