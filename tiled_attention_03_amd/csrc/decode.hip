@@ -131,6 +131,40 @@ __device__ __forceinline__ float pair_max32(float x) {
     return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
+// Sum and max over the 32 lanes of each half-wave (quad steps, half-row and
+// row mirrors, then the row swap); every lane of a half ends with the same
+// value.
+__device__ __forceinline__ float sum32(float x) {
+    x += dpp<kQuadXor1>(x);
+    x += dpp<kQuadXor2>(x);
+    x += dpp<kRowHalfMirror>(x);
+    x += dpp<kRowMirror>(x);
+    return pair_sum16(x);
+}
+__device__ __forceinline__ float max32(float x) {
+    x = fmaxf(x, dpp<kQuadXor1>(x));
+    x = fmaxf(x, dpp<kQuadXor2>(x));
+    x = fmaxf(x, dpp<kRowHalfMirror>(x));
+    x = fmaxf(x, dpp<kRowMirror>(x));
+    return pair_max16(x);
+}
+
+// Split partials cross work-groups (and L2s): written and read with 64-bit
+// device-scope atomic accesses (p 8-byte aligned), which go to the
+// coherence point.
+__device__ __forceinline__ void store_pair(float* p, float lo, float hi) {
+    const unsigned long long u =
+        ((unsigned long long)__float_as_uint(hi) << 32) | (unsigned long long)__float_as_uint(lo);
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_pair(const float* p) {
+    const unsigned long long u =
+        __hip_atomic_load(reinterpret_cast<unsigned long long*>(const_cast<float*>(p)),
+                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((unsigned)u), __uint_as_float((unsigned)(u >> 32)));
+}
+
 // LDS written by this wave's lanes becomes readable by its other lanes: DS
 // instructions of one wave execute in order, so waiting for the wave's own
 // LDS operations (lgkmcnt = 0; vector memory counters untouched) suffices.
@@ -394,22 +428,27 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
         }
         return;
     }
-    for (int i = tid; i < nh * D; i += kBlock) {
-        const int h = i / D, d = i % D;
+    // Two columns per thread, published with 64-bit stores (rows are D + 2
+    // floats, so every pair starts 8-byte aligned).
+    for (int i = tid; i < nh * D / 2; i += kBlock) {
+        const int h = 2 * i / D, d = 2 * i % D;
         float M = Mw[0][h];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, Mw[w][h]);
-        float o = 0.f;
+        float o0 = 0.f, o1 = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) o = fmaf(Ow[w][h * D + d], __builtin_amdgcn_exp2f(Mw[w][h] - M), o);
+        for (int w = 0; w < kWaves; ++w) {
+            const float wt = __builtin_amdgcn_exp2f(Mw[w][h] - M);
+            o0 = fmaf(Ow[w][h * D + d], wt, o0);
+            o1 = fmaf(Ow[w][h * D + d + 1], wt, o1);
+        }
         float* part = ws + ((size_t)(head0 + h) * a.n_splits + split) * row;
-        __hip_atomic_store(part + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_pair(part + d, o0, o1);
         if (d == 0) {
             float L = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) L = fmaf(Lw[w][h], __builtin_amdgcn_exp2f(Mw[w][h] - M), L);
-            __hip_atomic_store(part + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(part + D + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            store_pair(part + D, M, L);
         }
     }
 
@@ -432,43 +471,50 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     __syncthreads();
     if (!last_flag) return;
 
-    // Merge: wave h serves head head0 + h, each lane D/64 columns. Up to 32
-    // splits are loaded in one batch (one round trip for the pages'
-    // configurations), with a running rescale across batches. Indices past
-    // the last split are clamped to it (no load sits behind a branch) and
-    // their weight is zeroed.
+    // Merge: wave h serves head head0 + h, each lane D/64 columns. Splits go
+    // in batches of 32: lane j (and j + 32) loads the (max, sum) pair of
+    // split j of the batch, every lane loads its columns of all 32 partial
+    // rows (33 loads, one round trip), the batch max and the weights
+    // w_j = 2^(m_j - M) come from cross-lane steps, and each w_j reaches the
+    // column sums through a lane read. Across batches the running (M, L, o)
+    // is rescaled as in the online update. Indices past the last split are
+    // clamped to it (no load sits behind a branch) and their weight is 0.
     if (wave < nh) {
         constexpr int DPL = D / 64;
         constexpr int NB = 32;
         const int head = head0 + wave;
         const float* hb = ws + (size_t)head * a.n_splits * row;
+        const int lj = lane & (NB - 1);
         float M = kNegBig, L = 0.f, o[DPL];
 #pragma unroll
         for (int c = 0; c < DPL; ++c) o[c] = 0.f;
         for (int s0 = 0; s0 < n_active; s0 += NB) {
-            float mv[NB], lv[NB], ov[NB][DPL];
+            const bool live = s0 + lj < n_active;
+            const float2 ml = load_pair(hb + (size_t)min(s0 + lj, n_active - 1) * row + D);
+            float ov[NB][DPL];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const float* p = hb + (size_t)min(s0 + j, n_active - 1) * row;
-                mv[j] = __hip_atomic_load(p + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                lv[j] = __hip_atomic_load(p + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                for (int c = 0; c < DPL; ++c)
-                    ov[j][c] = __hip_atomic_load(p + lane * DPL + c, __ATOMIC_RELAXED,
+                const float* p = hb + (size_t)min(s0 + j, n_active - 1) * row + lane * DPL;
+                if constexpr (DPL == 2) {
+                    const float2 x = load_pair(p);
+                    ov[j][0] = x.x;
+                    ov[j][1] = x.y;
+                } else {
+                    ov[j][0] = __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
-            float bm = M;
-#pragma unroll
-            for (int j = 0; j < NB; ++j) bm = fmaxf(bm, mv[j]);  // clamped repeats change nothing
+            const float mj = live ? ml.x : kNegBig;
+            const float bm = fmaxf(M, max32(mj));
             const float r = __builtin_amdgcn_exp2f(M - bm);
-            L *= r;
+            M = bm;
+            const float wj = live ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
+            L = fmaf(L, r, sum32(ml.y * wj));
 #pragma unroll
             for (int c = 0; c < DPL; ++c) o[c] *= r;
-            M = bm;
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                const float w = s0 + j < n_active ? __builtin_amdgcn_exp2f(mv[j] - M) : 0.f;
-                L = fmaf(lv[j], w, L);
+                const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
 #pragma unroll
                 for (int c = 0; c < DPL; ++c) o[c] = fmaf(ov[j][c], w, o[c]);
             }
