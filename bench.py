@@ -74,27 +74,86 @@ def decode_bytes(w, kv_pos, with_lse=False):
     return b
 
 
+# ------------------------------------------------------------ clocks
+
+class ClockSampler:
+    """Samples the graphics clock the driver reports (the level marked
+    current in pp_dpm_sclk) every `period` seconds while the block runs.
+    Reading sysfs needs no privileges; without the file it reports None."""
+
+    def __init__(self, period=0.02):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period
+        self.samples = []
+        self._threading = threading
+        self._stop = None
+        self._thread = None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return int(re.search(r"(\d+)\s*[Mm]hz", line).group(1))
+        except (OSError, AttributeError, ValueError):
+            return None
+        return None
+
+    def _run(self):
+        stop = self._stop
+        while not stop.is_set():
+            mhz = self._read()
+            if mhz is not None:
+                self.samples.append(mhz)
+            stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path is not None:
+            self._stop = self._threading.Event()
+            self._thread = self._threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"min": min(self.samples), "median": int(np.median(self.samples)),
+                "max": max(self.samples), "samples": len(self.samples)}
+
+
 # ------------------------------------------------------------ GPU timing
 
-def time_calls(fn, n, torch):
+def time_calls(fn, n, torch, clock=None):
     """Average per-call duration (s) from events around each call, on the
-    current stream, plus the wall time of the n calls."""
+    current stream, plus the wall time of the n calls. `clock` (a
+    ClockSampler) samples the graphics clock over the timed calls only."""
+    import contextlib
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(n):
-        starts[i].record()
-        fn(i)
-        ends[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with clock if clock is not None else contextlib.nullcontext():
+        t0 = time.perf_counter()
+        for i in range(n):
+            starts[i].record()
+            fn(i)
+            ends[i].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     durs = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
     return float(np.mean(durs)), float(np.min(durs)), wall
 
 
 def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None,
-                  fused_qkv=False):
+                  fused_qkv=False, clock=None):
     """Prefill timing. With graph_replays > 0 the call is captured once in a
     HIP graph and replayed back to back (for kernels shorter than a Python
     launch); otherwise each call is launched eagerly between events. With
@@ -167,7 +226,7 @@ def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None,
                 "tflops_kernel": flops / mean_s / 1e12, "tflops_wall": None}
     for i in range(warmup):
         call(i)
-    mean_s, min_s, wall = time_calls(call, steps, torch)
+    mean_s, min_s, wall = time_calls(call, steps, torch, clock)
     return {"flops": flops, "mean_s": mean_s, "min_s": min_s, "wall_s": wall,
             "tflops_kernel": flops / mean_s / 1e12, "tflops_wall": flops * steps / wall / 1e12}
 
@@ -203,14 +262,16 @@ def bench_backward(w, steps, warmup, torch, ta):
             "tflops_kernel": flops / mean_s / 1e12}
 
 
-def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8, page_size=None):
+def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8, page_size=None, clock=None):
     """Decode device time. The cache is rotated over `copies` independent
     allocations (copies x 64 MiB > the 256 MB Infinity Cache), and the
     `copies` calls are captured once in a HIP graph and replayed, so the
     GPU runs the calls back to back instead of waiting on Python launches.
     kv_pos lives in device memory: the same graph serves every kv_pos.
     With page_size, the cache is a pool of shuffled pages (64 unused pages
-    mixed in) read through a page table (attn_decode_paged)."""
+    mixed in) read through a page table (attn_decode_paged). `clock`
+    samples the graphics clock over the timed replays only."""
+    import contextlib
     dev = torch.device("cuda:0")
     q, k, v = inputs.make_decode(w)
     qd = torch.from_numpy(q).to(dev)
@@ -260,11 +321,12 @@ def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8, page_size=None)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        start.record()
-        for _ in range(replays):
-            graph.replay()
-        end.record()
-        torch.cuda.synchronize()
+        with clock if clock is not None else contextlib.nullcontext():
+            start.record()
+            for _ in range(replays):
+                graph.replay()
+            end.record()
+            torch.cuda.synchronize()
         per_call = start.elapsed_time(end) * 1e-3 / (replays * copies)
         b = decode_bytes(w, kv_pos)
         res[str(kv_pos)] = {"us": round(per_call * 1e6, 2),
@@ -287,14 +349,19 @@ def copy_calibration(torch, mib=1024, reps=3):
 
 # ------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(w, budget_s=10.0, block=256, max_blocks=8):
+def cpu_baseline(w, wd, budget_s=10.0, block=256, max_blocks=8, decode_budget_s=2.0):
     """The float64 checker on the host cores, on the heaviest row blocks of
     the same workload (all heads), walked from the last row backwards until
-    `budget_s` of CPU work or `max_blocks` blocks."""
+    `budget_s` of CPU work or `max_blocks` blocks; beside it, the checker's
+    decode at the largest kv_pos of the decode workload, repeated for about
+    `decode_budget_s`."""
     import oracle
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in info]
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
     except Exception:
         threads = os.cpu_count() or 1
     q, k, v = inputs.make_prefill(w)
@@ -310,12 +377,29 @@ def cpu_baseline(w, budget_s=10.0, block=256, max_blocks=8):
         flops += prefill_flops(w, rows)
         hi -= block
         done += 1
+    del q, k, v
+    qd, kd, vd = inputs.make_decode(wd)
+    kv_pos = wd.kv_pos_values[-1]
+    dec_s, calls = 0.0, 0
+    while dec_s < decode_budget_s and calls < 100:
+        t0 = time.perf_counter()
+        oracle.decode_forward(qd, kd, vd, kv_pos=kv_pos, num_heads=wd.num_heads,
+                              num_kv_heads=wd.num_kv_heads, head_dim=wd.head_dim,
+                              max_seq=wd.max_seq, scale=wd.scale)
+        dec_s += time.perf_counter() - t0
+        calls += 1
+    dec_bytes = decode_bytes(wd, kv_pos)
     return {"value": flops / total_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"rows [{hi}, {w.q_seq}) x {w.num_heads} heads of {w.name}, "
                       f"float64 numpy, {total_s:.1f} s, {flops / 1e9:.1f} GFLOP",
+            "seconds": round(total_s, 3),
             "host_cpus": os.cpu_count(),
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas": blas,
+            "decode": {"workload": wd.name, "kv_pos": kv_pos, "calls": calls,
+                       "ms_per_call": round(dec_s / calls * 1e3, 3),
+                       "GB/s": round(dec_bytes * calls / dec_s / 1e9, 3)}}
 
 
 # ------------------------------------------------------------ traffic
@@ -393,6 +477,7 @@ def main():
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": "f32", "data": "synthetic"}
+    clocks = {}
 
     if args.only == "reported":
         rep = {}
@@ -408,7 +493,9 @@ def main():
     if args.only != "decode":
         print(f"[bench] prefill {w.name}: {args.warmup} warmup + {args.steps} timed",
               flush=True)
-        p = bench_prefill(w, args.steps, args.warmup, torch, ta)
+        clk_prefill = ClockSampler()
+        p = bench_prefill(w, args.steps, args.warmup, torch, ta, clock=clk_prefill)
+        clocks["prefill"] = clk_prefill.summary()
         result.update({
             "value": round(p["tflops_wall"], 3), "unit": "TFLOP/s",
             "ms_per_step": round(p["wall_s"] / args.steps * 1e3, 3),
@@ -462,7 +549,9 @@ def main():
     if args.only != "prefill":
         wd = inputs.DECODE_8K
         print(f"[bench] decode {wd.name}", flush=True)
-        d = bench_decode(wd, wd.kv_pos_values, 25, torch, ta)
+        clk_decode = ClockSampler(period=0.005)
+        d = bench_decode(wd, wd.kv_pos_values, 25, torch, ta, clock=clk_decode)
+        clocks["decode"] = clk_decode.summary()
         head = d[str(wd.kv_pos_values[-1])]
         result["decode"] = {
             "workload": wd.name, "unit": "GB/s", "kv_pos": d,
@@ -489,10 +578,11 @@ def main():
 
     if not args.no_cpu_baseline and args.only is None:
         print("[bench] cpu baseline (float64 checker on host cores)", flush=True)
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(w, inputs.DECODE_8K)
 
     props = torch.cuda.get_device_properties(0)
-    result["device"] = {"name": props.name, "cus": props.multi_processor_count}
+    result["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                        "sclk_mhz_seen": clocks}
     print(json.dumps(result), flush=True)
 
 
