@@ -254,6 +254,48 @@ def test_strided_fused_qkv_and_padded_out():
     assert np.all(np.isnan(got[:, H * d:])), "padding columns were written"
 
 
+def test_long_causal_fused_qkv_sampled_rows():
+    """The 16384-row causal workload read from one fused [16384, 6144] QKV
+    buffer with out written at a 4160-float row stride (the strided launch
+    the benchmark times): sampled rows against the checker, and the whole
+    output and lse bit for bit equal to the contiguous call (row strides
+    change addresses only)."""
+    import torch
+    import tiled_attention_03_amd as ta
+    w = inputs.CAUSAL_16K
+    log(f"prefill parity fused QKV (sampled rows) {w.name}")
+    H, Hkv, d, n = w.num_heads, w.num_kv_heads, w.head_dim, w.q_seq
+    qd_, kvd = H * d, Hkv * d
+    q, k, v = inputs.make_prefill(w)
+    dev = device()
+    fused = torch.empty((n, qd_ + 2 * kvd), device=dev)
+    for lo, x in ((0, q), (qd_, k), (qd_ + kvd, v)):
+        fused[:, lo:lo + x.shape[1]].copy_(torch.from_numpy(x))
+    out_wide = torch.full((n, qd_ + 64), float("nan"), device=dev)
+    lse = torch.empty((n, H, 2), device=dev)
+    width = qd_ + 2 * kvd
+    ta.attn_fwd_ex(fused[:, :qd_], width, fused[:, qd_:qd_ + kvd], width,
+                   fused[:, qd_ + kvd:], width, out_wide, qd_ + 64, lse, 0, n, n, H, Hkv, d,
+                   CAUSAL, 0, w.scale)
+    torch.cuda.synchronize()
+    got_o = out_wide[:, :qd_].cpu().numpy()
+    assert torch.isnan(out_wide[:, qd_:]).all().item(), "padding columns were written"
+    got_l = lse.cpu().numpy()
+    del fused, out_wide
+    dense_o, dense_l = gpu_prefill(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d,
+                                   mode=CAUSAL, kv_len=n, start_pos=0, scale=w.scale)
+    assert np.array_equal(got_o, dense_o), "strided out differs from the contiguous call"
+    assert np.array_equal(got_l, dense_l), "strided lse differs from the contiguous call"
+    rng = np.random.default_rng(5098)
+    rows = np.unique(np.concatenate([[0, 31, 32, 8191, 16383],
+                                     rng.choice(n, 11, replace=False)]))
+    ro, rl = oracle_prefill(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=CAUSAL,
+                            kv_len=n, start_pos=0, scale=w.scale, rows=rows)
+    e_o = check_out(got_o[rows], ro, "fused qkv 16K")
+    e_l = check_lse(got_l[rows], rl, "fused qkv 16K")
+    log(f"  rows={len(rows)} max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
+
+
 @pytest.mark.parametrize("mode,sp", [(CAUSAL, 37), (CROSS, 0), (FULL, 0)])
 def test_sub_batches_with_q_base(mode, sp):
     """Splitting the query batch into sub-batch calls with q_base (the
