@@ -187,11 +187,19 @@ int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStr
  *   dk, dv        [kv_len, num_kv_heads*head_dim], written in full (0 for
  *                 keys no row sees)
  *   mode, start_pos, scale  as the forward
- *   workspace     device scratch of attn_bwd_workspace_bytes(q_seq,
- *                 num_heads) bytes, 16-byte aligned; overwritten
+ *   workspace     device scratch, 16-byte aligned, overwritten: at least
+ *                 attn_bwd_workspace_bytes(q_seq, num_heads) bytes (D_i);
+ *                 with attn_bwd_workspace_bytes_stored(q_seq, kv_len,
+ *                 num_heads, mode, start_pos) bytes or more it also holds
+ *                 every score gradient dS_ij of the call in 16 x 16 tiles
+ *                 (4 bytes per (row, key) pair in the windows, per head,
+ *                 rounded up to whole tiles), which lets dq be formed from
+ *                 them instead of recomputing the scores
  *
- * Two kernel launches on stream, no allocation, no atomics (results are
- * run-to-run identical). Errors: as attn_fwd for the sizes and mode;
+ * Stored path: three kernel launches (D_i; dk, dv and the dS tiles; dq from
+ * the tiles). Otherwise two (dq with D_i, recomputing the scores; dk, dv).
+ * Both run on stream with no allocation and no atomics (results are
+ * run-to-run identical; the two paths agree to rounding). Errors: as attn_fwd for the sizes and mode;
  * TA03_ERR_NULL for a NULL q, out, dout, lse, dq or workspace (q_seq > 0) or
  * k, v, dk, dv (kv_len > 0); TA03_ERR_WORKSPACE for a short workspace;
  * TA03_ERR_UNSUPPORTED for q_seq*num_heads*head_dim or
@@ -199,6 +207,11 @@ int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStr
  * q_seq == 0 and kv_len == 0 is a no-op; q_seq == 0 alone writes zero dk, dv.
  */
 size_t attn_bwd_workspace_bytes(int q_seq, int num_heads);
+/* Workspace bytes for the stored path: attn_bwd_workspace_bytes(q_seq,
+ * num_heads) + num_heads * T * 1024, T the 16 x 16 tiles of one head's
+ * windows; 0 for sizes attn_bwd rejects. */
+size_t attn_bwd_workspace_bytes_stored(int q_seq, int kv_len, int num_heads, int mode,
+                                       int start_pos);
 int attn_bwd(const float* q, const float* k, const float* v, const float* out, const float* dout,
              const float* lse, float* dq, float* dk, float* dv, int q_seq, int kv_len,
              int num_heads, int num_kv_heads, int head_dim, int mode, int start_pos, float scale,

@@ -7,6 +7,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 from tiled_attention_03_amd import binding
@@ -15,6 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ta03.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6
+CAUSAL, FULL, CROSS = 0, 1, 2
 A = 0x10000   # fake 16-byte-aligned addresses: never dereferenced, every call
 B = 0x20000   # below fails validation (or is a no-op) before any HIP call
 C = 0x30000
@@ -37,7 +39,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_bytes",
-                                    "attn_decode", "attn_decode_paged",
+                                    "attn_bwd_workspace_bytes_stored", "attn_decode", "attn_decode_paged",
                                     "attn_decode_workspace_bytes",
                                     "attn_decode_workspace_init", "attn_fwd", "attn_fwd_ex",
                                     "attn_fwd_rope", "attn_rope_table", "attn_strerror"]
@@ -192,6 +194,49 @@ def test_bwd_workspace_bytes(lib):
     assert lib.attn_bwd_workspace_bytes(0, 4) == 0
     assert lib.attn_bwd_workspace_bytes(-1, 4) == 0
     assert lib.attn_bwd_workspace_bytes(4, 0) == 0
+
+
+def _stored_tiles_brute(q_seq, kv_len, mode, start_pos):
+    """16 x 16 dS tiles of one head, counted query tile by query tile: tile
+    qt covers the keys of its last row's window."""
+    n = 0
+    for qt in range((q_seq + 15) // 16):
+        rows_hi = min(16 * (qt + 1), q_seq)
+        w = min(start_pos + rows_hi, kv_len) if mode == CAUSAL else kv_len
+        n += (w + 15) // 16
+    return n
+
+
+def test_bwd_workspace_bytes_stored(lib):
+    f = lib.attn_bwd_workspace_bytes_stored
+    rng = np.random.default_rng(77)
+    cases = [(16384, 16384, 32, CAUSAL, 0), (1, 1, 1, CAUSAL, 0), (17, 17, 2, CAUSAL, 0),
+             (512, 2048, 32, CAUSAL, 1536), (300, 333, 8, CAUSAL, 33), (5, 3, 8, CROSS, 0),
+             (1024, 1024, 8, FULL, 0), (512, 2048, 8, CROSS, 0), (16, 31, 4, CAUSAL, 15)]
+    for _ in range(300):
+        mode = int(rng.integers(0, 3))
+        q = int(rng.integers(1, 700))
+        if mode == CAUSAL:
+            sp = int(rng.integers(0, 90))
+            kv = q + sp + int(rng.integers(0, 40))
+        elif mode == FULL:
+            sp, kv = 0, q
+        else:
+            sp, kv = 0, int(rng.integers(0, 700))
+        cases.append((q, kv, int(rng.integers(1, 9)), mode, sp))
+    for q, kv, H, mode, sp in cases:
+        tiles = _stored_tiles_brute(q, kv, mode, sp)
+        want = lib.attn_bwd_workspace_bytes(q, H) + H * tiles * 1024
+        assert f(q, kv, H, mode, sp) == want, (q, kv, H, mode, sp)
+    assert f(16384, 16384, 32, CAUSAL, 0) == 16384 * 32 * 4 + 32 * (1024 * 1025 // 2) * 1024
+    # sizes attn_bwd rejects
+    assert f(10, 9, 4, CAUSAL, 0) == 0        # start_pos + q_seq > kv_len
+    assert f(10, 12, 4, FULL, 0) == 0         # full needs kv_len == q_seq
+    assert f(10, 12, 4, CROSS, 1) == 0        # start_pos only for causal
+    assert f(10, 12, 0, CROSS, 0) == 0
+    assert f(-1, 12, 4, CROSS, 0) == 0
+    assert f(10, 12, 4, 7, 0) == 0
+    assert f(0, 12, 4, CROSS, 0) == 0
 
 
 def test_validation_order_sizes_before_pointers(lib):

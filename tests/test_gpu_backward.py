@@ -17,9 +17,11 @@ CAUSAL, FULL, CROSS = inputs.CAUSAL, inputs.FULL, inputs.CROSS
 
 
 def gpu_fwd_bwd(q, k, v, g, *, num_heads, num_kv_heads, head_dim, mode, kv_len, start_pos,
-                scale, poison=True):
-    """GPU forward (out, lse), then attn_bwd; outputs pre-filled with NaN so
-    that an element the kernels skip shows."""
+                scale, poison=True, stored=True, ws_short=0):
+    """GPU forward (out, lse), then attn_bwd; outputs and workspace pre-filled
+    with NaN so that an element the kernels skip (or a tile they never write)
+    shows. stored: workspace for the stored-dS path, else the minimal one;
+    ws_short: bytes taken off the stored size."""
     import torch
     import tiled_attention_03_amd as ta
     dev = device()
@@ -33,6 +35,9 @@ def gpu_fwd_bwd(q, k, v, g, *, num_heads, num_kv_heads, head_dim, mode, kv_len, 
     dk = torch.full((kv_len, Hkv * d), fill, device=dev)
     dv = torch.full((kv_len, Hkv * d), fill, device=dev)
     nbytes = ta.attn_bwd_workspace_bytes(n, H)
+    if stored:
+        nbytes = max(nbytes, ta.attn_bwd_workspace_bytes_stored(n, kv_len, H, mode, start_pos)
+                     - ws_short)
     ws = torch.full((max(nbytes, 4) // 4,), fill, device=dev)
     ta.attn_bwd(qd, kd, vd, out, gd, lse, dq, dk, dv, n, kv_len, H, Hkv, d, mode, start_pos,
                 scale, ws, nbytes)
@@ -45,6 +50,19 @@ def _kw(w):
                 mode=w.mode, kv_len=w.kv_len, start_pos=w.start_pos, scale=w.scale)
 
 
+# Backward paths: "stored" (workspace for the dS tiles; dq from them),
+# "recompute" (minimal workspace; dq recomputes the scores, 16-key dk/dv
+# kernel) and "keys32" (minimal workspace, the 32-key dk/dv kernel forced by
+# the library's TA03_BWD_KEYS).
+PATHS = ["stored", "recompute", "keys32"]
+
+
+def _use_path(path, monkeypatch):
+    if path == "keys32":
+        monkeypatch.setenv("TA03_BWD_KEYS", "32")
+    return path == "stored"
+
+
 def _check_all(got, ref, w, what):
     """ref: the checker's (dq, dk, dv, dq_m, dk_m, dv_m)."""
     terms = (w.kv_len, w.q_seq * w.group, w.q_seq * w.group)
@@ -52,35 +70,33 @@ def _check_all(got, ref, w, what):
             for name, a, b, m, n in zip(("dq", "dk", "dv"), got, ref[:3], ref[3:], terms)]
 
 
-@pytest.mark.parametrize("keys", ["auto", "16", "32"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("w", [inputs.CAUSAL_SMALL, inputs.FULL_1K, inputs.CROSS_512x2K,
                                inputs.CONTINUE_512], ids=lambda w: w.name)
-def test_backward_pages_workloads(w, keys, monkeypatch):
-    """The pages' prefill workloads; keys: the dk/dv kernel the launch picks,
-    or the 16-key / 32-key one forced by the library's TA03_BWD_KEYS."""
-    if keys != "auto":
-        monkeypatch.setenv("TA03_BWD_KEYS", keys)
-    log(f"backward parity {w.name} keys={keys}")
+def test_backward_pages_workloads(w, path, monkeypatch):
+    """The pages' prefill workloads through each backward path."""
+    stored = _use_path(path, monkeypatch)
+    log(f"backward parity {w.name} path={path}")
     q, k, v = inputs.make_prefill(w)
     g = inputs.normal(q.shape, w.seed_base + 7)
-    got = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    got = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
     ref = oracle.attention_backward(q, k, v, g, magnitudes=True, **_kw(w))
     e = _check_all(got, ref, w, w.name)
     log("  max|d| dq={:.2e} dk={:.2e} dv={:.2e}".format(*e))
 
 
-@pytest.mark.parametrize("keys", ["auto", "32"])
-def test_backward_long_causal_sampled(keys, monkeypatch):
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_long_causal_sampled(path, monkeypatch):
     """The 16384-row causal pass with heavy K rows: dq on sampled rows and
     dk, dv on sampled keys of KV head 0 (the checker computes the query heads
-    of that KV head in full, the rest is left out)."""
-    if keys != "auto":
-        monkeypatch.setenv("TA03_BWD_KEYS", keys)
+    of that KV head in full, the rest is left out). The stored path is the
+    launch the benchmark times (17.2 GB of dS tiles)."""
+    stored = _use_path(path, monkeypatch)
     w = inputs.CAUSAL_16K
-    log(f"backward parity (sampled) {w.name}")
+    log(f"backward parity (sampled) {w.name} path={path}")
     q, k, v = inputs.make_prefill(w)
     g = inputs.normal(q.shape, w.seed_base + 7)
-    dq, dk, dv = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
     rng = np.random.default_rng(7099)
     rows = np.unique(np.concatenate([[0, 1, 31, 32, 8191, 16383],
                                      rng.choice(w.q_seq, 10, replace=False)]))
@@ -119,22 +135,32 @@ BWD_SWEEP = [
 ]
 
 
-@pytest.mark.parametrize("keys", ["auto", "16", "32"])
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("case", BWD_SWEEP, ids=lambda c: "m{}_q{}_kv{}_h{}x{}_d{}_sp{}".format(*c))
-def test_backward_ragged_sweep(case, keys, monkeypatch):
+def test_backward_ragged_sweep(case, path, monkeypatch):
     """Ragged shapes: partial query and key tiles, GQA groups of 1 to 8,
-    continuation windows, single-key windows; through both dk/dv kernels."""
-    if keys != "auto":
-        monkeypatch.setenv("TA03_BWD_KEYS", keys)
+    continuation windows, single-key windows; through each backward path."""
+    stored = _use_path(path, monkeypatch)
     mode, n, kv, H, Hkv, d, sp = case
     w, q, k, v = inputs.random_case(1100 + n * 7 + kv, mode, n, kv, H, Hkv, d, start_pos=sp,
                                     kv_rows=kv + 5)
     k[kv:] = np.nan  # rows past kv_len must never be read into a result
     v[kv:] = np.nan
     g = inputs.normal(q.shape, 1101 + n)
-    got = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    got = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
     ref = oracle.attention_backward(q, k, v, g, magnitudes=True, **_kw(w))
     _check_all(got, ref, w, str(case))
+
+
+def test_backward_workspace_short_of_stored_falls_back():
+    """A workspace one tile short of the stored size takes the recompute
+    path: same gradients as the minimal workspace, bit for bit."""
+    w, q, k, v = inputs.random_case(1120, CAUSAL, 90, 120, 4, 2, 64, start_pos=30)
+    g = inputs.normal(q.shape, 1121)
+    a = gpu_fwd_bwd(q, k, v, g, stored=True, ws_short=1024, **_kw(w))
+    b = gpu_fwd_bwd(q, k, v, g, stored=False, **_kw(w))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
 
 
 def test_backward_single_key_windows():
@@ -177,16 +203,18 @@ def test_backward_zero_keys():
     assert np.array_equal(dq, np.zeros_like(dq)) and dk.size == 0 and dv.size == 0
 
 
-def test_backward_deterministic():
+@pytest.mark.parametrize("stored", [True, False])
+def test_backward_deterministic(stored):
     w, q, k, v = inputs.random_case(1180, CAUSAL, 300, 300, 8, 2, 128)
     g = inputs.normal(q.shape, 1181)
-    a = gpu_fwd_bwd(q, k, v, g, **_kw(w))
-    b = gpu_fwd_bwd(q, k, v, g, **_kw(w))
+    a = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
+    b = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
 
 
-def test_backward_graph_replay():
+@pytest.mark.parametrize("stored", [True, False])
+def test_backward_graph_replay(stored):
     """Forward and backward captured in one graph, replayed with the
     program's own work in between: every replay matches the eager result."""
     import torch
@@ -201,7 +229,8 @@ def test_backward_graph_replay():
     dq = torch.empty((n, H * d), device=dev)
     dk = torch.empty((n, Hkv * d), device=dev)
     dv = torch.empty((n, Hkv * d), device=dev)
-    nbytes = ta.attn_bwd_workspace_bytes(n, H)
+    nbytes = (ta.attn_bwd_workspace_bytes_stored(n, n, H, CAUSAL, 0) if stored
+              else ta.attn_bwd_workspace_bytes(n, H))
     ws = torch.empty((nbytes // 4,), device=dev)
 
     def step():

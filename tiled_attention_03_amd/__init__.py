@@ -6,11 +6,12 @@ its input generators) needs no GPU and no built library.
 """
 
 from .binding import (CAUSAL, CROSS, FULL, Ta03Error, attention, attention_backward, attn_bwd,
-                      attn_bwd_workspace_bytes, attn_decode,
+                      attn_bwd_workspace_bytes, attn_bwd_workspace_bytes_stored, attn_decode,
                       attn_decode_paged, attn_decode_workspace_bytes, attn_decode_workspace_init,
                       attn_fwd, attn_fwd_ex, attn_fwd_rope, attn_rope_table, attn_strerror, lib)
 
 __all__ = ["CAUSAL", "FULL", "CROSS", "Ta03Error", "attention", "attention_backward", "attn_bwd",
-           "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_ex",
+           "attn_bwd_workspace_bytes", "attn_bwd_workspace_bytes_stored", "attn_fwd",
+           "attn_fwd_ex",
            "attn_fwd_rope", "attn_rope_table", "attn_decode", "attn_decode_paged",
            "attn_decode_workspace_bytes", "attn_decode_workspace_init", "attn_strerror", "lib"]

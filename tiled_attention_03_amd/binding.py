@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.attn_rope_table.restype = I
         L.attn_bwd_workspace_bytes.argtypes = [I, I]
         L.attn_bwd_workspace_bytes.restype = S
+        L.attn_bwd_workspace_bytes_stored.argtypes = [I, I, I, I, I]
+        L.attn_bwd_workspace_bytes_stored.restype = S
         L.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, S, P]
         L.attn_bwd.restype = I
         L.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
@@ -194,6 +196,11 @@ def attn_bwd_workspace_bytes(q_seq: int, num_heads: int) -> int:
     return int(lib().attn_bwd_workspace_bytes(q_seq, num_heads))
 
 
+def attn_bwd_workspace_bytes_stored(q_seq: int, kv_len: int, num_heads: int, mode: int,
+                                    start_pos: int = 0) -> int:
+    return int(lib().attn_bwd_workspace_bytes_stored(q_seq, kv_len, num_heads, mode, start_pos))
+
+
 def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, q_seq: int, kv_len: int, num_heads: int,
              num_kv_heads: int, head_dim: int, mode: int, start_pos: int, scale: float,
              workspace, workspace_bytes: int, stream=None) -> None:
@@ -211,9 +218,12 @@ def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, q_seq: int, kv_len: int, num_h
 
 def attention_backward(q, k, v, out, dout, lse, *, num_heads: int, num_kv_heads: int,
                        head_dim: int, mode: int, kv_len: Optional[int] = None,
-                       start_pos: int = 0, scale: Optional[float] = None, stream=None):
+                       start_pos: int = 0, scale: Optional[float] = None,
+                       store_scores: bool = True, stream=None):
     """Allocate dq, dk, dv and the scratch with torch and call attn_bwd;
-    returns (dq, dk, dv) with dk, dv of kv_len rows."""
+    returns (dq, dk, dv) with dk, dv of kv_len rows. store_scores sizes the
+    scratch for the stored-dS path (4 bytes per (row, key) pair per head);
+    False gives the minimal scratch (dq recomputes the scores)."""
     import torch
     q_seq = q.shape[0]
     if kv_len is None:
@@ -224,7 +234,8 @@ def attention_backward(q, k, v, out, dout, lse, *, num_heads: int, num_kv_heads:
     dq = torch.empty((q_seq, num_heads * head_dim), dtype=torch.float32, device=dev)
     dk = torch.empty((kv_len, num_kv_heads * head_dim), dtype=torch.float32, device=dev)
     dv = torch.empty((kv_len, num_kv_heads * head_dim), dtype=torch.float32, device=dev)
-    nbytes = attn_bwd_workspace_bytes(q_seq, num_heads)
+    nbytes = (attn_bwd_workspace_bytes_stored(q_seq, kv_len, num_heads, mode, start_pos)
+              if store_scores else 0) or attn_bwd_workspace_bytes(q_seq, num_heads)
     ws = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=dev)
     attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, q_seq, kv_len, num_heads, num_kv_heads,
              head_dim, mode, start_pos, scale, ws, nbytes, stream)

@@ -85,6 +85,9 @@ struct BwdArgs {
     float scale;
     int hg, rs, ks, n_head_blocks, n_row_blocks;  // dq kernel block shape (ks: key splits)
     int n_key_blocks;                         // dk/dv kernel: 128-key blocks per KV head
+    DsLayout ds;                              // stored dS tiles (when kept)
+    long long ds_tph;                         // dS tiles per head
+    int dq_hg, dq_rs, dq_n_head_blocks, dq_n_row_blocks;  // dq-from-dS block shape
 };
 
 // Issue this wave's share (inst = first, first + step, ...) of a 32-row, D-wide
@@ -518,12 +521,13 @@ __device__ __forceinline__ float comp4(const float4& x, int i) {
 constexpr int k16Keys = 16;  // keys per wave
 constexpr int k16Rows = 16;  // query rows per tile
 
-template <int D, int W>
+template <int D, int W, bool STORE>
 __global__ void __launch_bounds__(64 * W, 8 / W)  // 8 waves per CU: two per SIMD
 bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                   const float* __restrict__ v, const float* __restrict__ dout,
                   const float* __restrict__ lse, const float* __restrict__ delta,
-                  float* __restrict__ dk, float* __restrict__ dv, BwdArgs a) {
+                  float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ ds,
+                  BwdArgs a) {
     constexpr int KS = D / 4;   // k-steps of the score products
     constexpr int NB = D / 16;  // 16-row blocks of dk^T, dv^T
     constexpr int CPR = D / 4;  // 16-byte chunks per row
@@ -645,6 +649,18 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 s[r] = p;
                 dp[r] = p * (dp[r] - dl);
             }
+            if constexpr (STORE) {
+                // The 16 x 16 dS tile (query rows x keys, row-major) of this
+                // head, query tile and key tile; masked entries are 0. Four
+                // stores of 4 x 64 contiguous bytes, issued before the dv / dk
+                // products so they complete under them.
+                const int h = kv_head * a.group + it / n_qt;
+                const int qt = qt0 + it % n_qt;
+                float* tile = ds + ((size_t)h * a.ds_tph + ds_tiles_before(a.ds, qt) +
+                                    key0 / k16Keys) * (k16Rows * k16Keys);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tile[(4 * g + r) * k16Keys + j] = dp[r];
+            }
             // dv^T += dout^T P, dk^T += Q^T dS: k-step t of lane group g is
             // query row 4g + t; lane (m, g) reads head-dims NB*m .. NB*m + NB.
 #pragma unroll
@@ -684,6 +700,207 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Backward from stored dS (three launches): D_i first, then the 16-key dk/dv
+// kernel, which also writes every 16 x 16 dS tile it forms, then dq as one
+// product over the stored tiles, dq = scale * dS K, so no score or dP is
+// formed twice. The tiles cost 1 KiB per 256 (row, key) pairs per head of
+// workspace.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL,
+                                                      0xF, 0xF, false));
+}
+
+// D_i = <dout_i, out_i> per (row, head): 16 lanes per pair, D/16 contiguous
+// floats each, summed over the 16 lanes with DPP (quad xor 1, quad xor 2,
+// half-row mirror, row mirror).
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_delta_kernel(const float* __restrict__ o, const float* __restrict__ dout,
+                 float* __restrict__ delta, long long n_pairs) {
+    constexpr int PER = D / 16;
+    const int tid = threadIdx.x;
+    const long long pair = (long long)blockIdx.x * 16 + (tid >> 4);
+    const int l16 = tid & 15;
+    // q, out and dout rows are num_heads * D wide: pair (row, head) starts at pair * D.
+    const long long pc = pair < n_pairs ? pair : n_pairs - 1;
+    const float* op = o + pc * D + l16 * PER;
+    const float* gp = dout + pc * D + l16 * PER;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < PER / 4; ++c) {
+        const float4 x = *reinterpret_cast<const float4*>(op + 4 * c);
+        const float4 y = *reinterpret_cast<const float4*>(gp + 4 * c);
+        acc = fmaf(x.x, y.x, acc);
+        acc = fmaf(x.y, y.y, acc);
+        acc = fmaf(x.z, y.z, acc);
+        acc = fmaf(x.w, y.w, acc);
+    }
+    acc += dpp_f<0xB1>(acc);
+    acc += dpp_f<0x4E>(acc);
+    acc += dpp_f<0x141>(acc);
+    acc += dpp_f<0x140>(acc);
+    if (l16 == 0 && pair < n_pairs) delta[pair] = acc;
+}
+
+// dq from stored dS. A block is 4 waves: dq_hg query heads of one GQA group
+// x dq_rs strips; a wave owns kDqRT query tiles of 16 rows of one head, and
+// the block streams the 16-key K tiles of its KV head through LDS (HBM ->
+// LDS directly, double-buffered), up to the window of its last query tile.
+// Per key tile and k-step t (keys 4g + t for lane group g), with
+// v_mfma_f32_16x16x4_f32:
+//   A: lane (j, g) gives dS[row j][key 4g + t] -- one 16-byte load of the
+//      row-major tile per query tile covers all four k-steps;
+//   B: lane (j, g) gives K[key 4g + t][d] for d = 64 (b / 4) + 4 j + b % 4 in
+//      column block b (4 j + b at head_dim 64), so each lane reads one or two
+//      16-byte runs of a K row and the 16 lanes of a group read 256
+//      contiguous bytes (no bank conflicts);
+//   result block b: register r of lane (j, g) is row 4g + r, column d, so a
+//      row's four column blocks store as one float4 per lane.
+// Tiles past a query tile's window (or query tiles past q_seq) are read
+// clamped to a valid tile and zeroed by a select.
+constexpr int kDqRT = 4;  // 16-row query tiles per wave
+
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
+                 float* __restrict__ dq, BwdArgs a) {
+    constexpr int NB = D / 16;
+    constexpr int CPR = D / 4;
+    constexpr int TILE_F = k16Keys * D;
+    constexpr int LOADS = TILE_F / 4 / 64;  // wave instructions per K tile (8 or 4)
+    constexpr int TF = k16Rows * k16Keys;   // floats per dS tile
+    extern __shared__ __attribute__((aligned(16))) float smem[];  // [2][K tile]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;
+    const int g = lane >> 4;
+
+    const int bid = blockIdx.x;
+    const int head_block = bid % a.dq_n_head_blocks;
+    const int seq = bid / a.dq_n_head_blocks;
+    const int rb = a.causal ? (a.dq_n_row_blocks - 1 - seq) : seq;  // heaviest first
+    const int head = head_block * a.dq_hg + wave % a.dq_hg;
+    const int strip = wave / a.dq_hg;
+    const int kv_head = head / a.group;
+    const int kvd = a.num_kv_heads * D;
+    const int n_qt = ds_query_tiles(a.ds);
+    const int qt_first = (rb * a.dq_rs + strip) * kDqRT;
+    const int blk_qt_last = min((rb + 1) * a.dq_rs * kDqRT, n_qt) - 1;
+    const int n_kt = blk_qt_last >= 0 ? ds_tiles_in(a.ds, blk_qt_last) : 0;
+
+    // Per query tile: first tile index (clamped query tile) and tile count.
+    long long tbase[kDqRT];
+    int tcount[kDqRT];
+    bool tlive[kDqRT];
+#pragma unroll
+    for (int rt = 0; rt < kDqRT; ++rt) {
+        const int qt = qt_first + rt;
+        const int qc = min(qt, n_qt - 1);
+        tlive[rt] = qt < n_qt;
+        tcount[rt] = ds_tiles_in(a.ds, qc);
+        tbase[rt] = (long long)head * a.ds_tph + ds_tiles_before(a.ds, qc);
+    }
+
+    auto issue_k = [&](int kt, int buf) {
+        float* dst = smem + buf * TILE_F;
+#pragma unroll
+        for (int inst = wave; inst < LOADS; inst += 4) {
+            const int s_ = inst * 64 + lane;
+            const int r = s_ / CPR, c = s_ % CPR;
+            const int key = min(kt * k16Keys + r, a.kv_len - 1);
+            __builtin_amdgcn_global_load_lds(k + (size_t)key * kvd + kv_head * D + 4 * c,
+                                             (lds_void*)(dst + inst * 256), 16, 0, 0);
+        }
+    };
+    auto load_ds = [&](int kt, float4 (&x)[kDqRT]) {
+#pragma unroll
+        for (int rt = 0; rt < kDqRT; ++rt) {
+            const long long t = tbase[rt] + min(kt, max(tcount[rt] - 1, 0));
+            x[rt] = *reinterpret_cast<const float4*>(ds + (size_t)t * TF + 16 * j + 4 * g);
+        }
+    };
+
+    f32x4 acc[kDqRT][NB];
+#pragma unroll
+    for (int rt = 0; rt < kDqRT; ++rt)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto step = [&](int kt, const float4 (&cur)[kDqRT], float4 (&nxt)[kDqRT]) {
+        wait_vmem();
+        __syncthreads();  // K tile kt landed for every wave; the other buffer is free
+        if (kt + 1 < n_kt) {  // block-uniform
+            issue_k(kt + 1, (kt + 1) & 1);
+            load_ds(kt + 1, nxt);
+        }
+        const float* Ks = smem + (kt & 1) * TILE_F;
+        float av[kDqRT][4];
+#pragma unroll
+        for (int rt = 0; rt < kDqRT; ++rt) {
+            const bool live = tlive[rt] && kt < tcount[rt];
+            av[rt][0] = live ? cur[rt].x : 0.f;
+            av[rt][1] = live ? cur[rt].y : 0.f;
+            av[rt][2] = live ? cur[rt].z : 0.f;
+            av[rt][3] = live ? cur[rt].w : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float* kr = Ks + (4 * g + t) * D + 4 * j;
+            float kb[NB];
+#pragma unroll
+            for (int h2 = 0; h2 < NB / 4; ++h2) {
+                const float4 x = *reinterpret_cast<const float4*>(kr + 64 * h2);
+                kb[4 * h2 + 0] = x.x;
+                kb[4 * h2 + 1] = x.y;
+                kb[4 * h2 + 2] = x.z;
+                kb[4 * h2 + 3] = x.w;
+            }
+#pragma unroll
+            for (int rt = 0; rt < kDqRT; ++rt)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[rt][b] = mfma16(av[rt][t], kb[b], acc[rt][b]);
+        }
+    };
+
+    float4 da[kDqRT], db[kDqRT];
+    if (n_kt > 0) {
+        issue_k(0, 0);
+        load_ds(0, da);
+    }
+    int kt = 0;
+    for (; kt + 1 < n_kt; kt += 2) {
+        step(kt, da, db);
+        step(kt + 1, db, da);
+    }
+    if (kt < n_kt) step(kt, da, db);
+    // The last products' results are read below by vector ALU instructions:
+    // keep the matrix-core result latency covered whatever path led here.
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+
+    const int qd = a.num_heads * D;
+#pragma unroll
+    for (int rt = 0; rt < kDqRT; ++rt) {
+        const int qt = qt_first + rt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = qt * k16Rows + 4 * g + r;
+            if (row >= a.q_seq) continue;
+            float* dst = dq + (size_t)row * qd + head * D + 4 * j;
+#pragma unroll
+            for (int h2 = 0; h2 < NB / 4; ++h2) {
+                *reinterpret_cast<float4*>(dst + 64 * h2) = make_float4(
+                    acc[rt][4 * h2 + 0][r] * a.scale, acc[rt][4 * h2 + 1][r] * a.scale,
+                    acc[rt][4 * h2 + 2][r] * a.scale, acc[rt][4 * h2 + 3][r] * a.scale);
+            }
+        }
+    }
+}
+
 int gcd_int(int x, int y) {
     while (y) {
         const int t = x % y;
@@ -693,18 +910,55 @@ int gcd_int(int x, int y) {
     return x;
 }
 
-template <int D, int W>
+template <int D, int W, bool STORE>
 hipError_t launch_dkdv16(long long grid, size_t lds, hipStream_t stream, const float* q,
                          const float* k, const float* v, const float* dout, const float* lse,
-                         const float* delta, float* dk, float* dv, const BwdArgs& a) {
+                         const float* delta, float* dk, float* dv, float* ds,
+                         const BwdArgs& a) {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(bwd_dkdv16_kernel<D, W>),
+        reinterpret_cast<const void*>(bwd_dkdv16_kernel<D, W, STORE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     if (grid > 0) {
-        hipLaunchKernelGGL((bwd_dkdv16_kernel<D, W>), dim3((unsigned)grid), dim3(64 * W), lds,
-                           stream, q, k, v, dout, lse, delta, dk, dv, a);
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<D, W, STORE>), dim3((unsigned)grid), dim3(64 * W),
+                           lds, stream, q, k, v, dout, lse, delta, dk, dv, ds, a);
     }
+    return hipSuccess;
+}
+
+template <int D, bool STORE>
+hipError_t launch_dkdv16_any(size_t lds, hipStream_t stream, const float* q, const float* k,
+                             const float* v, const float* dout, const float* lse,
+                             const float* delta, float* dk, float* dv, float* ds,
+                             const BwdArgs& a) {
+    // 8 waves of 16 keys per block, or 4 when that leaves compute units
+    // without a block.
+    const auto blocks = [&](int w) {
+        return (long long)a.num_kv_heads * ((a.kv_len + w * k16Keys - 1) / (w * k16Keys));
+    };
+    if (blocks(8) >= kNumCUs)
+        return launch_dkdv16<D, 8, STORE>(blocks(8), lds, stream, q, k, v, dout, lse, delta, dk,
+                                          dv, ds, a);
+    return launch_dkdv16<D, 4, STORE>(blocks(4), lds, stream, q, k, v, dout, lse, delta, dk, dv,
+                                      ds, a);
+}
+
+template <int D>
+hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, const float* o,
+                             const float* dout, const float* lse, float* dq, float* dk,
+                             float* dv, float* delta, float* ds, const BwdArgs& a,
+                             hipStream_t stream) {
+    const long long n_pairs = (long long)a.q_seq * a.num_heads;
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((n_pairs + 15) / 16)), dim3(256), 0,
+                       stream, o, dout, delta, n_pairs);
+    const size_t lds16 = 2 * 2 * (size_t)k16Rows * D * sizeof(float) + 2 * 64 * sizeof(float);
+    const hipError_t e = launch_dkdv16_any<D, true>(lds16, stream, q, k, v, dout, lse, delta, dk,
+                                                    dv, ds, a);
+    if (e != hipSuccess) return e;
+    const size_t lds_dq = 2 * (size_t)k16Keys * D * sizeof(float);
+    const long long grid = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks;
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D>), dim3((unsigned)grid), dim3(256), lds_dq, stream, k,
+                       ds, dq, a);
     return hipSuccess;
 }
 
@@ -732,15 +986,9 @@ hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, c
     const char* force = std::getenv("TA03_BWD_KEYS");
     const bool keys16 = force == nullptr || std::strcmp(force, "32") != 0;
     if (keys16) {
-        // 8 waves of 16 keys per block, or 4 when that leaves compute units
-        // without a block.
         const size_t lds16 = 2 * 2 * (size_t)k16Rows * D * sizeof(float) + 2 * 64 * sizeof(float);
-        const auto blocks = [&](int w) {
-            return (long long)a.num_kv_heads * ((a.kv_len + w * k16Keys - 1) / (w * k16Keys));
-        };
-        if (blocks(8) >= kNumCUs)
-            return launch_dkdv16<D, 8>(blocks(8), lds16, stream, q, k, v, dout, lse, delta, dk, dv, a);
-        return launch_dkdv16<D, 4>(blocks(4), lds16, stream, q, k, v, dout, lse, delta, dk, dv, a);
+        return launch_dkdv16_any<D, false>(lds16, stream, q, k, v, dout, lse, delta, dk, dv,
+                                           nullptr, a);
     }
     const long long g2 = (long long)a.num_kv_heads * a.n_key_blocks;
     if (g2 > 0) {
@@ -754,7 +1002,7 @@ hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, c
 
 hipError_t launch_backward(const float* q, const float* k, const float* v, const float* o,
                            const float* dout, const float* lse, float* dq, float* dk, float* dv,
-                           float* delta, const PrefillShape& s, hipStream_t stream) {
+                           float* delta, float* ds, const PrefillShape& s, hipStream_t stream) {
     BwdArgs a;
     a.q_seq = s.q_seq;
     a.kv_len = s.kv_len;
@@ -780,7 +1028,24 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
     a.n_head_blocks = s.num_heads / a.hg;
     a.n_row_blocks = (s.q_seq + a.rs * kBM - 1) / (a.rs * kBM);
     a.n_key_blocks = (s.kv_len + kWaves * kBN - 1) / (kWaves * kBN);
+    a.ds = DsLayout{s.causal, s.start_pos, s.q_seq, s.kv_len};
+    a.ds_tph = ds_tiles_per_head(a.ds);
+    a.dq_hg = gcd_int(a.group, kWaves);
+    a.dq_rs = kWaves / a.dq_hg;
+    a.dq_n_head_blocks = s.num_heads / a.dq_hg;
+    a.dq_n_row_blocks = (ds_query_tiles(a.ds) + a.dq_rs * kDqRT - 1) / (a.dq_rs * kDqRT);
+    const char* force = std::getenv("TA03_BWD_KEYS");
+    const bool keys16 = force == nullptr || std::strcmp(force, "32") != 0;
     hipError_t e;
+    if (ds != nullptr && keys16 && s.q_seq > 0 && s.kv_len > 0) {
+        if (s.head_dim == 128) {
+            e = launch_bwd_stored<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, stream);
+        } else {
+            e = launch_bwd_stored<64>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, stream);
+        }
+        if (e != hipSuccess) return e;
+        return hipGetLastError();
+    }
     if (s.head_dim == 128) {
         e = launch_bwd_instance<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, a, stream);
     } else {

@@ -104,6 +104,19 @@ size_t attn_bwd_workspace_bytes(int q_seq, int num_heads) {
     return (n + 255) / 256 * 256;
 }
 
+size_t attn_bwd_workspace_bytes_stored(int q_seq, int kv_len, int num_heads, int mode,
+                                       int start_pos) {
+    if (q_seq < 0 || kv_len < 0 || start_pos < 0 || num_heads < 1) return 0;
+    if (mode != TA03_CAUSAL && mode != TA03_FULL && mode != TA03_CROSS) return 0;
+    if (mode != TA03_CAUSAL && start_pos != 0) return 0;
+    if (mode == TA03_CAUSAL && (long long)start_pos + q_seq > kv_len) return 0;
+    if (mode == TA03_FULL && kv_len != q_seq) return 0;
+    const ta03::DsLayout l{mode == TA03_CAUSAL ? 1 : 0, start_pos, q_seq, kv_len};
+    const size_t tile_bytes = (size_t)ta03::kDsTile * ta03::kDsTile * sizeof(float);
+    return attn_bwd_workspace_bytes(q_seq, num_heads) +
+           (size_t)num_heads * (size_t)ta03::ds_tiles_per_head(l) * tile_bytes;
+}
+
 int attn_bwd(const float* q, const float* k, const float* v, const float* out, const float* dout,
              const float* lse, float* dq, float* dk, float* dv, int q_seq, int kv_len,
              int num_heads, int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
@@ -141,8 +154,14 @@ int attn_bwd(const float* q, const float* k, const float* v, const float* out, c
     s.scale = scale;
     s.q_stride = s.out_stride = (long long)num_heads * head_dim;
     s.k_stride = s.v_stride = (long long)num_kv_heads * head_dim;
+    // With room for every dS tile the scores are formed once (stored path).
+    const size_t base = attn_bwd_workspace_bytes(q_seq, num_heads);
+    const size_t stored = attn_bwd_workspace_bytes_stored(q_seq, kv_len, num_heads, mode,
+                                                          start_pos);
+    float* ds = stored > base && workspace_bytes >= stored
+        ? static_cast<float*>(workspace) + base / sizeof(float) : nullptr;
     const hipError_t e = ta03::launch_backward(q, k, v, out, dout, lse, dq, dk, dv,
-                                               static_cast<float*>(workspace), s, stream);
+                                               static_cast<float*>(workspace), ds, s, stream);
     return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
 }
 

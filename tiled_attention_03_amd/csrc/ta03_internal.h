@@ -47,9 +47,44 @@ hipError_t launch_prefill16(const float* q, const float* k, const float* v, floa
 
 // Attention backward (dense rows): dq [q_seq, H*d]; dk, dv [kv_len, Hkv*d];
 // delta: q_seq*H floats of scratch (D_i = <dout_i, out_i> per row and head).
+// Stored score gradients of the backward: dS in 16 x 16 tiles (query rows x
+// keys, row-major, 1 KiB each), one run of tiles per head, and inside a head
+// the tiles of query tile qt (rows [16 qt, 16 qt + 16)) for key tiles
+// kt < tiles_in(qt) one after another. tiles_in(qt) covers the keys of the
+// tile's last row window: causal min(start_pos + min(16 qt + 16, q_seq),
+// kv_len), else kv_len. A causal call has start_pos + q_seq <= kv_len, so
+// every query tile but the last holds qt + 1 + ceil(start_pos / 16) tiles
+// and the tiles before qt sum in closed form. Host (workspace size) and
+// device (addresses) use these same functions.
+struct DsLayout {
+    int causal, start_pos, q_seq, kv_len;
+};
+constexpr int kDsTile = 16;
+__host__ __device__ inline int ds_query_tiles(const DsLayout& l) {
+    return (l.q_seq + kDsTile - 1) / kDsTile;
+}
+__host__ __device__ inline int ds_tiles_in(const DsLayout& l, int qt) {
+    if (!l.causal) return (l.kv_len + kDsTile - 1) / kDsTile;
+    const int rows_hi = (qt + 1) * kDsTile < l.q_seq ? (qt + 1) * kDsTile : l.q_seq;
+    long long w = (long long)l.start_pos + rows_hi;
+    if (w > l.kv_len) w = l.kv_len;
+    return (int)((w + kDsTile - 1) / kDsTile);
+}
+__host__ __device__ inline long long ds_tiles_before(const DsLayout& l, int qt) {
+    if (!l.causal) return (long long)qt * ((l.kv_len + kDsTile - 1) / kDsTile);
+    const long long c = (l.start_pos + kDsTile - 1) / kDsTile;
+    return (long long)qt * (qt + 1) / 2 + c * qt;
+}
+__host__ __device__ inline long long ds_tiles_per_head(const DsLayout& l) {
+    const int n = ds_query_tiles(l);
+    return n == 0 ? 0 : ds_tiles_before(l, n - 1) + ds_tiles_in(l, n - 1);
+}
+
+// ds == nullptr: dq recomputes the scores (two launches); otherwise the dk/dv
+// kernel stores dS in `ds` (DsLayout) and dq is computed from it.
 hipError_t launch_backward(const float* q, const float* k, const float* v, const float* o,
                            const float* dout, const float* lse, float* dq, float* dk, float* dv,
-                           float* delta, const PrefillShape& s, hipStream_t stream);
+                           float* delta, float* ds, const PrefillShape& s, hipStream_t stream);
 
 // Rotary table: entry (p, e) = (cos, sin) of p * theta^(-2e/head_dim).
 hipError_t launch_rope_table(float* cs, int rows, int head_dim, double theta, hipStream_t stream);
