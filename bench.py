@@ -231,10 +231,11 @@ def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None,
             "tflops_kernel": flops / mean_s / 1e12, "tflops_wall": flops * steps / wall / 1e12}
 
 
-def bench_backward(w, steps, warmup, torch, ta):
-    """attn_bwd (both kernels) on the workload, fed by one forward pass;
-    FLOPs are the algorithmic five products per unmasked pair (recomputed
-    scores, dP, dV, dK, dQ): 2.5x the forward's."""
+def bench_backward(w, steps, warmup, torch, ta, stored=True):
+    """attn_bwd on the workload, fed by one forward pass; FLOPs are the
+    algorithmic five products per unmasked pair (scores, dP, dV, dK, dQ):
+    2.5x the forward's. stored: workspace for the stored-dS path (three
+    launches); else the minimal one (dq recomputes scores and dP)."""
     dev = torch.device("cuda:0")
     q, k, v = inputs.make_prefill(w)
     g = inputs.normal(q.shape, w.seed_base + 7)
@@ -247,7 +248,8 @@ def bench_backward(w, steps, warmup, torch, ta):
     dq = torch.empty_like(out)
     dk = torch.empty((w.kv_len, Hkv * d), device=dev)
     dv = torch.empty_like(dk)
-    nbytes = ta.attn_bwd_workspace_bytes(w.q_seq, H)
+    nbytes = (ta.attn_bwd_workspace_bytes_stored(w.q_seq, w.kv_len, H, w.mode, w.start_pos)
+              if stored else ta.attn_bwd_workspace_bytes(w.q_seq, H))
     ws = torch.empty((nbytes // 4,), device=dev)
 
     def call(_i):
@@ -259,7 +261,7 @@ def bench_backward(w, steps, warmup, torch, ta):
     mean_s, min_s, wall = time_calls(call, steps, torch)
     flops = 2.5 * prefill_flops(w)
     return {"flops": flops, "mean_s": mean_s, "min_s": min_s,
-            "tflops_kernel": flops / mean_s / 1e12}
+            "tflops_kernel": flops / mean_s / 1e12, "workspace_bytes": nbytes}
 
 
 def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8, page_size=None, clock=None):
@@ -539,11 +541,20 @@ def main():
                 "kernel": "prefill_kernel<128, true>"}
             print(f"[bench] rotary {result['prefill_rope']}", flush=True)
             r = bench_backward(w, 3, 1, torch, ta)
+            rr = bench_backward(w, 3, 1, torch, ta, stored=False)
             result["backward"] = {
                 "workload": w.name, "ms": round(r["mean_s"] * 1e3, 3),
                 "flops_per_call": r["flops"], "TFLOP/s": round(r["tflops_kernel"], 3),
                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                "kernels": "bwd_dq_kernel<128> + bwd_dkdv16_kernel<128>"}
+                "workspace_bytes": r["workspace_bytes"],
+                "kernels": "bwd_delta_kernel<128> + bwd_dkdv16_kernel<128, 8, true> + "
+                           "bwd_dq_ds_kernel<128>",
+                "recompute_path": {"ms": round(rr["mean_s"] * 1e3, 3),
+                                   "TFLOP/s": round(rr["tflops_kernel"], 3),
+                                   "frac": round(rr["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
+                                   "workspace_bytes": rr["workspace_bytes"],
+                                   "kernels": "bwd_dq_kernel<128> + "
+                                              "bwd_dkdv16_kernel<128, 8, false>"}}
             print(f"[bench] backward {result['backward']}", flush=True)
 
     if args.only != "prefill":

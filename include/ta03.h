@@ -198,7 +198,11 @@ int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStr
  *
  * Stored path: three kernel launches (D_i; dk, dv and the dS tiles; dq from
  * the tiles). Otherwise two (dq with D_i, recomputing the scores; dk, dv).
- * Both run on stream with no allocation and no atomics (results are
+ * The stored path is taken when the workspace holds the tiles and the call
+ * is long enough for it to pay: the dq grid over the tiles has at least 256
+ * blocks of 4 waves (one per compute unit); shorter calls recompute.
+ * Environment override (testing): TA03_BWD_PATH=stored or recompute. Both
+ * paths run on stream with no allocation and no atomics (results are
  * run-to-run identical; the two paths agree to rounding). Errors: as attn_fwd for the sizes and mode;
  * TA03_ERR_NULL for a NULL q, out, dout, lse, dq or workspace (q_seq > 0) or
  * k, v, dk, dv (kv_len > 0); TA03_ERR_WORKSPACE for a short workspace;

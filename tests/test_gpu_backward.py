@@ -50,16 +50,19 @@ def _kw(w):
                 mode=w.mode, kv_len=w.kv_len, start_pos=w.start_pos, scale=w.scale)
 
 
-# Backward paths: "stored" (workspace for the dS tiles; dq from them),
-# "recompute" (minimal workspace; dq recomputes the scores, 16-key dk/dv
-# kernel) and "keys32" (minimal workspace, the 32-key dk/dv kernel forced by
-# the library's TA03_BWD_KEYS).
+# Backward paths: "stored" (workspace for the dS tiles, the stored path
+# forced by the library's TA03_BWD_PATH even where its size rule would
+# recompute; dq from the tiles), "recompute" (minimal workspace; dq
+# recomputes the scores, 16-key dk/dv kernel) and "keys32" (minimal
+# workspace, the 32-key dk/dv kernel forced by TA03_BWD_KEYS).
 PATHS = ["stored", "recompute", "keys32"]
 
 
 def _use_path(path, monkeypatch):
     if path == "keys32":
         monkeypatch.setenv("TA03_BWD_KEYS", "32")
+    if path == "stored":
+        monkeypatch.setenv("TA03_BWD_PATH", "stored")
     return path == "stored"
 
 
@@ -152,9 +155,11 @@ def test_backward_ragged_sweep(case, path, monkeypatch):
     _check_all(got, ref, w, str(case))
 
 
-def test_backward_workspace_short_of_stored_falls_back():
+def test_backward_workspace_short_of_stored_falls_back(monkeypatch):
     """A workspace one tile short of the stored size takes the recompute
-    path: same gradients as the minimal workspace, bit for bit."""
+    path even when the stored path is asked for: same gradients as the
+    minimal workspace, bit for bit."""
+    monkeypatch.setenv("TA03_BWD_PATH", "stored")
     w, q, k, v = inputs.random_case(1120, CAUSAL, 90, 120, 4, 2, 64, start_pos=30)
     g = inputs.normal(q.shape, 1121)
     a = gpu_fwd_bwd(q, k, v, g, stored=True, ws_short=1024, **_kw(w))
@@ -204,7 +209,9 @@ def test_backward_zero_keys():
 
 
 @pytest.mark.parametrize("stored", [True, False])
-def test_backward_deterministic(stored):
+def test_backward_deterministic(stored, monkeypatch):
+    if stored:
+        monkeypatch.setenv("TA03_BWD_PATH", "stored")
     w, q, k, v = inputs.random_case(1180, CAUSAL, 300, 300, 8, 2, 128)
     g = inputs.normal(q.shape, 1181)
     a = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
@@ -214,9 +221,11 @@ def test_backward_deterministic(stored):
 
 
 @pytest.mark.parametrize("stored", [True, False])
-def test_backward_graph_replay(stored):
+def test_backward_graph_replay(stored, monkeypatch):
     """Forward and backward captured in one graph, replayed with the
     program's own work in between: every replay matches the eager result."""
+    if stored:
+        monkeypatch.setenv("TA03_BWD_PATH", "stored")
     import torch
     import tiled_attention_03_amd as ta
     H, Hkv, d, n = 8, 2, 64, 160
@@ -256,3 +265,22 @@ def test_backward_graph_replay(stored):
         torch.cuda.synchronize()
         for x, y in zip((dq, dk, dv), eager):
             assert torch.equal(x, y), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("w", [inputs.FULL_1K, inputs.CAUSAL_16K], ids=lambda w: w.name)
+def test_backward_path_choice_by_size(w, monkeypatch):
+    """Without an override the library picks the path by size, given the
+    stored workspace: full 1024^2 (32 dq blocks from the tiles) recomputes,
+    bitwise equal to the minimal workspace; the 16K causal pass takes the
+    stored path, bitwise equal to forcing it."""
+    monkeypatch.delenv("TA03_BWD_PATH", raising=False)
+    q, k, v = inputs.make_prefill(w)
+    g = inputs.normal(q.shape, w.seed_base + 7)
+    auto = gpu_fwd_bwd(q, k, v, g, stored=True, **_kw(w))
+    if w is inputs.FULL_1K:
+        other = gpu_fwd_bwd(q, k, v, g, stored=False, **_kw(w))
+    else:
+        monkeypatch.setenv("TA03_BWD_PATH", "stored")
+        other = gpu_fwd_bwd(q, k, v, g, stored=True, **_kw(w))
+    for x, y in zip(auto, other):
+        assert np.array_equal(x, y)

@@ -87,7 +87,7 @@ struct BwdArgs {
     int n_key_blocks;                         // dk/dv kernel: 128-key blocks per KV head
     DsLayout ds;                              // stored dS tiles (when kept)
     long long ds_tph;                         // dS tiles per head
-    int dq_hg, dq_rs, dq_n_head_blocks, dq_n_row_blocks;  // dq-from-dS block shape
+    int dq_hg, dq_rs, dq_rt, dq_n_head_blocks, dq_n_row_blocks;  // dq-from-dS block shape
 };
 
 // Issue this wave's share (inst = first, first + step, ...) of a 32-row, D-wide
@@ -760,10 +760,10 @@ bwd_delta_kernel(const float* __restrict__ o, const float* __restrict__ dout,
 //   result block b: register r of lane (j, g) is row 4g + r, column d, so a
 //      row's four column blocks store as one float4 per lane.
 // Tiles past a query tile's window (or query tiles past q_seq) are read
-// clamped to a valid tile and zeroed by a select.
-constexpr int kDqRT = 4;  // 16-row query tiles per wave
-
-template <int D>
+// clamped to a valid tile and zeroed by a select. kDqRT query tiles per wave:
+// 4 for long sequences (each K operand read serves 4 products), 1 where that
+// would leave the grid short of blocks.
+template <int D, int kDqRT>
 __global__ void __launch_bounds__(256, 2)
 bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
                  float* __restrict__ dq, BwdArgs a) {
@@ -957,8 +957,13 @@ hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, con
     if (e != hipSuccess) return e;
     const size_t lds_dq = 2 * (size_t)k16Keys * D * sizeof(float);
     const long long grid = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks;
-    hipLaunchKernelGGL((bwd_dq_ds_kernel<D>), dim3((unsigned)grid), dim3(256), lds_dq, stream, k,
-                       ds, dq, a);
+    if (a.dq_rt == 4) {
+        hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 4>), dim3((unsigned)grid), dim3(256), lds_dq,
+                           stream, k, ds, dq, a);
+    } else {
+        hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 1>), dim3((unsigned)grid), dim3(256), lds_dq,
+                           stream, k, ds, dq, a);
+    }
     return hipSuccess;
 }
 
@@ -1033,11 +1038,22 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
     a.dq_hg = gcd_int(a.group, kWaves);
     a.dq_rs = kWaves / a.dq_hg;
     a.dq_n_head_blocks = s.num_heads / a.dq_hg;
-    a.dq_n_row_blocks = (ds_query_tiles(a.ds) + a.dq_rs * kDqRT - 1) / (a.dq_rs * kDqRT);
+    const auto dq_rows = [&](int rt) {
+        return (ds_query_tiles(a.ds) + a.dq_rs * rt - 1) / (a.dq_rs * rt);
+    };
+    // 4 query tiles per wave while that still gives two blocks per CU.
+    a.dq_rt = (long long)a.dq_n_head_blocks * dq_rows(4) >= 2 * kNumCUs ? 4 : 1;
+    a.dq_n_row_blocks = dq_rows(a.dq_rt);
     const char* force = std::getenv("TA03_BWD_KEYS");
     const bool keys16 = force == nullptr || std::strcmp(force, "32") != 0;
+    // The stored path pays once the dq grid from the tiles fills the compute
+    // units; shorter calls recompute (TA03_BWD_PATH=stored / recompute forces
+    // one, the first only with a workspace that holds the tiles).
+    const char* path = std::getenv("TA03_BWD_PATH");
+    const bool big = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks >= kNumCUs;
+    const bool use_ds = path != nullptr ? std::strcmp(path, "stored") == 0 : big;
     hipError_t e;
-    if (ds != nullptr && keys16 && s.q_seq > 0 && s.kv_len > 0) {
+    if (ds != nullptr && use_ds && keys16 && s.q_seq > 0 && s.kv_len > 0) {
         if (s.head_dim == 128) {
             e = launch_bwd_stored<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, stream);
         } else {
