@@ -12,25 +12,28 @@
 //   dk_j  = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i
 // summed over the query heads of each KV head for dk, dv (GQA).
 //
-// Two kernels, no atomics (run-to-run bitwise deterministic):
-//   * dq kernel (query-parallel, the forward's decomposition): a wave owns 32
-//     query rows of one head, holds Q^T (pre-scaled to log2 units) and dout^T
-//     as MFMA B operands in registers, and streams K/V tiles of 32 keys
-//     through LDS (HBM -> LDS directly, double-buffered, both XOR-swizzled).
-//     Per tile: S^T = K Q^T and dP^T = V dout^T (keys x rows), P^T and dS^T
-//     elementwise in the accumulator registers, dq^T += K^T dS^T with dS^T
-//     reused in place as the B operand (the forward's P.V pairing). It also
-//     computes D_i from out and dout and stores it for the second kernel;
-//   * dk/dv kernel (key-parallel): a wave owns 32 keys of one KV head, holds
-//     K and V as B operands in registers, and walks the query row tiles of
-//     every head of its group that can see its keys (causal: rows from
-//     key - start_pos on), Q and dout tiles streamed through LDS with their
-//     (m, log l) and D. Per tile: S = Q K^T and dP = dout V^T (rows x keys),
-//     then dv^T += dout^T P and dk^T += Q^T dS with P and dS in place.
-// The dq kernel runs two waves per SIMD (two 64 KiB blocks per CU; at d 128
-// the compiler spills a few registers, which measured cheaper than one wave
-// per SIMD); the dk/dv kernel two at d 64 and one at d 128, where dk^T and
-// dv^T sit in the accumulation registers beside K and V.
+// No atomics anywhere (run-to-run bitwise deterministic). Two paths:
+//   * stored path (workspace for every 16 x 16 dS tile): D_i kernel; dk/dv
+//     kernel that also writes the dS tiles it forms; dq = scale * dS K as one
+//     product over the stored tiles. The matrix work is the algorithmic five
+//     products (S, dP, dV, dK, dQ);
+//   * recompute path (minimal workspace, or calls too short for the stored
+//     path to pay): dq kernel (query-parallel, the forward's decomposition):
+//     a wave owns 32 query rows of one head, holds Q^T (pre-scaled to log2
+//     units) and dout^T as MFMA B operands in registers, and streams K/V
+//     tiles of 32 keys through LDS (HBM -> LDS directly, double-buffered,
+//     XOR-swizzled). Per tile: S^T = K Q^T and dP^T = V dout^T (keys x rows),
+//     P^T and dS^T elementwise in the accumulator registers, dq^T += K^T dS^T
+//     with dS^T reused in place as the B operand (the forward's P.V
+//     pairing); it also computes D_i for the second kernel. Then the dk/dv
+//     kernel. S and dP are formed in both kernels (seven products).
+// The dk/dv kernel (key-parallel) in both paths: a wave owns 16 keys of one
+// KV head, holds K and V as B operands, and walks the 16-row query tiles of
+// every head of its group that can see its keys (causal: rows from
+// key - start_pos on), Q and dout tiles streamed through LDS with their
+// (m, log l) and D. Per tile: S = Q K^T and dP = dout V^T (rows x keys), then
+// dv^T += dout^T P and dk^T += Q^T dS with P and dS in place. A first 32-key
+// version stays as an independent cross-check (TA03_BWD_KEYS=32).
 
 #include <hip/hip_runtime.h>
 
@@ -499,15 +502,16 @@ bwd_dkdv_kernel(const float* __restrict__ q, const float* __restrict__ k,
 // dk/dv with 16-key waves on v_mfma_f32_16x16x4_f32: per wave K, V (B
 // operands) and the dk^T, dv^T accumulators take 32 registers each at
 // head_dim 128 (half of the 32-key kernel), so two waves share a SIMD.
-// Block: W waves x 16 keys of one KV head (W = 8, or 4 to give short key
-// ranges more blocks); query tiles of 16 rows (and their
+// Block: W = 4 waves x 16 keys of one KV head, two blocks per CU; query
+// tiles of 16 rows (and their
 // dout rows, (m, log l) and D) are staged in XOR-swizzled LDS, double-
 // buffered. S = Q K^T: k-step s of lane group g carries head-dim g*D/4 + s
 // (each lane reads d/4 contiguous floats of its query row); the result's
 // register r of lane (j, g) is query 4g + r, key j, so in dv^T += dout^T P
 // and dk^T += Q^T dS the k-step t of lane group g pairs query 4g + t with
 // register t -- P and dS stay in registers. dk^T / dv^T block b row m is
-// head-dim (d/16)*m + b.
+// head-dim 64 (b / 4) + 4 m + b % 4, so the 16 lanes of a group read 256
+// contiguous bytes of a Q / dout row (no bank conflicts).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
@@ -662,13 +666,14 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 for (int r = 0; r < 4; ++r) tile[(4 * g + r) * k16Keys + j] = dp[r];
             }
             // dv^T += dout^T P, dk^T += Q^T dS: k-step t of lane group g is
-            // query row 4g + t; lane (m, g) reads head-dims NB*m .. NB*m + NB.
+            // query row 4g + t; lane (m, g) reads head-dims 4m .. 4m + 3 (and
+            // 64 + 4m .. 64 + 4m + 3 at head_dim 128).
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int ir = 4 * g + t;
 #pragma unroll
                 for (int c = 0; c < NB / 4; ++c) {
-                    const int pos = (((NB * j) / 4 + c) ^ (ir & 15)) * 4;
+                    const int pos = ((j + 16 * c) ^ (ir & 15)) * 4;
                     const float4 gg = *reinterpret_cast<const float4*>(Gs + ir * D + pos);
                     const float4 qq = *reinterpret_cast<const float4*>(Qs + ir * D + pos);
 #pragma unroll
@@ -682,14 +687,15 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 
     if (!strip_live || key >= a.kv_len) return;
-    // dk^T / dv^T block b, register r of lane (j, g): head-dim NB*(4g + r) + b.
+    // dk^T / dv^T block b, register r of lane (j, g): head-dim
+    // 64 (b / 4) + 4 (4g + r) + b % 4.
     float* krow = dk + (size_t)key * kvd + kv_head * D;
     float* vrow = dv + (size_t)key * kvd + kv_head * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
         for (int c = 0; c < NB / 4; ++c) {
-            const int d0 = NB * (4 * g + r) + 4 * c;
+            const int d0 = 64 * c + 4 * (4 * g + r);
             *reinterpret_cast<float4*>(krow + d0) =
                 make_float4(dka[4 * c + 0][r] * a.scale, dka[4 * c + 1][r] * a.scale,
                             dka[4 * c + 2][r] * a.scale, dka[4 * c + 3][r] * a.scale);
@@ -931,15 +937,12 @@ hipError_t launch_dkdv16_any(size_t lds, hipStream_t stream, const float* q, con
                              const float* v, const float* dout, const float* lse,
                              const float* delta, float* dk, float* dv, float* ds,
                              const BwdArgs& a) {
-    // 8 waves of 16 keys per block, or 4 when that leaves compute units
-    // without a block.
-    const auto blocks = [&](int w) {
-        return (long long)a.num_kv_heads * ((a.kv_len + w * k16Keys - 1) / (w * k16Keys));
-    };
-    if (blocks(8) >= kNumCUs)
-        return launch_dkdv16<D, 8, STORE>(blocks(8), lds, stream, q, k, v, dout, lse, delta, dk,
-                                          dv, ds, a);
-    return launch_dkdv16<D, 4, STORE>(blocks(4), lds, stream, q, k, v, dout, lse, delta, dk, dv,
+    // Blocks of 4 waves (64 keys), two per compute unit: while one block's
+    // waves wait at a barrier the other block's share each SIMD (8-wave
+    // blocks, one per CU, measured ~1 ms slower on the 16K causal pass).
+    const long long blocks =
+        (long long)a.num_kv_heads * ((a.kv_len + 4 * k16Keys - 1) / (4 * k16Keys));
+    return launch_dkdv16<D, 4, STORE>(blocks, lds, stream, q, k, v, dout, lse, delta, dk, dv,
                                       ds, a);
 }
 
