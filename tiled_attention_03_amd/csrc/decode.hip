@@ -9,22 +9,26 @@
 // The page runs one workgroup per head over every cache row in sequence, and
 // each head of a GQA group re-reads the same K/V rows. This path is bound by
 // HBM bandwidth, so it is built to read each K/V byte once with the chip
-// full of requests:
-//   * grid (split, kv head x head block); a block reads kv_pos, derives the
-//     cache length and its chunk on the device (a recorded launch stays valid
-//     as kv_pos grows) and serves up to 4 query heads of one GQA group;
+// full of requests and as little work as possible between a load's arrival
+// and its refill:
+//   * the cache is cut into units of 64 keys dealt round-robin to the
+//     splits (split s takes units s, s + n, s + 2n, ... of the n active
+//     splits), so at any moment the chip streams neighbouring rows rather
+//     than rows 1 MiB apart; a block reads kv_pos and derives the cache
+//     length and its units on the device (a recorded launch stays valid as
+//     kv_pos grows) and serves up to 4 query heads of one GQA group;
 //   * inside a block the 4 waves are independent: wave w owns keys
-//     [16w, 16w+16) of every 64-key sub-tile, with its own online-softmax
-//     state per head;
-//   * K rows go HBM -> registers directly in the score layout: lane (key,
-//     quarter) holds interleaved 16-byte pieces of its key (each load
-//     instruction covers 64 contiguous bytes of 16 rows) and forms 4-head
-//     dot products against Q broadcast from LDS; two DPP quad steps finish
-//     them, and max and sum over the wave's 16 keys use DPP mirrors and the
-//     row / half-wave swaps (no LDS permutes on the path). Staging K
-//     through LDS measured markedly slower here;
-//   * V rows go HBM -> registers directly in the P.V layout (lane = 4
-//     head-dim columns of one key, 128-bit coalesced);
+//     [16w, 16w+16) of every unit, with its own online-softmax state;
+//   * both products run on the matrix cores as v_mfma_f32_4x4x1_16b_f32
+//     (16 independent 4x4 blocks, so the 4 heads of a group fill every
+//     column): S = K Q^T with K rows straight from HBM as the A operand
+//     (each load instruction covers 64 contiguous bytes of 16 rows) and Q
+//     in registers as the B operand, four head-dim slices in four blocks
+//     summed by two DPP row rotations; then O^T += V^T P with V rows
+//     straight from HBM as the A operand (whole rows per instruction) and P
+//     as the B operand -- each lane already holds the weights of its head
+//     (column), and one row-pair swap hands it the keys its V rows hold.
+//     The vector ALU keeps only the softmax of one head per lane;
 //   * two register sets per wave, both in flight before the first wait and
 //     each refilled as soon as it has been consumed; Q is loaded ahead of
 //     them (vector loads complete in issue order);
@@ -54,18 +58,14 @@ namespace {
 #endif
 constexpr int kWaves = TA03_DECODE_WAVES;
 constexpr int kBlock = 64 * kWaves;
-constexpr int kT = 16 * kWaves;   // keys per sub-tile (16 per wave)
-constexpr int kKW = kT / kWaves;  // keys per wave per sub-tile
+constexpr int kT = 16 * kWaves;   // keys per unit (16 per wave)
+constexpr int kKW = kT / kWaves;  // keys per wave per unit
 constexpr int kG = 4;             // query heads per block
 static_assert(kWaves >= kG, "the merge serves one head per wave");
 #ifndef TA03_DECODE_TARGET_BLOCKS
 #define TA03_DECODE_TARGET_BLOCKS 256
 #endif
 constexpr int kTargetBlocks = TA03_DECODE_TARGET_BLOCKS;
-#ifndef TA03_DECODE_MIN_SUB
-#define TA03_DECODE_MIN_SUB 2
-#endif
-constexpr int kMinChunk = TA03_DECODE_MIN_SUB * kT;  // keys per block at least
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -82,17 +82,19 @@ struct Args {
     int page_size, num_pages;
 };
 
-// Cache length and chunking, derived identically by every block.
+// Cache length, unit count and active splits, derived identically by every
+// block.
 __device__ __forceinline__ void chunking(const uint32_t* kv_pos, const Args& a,
-                                         int* kv_len, int* chunk, int* n_active) {
+                                         int* kv_len, int* n_units, int* n_active) {
     const unsigned long long len = (unsigned long long)(*kv_pos) + 1ull;
     const int L = (int)(len < (unsigned long long)a.max_seq ? len : (unsigned long long)a.max_seq);
-    int c = (L + a.n_splits - 1) / a.n_splits;
-    c = (c + kT - 1) / kT * kT;
-    c = c < kMinChunk ? kMinChunk : c;  // both ping-pong sub-tiles of a wave in flight
     *kv_len = L;
-    *chunk = c;
-    *n_active = (L + c - 1) / c;
+    *n_units = (L + kT - 1) / kT;
+    // Two units per active split at least (both register sets of a wave
+    // carry data), at most n_splits splits; split s takes units s,
+    // s + n_active, s + 2 n_active, ...
+    const int half = *n_units / 2 > 1 ? *n_units / 2 : 1;
+    *n_active = half < a.n_splits ? half : a.n_splits;
 }
 
 // Cross-lane steps that do not go through the LDS permute unit: DPP moves
@@ -104,6 +106,10 @@ constexpr int kQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
 constexpr int kQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
 constexpr int kRowMirror = 0x140;     // lane i <- 15 - i within a row of 16
 constexpr int kRowHalfMirror = 0x141; // lane i <- 7 - i within each half-row
+constexpr int kRowRor4 = 0x124;       // lane i <- lane (i - 4) mod 16 within a row
+constexpr int kRowRor8 = 0x128;       // lane i <- lane (i - 8) mod 16 within a row
+
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -165,242 +171,217 @@ __device__ __forceinline__ float2 load_pair(const float* p) {
     return make_float2(__uint_as_float((unsigned)u), __uint_as_float((unsigned)(u >> 32)));
 }
 
-// LDS written by this wave's lanes becomes readable by its other lanes: DS
-// instructions of one wave execute in order, so waiting for the wave's own
-// LDS operations (lgkmcnt = 0; vector memory counters untouched) suffices.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_wave_barrier();
-}
-
 template <int D>
 __global__ void __launch_bounds__(kBlock)
 decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
               const float* __restrict__ v, const uint32_t* __restrict__ kv_pos,
               float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws,
               Args a) {
-    constexpr int QI = D / 16;    // 16-float pieces per K row: K float4 per lane per sub-tile
-    constexpr int LPR = D / 4;    // lanes per V row in P.V (one float4 each)
-    constexpr int KR = 64 / LPR;  // key groups per wave in P.V
-    constexpr int VK = kKW / KR;  // V rows per lane per sub-tile
+    constexpr int QT = D / 16;    // K float4 loads per lane per set (16 dims per load row)
+    constexpr int LPR = D / 4;    // lanes per V row (one float4 each)
+    constexpr int KR = 64 / LPR;  // V rows per load instruction
+    constexpr int VK = kKW / KR;  // V float4 loads per lane per set
+    static_assert(LPR == 16 || LPR == 32, "head_dim 64 or 128");
 
-    __shared__ __attribute__((aligned(16))) float Qs[kG * D];
-    __shared__ __attribute__((aligned(16))) float Ps[kWaves][kKW * kG];
     __shared__ __attribute__((aligned(16))) float Ow[kWaves][kG * D];
     __shared__ float Mw[kWaves][kG], Lw[kWaves][kG];
     __shared__ int last_flag;
-    extern __shared__ int tbl[];  // this block's slice of the page table (paged cache)
+    extern __shared__ int tbl[];  // this block's page-table entries (paged cache)
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = blockIdx.y;  // kv_head * blks_per_kv + hsub
     const int kv_head = grp / a.blks_per_kv;
     const int hsub = grp % a.blks_per_kv;
     const int head0 = kv_head * a.group + hsub * a.heads_per_blk;
     const int nh = min(a.heads_per_blk, a.group - hsub * a.heads_per_blk);
 
-    // Q is loaded first: it does not depend on kv_pos, and vector loads
-    // complete in issue order, so waiting for Q further down does not wait
-    // for the K/V loads issued after it.
-    constexpr int QPT = (kG * D + kBlock - 1) / kBlock;  // Q floats per thread
-    float qreg[QPT];
+    // Lane roles. Matrix blocks are lanes 4b..4b+3; column j = lane % 4 is
+    // the query head head0 + j throughout. Scores: block b = 4 kg + sl holds
+    // keys 4 kg .. 4 kg + 3 (rows) over the head-dim slice sl.
+    const int j = lane & 3;
+    const int sl = (lane >> 2) & 3;
+    const int kg = lane >> 4;
+
+    // Q first (it does not depend on kv_pos): lane (sl, j) keeps head j's
+    // elements 16 t + 4 sl + c, pre-scaled, as the B operand of the score
+    // products. Heads past the block's count are zero.
+    float4 qr[QT];
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-        const int i = tid + j * kBlock;
-        const int h = i / D;
-        qreg[j] = (i < kG * D && h < nh) ? q[(size_t)(head0 + h) * D + (i % D)] : 0.f;
+    for (int t = 0; t < QT; ++t) {
+        qr[t] = j < nh ? *reinterpret_cast<const float4*>(q + (size_t)(head0 + j) * D + 16 * t + 4 * sl)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
-    int kv_len, chunk, n_active;
-    chunking(kv_pos, a, &kv_len, &chunk, &n_active);
+    int kv_len, n_units, n_active;
+    chunking(kv_pos, a, &kv_len, &n_units, &n_active);
     const int split = blockIdx.x;
     if (split >= n_active) return;  // whole block: nothing of this cache to read
 
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kvdim = a.num_kv_heads * D;
-    const int c0 = split * chunk;
-    const int c1 = min(c0 + chunk, kv_len);
+    const int c1 = kv_len;
+    const int n_mine = (n_units - split + n_active - 1) / n_active;  // units of this block
+    const int n_pairs = (n_mine + 1) / 2;
 
     const float* kbase = k + kv_head * D;
     const float* vbase = v + kv_head * D;
 
-    // Per-lane roles.
-    const int kk = lane >> 2;   // scores: key within the wave's 16
-    const int qq = lane & 3;    // scores: which 16-byte piece of each 64 bytes
-    const int dq = lane % LPR;  // P.V: head-dim float4 index
-    const int kr = lane / LPR;  // P.V: key group
-
-    // Paged cache: stage this chunk's table entries in LDS, each clamped to
-    // a valid page so that no table content can send a load out of bounds.
     const bool paged = a.table != nullptr;
-    const int b0 = paged ? c0 / a.page_size : 0;
     if (paged) {
-        const int nb = (c1 - 1) / a.page_size - b0 + 1;
-        for (int i = tid; i < nb; i += kBlock)
-            tbl[i] = min(max(a.table[b0 + i], 0), a.num_pages - 1);
+        // Entry u * kWaves + w: the page of wave w's 16-key slice of the
+        // block's unit u (slices past the cache read its last row, as the
+        // loads do), clamped to a valid page.
+        for (int i = tid; i < 2 * n_pairs * kWaves; i += kBlock) {
+            const int tok = min((split + (i / kWaves) * n_active) * kT + (i % kWaves) * kKW, c1 - 1);
+            tbl[i] = min(max(a.table[tok / a.page_size], 0), a.num_pages - 1);
+        }
         __syncthreads();
     }
 
-    // K arrives straight in the score layout: lane (kk, qq) holds the pieces
-    // [16 i + 4 qq, +4) of its key for i < QI (each load instruction covers
-    // 64 contiguous bytes of 16 rows). V arrives in the P.V layout. Rows past
-    // the chunk end are read as the chunk's last row (in bounds, no branch
-    // around the load); their scores are masked and their weight is 0. In a
-    // paged cache every key of the wave's slice (after that clamp) lies in the
-    // page of min(slice start, c1 - 1): one row offset per slice.
-    auto gload = [&](float4 (&kx)[QI], float4 (&vx)[VK], int base) {
-        const int wbase = base + wave * kKW;
+    // K arrives as the A operand of the score products: lane (kg, sl, i)
+    // holds key 4 kg + i, elements [16 t + 4 sl, +4) (each load instruction
+    // covers 64 contiguous bytes of 16 rows). V arrives as the A operand of
+    // the P.V products: lane l holds elements [4 (l % LPR), +4) of key
+    // t + (kKW / KR)(l / LPR) (each instruction KR whole rows). Rows past the
+    // cache are read as its last row (in bounds, no branch around the
+    // load); their scores are masked and their weight is 0.
+    auto gload = [&](float4 (&kx)[QT], float4 (&vx)[VK], int u) {
+        const int wbase = (split + u * n_active) * kT + wave * kKW;
         long long shift = 0;  // physical row - token index
         if (paged) {
             const int blk = min(wbase, c1 - 1) / a.page_size;
-            shift = (long long)(tbl[blk - b0] - blk) * a.page_size;
+            shift = (long long)(tbl[u * kWaves + wave] - blk) * a.page_size;
         }
-        const long long key = min(wbase + kk, c1 - 1) + shift;
-        const float* kp = kbase + (size_t)key * kvdim + 4 * qq;
+        const long long key = min(wbase + 4 * kg + j, c1 - 1) + shift;
+        const float* kp = kbase + (size_t)key * kvdim + 4 * sl;
 #pragma unroll
-        for (int i = 0; i < QI; ++i) kx[i] = *reinterpret_cast<const float4*>(kp + 16 * i);
+        for (int t = 0; t < QT; ++t) kx[t] = *reinterpret_cast<const float4*>(kp + 16 * t);
 #pragma unroll
-        for (int i = 0; i < VK; ++i) {
-            const long long vkey = min(wbase + kr * VK + i, c1 - 1) + shift;
-            vx[i] = *reinterpret_cast<const float4*>(vbase + (size_t)vkey * kvdim + 4 * dq);
+        for (int t = 0; t < VK; ++t) {
+            const long long vkey = min(wbase + t + VK * (lane / LPR), c1 - 1) + shift;
+            vx[t] = *reinterpret_cast<const float4*>(vbase + (size_t)vkey * kvdim + 4 * (lane % LPR));
         }
     };
 
-    // Both register sets in flight before anything waits. Loads are never
-    // behind a branch (rows are clamped into the chunk), so the compiler's
-    // wait counts stay exact: waiting for one set never waits for the other.
-    float4 ka[QI], va[VK], kb[QI], vb[VK];
-    gload(ka, va, c0);
-    gload(kb, vb, c0 + kT);
-
+    float4 ka[QT], va[VK], kb[QT], vb[VK];
+    gload(ka, va, 0);
+    gload(kb, vb, 1);
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-        const int i = tid + j * kBlock;
-        if (i < kG * D) Qs[i] = qreg[j] * a.qscale;
+    for (int t = 0; t < QT; ++t) {
+        qr[t].x *= a.qscale;
+        qr[t].y *= a.qscale;
+        qr[t].z *= a.qscale;
+        qr[t].w *= a.qscale;
     }
-    __syncthreads();
 
-    float m_run[kG], l_run[kG];
-    float4 acc[kG];
+    // Online-softmax state of head j (the same in every lane of column j)
+    // and the unnormalised output: oc[c] register i = element
+    // 16 (b % (LPR / 4)) + 4 i + c of head j, b = lane / 4, summed over the
+    // key groups of the lane's V rows.
+    float m_run = kNegBig, l_run = 0.f;
+    v4f oc[4];
 #pragma unroll
-    for (int h = 0; h < kG; ++h) {
-        m_run[h] = kNegBig;
-        l_run[h] = 0.f;
-        acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    float* ps = Ps[wave];
+    for (int c = 0; c < 4; ++c) oc[c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    auto process = [&](const float4 (&kx)[QI], const float4 (&vx)[VK], int base) {
-        // Scores for key kk, 4 heads, over this lane's pieces; a quad
-        // shuffle completes the dot products.
-        float s[kG];
+    auto process = [&](const float4 (&kx)[QT], const float4 (&vx)[VK], int u) {
+        const int wbase = (split + u * n_active) * kT + wave * kKW;
+        // S (keys x heads) on the matrix cores, two accumulators in turn.
+        v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < kG; ++h) s[h] = 0.f;
+        for (int t = 0; t < QT; ++t) {
+            s0 = __builtin_amdgcn_mfma_f32_4x4x1f32(kx[t].x, qr[t].x, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_4x4x1f32(kx[t].y, qr[t].y, s1, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_4x4x1f32(kx[t].z, qr[t].z, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_4x4x1f32(kx[t].w, qr[t].w, s1, 0, 0, 0);
+        }
+        // Sum the four head-dim slices (lanes 4 apart in each row of 16):
+        // register r of lane (kg, sl, j) is then the score of key 4 kg + r
+        // for head j.
+        float x[4];
 #pragma unroll
-        for (int i = 0; i < QI; ++i) {
+        for (int r = 0; r < 4; ++r) {
+            float sc = s0[r] + s1[r];
+            sc += dpp<kRowRor4>(sc);
+            sc += dpp<kRowRor8>(sc);
+            x[r] = wbase + 4 * kg + r < c1 ? sc : -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = pair_max32(pair_max16(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        float p[4];
 #pragma unroll
-            for (int h = 0; h < kG; ++h) {
-                const float4 qx = *reinterpret_cast<const float4*>(Qs + h * D + 16 * i + 4 * qq);
-                s[h] = fmaf(qx.x, kx[i].x, s[h]);
-                s[h] = fmaf(qx.y, kx[i].y, s[h]);
-                s[h] = fmaf(qx.z, kx[i].z, s[h]);
-                s[h] = fmaf(qx.w, kx[i].w, s[h]);
+        for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m_new);
+        const float sm = pair_sum32(pair_sum16((p[0] + p[1]) + (p[2] + p[3])));
+        l_run = l_run * corr + sm;
+        m_run = m_new;
+
+        // P as the B operand: the weight of head j for the key that the
+        // lane's V rows hold in load t (key t + VK (lane / LPR)).
+        float pb[VK];
+        if constexpr (LPR == 32) {
+            // Keys t + 8 h for the half h: the row pair's even row holds
+            // keys 8 h + r, its odd row 8 h + 4 + r.
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const auto e = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[r]),
+                                                                __float_as_uint(p[r]), false, false);
+                pb[r] = __uint_as_float(e[0]);
+                pb[4 + r] = __uint_as_float(e[1]);
             }
-        }
-        const bool valid = base + wave * kKW + kk < c1;
-        float p[kG], corr[kG];
+        } else {
+            // Keys t + 4 kg: the lane's own registers.
 #pragma unroll
-        for (int h = 0; h < kG; ++h) {
-            s[h] += dpp<kQuadXor1>(s[h]);
-            s[h] += dpp<kQuadXor2>(s[h]);
-            // From here each value is the same on the 4 lanes of its key's
-            // quad: the half-row mirror pairs neighbouring keys, the row
-            // mirror pairs key pairs, the swaps pair rows and half-waves, so
-            // each key enters the max and the sum once.
-            const float x = valid ? s[h] : -INFINITY;
-            float mx = fmaxf(x, dpp<kRowHalfMirror>(x));
-            mx = fmaxf(mx, dpp<kRowMirror>(mx));
-            mx = pair_max32(pair_max16(mx));
-            const float m_new = fmaxf(m_run[h], mx);
-            corr[h] = __builtin_amdgcn_exp2f(m_run[h] - m_new);
-            p[h] = __builtin_amdgcn_exp2f(x - m_new);
-            float sm = p[h] + dpp<kRowHalfMirror>(p[h]);
-            sm += dpp<kRowMirror>(sm);
-            sm = pair_sum32(pair_sum16(sm));
-            l_run[h] = l_run[h] * corr[h] + sm;
-            m_run[h] = m_new;
-        }
-        if (qq == 0)
-            *reinterpret_cast<float4*>(ps + kk * kG) = make_float4(p[0], p[1], p[2], p[3]);
-        wave_lds_sync();
-
-        // O += P V over the wave's keys kr*VK .. kr*VK+VK-1, 4 columns per lane.
-#pragma unroll
-        for (int h = 0; h < kG; ++h) {
-            acc[h].x *= corr[h];
-            acc[h].y *= corr[h];
-            acc[h].z *= corr[h];
-            acc[h].w *= corr[h];
+            for (int r = 0; r < 4; ++r) pb[r] = p[r];
         }
 #pragma unroll
-        for (int i = 0; i < VK; ++i) {
-            const float4 pk = *reinterpret_cast<const float4*>(ps + (kr * VK + i) * kG);
-            const float pv[kG] = {pk.x, pk.y, pk.z, pk.w};
+        for (int c = 0; c < 4; ++c) oc[c] *= corr;
 #pragma unroll
-            for (int h = 0; h < kG; ++h) {
-                acc[h].x = fmaf(pv[h], vx[i].x, acc[h].x);
-                acc[h].y = fmaf(pv[h], vx[i].y, acc[h].y);
-                acc[h].z = fmaf(pv[h], vx[i].z, acc[h].z);
-                acc[h].w = fmaf(pv[h], vx[i].w, acc[h].w);
-            }
+        for (int t = 0; t < VK; ++t) {
+            oc[0] = __builtin_amdgcn_mfma_f32_4x4x1f32(vx[t].x, pb[t], oc[0], 0, 0, 0);
+            oc[1] = __builtin_amdgcn_mfma_f32_4x4x1f32(vx[t].y, pb[t], oc[1], 0, 0, 0);
+            oc[2] = __builtin_amdgcn_mfma_f32_4x4x1f32(vx[t].z, pb[t], oc[2], 0, 0, 0);
+            oc[3] = __builtin_amdgcn_mfma_f32_4x4x1f32(vx[t].w, pb[t], oc[3], 0, 0, 0);
         }
-        wave_lds_sync();  // P reads done before the next sub-tile rewrites it
     };
 
-    // Sub-tiles go in pairs, one per register set, each set refilled as soon
-    // as it has been consumed, so two sub-tiles per wave stay in flight. The
-    // last pair is peeled off (no refills): every iteration of the loop then
-    // has the same loads in flight, and nothing is requested that is not
-    // used. A sub-tile wholly past the chunk end (an odd count) reads the
-    // chunk's last row and contributes nothing: its scores are masked, so its
-    // weights are 0 and the running max is kept.
-    const int n_pairs = (c1 - c0 + 2 * kT - 1) / (2 * kT);
-    int base = c0;
-    for (int pr = 1; pr < n_pairs; ++pr, base += 2 * kT) {
-        process(ka, va, base);
-        gload(ka, va, base + 2 * kT);
-        process(kb, vb, base + kT);
-        gload(kb, vb, base + 3 * kT);
+    // Units go in pairs, one per register set, each set refilled as soon as
+    // it has been consumed, so two units per wave stay in flight. The last
+    // pair is peeled off (no refills). A unit past the block's count (an odd
+    // count) reads the cache's last row and contributes nothing: its scores
+    // are masked, so its weights are 0 and the running max is kept.
+    int ub = 0;
+    for (int pr = 1; pr < n_pairs; ++pr, ub += 2) {
+        process(ka, va, ub);
+        gload(ka, va, ub + 2);
+        process(kb, vb, ub + 1);
+        gload(kb, vb, ub + 3);
     }
-    process(ka, va, base);
-    process(kb, vb, base + kT);
+    process(ka, va, ub);
+    process(kb, vb, ub + 1);
 
-    // Sum the key groups of the wave (same running max within a wave).
+    // Sum the key groups of the wave's V rows (lane bits 4-5 for head_dim
+    // 64, bit 5 for 128); every running max of the wave is the same.
 #pragma unroll
-    for (int h = 0; h < kG; ++h) {
-        if constexpr (LPR == 16) {  // key groups in lane bits 4 and 5
-            acc[h].x = pair_sum16(acc[h].x);
-            acc[h].y = pair_sum16(acc[h].y);
-            acc[h].z = pair_sum16(acc[h].z);
-            acc[h].w = pair_sum16(acc[h].w);
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float o = oc[c][r];
+            if constexpr (LPR == 16) o = pair_sum16(o);
+            oc[c][r] = pair_sum32(o);
         }
-        static_assert(LPR == 16 || LPR == 32, "head_dim 64 or 128");
-        acc[h].x = pair_sum32(acc[h].x);
-        acc[h].y = pair_sum32(acc[h].y);
-        acc[h].z = pair_sum32(acc[h].z);
-        acc[h].w = pair_sum32(acc[h].w);
     }
-    if (kr == 0) {
+    if (lane < LPR) {
+        const int b = lane >> 2;
 #pragma unroll
-        for (int h = 0; h < kG; ++h)
-            *reinterpret_cast<float4*>(&Ow[wave][h * D + 4 * dq]) = acc[h];
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<float4*>(&Ow[wave][j * D + 16 * b + 4 * r]) =
+                make_float4(oc[0][r], oc[1][r], oc[2][r], oc[3][r]);
     }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < kG; ++h) {
-            Mw[wave][h] = m_run[h];
-            Lw[wave][h] = l_run[h];
-        }
+    if (lane < kG) {
+        Mw[wave][j] = m_run;
+        Lw[wave][j] = l_run;
     }
     __syncthreads();
 
@@ -564,12 +545,16 @@ hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t str
 }
 
 size_t decode_table_lds_bytes(const DecodeShape& s, const DecodePlan& p, int page_size) {
-    // The largest chunk any kv_pos can give (the cache full), as chunking()
-    // computes it, and the table entries a chunk can touch.
-    long long c = ((long long)s.max_seq + p.n_splits - 1) / p.n_splits;
-    c = (c + kT - 1) / kT * kT;
-    if (c < kMinChunk) c = kMinChunk;
-    return (size_t)(c / page_size + 2) * sizeof(int);
+    // One entry per wave slice of each unit a block can take (the cache
+    // full), the unit count rounded up to the pairs the loop runs.
+    (void)page_size;
+    // A block takes at most ceil(units / n_splits) units, or 3 when fewer
+    // splits are active than n_splits.
+    const long long units = ((long long)s.max_seq + kT - 1) / kT;
+    long long cnt = (units + p.n_splits - 1) / p.n_splits;
+    if (cnt < 3) cnt = 3;
+    cnt = (cnt + 1) / 2 * 2;
+    return (size_t)(cnt * kWaves) * sizeof(int);
 }
 
 hipError_t launch_decode(const float* q, const float* k, const float* v,

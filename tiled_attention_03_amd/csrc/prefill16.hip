@@ -123,7 +123,6 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int w_row = a.causal ? min(a.start_pos + row + 1, a.kv_len) : a.kv_len;
     const int w_max = !wave_live ? 0
         : (a.causal ? min(a.start_pos + min(row0 + kRows, a.q_seq), a.kv_len) : a.kv_len);
-    const int w_min = a.causal ? min(a.start_pos + row0 + 1, a.kv_len) : a.kv_len;
 
     const int n_tiles = (w_max + kKeys - 1) / kKeys;
     const int nt = (n_tiles + a.ks - 1) / a.ks;
