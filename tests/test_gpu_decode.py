@@ -80,6 +80,7 @@ DEC_SWEEP = [
     (32, 8, 128, 4096, 1),
     (6, 3, 128, 2049, 2000),
     (8, 8, 64, 9000, 8999),
+    (32, 8, 128, 8192, 6000),   # 94 units over 32 splits: most blocks take 3
 ]
 
 

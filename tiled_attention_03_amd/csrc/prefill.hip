@@ -103,6 +103,7 @@ struct Args {
     int causal, start_pos;
     float qscale;  // scale * log2(e)
     long long q_stride, k_stride, v_stride, out_stride;  // row strides (floats)
+    int small_strides;  // 31 * max(k_stride, v_stride) + head_dim < 2^31: 32-bit tile offsets
     int hg;        // heads per block
     int rs;        // 32-row strips per block
     int ks;        // key-range splits per block
@@ -219,10 +220,44 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // Issue this wave's share of tile t's K and V into buffer buf. LDS slot s
     // (16 bytes) of a tile holds row s/CPR; for K its chunk position p holds
     // logical chunk p ^ (row % 16), for V the natural chunk.
+    // Per-lane element offsets inside a tile (row s / CPR, chunk s % CPR of
+    // the wave's load slot s), the same for every tile. A tile that lies
+    // inside the block's window then costs one address add per load; the
+    // last tile of a window takes the clamped path below. At most LOADS / gw
+    // slots per wave: head_dim 128 runs at most 2 key splits (gw >= 2),
+    // head_dim 64 at most 4 (gw >= 1). The rotary instance keeps the general
+    // path (its registers are spoken for).
+    constexpr int MAXI = D == 128 ? LOADS / 2 : LOADS;
+    unsigned koff[MAXI], voff[MAXI];
+#pragma unroll
+    for (int u = 0; u < MAXI; ++u) {
+        const unsigned s = (unsigned)((wg + u * gw) * 64 + lane);
+        const unsigned r = s / CPR, c = s % CPR;
+        koff[u] = r * (unsigned)a.k_stride + 4u * (c ^ (r & 15u));
+        voff[u] = r * (unsigned)a.v_stride + 4u * c;
+    }
     auto issue_tile = [&](int t, int buf) {
         float* kd = my_lds + (size_t)buf * 2 * TILE_F;
         float* vd = kd + TILE_F;
         const int kv0 = t * kBN;
+        if (!ROPE && a.small_strides && kv0 + kBN <= w_block) {
+            const float* kt = kbase + (size_t)kv0 * a.k_stride;
+            const float* vt = vbase + (size_t)kv0 * a.v_stride;
+#pragma unroll
+            for (int u = 0; u < MAXI; ++u) {
+                const int inst = wg + u * gw;
+                if (inst < LOADS) {
+                    // (the addresses go through named locals: written inline
+                    // as builtin arguments, they made the host pass drop the
+                    // kernel stubs without a diagnostic)
+                    const float* kg = kt + koff[u];
+                    const float* vg = vt + voff[u];
+                    __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kd + inst * 256), 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(vg, (lds_void*)(vd + inst * 256), 16, 0, 0);
+                }
+            }
+            return;
+        }
 #pragma unroll 1
         for (int inst = wg; inst < LOADS; inst += gw) {
             const int s = inst * 64 + lane;
@@ -489,6 +524,10 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     a.k_stride = s.k_stride;
     a.v_stride = s.v_stride;
     a.out_stride = s.out_stride;
+    {
+        const long long big = s.k_stride > s.v_stride ? s.k_stride : s.v_stride;
+        a.small_strides = 31 * big + s.head_dim < (1ll << 31) ? 1 : 0;
+    }
 
     // Block shape: heads of one GQA group x row strips x key splits = 4 waves.
     // Key splits only when one wave per (32 rows, head) leaves the chip short
