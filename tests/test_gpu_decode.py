@@ -147,12 +147,15 @@ def test_workspace_reused_across_calls(decode_8k):
     nbytes = ta.attn_decode_workspace_bytes(w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq)
     ws = torch.full((nbytes // 4,), float("nan"), device=device())
     ta.attn_decode_workspace_init(ws, nbytes, w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq)
+    # the words the init zero-filled are the counter region (the rest stays NaN)
+    counter_words = (ws == 0).cpu().numpy()
+    assert counter_words.sum() >= w.num_kv_heads
     for p in (8191, 5, 700, 8191, 64, 63, 4096):
         go, gl = gpu_decode(q, k, v, p, k_dev=kd, v_dev=vd, ws=ws, **kw)
         ro, rl = ref_decode(q, k, v, p, **kw)
         check_out(go, ro, f"reuse p={p}")
         check_lse(gl, rl, f"reuse lse p={p}")
-    counters = ws[-(w.num_kv_heads):].view(torch.int32).cpu().numpy()
+    counters = ws.view(torch.int32).cpu().numpy()[counter_words]
     assert np.all(counters == 0)
 
 

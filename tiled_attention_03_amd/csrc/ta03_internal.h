@@ -29,7 +29,8 @@ struct DecodePlan {
     int blks_per_kv;    // blocks per KV head along the head axis
     int n_splits;       // splits of the cache axis
     size_t cnt_offset;  // floats from the workspace start to the ticket counters
-    size_t n_counters;  // one ticket counter per (kv head, head block)
+    size_t n_counters;  // words of the counter region: one ticket per (kv head, head block),
+                        // each in its own slot
     size_t ws_floats;   // workspace size in floats
 };
 
