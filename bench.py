@@ -547,14 +547,14 @@ def main():
                 "flops_per_call": r["flops"], "TFLOP/s": round(r["tflops_kernel"], 3),
                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
                 "workspace_bytes": r["workspace_bytes"],
-                "kernels": "bwd_delta_kernel<128> + bwd_dkdv16_kernel<128, 8, true> + "
-                           "bwd_dq_ds_kernel<128>",
+                "kernels": "bwd_delta_kernel<128> + bwd_dkdv16_kernel<128, 4, true> + "
+                           "bwd_dq_ds_kernel<128, 4>",
                 "recompute_path": {"ms": round(rr["mean_s"] * 1e3, 3),
                                    "TFLOP/s": round(rr["tflops_kernel"], 3),
                                    "frac": round(rr["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
                                    "workspace_bytes": rr["workspace_bytes"],
                                    "kernels": "bwd_dq_kernel<128> + "
-                                              "bwd_dkdv16_kernel<128, 8, false>"}}
+                                              "bwd_dkdv16_kernel<128, 4, false>"}}
             print(f"[bench] backward {result['backward']}", flush=True)
 
     if args.only != "prefill":
