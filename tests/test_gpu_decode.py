@@ -81,6 +81,8 @@ DEC_SWEEP = [
     (6, 3, 128, 2049, 2000),
     (8, 8, 64, 9000, 8999),
     (32, 8, 128, 8192, 6000),   # 94 units over 32 splits: most blocks take 3
+    (16, 4, 64, 700, 650),      # group 4 at head_dim 64: every matrix column a head
+    (16, 2, 64, 333, 332),      # group 8 at head_dim 64: two head blocks per KV head
 ]
 
 
