@@ -214,8 +214,8 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     float4 qr[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-        qr[t] = j < nh ? *reinterpret_cast<const float4*>(q + (size_t)(head0 + j) * D + 16 * t + 4 * sl)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float* qp = q + (size_t)(head0 + j) * D + 16 * t + 4 * sl;
+        qr[t] = j < nh ? *reinterpret_cast<const float4*>(qp) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
     int kv_len, n_units, n_active;

@@ -345,9 +345,6 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             const float* Ks = my_lds + (size_t)(it & 1) * 2 * TILE_F;
             const float* Vs = Ks + TILE_F;
 
-            // Matrix-core sections run at raised wave priority so the SIMD's
-            // other wave fills the gaps with its softmax work.
-            __builtin_amdgcn_s_setprio(1);
             // S^T = K Q^T for this tile (already in log2 units).
             f32x16 s;
 #pragma unroll
@@ -363,7 +360,6 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 s = mfma32(kk.w, qr[4 * g + 3], s);
             }
 
-            __builtin_amdgcn_s_setprio(0);
             if (kv0 + kBN > w_wave_min) {  // some key of the tile is outside some window
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
@@ -395,6 +391,9 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                     for (int r = 0; r < 16; ++r) o[b][r] *= corr;
             }
 
+            // The P.V section runs at raised wave priority so the SIMD's other
+            // wave fills its gaps with softmax work (raising it around the
+            // score products as well measured slightly slower).
             __builtin_amdgcn_s_setprio(1);
             // O^T += V^T P^T: k-step t pairs keys acc_row(t, 0) and acc_row(t, 1).
 #pragma unroll
