@@ -83,6 +83,8 @@ DEC_SWEEP = [
     (32, 8, 128, 8192, 6000),   # 94 units over 32 splits: most blocks take 3
     (16, 4, 64, 700, 650),      # group 4 at head_dim 64: every matrix column a head
     (16, 2, 64, 333, 332),      # group 8 at head_dim 64: two head blocks per KV head
+    (12, 2, 128, 500, 450),     # group 6: a second head block of 2 heads
+    (10, 2, 64, 257, 256),      # group 5: a second head block of 1 head
 ]
 
 
