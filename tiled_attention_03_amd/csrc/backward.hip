@@ -543,6 +543,14 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     constexpr int LOADS = TILE_F / 4 / 64;  // wave instructions per tile (<= 8)
     // [2][SUB][Q tile | dout tile], then [2][SUB][64 floats: (m, log l) x 16 rows, D x 16 rows]
     constexpr int SUB = kDkdvSub;  // query tiles per stage (one barrier per stage)
+    // Row r of a tile stores logical 16-byte chunk c at position c ^ swz(r).
+    // A ds_read_b128 is served 16 lanes at a time over 64 four-byte banks (16
+    // chunk positions per 256 bytes): in each half-wave the lane quads whose
+    // index (lane >> 2) has even bit parity form one pass, the odd ones the
+    // other. The score read (lane (j, g): row j, chunk g * KS / 4 + c) and the
+    // dv / dk read (row 4g + t, chunk j + 16c) both hit 16 distinct positions
+    // per pass with the masks below; r & 15 left both 2-way.
+    auto swz = [](int r) { return D == 128 ? (r & 3) | ((r >> 1) & 4) : r & 11; };
     extern __shared__ __attribute__((aligned(16))) float smem[];
     float* vecs = smem + 2 * SUB * 2 * TILE_F;
 
@@ -599,11 +607,11 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         float* qdst = smem + (size_t)slot * 2 * TILE_F;
 #pragma unroll 1
         for (int inst = wave; inst < LOADS; inst += W) {
-            // slot s holds row s / CPR, position s % CPR = logical chunk ^ (row % 16)
+            // slot s holds row s / CPR, position s % CPR = logical chunk ^ swz(tile row)
             const int s_ = inst * 64 + lane;
             const int r = s_ / CPR, p = s_ % CPR;
             const int row = min(row0 + r, a.q_seq - 1);
-            const size_t src = (size_t)row * qd + h * D + 4 * (p ^ (r & 15));
+            const size_t src = (size_t)row * qd + h * D + 4 * (p ^ swz(r));
             __builtin_amdgcn_global_load_lds(q + src, (lds_void*)(qdst + inst * 256), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(dout + src, (lds_void*)(qdst + TILE_F + inst * 256),
                                              16, 0, 0);
@@ -646,7 +654,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < KS / 4; ++c) {
-                    const int pos = ((g * KS / 4 + c) ^ (j & 15)) * 4;
+                    const int pos = ((g * KS / 4 + c) ^ swz(j)) * 4;
                     const float4 qq = *reinterpret_cast<const float4*>(Qs + j * D + pos);
                     const float4 gg = *reinterpret_cast<const float4*>(Gs + j * D + pos);
 #pragma unroll
@@ -689,7 +697,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                     const int ir = 4 * g + t;
 #pragma unroll
                     for (int c = 0; c < NB / 4; ++c) {
-                        const int pos = ((j + 16 * c) ^ (ir & 15)) * 4;
+                        const int pos = ((j + 16 * c) ^ swz(ir)) * 4;
                         const float4 gg = *reinterpret_cast<const float4*>(Gs + ir * D + pos);
                         const float4 qq = *reinterpret_cast<const float4*>(Qs + ir * D + pos);
 #pragma unroll
