@@ -334,7 +334,11 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const int t = t_begin + it;
         const bool have = t < t_end;
         wait_vmem();
-        __syncthreads();  // tile t landed for every wave; buffer (it+1)&1 is free
+        // Tile t landed for every wave; buffer (it+1)&1 is free. A key split
+        // served by one wave loads and reads only its own buffers, so its
+        // wait suffices and the waves of the block run decoupled (full
+        // 1024x1024, four splits: 30.5 -> 29.3 us).
+        if (gw > 1) __syncthreads();
         const bool next = have && t + 1 < t_end;
         if (next) {
             issue_tile(t + 1, (it + 1) & 1);
