@@ -551,8 +551,15 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // dv / dk read (row 4g + t, chunk j + 16c) both hit 16 distinct positions
     // per pass with the masks below; r & 15 left both 2-way.
     auto swz = [](int r) { return D == 128 ? (r & 3) | ((r >> 1) & 4) : r & 11; };
-    extern __shared__ __attribute__((aligned(16))) float smem[];
-    float* vecs = smem + 2 * SUB * 2 * TILE_F;
+    // The two stage buffers are separate LDS objects, each named directly at
+    // every copy and read (the stage loop is unrolled by two): the compiler
+    // then knows that the copies into one buffer do not touch the other, and
+    // does not make the reads of the current stage wait for the next stage's
+    // copies to land (with offsets into one array it did).
+    __shared__ __attribute__((aligned(16))) float tl0[SUB * 2 * TILE_F];
+    __shared__ __attribute__((aligned(16))) float tl1[SUB * 2 * TILE_F];
+    __shared__ __attribute__((aligned(16))) float vc0[SUB * 64];
+    __shared__ __attribute__((aligned(16))) float vc1[SUB * 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -601,10 +608,10 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int n_qt = i_lo < a.q_seq ? (a.q_seq + k16Rows - 1) / k16Rows - qt0 : 0;
     const int total = a.group * n_qt;
 
-    auto issue1 = [&](int it, int slot) {
+    auto issue1 = [&](int it, int sub, float* tb, float* vb) __attribute__((always_inline)) {
         const int h = kv_head * a.group + it / n_qt;
         const int row0 = (qt0 + it % n_qt) * k16Rows;
-        float* qdst = smem + (size_t)slot * 2 * TILE_F;
+        float* qdst = tb + (size_t)sub * 2 * TILE_F;
 #pragma unroll 1
         for (int inst = wave; inst < LOADS; inst += W) {
             // slot s holds row s / CPR, position s % CPR = logical chunk ^ swz(tile row)
@@ -621,33 +628,32 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
             const float* src = lane < 32
                 ? lse + ((size_t)min(row0 + (lane >> 1), a.q_seq - 1) * a.num_heads + h) * 2 + (lane & 1)
                 : delta + (size_t)min(row0 + (lane & 15), a.q_seq - 1) * a.num_heads + h;
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(vecs + slot * 64), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(vb + sub * 64), 4, 0, 0);
         }
     };
-    auto issue = [&](int st, int buf) {
+    auto issue = [&](int st, float* tb, float* vb) __attribute__((always_inline)) {
 #pragma unroll
         for (int sub = 0; sub < SUB; ++sub)
-            if (st * SUB + sub < total) issue1(st * SUB + sub, buf * SUB + sub);
+            if (st * SUB + sub < total) issue1(st * SUB + sub, sub, tb, vb);
     };
 
     const int n_st = (total + SUB - 1) / SUB;
-    if (total > 0) issue(0, 0);
-    for (int st = 0; st < n_st; ++st) {
+    auto stage = [&](int st, const float* rt, const float* rv, float* wt, float* wv)
+        __attribute__((always_inline)) {
         wait_vmem();
-        __syncthreads();  // stage st landed for every wave; buffer (st+1)&1 is free
-        if (st + 1 < n_st) issue(st + 1, (st + 1) & 1);
+        __syncthreads();  // stage st landed for every wave; the other buffer is free
+        if (st + 1 < n_st) issue(st + 1, wt, wv);
 #pragma unroll
         for (int sub = 0; sub < SUB; ++sub) {
             const int it = st * SUB + sub;
-            const int slot = (st & 1) * SUB + sub;
             if (it >= total) break;
             const int row0 = (qt0 + it % n_qt) * k16Rows;
             const int rows_hi = min(row0 + k16Rows, a.q_seq);
             const int w_max = a.causal ? min(a.start_pos + rows_hi, a.kv_len) : a.kv_len;
             if (strip_live && key0 < w_max) {  // wave-uniform
-                const float* Qs = smem + (size_t)slot * 2 * TILE_F;
+                const float* Qs = rt + (size_t)sub * 2 * TILE_F;
                 const float* Gs = Qs + TILE_F;
-                const float* vd = vecs + slot * 64;
+                const float* vd = rv + sub * 64;
                 // S = Q K^T, dP = dout V^T: register r of lane (j, g) is query
                 // row0 + 4g + r, key key0 + j.
                 f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -709,6 +715,11 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 }
             }
         }
+    };
+    if (total > 0) issue(0, tl0, vc0);
+    for (int st = 0; st < n_st; st += 2) {
+        stage(st, tl0, vc0, tl1, vc1);
+        if (st + 1 < n_st) stage(st + 1, tl1, vc1, tl0, vc0);
     }
 
     if (!strip_live || key >= a.kv_len) return;
@@ -803,7 +814,10 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     constexpr int TILE_F = k16Keys * D;
     constexpr int LOADS = TILE_F / 4 / 64;  // wave instructions per K tile (8 or 4)
     constexpr int TF = k16Rows * k16Keys;   // floats per dS tile
-    extern __shared__ __attribute__((aligned(16))) float smem[];  // [2][K tile]
+    // K tile double buffer as two LDS objects, named directly at every copy
+    // and read, so the reads of tile kt do not wait for tile kt+1's copies.
+    __shared__ __attribute__((aligned(16))) float kb0[TILE_F];
+    __shared__ __attribute__((aligned(16))) float kb1[TILE_F];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -837,8 +851,7 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
         tbase[rt] = (long long)head * a.ds_tph + ds_tiles_before(a.ds, qc);
     }
 
-    auto issue_k = [&](int kt, int buf) {
-        float* dst = smem + buf * TILE_F;
+    auto issue_k = [&](int kt, float* dst) __attribute__((always_inline)) {
 #pragma unroll
         for (int inst = wave; inst < LOADS; inst += 4) {
             const int s_ = inst * 64 + lane;
@@ -862,14 +875,14 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](int kt, const float4 (&cur)[kDqRT], float4 (&nxt)[kDqRT]) {
+    auto step = [&](int kt, const float4 (&cur)[kDqRT], float4 (&nxt)[kDqRT], const float* Ks,
+                    float* knext) __attribute__((always_inline)) {
         wait_vmem();
         __syncthreads();  // K tile kt landed for every wave; the other buffer is free
         if (kt + 1 < n_kt) {  // block-uniform
-            issue_k(kt + 1, (kt + 1) & 1);
+            issue_k(kt + 1, knext);
             load_ds(kt + 1, nxt);
         }
-        const float* Ks = smem + (kt & 1) * TILE_F;
         float av[kDqRT][4];
 #pragma unroll
         for (int rt = 0; rt < kDqRT; ++rt) {
@@ -900,15 +913,15 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
 
     float4 da[kDqRT], db[kDqRT];
     if (n_kt > 0) {
-        issue_k(0, 0);
+        issue_k(0, kb0);
         load_ds(0, da);
     }
     int kt = 0;
     for (; kt + 1 < n_kt; kt += 2) {
-        step(kt, da, db);
-        step(kt + 1, db, da);
+        step(kt, da, db, kb0, kb1);
+        step(kt + 1, db, da, kb1, kb0);
     }
-    if (kt < n_kt) step(kt, da, db);
+    if (kt < n_kt) step(kt, da, db, kb0, kb1);
     // The last products' results are read below by vector ALU instructions:
     // keep the matrix-core result latency covered whatever path led here.
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
@@ -979,11 +992,11 @@ hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, con
     const long long n_pairs = (long long)a.q_seq * a.num_heads;
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((n_pairs + 15) / 16)), dim3(256), 0,
                        stream, o, dout, delta, n_pairs);
-    const size_t lds16 = 2 * kDkdvSub * (2 * (size_t)k16Rows * D + 64) * sizeof(float);
+    const size_t lds16 = 0;  // static LDS
     const hipError_t e = launch_dkdv16_any<D, true>(lds16, stream, q, k, v, dout, lse, delta, dk,
                                                     dv, ds, a);
     if (e != hipSuccess) return e;
-    const size_t lds_dq = 2 * (size_t)k16Keys * D * sizeof(float);
+    const size_t lds_dq = 0;  // static LDS
     const long long grid = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks;
     if (a.dq_rt == 4) {
         hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 4>), dim3((unsigned)grid), dim3(256), lds_dq,
@@ -1019,7 +1032,7 @@ hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, c
     const char* force = std::getenv("TA03_BWD_KEYS");
     const bool keys16 = force == nullptr || std::strcmp(force, "32") != 0;
     if (keys16) {
-        const size_t lds16 = 2 * kDkdvSub * (2 * (size_t)k16Rows * D + 64) * sizeof(float);
+        const size_t lds16 = 0;  // static LDS
         return launch_dkdv16_any<D, false>(lds16, stream, q, k, v, dout, lse, delta, dk, dv,
                                            nullptr, a);
     }
