@@ -115,8 +115,9 @@ struct Args {
 template <int D>
 constexpr int rope_rmax() { return D == 128 ? 2 : 4; }
 
-template <int D, bool ROPE>
-__global__ void __launch_bounds__(kBlock, 2)
+// Two blocks per CU while their LDS (KS * D * 512 bytes) allows it.
+template <int D, bool ROPE, int KS>
+__global__ void __launch_bounds__(kBlock, KS * D <= 128 ? 2 : 1)
 prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                const float* __restrict__ v, float* __restrict__ out,
                float* __restrict__ lse, Args a) {
@@ -128,7 +129,13 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     constexpr int HC = CPR / 2;               // 16-byte chunks per half row
     constexpr int RP_INST = kBN * HC / 64;    // rotary: chunk-pair instructions per K tile
     constexpr int RMAX = rope_rmax<D>();
-    extern __shared__ __attribute__((aligned(16))) float smem[];
+    // The two tile buffers ([key split][K tile | V tile] each) are separate
+    // LDS objects, each named directly at every copy and read (the tile loop
+    // is unrolled by two): the compiler then knows that the next tile's
+    // copies do not write the buffer being read and does not make the reads
+    // wait for them to land, which with offsets into one array it did.
+    __shared__ __attribute__((aligned(16))) float lb0[KS * 2 * TILE_F];
+    __shared__ __attribute__((aligned(16))) float lb1[KS * 2 * TILE_F];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -167,8 +174,9 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int t_begin = kvs * nt;
     const int t_end = min(t_begin + nt, n_tiles_all);
 
-    // This key split's two LDS buffers: [buf][K tile | V tile].
-    float* my_lds = smem + (size_t)kvs * 2 * 2 * TILE_F;
+    // This key split's K | V tiles in the two buffers.
+    float* my0 = lb0 + (size_t)kvs * 2 * TILE_F;
+    float* my1 = lb1 + (size_t)kvs * 2 * TILE_F;
 
     // Q^T operand: lane (j, hh) holds q[row][8*g + 4*hh + c] for k-step 4*g+c.
     float qr[D / 2];
@@ -236,8 +244,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         koff[u] = r * (unsigned)a.k_stride + 4u * (c ^ (r & 15u));
         voff[u] = r * (unsigned)a.v_stride + 4u * c;
     }
-    auto issue_tile = [&](int t, int buf) {
-        float* kd = my_lds + (size_t)buf * 2 * TILE_F;
+    auto issue_tile = [&](int t, float* kd) __attribute__((always_inline)) {
         float* vd = kd + TILE_F;
         const int kv0 = t * kBN;
         if (!ROPE && a.small_strides && kv0 + kBN <= w_block) {
@@ -295,8 +302,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             }
         }
     };
-    auto store_k_rot = [&](int buf) {
-        float* kd = my_lds + (size_t)buf * 2 * TILE_F;
+    auto store_k_rot = [&](float* kd) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < RMAX; ++u) {
             const int inst = wg + u * gw;
@@ -322,15 +328,17 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     };
 
     if (t_begin < t_end) {
-        issue_tile(t_begin, 0);
+        issue_tile(t_begin, my0);
         if constexpr (ROPE) {
             load_k_rot(t_begin);
             wait_vmem();
-            store_k_rot(0);
+            store_k_rot(my0);
         }
     }
 
-    for (int it = 0; it < nt; ++it) {
+    // One tile: Ks is this split's K | V tiles of tile it, wb the buffer that
+    // tile it + 1 is copied into.
+    auto step = [&](int it, const float* Ks, float* wb) __attribute__((always_inline)) {
         const int t = t_begin + it;
         const bool have = t < t_end;
         wait_vmem();
@@ -341,12 +349,11 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         if (gw > 1) __syncthreads();
         const bool next = have && t + 1 < t_end;
         if (next) {
-            issue_tile(t + 1, (it + 1) & 1);
+            issue_tile(t + 1, wb);
             if constexpr (ROPE) load_k_rot(t + 1);
         }
         const int kv0 = t * kBN;
         if (have && kv0 < w_wave_max) {  // wave-uniform
-            const float* Ks = my_lds + (size_t)(it & 1) * 2 * TILE_F;
             const float* Vs = Ks + TILE_F;
 
             // S^T = K Q^T for this tile (already in log2 units).
@@ -420,9 +427,13 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         if constexpr (ROPE) {
             if (next) {  // next tile's keys: turned and written after this tile's math
                 wait_vmem();
-                store_k_rot((it + 1) & 1);
+                store_k_rot(wb);
             }
         }
+    };
+    for (int it = 0; it < nt; it += 2) {
+        step(it, my0, my1);
+        if (it + 1 < nt) step(it + 1, my1, my0);
     }
 
     if (a.ks > 1) {
@@ -430,7 +441,11 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         // (m, l, O) through LDS in register order, split 0 rescales and adds.
         __syncthreads();  // every wave is done with the tile buffers
         constexpr int PART = 2 + NB * 16;  // floats per lane
-        float* part = smem + (size_t)(wave * PART) * 64;
+        // Splits 1.. of each (head, strip) group take consecutive slots of
+        // the first tile buffer: group rest, split kvs -> rest * (ks - 1) + kvs - 1.
+        static_assert((kWaves / KS) * (KS - 1) * PART * 64 <= (KS > 1 ? KS * 2 * TILE_F : 1 << 30),
+                      "merge slots fit the first tile buffer");
+        float* part = lb0 + (size_t)((rest * (a.ks - 1) + kvs - 1) * PART) * 64;
         if (kvs > 0) {
             part[lane] = m_run;
             part[64 + lane] = l_run;
@@ -442,7 +457,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         __syncthreads();
         if (kvs > 0) return;
         for (int p = 1; p < a.ks; ++p) {
-            const float* pp = smem + (size_t)((wave + p) * PART) * 64;
+            const float* pp = lb0 + (size_t)((rest * (a.ks - 1) + p - 1) * PART) * 64;
             const float mp = pp[lane], lp = pp[64 + lane];
             const float M = fmaxf(m_run, mp);
             const float f0 = __builtin_amdgcn_exp2f(m_run - M);
@@ -483,21 +498,29 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 }
 
-// Largest dynamic LDS an instance is launched with: the most key splits its
-// head_dim allows, 2 buffers x (K, V) each.
-template <int D, bool ROPE>
-hipError_t launch_instance(long long grid, size_t lds, hipStream_t stream, const float* q,
-                           const float* k, const float* v, float* out, float* lse,
-                           const Args& a) {
-    constexpr int max_splits = D == 128 ? 2 : 4;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(prefill_kernel<D, ROPE>),
-        hipFuncAttributeMaxDynamicSharedMemorySize,
-        max_splits * 2 * 2 * kBN * D * (int)sizeof(float));
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((prefill_kernel<D, ROPE>), dim3((unsigned)grid), dim3(kBlock), lds, stream,
-                       q, k, v, out, lse, a);
+// One instance per key-split count (its LDS is static: KS x 2 buffers x
+// (K, V) tiles).
+template <int D, bool ROPE, int KS>
+hipError_t launch_ks(long long grid, hipStream_t stream, const float* q, const float* k,
+                     const float* v, float* out, float* lse, const Args& a) {
+    hipLaunchKernelGGL((prefill_kernel<D, ROPE, KS>), dim3((unsigned)grid), dim3(kBlock), 0,
+                       stream, q, k, v, out, lse, a);
     return hipSuccess;
+}
+
+template <int D, bool ROPE>
+hipError_t launch_instance(long long grid, hipStream_t stream, const float* q, const float* k,
+                           const float* v, float* out, float* lse, const Args& a) {
+    if constexpr (D == 128 && ROPE) {
+        return launch_ks<D, ROPE, 1>(grid, stream, q, k, v, out, lse, a);
+    } else if constexpr (D == 128) {
+        return a.ks == 1 ? launch_ks<D, ROPE, 1>(grid, stream, q, k, v, out, lse, a)
+                         : launch_ks<D, ROPE, 2>(grid, stream, q, k, v, out, lse, a);
+    } else {
+        return a.ks == 1   ? launch_ks<D, ROPE, 1>(grid, stream, q, k, v, out, lse, a)
+               : a.ks == 2 ? launch_ks<D, ROPE, 2>(grid, stream, q, k, v, out, lse, a)
+                           : launch_ks<D, ROPE, 4>(grid, stream, q, k, v, out, lse, a);
+    }
 }
 
 int gcd_int(int x, int y) {
@@ -561,15 +584,13 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
         const bool use16 = force != nullptr ? std::strcmp(force, "16") == 0 : grid < kNumCUs;
         if (use16) return launch_prefill16(q, k, v, out, lse, s, stream);
     }
-    const size_t tile_bytes = (size_t)kBN * s.head_dim * sizeof(float);
-    const size_t lds = (size_t)ks * 2 * 2 * tile_bytes;  // per split: 2 buffers x (K, V)
     hipError_t e;
     if (s.head_dim == 128) {
-        e = rope ? launch_instance<128, true>(grid, lds, stream, q, k, v, out, lse, a)
-                 : launch_instance<128, false>(grid, lds, stream, q, k, v, out, lse, a);
+        e = rope ? launch_instance<128, true>(grid, stream, q, k, v, out, lse, a)
+                 : launch_instance<128, false>(grid, stream, q, k, v, out, lse, a);
     } else {
-        e = rope ? launch_instance<64, true>(grid, lds, stream, q, k, v, out, lse, a)
-                 : launch_instance<64, false>(grid, lds, stream, q, k, v, out, lse, a);
+        e = rope ? launch_instance<64, true>(grid, stream, q, k, v, out, lse, a)
+                 : launch_instance<64, false>(grid, stream, q, k, v, out, lse, a);
     }
     if (e != hipSuccess) return e;
     return hipGetLastError();
