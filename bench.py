@@ -510,7 +510,7 @@ def main():
                          "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(p["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
                          "traffic": stored_traffic(PREFILL_TRAFFIC),
-                         "kernel": "prefill_kernel<128, false>",
+                         "kernel": "prefill_kernel<128, false, 1>",
                          "kernel_ms_mean": round(p["mean_s"] * 1e3, 3),
                          "kernel_ms_min": round(p["min_s"] * 1e3, 3)},
         })
@@ -531,14 +531,14 @@ def main():
                 "layout": "q, k, v column slices of one [16384, 6144] buffer; out row stride 4160",
                 "ms": round(r["mean_s"] * 1e3, 3), "TFLOP/s": round(r["tflops_kernel"], 3),
                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                "kernel": "prefill_kernel<128, false>"}
+                "kernel": "prefill_kernel<128, false, 1>"}
             print(f"[bench] strided {result['prefill_strided']}", flush=True)
             r = bench_prefill(w, 3, 1, torch, ta, rope_theta=10000.0)
             result["prefill_rope"] = {
                 "workload": w.name + "_rope_theta10000",
                 "ms": round(r["mean_s"] * 1e3, 3), "TFLOP/s": round(r["tflops_kernel"], 3),
                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                "kernel": "prefill_kernel<128, true>"}
+                "kernel": "prefill_kernel<128, true, 1>"}
             print(f"[bench] rotary {result['prefill_rope']}", flush=True)
             r = bench_backward(w, 3, 1, torch, ta)
             rr = bench_backward(w, 3, 1, torch, ta, stored=False)
