@@ -440,35 +440,46 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         // Merge the key splits of the same (head, rows): splits 1.. publish
         // (m, l, O) through LDS in register order, split 0 rescales and adds.
         __syncthreads();  // every wave is done with the tile buffers
-        constexpr int PART = 2 + NB * 16;  // floats per lane
+        // Per lane, contiguous: (m, l, -, -), then O block b registers 0..15
+        // (4 + 16 NB floats: a lane stride of an odd number of 16-byte
+        // chunks, so the 128-bit accesses are bank-conflict free).
+        constexpr int PART = 4 + NB * 16;
         // Splits 1.. of each (head, strip) group take consecutive slots of
         // the first tile buffer: group rest, split kvs -> rest * (ks - 1) + kvs - 1.
         static_assert((kWaves / KS) * (KS - 1) * PART * 64 <= (KS > 1 ? KS * 2 * TILE_F : 1 << 30),
                       "merge slots fit the first tile buffer");
-        float* part = lb0 + (size_t)((rest * (a.ks - 1) + kvs - 1) * PART) * 64;
+        float4* part = reinterpret_cast<float4*>(lb0) +
+                       ((size_t)(rest * (a.ks - 1) + kvs - 1) * 64 + lane) * (PART / 4);
         if (kvs > 0) {
-            part[lane] = m_run;
-            part[64 + lane] = l_run;
+            part[0] = make_float4(m_run, l_run, 0.f, 0.f);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) part[(2 + b * 16 + r) * 64 + lane] = o[b][r];
+                for (int r = 0; r < 4; ++r)
+                    part[1 + 4 * b + r] = make_float4(o[b][4 * r], o[b][4 * r + 1], o[b][4 * r + 2],
+                                                      o[b][4 * r + 3]);
         }
         __syncthreads();
         if (kvs > 0) return;
         for (int p = 1; p < a.ks; ++p) {
-            const float* pp = lb0 + (size_t)((rest * (a.ks - 1) + p - 1) * PART) * 64;
-            const float mp = pp[lane], lp = pp[64 + lane];
-            const float M = fmaxf(m_run, mp);
+            const float4* pp = reinterpret_cast<const float4*>(lb0) +
+                               ((size_t)(rest * (a.ks - 1) + p - 1) * 64 + lane) * (PART / 4);
+            const float4 ml = pp[0];
+            const float M = fmaxf(m_run, ml.x);
             const float f0 = __builtin_amdgcn_exp2f(m_run - M);
-            const float f1 = __builtin_amdgcn_exp2f(mp - M);
-            l_run = l_run * f0 + lp * f1;
+            const float f1 = __builtin_amdgcn_exp2f(ml.x - M);
+            l_run = l_run * f0 + ml.y * f1;
             m_run = M;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    o[b][r] = o[b][r] * f0 + pp[(2 + b * 16 + r) * 64 + lane] * f1;
+                for (int r = 0; r < 4; ++r) {
+                    const float4 x = pp[1 + 4 * b + r];
+                    o[b][4 * r + 0] = o[b][4 * r + 0] * f0 + x.x * f1;
+                    o[b][4 * r + 1] = o[b][4 * r + 1] * f0 + x.y * f1;
+                    o[b][4 * r + 2] = o[b][4 * r + 2] * f0 + x.z * f1;
+                    o[b][4 * r + 3] = o[b][4 * r + 3] * f0 + x.w * f1;
+                }
         }
     }
 
