@@ -231,31 +231,34 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     if (a.ks > 1) {
         // Key splits 1.. publish (m, l, O) through LDS in register order,
         // split 0 rescales and adds.
-        constexpr int PART = 2 + 4 * NB;  // floats per lane
-        float* part = smem + (size_t)(wave * PART) * 64;
+        // Per lane, contiguous: (m, l, -, -), then O block b (4 + 4 NB floats,
+        // an odd number of 16-byte chunks: conflict-free 128-bit accesses).
+        constexpr int PART = 4 + 4 * NB;
+        float4* part = reinterpret_cast<float4*>(smem) + ((size_t)wave * 64 + lane) * (PART / 4);
         if (kvs > 0) {
-            part[lane] = m_run;
-            part[64 + lane] = l_run;
+            part[0] = make_float4(m_run, l_run, 0.f, 0.f);
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) part[(2 + 4 * b + r) * 64 + lane] = o[b][r];
+            for (int b = 0; b < NB; ++b) part[1 + b] = make_float4(o[b][0], o[b][1], o[b][2], o[b][3]);
         }
         __syncthreads();
         if (kvs > 0) return;
         for (int p = 1; p < a.ks; ++p) {
-            const float* pp = smem + (size_t)((wave + p) * PART) * 64;
-            const float mp = pp[lane], lp = pp[64 + lane];
-            const float M = fmaxf(m_run, mp);
+            const float4* pp =
+                reinterpret_cast<const float4*>(smem) + ((size_t)(wave + p) * 64 + lane) * (PART / 4);
+            const float4 ml = pp[0];
+            const float M = fmaxf(m_run, ml.x);
             const float f0 = __builtin_amdgcn_exp2f(m_run - M);
-            const float f1 = __builtin_amdgcn_exp2f(mp - M);
-            l_run = l_run * f0 + lp * f1;
+            const float f1 = __builtin_amdgcn_exp2f(ml.x - M);
+            l_run = l_run * f0 + ml.y * f1;
             m_run = M;
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o[b][r] = o[b][r] * f0 + pp[(2 + 4 * b + r) * 64 + lane] * f1;
+            for (int b = 0; b < NB; ++b) {
+                const float4 x = pp[1 + b];
+                o[b][0] = o[b][0] * f0 + x.x * f1;
+                o[b][1] = o[b][1] * f0 + x.y * f1;
+                o[b][2] = o[b][2] * f0 + x.z * f1;
+                o[b][3] = o[b][3] * f0 + x.w * f1;
+            }
         }
     }
 
@@ -298,7 +301,7 @@ hipError_t launch16(long long grid, size_t lds, hipStream_t stream, const float*
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(prefill16_kernel<D>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
-        kWaves * (2 + D / 4) * 64 * (int)sizeof(float));
+        kWaves * (4 + D / 4) * 64 * (int)sizeof(float));
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((prefill16_kernel<D>), dim3((unsigned)grid), dim3(kBlock), lds, stream, q,
                        k, v, out, lse, a);
@@ -337,7 +340,7 @@ hipError_t launch_prefill16(const float* q, const float* k, const float* v, floa
     a.n_row_blocks = (s.q_seq + a.rs * kRows - 1) / (a.rs * kRows);
     const long long grid = (long long)a.n_head_blocks * a.n_row_blocks;
     if (grid <= 0) return hipSuccess;
-    const size_t lds = ks > 1 ? (size_t)kWaves * (2 + s.head_dim / 4) * 64 * sizeof(float) : 0;
+    const size_t lds = ks > 1 ? (size_t)kWaves * (4 + s.head_dim / 4) * 64 * sizeof(float) : 0;
     hipError_t e = s.head_dim == 128
         ? launch16<128>(grid, lds, stream, q, k, v, out, lse, a)
         : launch16<64>(grid, lds, stream, q, k, v, out, lse, a);
