@@ -436,7 +436,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         if (it + 1 < nt) step(it + 1, my1, my0);
     }
 
-    if (a.ks > 1) {
+    if constexpr (KS > 1) {
         // Merge the key splits of the same (head, rows): splits 1.. publish
         // (m, l, O) through LDS in register order, split 0 rescales and adds.
         __syncthreads();  // every wave is done with the tile buffers
