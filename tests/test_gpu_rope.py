@@ -109,6 +109,9 @@ RAGGED = [
     (CROSS, 40, 301, 8, 8, 128, 0),
     (FULL, 130, 130, 4, 1, 128, 0),
     (CROSS, 1, 5, 2, 1, 64, 0),
+    # 16-31 key tiles over few row strips: the launch runs two key splits per block
+    (CROSS, 40, 600, 8, 8, 64, 0),
+    (CAUSAL, 50, 700, 4, 2, 64, 600),
 ]
 
 
