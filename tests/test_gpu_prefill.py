@@ -91,6 +91,9 @@ SWEEP = [
     (CROSS, 33, 31, 2, 2, 128, 0),
     (CROSS, 64, 257, 4, 4, 128, 0),
     (CROSS, 100, 45, 12, 4, 64, 0),
+    # >= 32 key tiles over few row strips: four key splits per block (32-row kernel)
+    (CAUSAL, 40, 1100, 4, 2, 64, 1060),
+    (CROSS, 70, 1500, 8, 8, 64, 0),
 ]
 
 
