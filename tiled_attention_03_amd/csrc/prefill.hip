@@ -244,6 +244,20 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         koff[u] = r * (unsigned)a.k_stride + 4u * (c ^ (r & 15u));
         voff[u] = r * (unsigned)a.v_stride + 4u * c;
     }
+    // Load u of this wave's share of tile t (fast path: the tile lies inside
+    // the block's window), issued between the score products of the
+    // current tile so the copies do not hold up the wave's issue.
+    auto issue_u = [&](int t, float* kd, int u) __attribute__((always_inline)) {
+        const int inst = wg + u * gw;
+        if (inst < LOADS) {
+            const float* kt = kbase + (size_t)(t * kBN) * a.k_stride;
+            const float* vt = vbase + (size_t)(t * kBN) * a.v_stride;
+            const float* kg = kt + koff[u];
+            const float* vg = vt + voff[u];
+            __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kd + inst * 256), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vg, (lds_void*)(kd + TILE_F + inst * 256), 16, 0, 0);
+        }
+    };
     auto issue_tile = [&](int t, float* kd) __attribute__((always_inline)) {
         float* vd = kd + TILE_F;
         const int kv0 = t * kBN;
@@ -348,12 +362,16 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         // 1024x1024, four splits: 30.5 -> 29.3 us).
         if (gw > 1) __syncthreads();
         const bool next = have && t + 1 < t_end;
-        if (next) {
+        const int kv0 = t * kBN;
+        const bool work = have && kv0 < w_wave_max;
+        // the next tile's copies go between this tile's score products when
+        // it lies inside the block's window (else, and without work, here)
+        const bool spread = !ROPE && next && work && a.small_strides && (t + 2) * kBN <= w_block;
+        if (next && !spread) {
             issue_tile(t + 1, wb);
             if constexpr (ROPE) load_k_rot(t + 1);
         }
-        const int kv0 = t * kBN;
-        if (have && kv0 < w_wave_max) {  // wave-uniform
+        if (work) {  // wave-uniform
             const float* Vs = Ks + TILE_F;
 
             // S^T = K Q^T for this tile (already in log2 units).
@@ -367,6 +385,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * c);
                 s = mfma32(kk.x, qr[4 * g + 0], s);
                 s = mfma32(kk.y, qr[4 * g + 1], s);
+                if (g < MAXI && spread) issue_u(t + 1, wb, g);
                 s = mfma32(kk.z, qr[4 * g + 2], s);
                 s = mfma32(kk.w, qr[4 * g + 3], s);
             }
