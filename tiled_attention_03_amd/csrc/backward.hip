@@ -631,6 +631,34 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
             __builtin_amdgcn_global_load_lds(src, (lds_void*)(vb + sub * 64), 4, 0, 0);
         }
     };
+    // One piece of stage st's copies (for spreading them between products):
+    // pieces 0..3 = Q / dout rows of sub-tile p >> 1, instruction p & 1;
+    // pieces 4, 5 = the (m, log l) / D vectors of sub-tile p - 4.
+    auto issue_piece = [&](int st, float* tb, float* vb, int pc) __attribute__((always_inline)) {
+        const int sub = pc < 4 ? pc >> 1 : pc - 4;
+        const int it = st * SUB + sub;
+        if (it >= total) return;
+        const int h = kv_head * a.group + it / n_qt;
+        const int row0 = (qt0 + it % n_qt) * k16Rows;
+        if (pc < 4) {
+            const int inst = wave + W * (pc & 1);
+            if (inst < LOADS) {
+                float* qdst = tb + (size_t)sub * 2 * TILE_F;
+                const int s_ = inst * 64 + lane;
+                const int r = s_ / CPR, p = s_ % CPR;
+                const int row = min(row0 + r, a.q_seq - 1);
+                const size_t src = (size_t)row * qd + h * D + 4 * (p ^ swz(r));
+                __builtin_amdgcn_global_load_lds(q + src, (lds_void*)(qdst + inst * 256), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(dout + src, (lds_void*)(qdst + TILE_F + inst * 256),
+                                                 16, 0, 0);
+            }
+        } else if (wave == W - 1) {
+            const float* src = lane < 32
+                ? lse + ((size_t)min(row0 + (lane >> 1), a.q_seq - 1) * a.num_heads + h) * 2 + (lane & 1)
+                : delta + (size_t)min(row0 + (lane & 15), a.q_seq - 1) * a.num_heads + h;
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(vb + sub * 64), 4, 0, 0);
+        }
+    };
     auto issue = [&](int st, float* tb, float* vb) __attribute__((always_inline)) {
 #pragma unroll
         for (int sub = 0; sub < SUB; ++sub)
@@ -642,7 +670,12 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         __attribute__((always_inline)) {
         wait_vmem();
         __syncthreads();  // stage st landed for every wave; the other buffer is free
-        if (st + 1 < n_st) issue(st + 1, wt, wv);
+        // The next stage's copies go between the first sub-tile's score
+        // products when this wave computes it, else here.
+        const int rows_hi0 = min((qt0 + (st * SUB) % n_qt) * k16Rows + k16Rows, a.q_seq);
+        const int w_max0 = a.causal ? min(a.start_pos + rows_hi0, a.kv_len) : a.kv_len;
+        const bool spread = st + 1 < n_st && strip_live && key0 < w_max0;
+        if (st + 1 < n_st && !spread) issue(st + 1, wt, wv);
 #pragma unroll
         for (int sub = 0; sub < SUB; ++sub) {
             const int it = st * SUB + sub;
@@ -667,6 +700,12 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                     for (int e = 0; e < 4; ++e) {
                         s = mfma16(comp4(qq, e), kr[4 * c + e], s);
                         dp = mfma16(comp4(gg, e), vr[4 * c + e], dp);
+                        // six pieces over the k-step groups (two per group at head_dim 64)
+                        constexpr int PPG = KS / 4 >= 6 ? 1 : 2;
+                        if (sub == 0 && spread && (e == 1 || (PPG == 2 && e == 3))) {
+                            const int pc = c * PPG + (e == 3 ? 1 : 0);
+                            if (pc < 6) issue_piece(st + 1, wt, wv, pc);
+                        }
                     }
                 }
                 // P in s, dS in dp. The window test is a select (no branch between
