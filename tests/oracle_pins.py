@@ -623,4 +623,73 @@ def pin_backward_magnitudes_bound_results(orc):
         assert np.all(m >= np.abs(b) - 1e-12), f"{nm} magnitudes below |gradient|"
 
 
+def _brute_magnitudes(q, k, v, g, H, Hkv, d, mode, kv_len, start_pos, scale):
+    """Scalar loops with math.fsum: the magnitude sums of the gradients'
+    terms, one number at a time. For each head h (KV head c), row i and key
+    j < w_i: P_ij, dP_ij = <dout_i, v_j>, D_i = sum_j P_ij dP_ij,
+    dS_ij = P_ij (dP_ij - D_i), E_ij = |dS_ij| + P_ij (|dP_ij| + |D_i|);
+    dq_m[i, h, e] = scale sum_j E_ij |K[j, c, e]|,
+    dk_m[j, c, e] = scale sum_{h in c, i} E_ij |Q[i, h, e]|,
+    dv_m[j, c, e] = sum_{h in c, i} P_ij |dout[i, h, e]|."""
+    n = q.shape[0]
+    group = H // Hkv
+    qf, kf, vf, gf = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g))
+    dq_m = np.zeros((n, H * d))
+    dk_terms = [[[] for _ in range(Hkv * d)] for _ in range(kv_len)]
+    dv_terms = [[[] for _ in range(Hkv * d)] for _ in range(kv_len)]
+    for h in range(H):
+        c = h // group
+        for i in range(n):
+            w = _window(mode, i, n, kv_len, start_pos)
+            if w == 0:
+                continue
+            s = [scale * math.fsum(qf[i, h * d + e] * kf[j, c * d + e] for e in range(d))
+                 for j in range(w)]
+            m = max(s)
+            z = math.fsum(math.exp(x - m) for x in s)
+            p = [math.exp(x - m) / z for x in s]
+            dp = [math.fsum(gf[i, h * d + e] * vf[j, c * d + e] for e in range(d))
+                  for j in range(w)]
+            dd = math.fsum(p[j] * dp[j] for j in range(w))
+            em = [abs(p[j] * (dp[j] - dd)) + p[j] * (abs(dp[j]) + abs(dd)) for j in range(w)]
+            for e in range(d):
+                dq_m[i, h * d + e] = scale * math.fsum(em[j] * abs(kf[j, c * d + e])
+                                                       for j in range(w))
+            for j in range(w):
+                for e in range(d):
+                    dk_terms[j][c * d + e].append(em[j] * abs(qf[i, h * d + e]))
+                    dv_terms[j][c * d + e].append(p[j] * abs(gf[i, h * d + e]))
+    dk_m = np.array([[scale * math.fsum(t) for t in row] for row in dk_terms]).reshape(
+        kv_len, Hkv * d)
+    dv_m = np.array([[math.fsum(t) for t in row] for row in dv_terms]).reshape(kv_len, Hkv * d)
+    return dq_m, dk_m, dv_m
+
+
+def pin_backward_magnitudes_scalar_loops(orc):
+    """The magnitude sums that widen the gradient tolerance, exactly (to
+    float64 rounding) against scalar loops over their terms: an inflated or
+    dropped term moves them either way and fails here."""
+    for mode, n, kv_len, sp, H, Hkv in ((CAUSAL, 5, 7, 2, 4, 2), (CROSS, 4, 6, 0, 2, 1),
+                                        (FULL, 4, 4, 0, 3, 3)):
+        d = 3
+        q, k, v, g = (_rand((n, H * d), 470 + mode), _rand((kv_len, Hkv * d), 471 + mode),
+                      _rand((kv_len, Hkv * d), 472 + mode), _rand((n, H * d), 473 + mode))
+        got = _bwd(orc, q, k, v, g, H, Hkv, d, mode, kv_len, sp, magnitudes=True)[3:]
+        want = _brute_magnitudes(q, k, v, g, H, Hkv, d, mode, kv_len, sp, 0.4)
+        for a, b, nm in zip(got, want, ("dq_m", "dk_m", "dv_m")):
+            assert np.all(b >= 0.0)
+            _close(a, b, 1e-12 * max(1.0, float(np.abs(b).max())), f"{nm} mode={mode}")
+
+
+def pin_backward_dv_magnitude_is_dv_of_abs_dout(orc):
+    """dv = P^T dout is linear in dout with P >= 0, so its magnitude sum
+    P^T |dout| is the checker's own dv for the input |dout|."""
+    H, Hkv, d, n = 4, 2, 4, 9
+    q, k, v, g = (_rand((n, H * d), 480), _rand((n, Hkv * d), 481), _rand((n, Hkv * d), 482),
+                  _rand((n, H * d), 483))
+    full = _bwd(orc, q, k, v, g, H, Hkv, d, CAUSAL, n, 0, magnitudes=True)
+    dv_abs = _bwd(orc, q, k, v, np.abs(g), H, Hkv, d, CAUSAL, n, 0)[2]
+    _close(full[5], dv_abs, 1e-12, "dv_m vs dv(|dout|)")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -47,6 +47,13 @@ MUTANTS = {
     "bwd_dq_from_v": ("scale * (ds[sel] @ kc)", "scale * (ds[sel] @ vc)"),
     "bwd_dk_overwritten": ("dk[:, c * d:(c + 1) * d] += scale", "dk[:, c * d:(c + 1) * d] = scale"),
     "bwd_dv_not_summed_over_group": ("dv[:, c * d:(c + 1) * d] += p", "dv[:, c * d:(c + 1) * d] = p"),
+    "bwd_magnitude_term_inflated": ("em = np.abs(ds) + p * (np.abs(dp) + np.abs(dd)[:, None])",
+                                    "em = np.abs(ds) + 2.0 * p * (np.abs(dp) + np.abs(dd)[:, None])"),
+    "bwd_magnitude_delta_dropped": ("em = np.abs(ds) + p * (np.abs(dp) + np.abs(dd)[:, None])",
+                                    "em = np.abs(ds) + p * np.abs(dp)"),
+    "bwd_magnitude_dv_inflated": ("dv_m[:, c * d:(c + 1) * d] += p[:, keys].T @ np.abs(gb)",
+                                  "dv_m[:, c * d:(c + 1) * d] += 3.0 * p[:, keys].T @ np.abs(gb)"),
+    "bwd_magnitude_dq_unscaled": ("scale * (em[sel] @ np.abs(kc))", "(em[sel] @ np.abs(kc))"),
     "rope_keys_unrotated": ("        k = apply_rope(k[:kv_len]", "        k = 1.0 * (k[:kv_len]"),
 }
 
