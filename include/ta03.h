@@ -201,7 +201,7 @@ int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStr
  * The stored path is taken when the workspace holds the tiles and the call
  * is long enough for it to pay: the dq grid over the tiles has at least 256
  * blocks of 4 waves (one per compute unit); shorter calls recompute.
- * Environment override (testing): TA03_BWD_PATH=stored or recompute. Both
+ * attn_set_kernel_override can force either path (testing). Both
  * paths run on stream with no allocation and no atomics (results are
  * run-to-run identical; the two paths agree to rounding). Errors: as attn_fwd for the sizes and mode;
  * TA03_ERR_NULL for a NULL q, out, dout, lse, dq or workspace (q_seq > 0) or
@@ -301,6 +301,24 @@ int attn_decode_paged(const float* q, const float* k_pool, const float* v_pool, 
                       float* out, float* lse, int num_heads, int num_kv_heads, int head_dim,
                       int max_seq, float scale, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * attn_set_kernel_override -- testing hook: force one kernel choice for every
+ * later call in this process (all threads), so that a shape can be run
+ * through each kernel that can serve it. value 0 restores the automatic
+ * choice, which every other caller should keep. Results of any choice match
+ * the definition to the stated tolerances; only speed differs.
+ *
+ *   TA03_OVERRIDE_PREFILL_ROWS  16 or 32: the 16-row or the 32-row prefill
+ *                               kernel for calls without rotation
+ *   TA03_OVERRIDE_BWD_PATH      1: attn_bwd takes the stored-dS path whenever
+ *                               its workspace holds every tile; 2: the
+ *                               recompute path
+ *
+ * Errors: TA03_ERR_SHAPE for an unknown knob or value. No HIP call is made.
+ */
+enum { TA03_OVERRIDE_PREFILL_ROWS = 1, TA03_OVERRIDE_BWD_PATH = 2 };
+int attn_set_kernel_override(int knob, int value);
 
 /* attn_strerror -- static description of a ta03_status value. */
 const char* attn_strerror(int status);

@@ -79,8 +79,14 @@ def check_grad(got, ref, mag, n_terms, what=""):
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
     assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
     err = np.abs(got - ref)
-    bound = (OUT_ATOL + OUT_RTOL * np.abs(ref)
-             + 4.0 * np.sqrt(max(n_terms, 1)) * 2.0 ** -24 * np.asarray(mag, dtype=np.float64))
+    fwd_bound = OUT_ATOL + OUT_RTOL * np.abs(ref)
+    bound = fwd_bound + 4.0 * np.sqrt(max(n_terms, 1)) * 2.0 ** -24 * np.asarray(
+        mag, dtype=np.float64)
+    if err.size:
+        # How much of the bound the errors use, and how they compare with the
+        # forward's bound alone (above 1: the summation term is needed).
+        log(f"  {what}: max err/bound {float((err / bound).max()):.3f}, "
+            f"max err/forward bound {float((err / fwd_bound).max()):.3f}")
     bad = err > bound
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} gradient elements off; "
                            f"worst {float((err - bound).max()):.3e} over bound, "

@@ -42,7 +42,8 @@ def test_header_declares_the_entry_points():
                                     "attn_bwd_workspace_bytes_stored", "attn_decode", "attn_decode_paged",
                                     "attn_decode_workspace_bytes",
                                     "attn_decode_workspace_init", "attn_fwd", "attn_fwd_ex",
-                                    "attn_fwd_rope", "attn_rope_table", "attn_strerror"]
+                                    "attn_fwd_rope", "attn_rope_table",
+                                    "attn_set_kernel_override", "attn_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -302,9 +303,9 @@ def test_workspace_bytes(lib):
     f = lib.attn_decode_workspace_bytes
     n = f(32, 8, 128, 8192)
     assert n > 0 and n % 16 == 0
-    # one split for a one-row cache: per head a head_dim row plus (max, sum),
-    # rounded up to 256 bytes, then one counter per KV head in a 256-byte slot
-    assert f(32, 8, 128, 1) == (32 * 130 * 4 + 255) // 256 * 256 + 8 * 256
+    # one split for a one-row cache: one counter per KV head in a 256-byte
+    # slot, then per head a head_dim row plus (max, sum), rounded up to 256 bytes
+    assert f(32, 8, 128, 1) == 8 * 256 + (32 * 130 * 4 + 255) // 256 * 256
     assert f(32, 7, 128, 8192) == 0
     assert f(32, 8, 96, 8192) == 0
     assert f(32, 8, 128, 0) == 0
@@ -336,3 +337,18 @@ def test_binding_checks_buffer_sizes():
     q = torch.zeros(4, 256)
     with pytest.raises(ValueError):
         binding.attn_fwd(q, q, q, q, None, 4, 4, 4, 2, 64, 0, 0, 0.125, stream=0)
+
+
+def test_kernel_override_validates_and_resets(lib):
+    """The testing hook accepts its documented knobs and values only (no HIP
+    call is made), and 0 restores the automatic choice."""
+    assert lib.attn_set_kernel_override(1, 16) == OK
+    assert lib.attn_set_kernel_override(1, 32) == OK
+    assert lib.attn_set_kernel_override(1, 0) == OK
+    assert lib.attn_set_kernel_override(1, 17) == ERR_SHAPE
+    assert lib.attn_set_kernel_override(2, 1) == OK
+    assert lib.attn_set_kernel_override(2, 2) == OK
+    assert lib.attn_set_kernel_override(2, 0) == OK
+    assert lib.attn_set_kernel_override(2, 3) == ERR_SHAPE
+    assert lib.attn_set_kernel_override(3, 0) == ERR_SHAPE
+    assert lib.attn_set_kernel_override(0, 0) == ERR_SHAPE

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+import tiled_attention_03_amd as ta
 from tests.gpu_util import check_grad, check_out, device, log, to_dev
 from tiled_attention_03_amd import inputs
 
@@ -23,7 +24,6 @@ def gpu_fwd_bwd(q, k, v, g, *, num_heads, num_kv_heads, head_dim, mode, kv_len, 
     shows. stored: workspace for the stored-dS path, else the minimal one;
     ws_short: bytes taken off the stored size."""
     import torch
-    import tiled_attention_03_amd as ta
     dev = device()
     H, Hkv, d = num_heads, num_kv_heads, head_dim
     n = q.shape[0]
@@ -51,18 +51,15 @@ def _kw(w):
 
 
 # Backward paths: "stored" (workspace for the dS tiles, the stored path
-# forced by the library's TA03_BWD_PATH even where its size rule would
-# recompute; dq from the tiles), "recompute" (minimal workspace; dq
-# recomputes the scores, 16-key dk/dv kernel) and "keys32" (minimal
-# workspace, the 32-key dk/dv kernel forced by TA03_BWD_KEYS).
-PATHS = ["stored", "recompute", "keys32"]
+# forced by the library's kernel-choice override even where its size rule
+# would recompute; dq from the tiles) and "recompute" (minimal workspace; dq
+# recomputes the scores, 16-key dk/dv kernel).
+PATHS = ["stored", "recompute"]
 
 
-def _use_path(path, monkeypatch):
-    if path == "keys32":
-        monkeypatch.setenv("TA03_BWD_KEYS", "32")
+def _use_path(path, kernel_override):
     if path == "stored":
-        monkeypatch.setenv("TA03_BWD_PATH", "stored")
+        kernel_override(ta.OVERRIDE_BWD_PATH, 1)
     return path == "stored"
 
 
@@ -76,9 +73,9 @@ def _check_all(got, ref, w, what):
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("w", [inputs.CAUSAL_SMALL, inputs.FULL_1K, inputs.CROSS_512x2K,
                                inputs.CONTINUE_512], ids=lambda w: w.name)
-def test_backward_pages_workloads(w, path, monkeypatch):
+def test_backward_pages_workloads(w, path, kernel_override):
     """The pages' prefill workloads through each backward path."""
-    stored = _use_path(path, monkeypatch)
+    stored = _use_path(path, kernel_override)
     log(f"backward parity {w.name} path={path}")
     q, k, v = inputs.make_prefill(w)
     g = inputs.normal(q.shape, w.seed_base + 7)
@@ -88,35 +85,44 @@ def test_backward_pages_workloads(w, path, monkeypatch):
     log("  max|d| dq={:.2e} dk={:.2e} dv={:.2e}".format(*e))
 
 
+_LONG_REF = {}
+
+
+def _long_causal_reference(w, q, k, v, g):
+    """The checker's gradients of the 16K workload on sampled rows and keys,
+    every KV head (computed once, shared by the paths)."""
+    if "ref" not in _LONG_REF:
+        rng = np.random.default_rng(7099)
+        rows = np.unique(np.concatenate([[0, 1, 15, 16, 31, 32, 8191, 16383],
+                                         rng.choice(w.q_seq, 10, replace=False)]))
+        heavy = inputs.heavy_rows(w.kv_len, w.heavy_frac, w.seed_base + 4)
+        keys = np.unique(np.concatenate([[0, 1, 15, 16, 127, 128, 8192, 16352, 16383],
+                                         heavy[:3], rng.choice(w.kv_len, 8, replace=False)]))
+        log(f"  checker gradients: {len(rows)} rows, {len(keys)} keys, all KV heads")
+        _LONG_REF["ref"] = (rows, keys, oracle.attention_backward(
+            q, k, v, g, rows=rows, keys=keys, magnitudes=True, **_kw(w)))
+    return _LONG_REF["ref"]
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("path", PATHS)
-def test_backward_long_causal_sampled(path, monkeypatch):
+def test_backward_long_causal_sampled(path, kernel_override):
     """The 16384-row causal pass with heavy K rows: dq on sampled rows and
-    dk, dv on sampled keys of KV head 0 (the checker computes the query heads
-    of that KV head in full, the rest is left out). The stored path is the
+    dk, dv on sampled keys, every head and KV head. The stored path is the
     launch the benchmark times (17.2 GB of dS tiles)."""
-    stored = _use_path(path, monkeypatch)
+    stored = _use_path(path, kernel_override)
     w = inputs.CAUSAL_16K
     log(f"backward parity (sampled) {w.name} path={path}")
     q, k, v = inputs.make_prefill(w)
     g = inputs.normal(q.shape, w.seed_base + 7)
     dq, dk, dv = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
-    rng = np.random.default_rng(7099)
-    rows = np.unique(np.concatenate([[0, 1, 31, 32, 8191, 16383],
-                                     rng.choice(w.q_seq, 10, replace=False)]))
-    heavy = inputs.heavy_rows(w.kv_len, w.heavy_frac, w.seed_base + 4)
-    keys = np.unique(np.concatenate([[0, 1, 127, 128, 8192, 16352, 16383], heavy[:3],
-                                     rng.choice(w.kv_len, 8, replace=False)]))
-    rq, rk, rv, mq, mk, mv = oracle.attention_backward(q, k, v, g, rows=rows, keys=keys,
-                                                       kv_heads=[0], magnitudes=True, **_kw(w))
-    group, d = w.group, w.head_dim
-    cq = slice(0, group * d)      # query heads of KV head 0
-    ck = slice(0, d)
-    n_rows = w.q_seq * group
-    e_q = check_grad(dq[rows][:, cq], rq[:, cq], mq[:, cq], w.kv_len, "dq sampled")
-    e_k = check_grad(dk[keys][:, ck], rk[:, ck], mk[:, ck], n_rows, "dk sampled")
-    e_v = check_grad(dv[keys][:, ck], rv[:, ck], mv[:, ck], n_rows, "dv sampled")
-    log(f"  rows={len(rows)} keys={len(keys)} max|d| dq={e_q:.2e} dk={e_k:.2e} dv={e_v:.2e}")
     assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+    rows, keys, (rq, rk, rv, mq, mk, mv) = _long_causal_reference(w, q, k, v, g)
+    n_rows = w.q_seq * w.group
+    e_q = check_grad(dq[rows], rq, mq, w.kv_len, "dq sampled")
+    e_k = check_grad(dk[keys], rk, mk, n_rows, "dk sampled")
+    e_v = check_grad(dv[keys], rv, mv, n_rows, "dv sampled")
+    log(f"  rows={len(rows)} keys={len(keys)} max|d| dq={e_q:.2e} dk={e_k:.2e} dv={e_v:.2e}")
 
 
 BWD_SWEEP = [
@@ -140,10 +146,10 @@ BWD_SWEEP = [
 
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("case", BWD_SWEEP, ids=lambda c: "m{}_q{}_kv{}_h{}x{}_d{}_sp{}".format(*c))
-def test_backward_ragged_sweep(case, path, monkeypatch):
+def test_backward_ragged_sweep(case, path, kernel_override):
     """Ragged shapes: partial query and key tiles, GQA groups of 1 to 8,
     continuation windows, single-key windows; through each backward path."""
-    stored = _use_path(path, monkeypatch)
+    stored = _use_path(path, kernel_override)
     mode, n, kv, H, Hkv, d, sp = case
     w, q, k, v = inputs.random_case(1100 + n * 7 + kv, mode, n, kv, H, Hkv, d, start_pos=sp,
                                     kv_rows=kv + 5)
@@ -155,11 +161,11 @@ def test_backward_ragged_sweep(case, path, monkeypatch):
     _check_all(got, ref, w, str(case))
 
 
-def test_backward_workspace_short_of_stored_falls_back(monkeypatch):
+def test_backward_workspace_short_of_stored_falls_back(kernel_override):
     """A workspace one tile short of the stored size takes the recompute
     path even when the stored path is asked for: same gradients as the
     minimal workspace, bit for bit."""
-    monkeypatch.setenv("TA03_BWD_PATH", "stored")
+    kernel_override(ta.OVERRIDE_BWD_PATH, 1)
     w, q, k, v = inputs.random_case(1120, CAUSAL, 90, 120, 4, 2, 64, start_pos=30)
     g = inputs.normal(q.shape, 1121)
     a = gpu_fwd_bwd(q, k, v, g, stored=True, ws_short=1024, **_kw(w))
@@ -182,7 +188,6 @@ def test_backward_single_key_windows():
 
 def test_backward_empty_query_batch_zeroes_key_gradients():
     import torch
-    import tiled_attention_03_amd as ta
     H, Hkv, d, kv = 4, 2, 64, 50
     dev = device()
     k = to_dev(inputs.normal((kv, Hkv * d), 1160))
@@ -209,9 +214,9 @@ def test_backward_zero_keys():
 
 
 @pytest.mark.parametrize("stored", [True, False])
-def test_backward_deterministic(stored, monkeypatch):
+def test_backward_deterministic(stored, kernel_override):
     if stored:
-        monkeypatch.setenv("TA03_BWD_PATH", "stored")
+        kernel_override(ta.OVERRIDE_BWD_PATH, 1)
     w, q, k, v = inputs.random_case(1180, CAUSAL, 300, 300, 8, 2, 128)
     g = inputs.normal(q.shape, 1181)
     a = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
@@ -221,13 +226,12 @@ def test_backward_deterministic(stored, monkeypatch):
 
 
 @pytest.mark.parametrize("stored", [True, False])
-def test_backward_graph_replay(stored, monkeypatch):
+def test_backward_graph_replay(stored, kernel_override):
     """Forward and backward captured in one graph, replayed with the
     program's own work in between: every replay matches the eager result."""
     if stored:
-        monkeypatch.setenv("TA03_BWD_PATH", "stored")
+        kernel_override(ta.OVERRIDE_BWD_PATH, 1)
     import torch
-    import tiled_attention_03_amd as ta
     H, Hkv, d, n = 8, 2, 64, 160
     w, q, k, v = inputs.random_case(1190, CAUSAL, n, n, H, Hkv, d)
     g = inputs.normal(q.shape, 1191)
@@ -268,19 +272,45 @@ def test_backward_graph_replay(stored, monkeypatch):
 
 
 @pytest.mark.parametrize("w", [inputs.FULL_1K, inputs.CAUSAL_16K], ids=lambda w: w.name)
-def test_backward_path_choice_by_size(w, monkeypatch):
+def test_backward_path_choice_by_size(w, kernel_override):
     """Without an override the library picks the path by size, given the
     stored workspace: full 1024^2 (32 dq blocks from the tiles) recomputes,
     bitwise equal to the minimal workspace; the 16K causal pass takes the
     stored path, bitwise equal to forcing it."""
-    monkeypatch.delenv("TA03_BWD_PATH", raising=False)
     q, k, v = inputs.make_prefill(w)
     g = inputs.normal(q.shape, w.seed_base + 7)
     auto = gpu_fwd_bwd(q, k, v, g, stored=True, **_kw(w))
     if w is inputs.FULL_1K:
         other = gpu_fwd_bwd(q, k, v, g, stored=False, **_kw(w))
     else:
-        monkeypatch.setenv("TA03_BWD_PATH", "stored")
+        kernel_override(ta.OVERRIDE_BWD_PATH, 1)
         other = gpu_fwd_bwd(q, k, v, g, stored=True, **_kw(w))
     for x, y in zip(auto, other):
         assert np.array_equal(x, y)
+
+
+def test_backward_on_a_side_stream_that_is_not_current():
+    """attention() and attention_backward() given stream=side while another
+    stream is current: their outputs and scratch belong to side, so work
+    allocated on the current stream meanwhile cannot take their memory; the
+    results equal those of the calls on the current stream, bit for bit."""
+    import torch
+    H, Hkv, d, n = 8, 2, 128, 300
+    w, q, k, v = inputs.random_case(1200, CAUSAL, n, n, H, Hkv, d)
+    g = inputs.normal(q.shape, 1201)
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    kw = dict(num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=CAUSAL, scale=w.scale)
+    out0, lse0 = ta.attention(qd, kd, vd, **kw)
+    ref = ta.attention_backward(qd, kd, vd, out0, gd, lse0, **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out1, lse1 = ta.attention(qd, kd, vd, stream=side, **kw)
+    got = ta.attention_backward(qd, kd, vd, out1, gd, lse1, stream=side, **kw)
+    # Allocations and writes on the current stream while side may still run.
+    junk = [torch.full((1 << 22,), float("nan"), device=device()) for _ in range(8)]
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+    for x, y in zip(ref, got):
+        assert torch.equal(x, y)

@@ -9,6 +9,7 @@ import pytest
 
 from tests.gpu_util import (check_lse, check_out, device, gpu_prefill, log,
                             oracle_prefill, to_dev)
+import tiled_attention_03_amd as ta
 from tiled_attention_03_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -30,9 +31,9 @@ def _run_both(w, q, k, v, rows=None, with_lse=True):
 @pytest.mark.parametrize("rows", ["auto", "16", "32"])
 @pytest.mark.parametrize("w", [inputs.CAUSAL_SMALL, inputs.FULL_1K, inputs.CROSS_512x2K,
                                inputs.CONTINUE_512], ids=lambda w: w.name)
-def test_pages_workloads_full_parity(w, rows, monkeypatch):
+def test_pages_workloads_full_parity(w, rows, kernel_override):
     if rows != "auto":
-        monkeypatch.setenv("TA03_PREFILL_ROWS", rows)
+        kernel_override(ta.OVERRIDE_PREFILL_ROWS, int(rows))
     log(f"prefill parity {w.name} rows={rows}")
     q, k, v = inputs.make_prefill(w)
     go, gl, ro, rl = _run_both(w, q, k, v)
@@ -41,15 +42,31 @@ def test_pages_workloads_full_parity(w, rows, monkeypatch):
     log(f"  max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
 
 
-@pytest.mark.parametrize("rows", ["auto", "16"])
-def test_long_causal_sampled_rows(rows, monkeypatch):
-    """16384-row causal pass with heavy K rows: sampled rows against the
-    checker, in the launch configuration the benchmark times (auto), and
-    through the 16-row kernel at this size."""
-    if rows != "auto":
-        monkeypatch.setenv("TA03_PREFILL_ROWS", rows)
+@pytest.mark.timeout(900)
+def test_long_causal_every_row():
+    """The 16384-row causal workload with heavy K rows, in the launch the
+    benchmark times: every row and head of out and lse against the checker,
+    compared in chunks of 1024 rows."""
     w = inputs.CAUSAL_16K
-    log(f"prefill parity (sampled rows) {w.name}")
+    log(f"prefill parity (every row) {w.name}")
+    q, k, v = inputs.make_prefill(w)
+    kw = dict(num_heads=w.num_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+              mode=w.mode, kv_len=w.kv_len, start_pos=w.start_pos, scale=w.scale)
+    go, gl = gpu_prefill(q, k, v, **kw)
+    e_o = e_l = 0.0
+    for r0 in range(0, w.q_seq, 1024):
+        rows = np.arange(r0, min(r0 + 1024, w.q_seq))
+        ro, rl = oracle_prefill(q, k, v, rows=rows, **kw)
+        e_o = max(e_o, check_out(go[rows], ro, f"{w.name} rows {r0}+"))
+        e_l = max(e_l, check_lse(gl[rows], rl, f"{w.name} rows {r0}+"))
+        log(f"  rows [{r0}, {rows[-1] + 1}) max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
+
+
+def test_long_causal_sampled_rows_16row_kernel(kernel_override):
+    """The same workload forced through the 16-row kernel: sampled rows."""
+    kernel_override(ta.OVERRIDE_PREFILL_ROWS, 16)
+    w = inputs.CAUSAL_16K
+    log(f"prefill parity (sampled rows, 16-row kernel) {w.name}")
     q, k, v = inputs.make_prefill(w)
     rng = np.random.default_rng(5099)
     rows = np.unique(np.concatenate([
@@ -100,12 +117,12 @@ SWEEP = [
 @pytest.mark.parametrize("rows", ["auto", "16", "32"])
 @pytest.mark.parametrize("case", SWEEP, ids=[f"m{c[0]}_q{c[1]}_kv{c[2]}_h{c[3]}x{c[4]}_d{c[5]}_sp{c[6]}"
                                              for c in SWEEP])
-def test_ragged_sweep(case, rows, monkeypatch):
+def test_ragged_sweep(case, rows, kernel_override):
     """Every shape through the launch's own choice and through each of the
     two prefill kernels (16-row and 32-row waves), forced by the library's
-    TA03_PREFILL_ROWS override."""
+    kernel-choice override."""
     if rows != "auto":
-        monkeypatch.setenv("TA03_PREFILL_ROWS", rows)
+        kernel_override(ta.OVERRIDE_PREFILL_ROWS, int(rows))
     mode, n, kv, H, Hkv, d, sp = case
     log(f"prefill sweep {case} rows={rows}")
     w, q, k, v = inputs.random_case(700 + SWEEP.index(case), mode, n, kv, H, Hkv, d,
@@ -120,7 +137,6 @@ def test_empty_query_batch_is_a_noop():
     dev = device()
     q = torch.zeros((0, 256), device=dev)
     out = torch.full((4, 256), 7.0, device=dev)
-    import tiled_attention_03_amd as ta
     ta.attn_fwd(q, None, None, out, None, 0, 0, 4, 2, 64, CROSS, 0, 0.125)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
@@ -128,7 +144,6 @@ def test_empty_query_batch_is_a_noop():
 
 def test_cross_over_zero_keys_writes_zeros_and_sentinel():
     import torch
-    import tiled_attention_03_amd as ta
     dev = device()
     n, H, d = 37, 4, 64
     q = to_dev(inputs.normal((n, H * d), 42))
@@ -144,7 +159,6 @@ def test_poisoned_cache_and_outputs():
     """Cache rows outside every window hold NaN and must not be read; out and
     lse start as NaN and must be fully overwritten."""
     import torch
-    import tiled_attention_03_amd as ta
     H, Hkv, d, n, sp, rows = 8, 2, 128, 77, 150, 400
     w, q, k, v = inputs.random_case(801, CAUSAL, n, sp + n, H, Hkv, d, start_pos=sp,
                                     kv_rows=rows)
@@ -193,7 +207,6 @@ def test_graph_replay_matches_checker():
     change in place (eager work and synchronisation between replays): every
     replay matches the checker on that replay's inputs."""
     import torch
-    import tiled_attention_03_amd as ta
     w = inputs.FULL_1K
     dev = device()
     q0, k0, v0 = inputs.make_prefill(w)
@@ -233,7 +246,6 @@ def test_strided_fused_qkv_and_padded_out():
     with padded rows: matches the checker on dense copies, and the padding
     columns are left untouched."""
     import torch
-    import tiled_attention_03_amd as ta
     H, Hkv, d, n, sp = 8, 2, 128, 300, 0
     dev = device()
     width = (H + 2 * Hkv) * d
@@ -264,7 +276,6 @@ def test_long_causal_fused_qkv_sampled_rows():
     output and lse bit for bit equal to the contiguous call (row strides
     change addresses only)."""
     import torch
-    import tiled_attention_03_amd as ta
     w = inputs.CAUSAL_16K
     log(f"prefill parity fused QKV (sampled rows) {w.name}")
     H, Hkv, d, n = w.num_heads, w.num_kv_heads, w.head_dim, w.q_seq
@@ -304,7 +315,6 @@ def test_sub_batches_with_q_base(mode, sp):
     """Splitting the query batch into sub-batch calls with q_base (the
     prefill page's sub-batched dispatch) reproduces the whole batch."""
     import torch
-    import tiled_attention_03_amd as ta
     H, Hkv, d, n = 4, 2, 64, 170
     kv = n + sp if mode != CROSS else 211
     w, q, k, v = inputs.random_case(820 + mode, mode, n, kv, H, Hkv, d, start_pos=sp)

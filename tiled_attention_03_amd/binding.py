@@ -19,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libta03.so")
 
 CAUSAL, FULL, CROSS = 0, 1, 2
+OVERRIDE_PREFILL_ROWS, OVERRIDE_BWD_PATH = 1, 2
 STATUS_NAMES = {0: "TA03_OK", -1: "TA03_ERR_NULL", -2: "TA03_ERR_SHAPE",
                 -3: "TA03_ERR_UNSUPPORTED", -4: "TA03_ERR_WORKSPACE",
                 -5: "TA03_ERR_HIP", -6: "TA03_ERR_ALIGN"}
@@ -39,6 +40,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run "
                                "`python -m tiled_attention_03_amd.build` first")
+        # torch first: its HIP runtime (bundled, loaded under another file
+        # name) must be the one the library binds to. Loaded the other way
+        # round, the process holds two HIP runtimes and torch's streams and
+        # memory are foreign to the library's launches.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         LL = ctypes.c_longlong
@@ -65,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode.restype = I
         L.attn_decode_paged.argtypes = [P, P, P, I, I, P, P, P, P, I, I, I, I, F, P, S, P]
         L.attn_decode_paged.restype = I
+        L.attn_set_kernel_override.argtypes = [I, I]
+        L.attn_set_kernel_override.restype = I
         L.attn_strerror.argtypes = [I]
         L.attn_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -73,6 +81,24 @@ def lib() -> ctypes.CDLL:
 
 def attn_strerror(status: int) -> str:
     return lib().attn_strerror(int(status)).decode()
+
+
+def attn_set_kernel_override(knob: int, value: int) -> None:
+    """Testing hook: force a kernel choice for later calls in this process
+    (0 restores the automatic choice; see include/ta03.h)."""
+    _check(lib().attn_set_kernel_override(int(knob), int(value)))
+
+
+def _alloc_stream(stream):
+    """The torch stream that tensors allocated for a call on `stream` must
+    belong to, so that the caching allocator does not hand their memory to
+    other work while the call's kernels may still use it."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
 
 
 def _ptr(t, min_numel: int, name: str, *, dtype_name="float32"):
@@ -231,14 +257,18 @@ def attention_backward(q, k, v, out, dout, lse, *, num_heads: int, num_kv_heads:
     if scale is None:
         scale = head_dim ** -0.5
     dev = q.device
-    dq = torch.empty((q_seq, num_heads * head_dim), dtype=torch.float32, device=dev)
-    dk = torch.empty((kv_len, num_kv_heads * head_dim), dtype=torch.float32, device=dev)
-    dv = torch.empty((kv_len, num_kv_heads * head_dim), dtype=torch.float32, device=dev)
+    s = _alloc_stream(stream)
     nbytes = (attn_bwd_workspace_bytes_stored(q_seq, kv_len, num_heads, mode, start_pos)
               if store_scores else 0) or attn_bwd_workspace_bytes(q_seq, num_heads)
-    ws = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=dev)
+    # Outputs and scratch belong to the stream the kernels run on: the scratch
+    # is dropped on return while the kernels may still be running.
+    with torch.cuda.stream(s):
+        dq = torch.empty((q_seq, num_heads * head_dim), dtype=torch.float32, device=dev)
+        dk = torch.empty((kv_len, num_kv_heads * head_dim), dtype=torch.float32, device=dev)
+        dv = torch.empty((kv_len, num_kv_heads * head_dim), dtype=torch.float32, device=dev)
+        ws = torch.empty((max(nbytes, 4) // 4,), dtype=torch.float32, device=dev)
     attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, q_seq, kv_len, num_heads, num_kv_heads,
-             head_dim, mode, start_pos, scale, ws, nbytes, stream)
+             head_dim, mode, start_pos, scale, ws, nbytes, s)
     return dq, dk, dv
 
 
@@ -323,9 +353,11 @@ def attention(q, k, v, *, num_heads: int, num_kv_heads: int, head_dim: int, mode
         kv_len = k.shape[0]
     if scale is None:
         scale = head_dim ** -0.5
-    out = torch.empty((q_seq, num_heads * head_dim), dtype=torch.float32, device=q.device)
-    lse = (torch.empty((q_seq, num_heads, 2), dtype=torch.float32, device=q.device)
-           if with_lse else None)
+    s = _alloc_stream(stream)
+    with torch.cuda.stream(s):
+        out = torch.empty((q_seq, num_heads * head_dim), dtype=torch.float32, device=q.device)
+        lse = (torch.empty((q_seq, num_heads, 2), dtype=torch.float32, device=q.device)
+               if with_lse else None)
     attn_fwd(q, k, v, out, lse, q_seq, kv_len, num_heads, num_kv_heads, head_dim, mode,
-             start_pos, scale, stream)
+             start_pos, scale, s)
     return out, lse

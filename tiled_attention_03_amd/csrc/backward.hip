@@ -37,9 +37,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
-#include <cstring>
-
 #include "ta03_internal.h"
 
 namespace ta03 {
@@ -53,8 +50,7 @@ constexpr int kWaves = 4;
 constexpr int kBM = 32;      // query rows per wave (dq) / per tile (dk, dv)
 constexpr int kBN = 32;      // keys per tile (dq) / per wave (dk, dv)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kNumCUs = 256;
-constexpr int kTargetWaves = 2048;  // two waves per SIMD
+constexpr int kWavesPerCU = 8;  // two waves per SIMD
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -87,7 +83,6 @@ struct BwdArgs {
     float qscale;  // scale * log2(e)
     float scale;
     int hg, rs, ks, n_head_blocks, n_row_blocks;  // dq kernel block shape (ks: key splits)
-    int n_key_blocks;                         // dk/dv kernel: 128-key blocks per KV head
     DsLayout ds;                              // stored dS tiles (when kept)
     long long ds_tph;                         // dS tiles per head
     int dq_hg, dq_rs, dq_rt, dq_n_head_blocks, dq_n_row_blocks;  // dq-from-dS block shape
@@ -312,193 +307,6 @@ bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 }
 
-template <int D>
-__global__ void __launch_bounds__(kBlock, D == 64 ? 2 : 1)
-bwd_dkdv_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                const float* __restrict__ v, const float* __restrict__ dout,
-                const float* __restrict__ lse, const float* __restrict__ delta,
-                float* __restrict__ dk, float* __restrict__ dv, BwdArgs a) {
-    constexpr int NB = D / 32;
-    constexpr int TILE_F = kBM * D;
-    // [2][Q tile | dout tile], then [2][64 floats: (m, log l) x 32 rows][64: D x 32, twice]
-    extern __shared__ __attribute__((aligned(16))) float smem[];
-    float* vecs = smem + 4 * TILE_F;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int j = lane & 31;
-    const int hh = lane >> 5;
-
-    const int bid = blockIdx.x;
-    const int kv_head = bid % a.num_kv_heads;
-    const int kb = bid / a.num_kv_heads;  // low keys first: the most rows see them
-    const int blk_key0 = kb * kWaves * kBN;
-    const int key0 = blk_key0 + wave * kBN;
-    const bool strip_live = key0 < a.kv_len;
-    const int key = key0 + j;
-    const int qd = a.num_heads * D;
-    const int kvd = a.num_kv_heads * D;
-
-    // K (log2 units) and V of key j as B operands: element 8g + 4hh + c in
-    // register 4g + c. Keys past kv_len read the last key (masked below).
-    float kr[D / 2], vr[D / 2];
-    {
-        const size_t off = (size_t)min(key, a.kv_len - 1) * kvd + kv_head * D + 4 * hh;
-#pragma unroll
-        for (int g = 0; g < D / 8; ++g) {
-            const float4 x = *reinterpret_cast<const float4*>(k + off + 8 * g);
-            const float4 y = *reinterpret_cast<const float4*>(v + off + 8 * g);
-            kr[4 * g + 0] = x.x * a.qscale;
-            kr[4 * g + 1] = x.y * a.qscale;
-            kr[4 * g + 2] = x.z * a.qscale;
-            kr[4 * g + 3] = x.w * a.qscale;
-            vr[4 * g + 0] = y.x;
-            vr[4 * g + 1] = y.y;
-            vr[4 * g + 2] = y.z;
-            vr[4 * g + 3] = y.w;
-        }
-    }
-
-    f32x16 dka[NB], dva[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            dka[b][r] = 0.f;
-            dva[b][r] = 0.f;
-        }
-
-    // Query rows that see some key of the block: causal rows from
-    // blk_key0 - start_pos on (window start_pos + i + 1 > blk_key0).
-    const int i_lo = a.causal ? max(0, blk_key0 - a.start_pos) : 0;
-    const int qt0 = i_lo / kBM;
-    const int n_qt = i_lo < a.q_seq ? (a.q_seq + kBM - 1) / kBM - qt0 : 0;
-    const int total = a.group * n_qt;
-
-    auto issue = [&](int it, int buf) {
-        const int h = kv_head * a.group + it / n_qt;
-        const int row0 = (qt0 + it % n_qt) * kBM;
-        float* qdst = smem + (size_t)buf * 2 * TILE_F;
-        issue_rows<D>(q + h * D, qd, row0, a.q_seq, qdst, wave, kWaves, lane);
-        issue_rows<D>(dout + h * D, qd, row0, a.q_seq, qdst + TILE_F, wave, kWaves, lane);
-        if (wave == 0) {
-            // lane l: (m, log l) component l % 2 of row l / 2; D of row l % 32
-            const int rl = min(row0 + (lane >> 1), a.q_seq - 1);
-            const int rd = min(row0 + (lane & 31), a.q_seq - 1);
-            float* vd = vecs + buf * 128;
-            __builtin_amdgcn_global_load_lds(lse + ((size_t)rl * a.num_heads + h) * 2 + (lane & 1),
-                                             (lds_void*)vd, 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(delta + (size_t)rd * a.num_heads + h,
-                                             (lds_void*)(vd + 64), 4, 0, 0);
-        }
-    };
-
-    if (total > 0) issue(0, 0);
-    for (int it = 0; it < total; ++it) {
-        wait_vmem();
-        __syncthreads();  // tile it landed for every wave; buffer (it+1)&1 is free
-        if (it + 1 < total) issue(it + 1, (it + 1) & 1);
-        const int row0 = (qt0 + it % n_qt) * kBM;
-        const int rows_hi = min(row0 + kBM, a.q_seq);
-        // Largest and smallest window over the tile's rows.
-        const int w_max = a.causal ? min(a.start_pos + rows_hi, a.kv_len) : a.kv_len;
-        const int w_min = a.causal ? min(a.start_pos + row0 + 1, a.kv_len) : a.kv_len;
-        if (strip_live && key0 < w_max) {  // wave-uniform
-            const float* Qs = smem + (size_t)(it & 1) * 2 * TILE_F;
-            const float* Gs = Qs + TILE_F;
-            const float* vd = vecs + (it & 1) * 128;
-            // S = Q K^T and dP = dout V^T (row: query, column: key j).
-            f32x16 s, dp;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[r] = 0.f;
-                dp[r] = 0.f;
-            }
-            const float* qrow = Qs + j * D;
-            const float* grow = Gs + j * D;
-#pragma unroll
-            for (int g = 0; g < D / 8; ++g) {
-                const int c = (2 * g + hh) ^ (j & 15);
-                const float4 qq = *reinterpret_cast<const float4*>(qrow + 4 * c);
-                const float4 gg = *reinterpret_cast<const float4*>(grow + 4 * c);
-                s = mfma32(qq.x, kr[4 * g + 0], s);
-                dp = mfma32(gg.x, vr[4 * g + 0], dp);
-                s = mfma32(qq.y, kr[4 * g + 1], s);
-                dp = mfma32(gg.y, vr[4 * g + 1], dp);
-                s = mfma32(qq.z, kr[4 * g + 2], s);
-                dp = mfma32(gg.z, vr[4 * g + 2], dp);
-                s = mfma32(qq.w, kr[4 * g + 3], s);
-                dp = mfma32(gg.w, vr[4 * g + 3], dp);
-            }
-            // P in place of S, dS in place of dP; rows past q_seq and keys
-            // outside a row's window weigh 0.
-            const bool need_mask = key0 + kBN > w_min || rows_hi - row0 < kBM;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ir = acc_row(r, hh);
-                const int i = row0 + ir;
-                const float lse2 = (vd[2 * ir] + vd[2 * ir + 1]) * kLog2e;
-                const float dl = vd[64 + ir];
-                bool valid = true;
-                if (need_mask) {
-                    const int w = a.causal ? min(a.start_pos + i + 1, a.kv_len) : a.kv_len;
-                    valid = i < a.q_seq && key < w;
-                }
-                const float p = valid ? __builtin_amdgcn_exp2f(s[r] - lse2) : 0.f;
-                s[r] = p;
-                dp[r] = p * (dp[r] - dl);
-            }
-            // dv^T += dout^T P and dk^T += Q^T dS: k-step t pairs rows
-            // acc_row(t, 0) and acc_row(t, 1); block b row m is head-dim
-            // NB*m + b.
-#pragma unroll
-            for (int tt = 0; tt < 16; ++tt) {
-                const int ir = acc_row(tt, hh);
-                const int cofs = ir * D + swz_cols<NB>(j, ir);
-                if constexpr (NB == 4) {
-                    const float4 gg = *reinterpret_cast<const float4*>(Gs + cofs);
-                    const float4 qq = *reinterpret_cast<const float4*>(Qs + cofs);
-                    dva[0] = mfma32(gg.x, s[tt], dva[0]);
-                    dka[0] = mfma32(qq.x, dp[tt], dka[0]);
-                    dva[1] = mfma32(gg.y, s[tt], dva[1]);
-                    dka[1] = mfma32(qq.y, dp[tt], dka[1]);
-                    dva[2] = mfma32(gg.z, s[tt], dva[2]);
-                    dka[2] = mfma32(qq.z, dp[tt], dka[2]);
-                    dva[3] = mfma32(gg.w, s[tt], dva[3]);
-                    dka[3] = mfma32(qq.w, dp[tt], dka[3]);
-                } else {
-                    const float2 gg = *reinterpret_cast<const float2*>(Gs + cofs);
-                    const float2 qq = *reinterpret_cast<const float2*>(Qs + cofs);
-                    dva[0] = mfma32(gg.x, s[tt], dva[0]);
-                    dka[0] = mfma32(qq.x, dp[tt], dka[0]);
-                    dva[1] = mfma32(gg.y, s[tt], dva[1]);
-                    dka[1] = mfma32(qq.y, dp[tt], dka[1]);
-                }
-            }
-        }
-    }
-
-    if (!strip_live || key >= a.kv_len) return;
-    float* krow = dk + (size_t)key * kvd + kv_head * D;
-    float* vrow = dv + (size_t)key * kvd + kv_head * D;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int i = acc_row(r, hh);
-        if constexpr (NB == 4) {
-            *reinterpret_cast<float4*>(krow + 4 * i) =
-                make_float4(dka[0][r] * a.scale, dka[1][r] * a.scale, dka[2][r] * a.scale,
-                            dka[3][r] * a.scale);
-            *reinterpret_cast<float4*>(vrow + 4 * i) =
-                make_float4(dva[0][r], dva[1][r], dva[2][r], dva[3][r]);
-        } else {
-            *reinterpret_cast<float2*>(krow + 2 * i) =
-                make_float2(dka[0][r] * a.scale, dka[1][r] * a.scale);
-            *reinterpret_cast<float2*>(vrow + 2 * i) = make_float2(dva[0][r], dva[1][r]);
-        }
-    }
-}
-
 // dk/dv with 16-key waves on v_mfma_f32_16x16x4_f32: per wave K, V (B
 // operands) and the dk^T, dv^T accumulators take 32 registers each at
 // head_dim 128 (half of the 32-key kernel), so two waves share a SIMD.
@@ -634,6 +442,9 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // One piece of stage st's copies (for spreading them between products):
     // pieces 0..3 = Q / dout rows of sub-tile p >> 1, instruction p & 1;
     // pieces 4, 5 = the (m, log l) / D vectors of sub-tile p - 4.
+    // The six pieces cover a stage only for two sub-tiles of at most two
+    // load instructions per wave each; a change to either must change them.
+    static_assert(SUB == 2 && LOADS <= 2 * W, "issue_piece covers every copy of a stage");
     auto issue_piece = [&](int st, float* tb, float* vb, int pc) __attribute__((always_inline)) {
         const int sub = pc < 4 ? pc >> 1 : pc - 4;
         const int it = st * SUB + sub;
@@ -1053,34 +864,19 @@ hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, c
                                float* dv, float* delta, const BwdArgs& a, hipStream_t stream) {
     const size_t tile_bytes = (size_t)kBN * D * sizeof(float);
     const size_t lds_dq = (size_t)a.ks * 2 * 2 * tile_bytes;  // per key split: 2 x (K, V)
-    const size_t lds_dkdv = 2 * 2 * tile_bytes + 2 * 128 * sizeof(float);
     static const hipError_t attr1 = hipFuncSetAttribute(
         reinterpret_cast<const void*>(bwd_dq_kernel<D>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)((D == 128 ? 2 : 4) * 2 * 2 * tile_bytes));
-    static const hipError_t attr2 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(bwd_dkdv_kernel<D>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_dkdv);
     if (attr1 != hipSuccess) return attr1;
-    if (attr2 != hipSuccess) return attr2;
     const long long g1 = (long long)a.n_head_blocks * a.n_row_blocks;
     if (g1 > 0) {
         hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)g1), dim3(kBlock), lds_dq, stream,
                            q, k, v, o, dout, lse, dq, delta, a);
     }
     // With no query rows the dk/dv blocks walk no tiles and write zeros.
-    const char* force = std::getenv("TA03_BWD_KEYS");
-    const bool keys16 = force == nullptr || std::strcmp(force, "32") != 0;
-    if (keys16) {
-        const size_t lds16 = 0;  // static LDS
-        return launch_dkdv16_any<D, false>(lds16, stream, q, k, v, dout, lse, delta, dk, dv,
-                                           nullptr, a);
-    }
-    const long long g2 = (long long)a.num_kv_heads * a.n_key_blocks;
-    if (g2 > 0) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)g2), dim3(kBlock), lds_dkdv,
-                           stream, q, k, v, dout, lse, delta, dk, dv, a);
-    }
-    return hipSuccess;
+    const size_t lds16 = 0;  // static LDS
+    return launch_dkdv16_any<D, false>(lds16, stream, q, k, v, dout, lse, delta, dk, dv, nullptr,
+                                       a);
 }
 
 }  // namespace
@@ -1106,13 +902,15 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
     const int key_tiles = (max_w + kBN - 1) / kBN;
     const int max_ks = s.head_dim == 128 ? 2 : 4;  // 2 buffers x (K, V) per split in 160 KB
     int ks = 1;
-    while (ks < max_ks && base_waves * ks < kTargetWaves && key_tiles >= 4 * ks * 2) ks *= 2;
+    const int cus = device_cu_count();
+    while (ks < max_ks && base_waves * ks < (long long)kWavesPerCU * cus &&
+           key_tiles >= 4 * ks * 2)
+        ks *= 2;
     a.ks = ks;
     a.hg = gcd_int(a.group, kWaves / ks);
     a.rs = kWaves / (ks * a.hg);
     a.n_head_blocks = s.num_heads / a.hg;
     a.n_row_blocks = (s.q_seq + a.rs * kBM - 1) / (a.rs * kBM);
-    a.n_key_blocks = (s.kv_len + kWaves * kBN - 1) / (kWaves * kBN);
     a.ds = DsLayout{s.causal, s.start_pos, s.q_seq, s.kv_len};
     a.ds_tph = ds_tiles_per_head(a.ds);
     a.dq_hg = gcd_int(a.group, kWaves);
@@ -1122,18 +920,16 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
         return (ds_query_tiles(a.ds) + a.dq_rs * rt - 1) / (a.dq_rs * rt);
     };
     // 4 query tiles per wave while that still gives two blocks per CU.
-    a.dq_rt = (long long)a.dq_n_head_blocks * dq_rows(4) >= 2 * kNumCUs ? 4 : 1;
+    a.dq_rt = (long long)a.dq_n_head_blocks * dq_rows(4) >= 2 * cus ? 4 : 1;
     a.dq_n_row_blocks = dq_rows(a.dq_rt);
-    const char* force = std::getenv("TA03_BWD_KEYS");
-    const bool keys16 = force == nullptr || std::strcmp(force, "32") != 0;
     // The stored path pays once the dq grid from the tiles fills the compute
-    // units; shorter calls recompute (TA03_BWD_PATH=stored / recompute forces
-    // one, the first only with a workspace that holds the tiles).
-    const char* path = std::getenv("TA03_BWD_PATH");
-    const bool big = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks >= kNumCUs;
-    const bool use_ds = path != nullptr ? std::strcmp(path, "stored") == 0 : big;
+    // units; shorter calls recompute (a testing override forces either path,
+    // the stored one only with a workspace that holds the tiles).
+    const int force = override_bwd_path();
+    const bool big = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks >= cus;
+    const bool use_ds = force != 0 ? force == 1 : big;
     hipError_t e;
-    if (ds != nullptr && use_ds && keys16 && s.q_seq > 0 && s.kv_len > 0) {
+    if (ds != nullptr && use_ds && s.q_seq > 0 && s.kv_len > 0) {
         if (s.head_dim == 128) {
             e = launch_bwd_stored<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, stream);
         } else {

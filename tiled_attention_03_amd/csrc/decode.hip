@@ -62,10 +62,6 @@ constexpr int kT = 16 * kWaves;   // keys per unit (16 per wave)
 constexpr int kKW = kT / kWaves;  // keys per wave per unit
 constexpr int kG = 4;             // query heads per block
 static_assert(kWaves >= kG, "the merge serves one head per wave");
-#ifndef TA03_DECODE_TARGET_BLOCKS
-#define TA03_DECODE_TARGET_BLOCKS 256
-#endif
-constexpr int kTargetBlocks = TA03_DECODE_TARGET_BLOCKS;
 // The completion counters sit 256 bytes apart: side by side in one line, the
 // atomics of all 256 blocks serialised on it (the last ticket of a call came
 // ~1.4 us after its block's stores; 17.2 -> 16.6 us at an 8192-row cache).
@@ -78,7 +74,7 @@ struct Args {
     int num_heads, num_kv_heads, max_seq;
     int group, heads_per_blk, blks_per_kv, n_splits;
     float qscale;  // scale * log2(e)
-    size_t cnt_offset;  // floats from ws to the ticket counters (kCntStride apart)
+    size_t part_offset;  // floats from ws to the split partials (the counters come first)
     // Paged cache (table == nullptr: one dense cache). Token t lives in row
     // t % page_size of page table[t / page_size]; page_size is a multiple of
     // 16, so a wave's 16-key slice never straddles two pages.
@@ -427,7 +423,7 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
             o0 = fmaf(Ow[w][h * D + d], wt, o0);
             o1 = fmaf(Ow[w][h * D + d + 1], wt, o1);
         }
-        float* part = ws + ((size_t)(head0 + h) * a.n_splits + split) * row;
+        float* part = ws + a.part_offset + ((size_t)(head0 + h) * a.n_splits + split) * row;
         store_pair(part + d, o0, o1);
         if (d == 0) {
             float L = 0.f;
@@ -447,8 +443,7 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // ticket would issue one per block, which costs more than the merge).
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
     __syncthreads();
-    unsigned int* cnt =
-        reinterpret_cast<unsigned int*>(ws + a.cnt_offset) + (size_t)blockIdx.y * kCntStride;
+    unsigned int* cnt = reinterpret_cast<unsigned int*>(ws) + (size_t)blockIdx.y * kCntStride;
     if (tid == 0) {
         const unsigned int t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
@@ -469,7 +464,7 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
         constexpr int DPL = D / 64;
         constexpr int NB = 32;
         const int head = head0 + wave;
-        const float* hb = ws + (size_t)head * a.n_splits * row;
+        const float* hb = ws + a.part_offset + (size_t)head * a.n_splits * row;
         const int lj = lane & (NB - 1);
         float M = kNegBig, L = 0.f, o[DPL];
 #pragma unroll
@@ -523,26 +518,29 @@ __global__ void zero_counters_kernel(unsigned int* p, int n) {
 
 }  // namespace
 
-DecodePlan decode_plan(const DecodeShape& s) {
+DecodePlan decode_plan(const DecodeShape& s, int target_blocks) {
     DecodePlan p;
     p.group = s.num_heads / s.num_kv_heads;
     p.heads_per_blk = p.group < kG ? p.group : kG;
     p.blks_per_kv = (p.group + p.heads_per_blk - 1) / p.heads_per_blk;
     const long long rows = (long long)s.num_kv_heads * p.blks_per_kv;
-    long long n = (kTargetBlocks + rows - 1) / rows;
+    // About one block per compute unit.
+    long long n = (target_blocks + rows - 1) / rows;
     const long long max_useful = (s.max_seq + kT - 1) / kT;
     if (n > max_useful) n = max_useful;
     if (n < 1) n = 1;
     p.n_splits = (int)n;
+    // The counters first (their region depends on the head counts only, so
+    // a zero fill needs no split count), then the partials.
+    p.n_counters = (size_t)rows * kCntStride;
+    p.part_offset = p.n_counters;
     const size_t part = (size_t)s.num_heads * (size_t)p.n_splits * (size_t)(s.head_dim + 2);
-    p.cnt_offset = (part + kCntStride - 1) / kCntStride * kCntStride;
-    p.n_counters = (size_t)rows * kCntStride;  // counter region in words, one counter per slot
-    p.ws_floats = p.cnt_offset + p.n_counters;
+    p.ws_floats = p.part_offset + (part + kCntStride - 1) / kCntStride * kCntStride;
     return p;
 }
 
 hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t stream) {
-    unsigned int* c = reinterpret_cast<unsigned int*>(ws + p.cnt_offset);
+    unsigned int* c = reinterpret_cast<unsigned int*>(ws);
     const int n = (int)p.n_counters;
     hipLaunchKernelGGL(zero_counters_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        stream, c, n);
@@ -575,7 +573,7 @@ hipError_t launch_decode(const float* q, const float* k, const float* v,
     a.blks_per_kv = p.blks_per_kv;
     a.n_splits = p.n_splits;
     a.qscale = s.scale * kLog2e;
-    a.cnt_offset = p.cnt_offset;
+    a.part_offset = p.part_offset;
     a.table = table;
     a.page_size = page_size;
     a.num_pages = num_pages;

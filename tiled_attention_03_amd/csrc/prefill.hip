@@ -47,9 +47,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
-#include <cstring>
-
 #include "ta03_internal.h"
 
 namespace ta03 {
@@ -62,8 +59,7 @@ constexpr int kBlock = 256;  // 4 waves
 constexpr int kWaves = 4;
 constexpr int kBM = 32;      // query rows per wave
 constexpr int kBN = 32;      // keys per tile
-constexpr int kTargetWaves = 2048;  // two waves per SIMD on 256 CUs
-constexpr int kNumCUs = 256;
+constexpr int kWavesPerCU = 8;  // two waves per SIMD
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -164,7 +160,6 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const bool wave_live = row0 < a.q_seq;
     const int w_wave_max = !wave_live ? 0
         : (a.causal ? min(a.start_pos + min(row0 + kBM, a.q_seq), a.kv_len) : a.kv_len);
-    const int w_wave_min = a.causal ? min(a.start_pos + row0 + 1, a.kv_len) : a.kv_len;
     const int row = row0 + j;
     const int w_row = a.causal ? min(a.start_pos + row + 1, a.kv_len) : a.kv_len;
 
@@ -390,11 +385,12 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 s = mfma32(kk.w, qr[4 * g + 3], s);
             }
 
-            if (kv0 + kBN > w_wave_min) {  // some key of the tile is outside some window
+            // The window mask is a select on every tile: behind a branch it
+            // would put a basic-block edge between the last score product and
+            // the first vector read of its result, where the wait the matrix
+            // unit's result needs was once found missing in generated code.
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kv0 + acc_row(r, hh) >= w_row) s[r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r) s[r] = kv0 + acc_row(r, hh) < w_row ? s[r] : -INFINITY;
 
             // Online softmax for query column j.
             float mx = s[0];
@@ -597,7 +593,9 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     const bool rope = s.rope_cs != nullptr;
     const int max_ks = s.head_dim == 128 ? (rope ? 1 : 2) : 4;
     int ks = 1;
-    while (ks < max_ks && base_waves * ks < kTargetWaves && key_tiles >= 4 * ks * 2) ks *= 2;
+    const int cus = device_cu_count();
+    const long long target_waves = (long long)kWavesPerCU * cus;
+    while (ks < max_ks && base_waves * ks < target_waves && key_tiles >= 4 * ks * 2) ks *= 2;
     a.ks = ks;
     a.hg = gcd_int(a.group, kWaves / ks);
     a.rs = kWaves / (ks * a.hg);
@@ -607,11 +605,10 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     if (grid <= 0) return hipSuccess;
     if (!rope) {
         // Fewer blocks than compute units: the 16-row kernel, which needs no
-        // shared tiles, spreads the work over more waves. The environment
-        // variable TA03_PREFILL_ROWS (16 or 32) overrides the choice, for
-        // testing both kernels on the same shapes.
-        const char* force = std::getenv("TA03_PREFILL_ROWS");
-        const bool use16 = force != nullptr ? std::strcmp(force, "16") == 0 : grid < kNumCUs;
+        // shared tiles, spreads the work over more waves (a testing override
+        // can force either kernel on any shape).
+        const int force = override_prefill_rows();
+        const bool use16 = force != 0 ? force == 16 : grid < cus;
         if (use16) return launch_prefill16(q, k, v, out, lse, s, stream);
     }
     hipError_t e;

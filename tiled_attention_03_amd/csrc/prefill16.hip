@@ -38,7 +38,7 @@ constexpr int kWaves = 8;
 constexpr int kBlock = 64 * kWaves;
 constexpr int kRows = 16;  // query rows per wave
 constexpr int kKeys = 16;  // keys per tile
-constexpr int kTargetWaves = 2048;
+constexpr int kWavesPerCU = 8;  // two waves per SIMD
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -332,7 +332,8 @@ hipError_t launch_prefill16(const float* q, const float* k, const float* v, floa
     const int max_w = s.causal ? min(s.start_pos + s.q_seq, s.kv_len) : s.kv_len;
     const int key_tiles = (max_w + kKeys - 1) / kKeys;
     int ks = 1;
-    while (ks < kWaves && base_waves * ks < kTargetWaves && key_tiles >= 2 * ks * 2) ks *= 2;
+    const long long target_waves = (long long)kWavesPerCU * device_cu_count();
+    while (ks < kWaves && base_waves * ks < target_waves && key_tiles >= 2 * ks * 2) ks *= 2;
     a.ks = ks;
     a.hg = gcd16(a.group, kWaves / ks);
     a.rs = kWaves / (ks * a.hg);

@@ -3,11 +3,38 @@
 // enqueues nothing and needs no device.
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
 #include "ta03.h"
 #include "ta03_internal.h"
+
+namespace ta03 {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0: not queried yet
+std::atomic<int> g_prefill_rows{0};
+std::atomic<int> g_bwd_path{0};
+}  // namespace
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        n = 256;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int override_prefill_rows() { return g_prefill_rows.load(std::memory_order_relaxed); }
+int override_bwd_path() { return g_bwd_path.load(std::memory_order_relaxed); }
+
+}  // namespace ta03
 
 namespace {
 
@@ -192,7 +219,7 @@ size_t attn_decode_workspace_bytes(int num_heads, int num_kv_heads, int head_dim
         return 0;
     if (!head_dim_supported(head_dim)) return 0;
     ta03::DecodeShape s{num_heads, num_kv_heads, head_dim, max_seq, 1.0f};
-    return ta03::decode_plan(s).ws_floats * sizeof(float);
+    return ta03::decode_plan(s, ta03::device_cu_count()).ws_floats * sizeof(float);
 }
 
 int attn_decode_workspace_init(void* workspace, size_t workspace_bytes, int num_heads,
@@ -203,7 +230,7 @@ int attn_decode_workspace_init(void* workspace, size_t workspace_bytes, int num_
     if (workspace == nullptr) return TA03_ERR_NULL;
     if (!aligned16(workspace)) return TA03_ERR_ALIGN;
     ta03::DecodeShape s{num_heads, num_kv_heads, head_dim, max_seq, 1.0f};
-    const ta03::DecodePlan p = ta03::decode_plan(s);
+    const ta03::DecodePlan p = ta03::decode_plan(s, ta03::device_cu_count());
     if (workspace_bytes < p.ws_floats * sizeof(float)) return TA03_ERR_WORKSPACE;
     const hipError_t e = ta03::launch_decode_ws_init(static_cast<float*>(workspace), p, stream);
     return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
@@ -226,7 +253,7 @@ int attn_decode(const float* q, const float* k_cache, const float* v_cache,
         (reinterpret_cast<uintptr_t>(kv_pos) & 3u) != 0)
         return TA03_ERR_ALIGN;
     ta03::DecodeShape s{num_heads, num_kv_heads, head_dim, max_seq, scale};
-    const ta03::DecodePlan p = ta03::decode_plan(s);
+    const ta03::DecodePlan p = ta03::decode_plan(s, ta03::device_cu_count());
     if (workspace_bytes < p.ws_floats * sizeof(float)) return TA03_ERR_WORKSPACE;
     const hipError_t e = ta03::launch_decode(q, k_cache, v_cache, kv_pos, out, lse, s, p,
                                              static_cast<float*>(workspace), stream);
@@ -254,13 +281,28 @@ int attn_decode_paged(const float* q, const float* k_pool, const float* v_pool, 
         (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
         return TA03_ERR_ALIGN;
     ta03::DecodeShape s{num_heads, num_kv_heads, head_dim, max_seq, scale};
-    const ta03::DecodePlan p = ta03::decode_plan(s);
+    const ta03::DecodePlan p = ta03::decode_plan(s, ta03::device_cu_count());
     if (workspace_bytes < p.ws_floats * sizeof(float)) return TA03_ERR_WORKSPACE;
     if (ta03::decode_table_lds_bytes(s, p, page_size) > 64 * 1024) return TA03_ERR_UNSUPPORTED;
     const hipError_t e = ta03::launch_decode(q, k_pool, v_pool, kv_pos, out, lse, s, p,
                                              static_cast<float*>(workspace), stream,
                                              block_table, page_size, num_pages);
     return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
+}
+
+int attn_set_kernel_override(int knob, int value) {
+    switch (knob) {
+        case TA03_OVERRIDE_PREFILL_ROWS:
+            if (value != 0 && value != 16 && value != 32) return TA03_ERR_SHAPE;
+            ta03::g_prefill_rows.store(value, std::memory_order_relaxed);
+            return TA03_OK;
+        case TA03_OVERRIDE_BWD_PATH:
+            if (value < 0 || value > 2) return TA03_ERR_SHAPE;
+            ta03::g_bwd_path.store(value, std::memory_order_relaxed);
+            return TA03_OK;
+        default:
+            return TA03_ERR_SHAPE;
+    }
 }
 
 const char* attn_strerror(int status) {

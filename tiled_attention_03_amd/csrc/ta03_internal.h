@@ -7,6 +7,20 @@
 
 namespace ta03 {
 
+// Compute units of the current device, queried once per device
+// (hipDeviceAttributeMultiprocessorCount) and cached; 256 if no device
+// answers. The launch heuristics (key splits, kernel choice, split counts)
+// size their grids with it.
+int device_cu_count();
+
+// Kernel-choice overrides set through attn_set_kernel_override (testing
+// only: every shape can be run through each kernel). 0 = automatic.
+//   prefill_rows: 16 or 32 forces the 16-row or the 32-row prefill kernel;
+//   bwd_path: 1 stored dS (when the workspace holds every tile), 2 the
+//   recompute path.
+int override_prefill_rows();
+int override_bwd_path();
+
 struct PrefillShape {
     int q_seq, kv_len, num_heads, num_kv_heads, head_dim;
     int causal, start_pos;  // start_pos: causal position of row 0 of q/out
@@ -21,28 +35,28 @@ struct DecodeShape {
     float scale;
 };
 
-// Split-KV plan of the decode path; a pure function of the sizes so that the
-// workspace query and the launch agree.
+// Split-KV plan of the decode path; a pure function of the sizes and the
+// block count aimed at (the device's compute units), so that the workspace
+// query and the launch agree on one device.
 struct DecodePlan {
-    int group;          // query heads per KV head
-    int heads_per_blk;  // query heads one block serves (<= 4)
-    int blks_per_kv;    // blocks per KV head along the head axis
-    int n_splits;       // splits of the cache axis
-    size_t cnt_offset;  // floats from the workspace start to the ticket counters
-    size_t n_counters;  // words of the counter region: one ticket per (kv head, head block),
-                        // each in its own slot
-    size_t ws_floats;   // workspace size in floats
+    int group;           // query heads per KV head
+    int heads_per_blk;   // query heads one block serves (<= 4)
+    int blks_per_kv;     // blocks per KV head along the head axis
+    int n_splits;        // splits of the cache axis
+    size_t n_counters;   // words of the counter region at the workspace start: one ticket
+                         // per (kv head, head block), each in its own 256-byte slot
+    size_t part_offset;  // floats from the workspace start to the split partials
+    size_t ws_floats;    // workspace size in floats
 };
 
-DecodePlan decode_plan(const DecodeShape& s);
+DecodePlan decode_plan(const DecodeShape& s, int target_blocks);
 
 hipError_t launch_prefill(const float* q, const float* k, const float* v, float* out,
                           float* lse, const PrefillShape& s, hipStream_t stream);
 
 // 16-row variant for launches with few query rows (no rotation); chosen by
 // launch_prefill when the 32-row kernel would launch fewer blocks than there
-// are compute units, or forced by the environment variable
-// TA03_PREFILL_ROWS = 16 | 32.
+// are compute units, or forced by override_prefill_rows().
 hipError_t launch_prefill16(const float* q, const float* k, const float* v, float* out,
                             float* lse, const PrefillShape& s, hipStream_t stream);
 
