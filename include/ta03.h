@@ -275,6 +275,32 @@ int attn_decode(const float* q, const float* k_cache, const float* v_cache,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): same arguments, results and
+ * errors as attn_decode, bit for bit, without the workspace. The split
+ * partials and completion counters live in a fixed 4 MiB device array inside
+ * the library, one per GPU, held until the process ends; the call allocates
+ * nothing and frees nothing. Its first call on a device looks up that
+ * array's address and enqueues the zero fill of its counters on `stream`;
+ * every call leaves the counters at zero.
+ *
+ * Limits: at most 256 (kv head, head block) groups, i.e. num_kv_heads *
+ * ceil(group / 4) <= 256, and num_heads * n_splits * (head_dim + 2) floats of
+ * partials <= 1032192, n_splits being about the device's compute units per
+ * group (on a 256-CU device at most 133120 floats for any head count);
+ * larger shapes return TA03_ERR_WORKSPACE before any HIP call.
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or threads) race and must be ordered by the
+ * caller, as calls that share an attn_decode workspace must.
+ */
+int attn_decode_noalloc(const float* q, const float* k_cache, const float* v_cache,
+                        const uint32_t* kv_pos, float* out, float* lse, int num_heads,
+                        int num_kv_heads, int head_dim, int max_seq, float scale,
+                        hipStream_t stream);
+
+/*
  * attn_decode_paged -- attn_decode over a paged KV cache. The pages call
  * caches too long for one binding "future paged-KV work" (cera
  * attention_prefill.wgsl, header) without giving a layout; this one is:

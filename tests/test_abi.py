@@ -39,7 +39,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_bytes",
-                                    "attn_bwd_workspace_bytes_stored", "attn_decode", "attn_decode_paged",
+                                    "attn_bwd_workspace_bytes_stored", "attn_decode", "attn_decode_noalloc",
+                                    "attn_decode_paged",
                                     "attn_decode_workspace_bytes",
                                     "attn_decode_workspace_init", "attn_fwd", "attn_fwd_ex",
                                     "attn_fwd_rope", "attn_rope_table",
@@ -352,3 +353,28 @@ def test_kernel_override_validates_and_resets(lib):
     assert lib.attn_set_kernel_override(2, 3) == ERR_SHAPE
     assert lib.attn_set_kernel_override(3, 0) == ERR_SHAPE
     assert lib.attn_set_kernel_override(0, 0) == ERR_SHAPE
+
+
+def noalloc(lib, q=A, k=B, v=C, pos=O, out=O + 0x1000, lse=None, H=32, Hkv=8, d=128,
+            max_seq=8192, scale=0.088):
+    return lib.attn_decode_noalloc(q, k, v, pos, out, lse, H, Hkv, d, max_seq, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ERR_NULL),
+    (dict(k=None), ERR_NULL),
+    (dict(pos=None), ERR_NULL),
+    (dict(out=None), ERR_NULL),
+    (dict(H=32, Hkv=7), ERR_SHAPE),
+    (dict(max_seq=0), ERR_SHAPE),
+    (dict(scale=float("nan")), ERR_SHAPE),
+    (dict(d=96), ERR_UNSUP),
+    (dict(q=A + 4), ERR_ALIGN),
+    (dict(pos=O + 2), ERR_ALIGN),
+    (dict(lse=O + 8), ERR_ALIGN),
+    # beyond the fixed scratch's 256 counter slots: 512 (kv head, head block) groups
+    (dict(H=512, Hkv=512, d=64, max_seq=1024), ERR_WS),
+    (dict(H=2048, Hkv=256, d=64, max_seq=1024), ERR_WS),
+])
+def test_attn_decode_noalloc_rejects_on_host(lib, kw, status):
+    assert noalloc(lib, **kw) == status

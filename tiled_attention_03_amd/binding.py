@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_workspace_init.restype = I
         L.attn_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P, S, P]
         L.attn_decode.restype = I
+        L.attn_decode_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P]
+        L.attn_decode_noalloc.restype = I
         L.attn_decode_paged.argtypes = [P, P, P, I, I, P, P, P, P, I, I, I, I, F, P, S, P]
         L.attn_decode_paged.restype = I
         L.attn_set_kernel_override.argtypes = [I, I]
@@ -317,6 +319,24 @@ def attn_decode(q, k_cache, v_cache, kv_pos, out, lse, num_heads: int, num_kv_he
         _ptr(v_cache, max_seq * kvd, "v_cache"), kvp, _ptr(out, qd, "out"),
         _ptr(lse, num_heads * 2, "lse"), num_heads, num_kv_heads, head_dim, max_seq,
         float(scale), wsp, int(workspace_bytes), _stream(stream))
+    _check(status)
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, kv_pos, out, lse, num_heads: int,
+                        num_kv_heads: int, head_dim: int, max_seq: int, scale: float,
+                        stream=None) -> None:
+    """Enqueue the single-token decode without a workspace: the library's own
+    fixed device scratch holds the split partials (see include/ta03.h)."""
+    import torch
+    qd, kvd = num_heads * head_dim, num_kv_heads * head_dim
+    kvp = _ptr(kv_pos, 1, "kv_pos",
+               dtype_name="int32" if kv_pos.dtype == torch.int32 else "uint32") \
+        if isinstance(kv_pos, torch.Tensor) else kv_pos
+    status = lib().attn_decode_noalloc(
+        _ptr(q, qd, "q"), _ptr(k_cache, max_seq * kvd, "k_cache"),
+        _ptr(v_cache, max_seq * kvd, "v_cache"), kvp, _ptr(out, qd, "out"),
+        _ptr(lse, num_heads * 2, "lse"), num_heads, num_kv_heads, head_dim, max_seq,
+        float(scale), _stream(stream))
     _check(status)
 
 

@@ -48,7 +48,19 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "ta03_internal.h"
+
+// Scratch of the allocation-free decode entry point (attn_decode_noalloc):
+// one copy per device, held until the process ends. Host code never names
+// it directly: the array's name on the host is a stand-in, not a device
+// address, so its device address is looked up once per device
+// (hipGetSymbolAddress) and that pointer is what the kernels get. Layout: a
+// fixed counter region of kNoallocCounterWords words (one ticket slot per
+// (kv head, head block), zero-filled once per device, left at zero by every
+// call), then the split partials.
+static __device__ __align__(256) float scratch[ta03::kNoallocScratchFloats];
 
 namespace ta03 {
 namespace {
@@ -545,6 +557,34 @@ hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t str
     hipLaunchKernelGGL(zero_counters_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        stream, c, n);
     return hipGetLastError();
+}
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[64];  // per device: device address of `scratch`, zero-filled counters
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t stream, float** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        // The counters must start at zero: one fill kernel on the caller's
+        // stream, ahead of the first decode there (no memset node).
+        const int n = (int)kNoallocCounterWords;
+        hipLaunchKernelGGL(zero_counters_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           stream, static_cast<unsigned int*>(p), n);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 size_t decode_table_lds_bytes(const DecodeShape& s, const DecodePlan& p, int page_size) {

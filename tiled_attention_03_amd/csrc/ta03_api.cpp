@@ -260,6 +260,37 @@ int attn_decode(const float* q, const float* k_cache, const float* v_cache,
     return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
 }
 
+int attn_decode_noalloc(const float* q, const float* k_cache, const float* v_cache,
+                        const uint32_t* kv_pos, float* out, float* lse, int num_heads,
+                        int num_kv_heads, int head_dim, int max_seq, float scale,
+                        hipStream_t stream) {
+    if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0 || max_seq < 1)
+        return TA03_ERR_SHAPE;
+    if (!std::isfinite(scale)) return TA03_ERR_SHAPE;
+    if (!head_dim_supported(head_dim)) return TA03_ERR_UNSUPPORTED;
+    if ((long long)max_seq * num_kv_heads * head_dim >= kMaxElems) return TA03_ERR_UNSUPPORTED;
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || kv_pos == nullptr ||
+        out == nullptr)
+        return TA03_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(lse) || (reinterpret_cast<uintptr_t>(kv_pos) & 3u) != 0)
+        return TA03_ERR_ALIGN;
+    ta03::DecodeShape s{num_heads, num_kv_heads, head_dim, max_seq, scale};
+    ta03::DecodePlan p = ta03::decode_plan(s, ta03::device_cu_count());
+    // The scratch's own layout: the fixed counter region, then the partials.
+    const size_t partials = p.ws_floats - p.part_offset;
+    if (p.n_counters > ta03::kNoallocCounterWords ||
+        partials > ta03::kNoallocScratchFloats - ta03::kNoallocCounterWords)
+        return TA03_ERR_WORKSPACE;
+    p.part_offset = ta03::kNoallocCounterWords;
+    p.ws_floats = ta03::kNoallocCounterWords + partials;
+    float* ws = nullptr;
+    hipError_t e = ta03::noalloc_scratch(stream, &ws);
+    if (e != hipSuccess) return TA03_ERR_HIP;
+    e = ta03::launch_decode(q, k_cache, v_cache, kv_pos, out, lse, s, p, ws, stream);
+    return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
+}
+
 int attn_decode_paged(const float* q, const float* k_pool, const float* v_pool, int num_pages,
                       int page_size, const int32_t* block_table, const uint32_t* kv_pos,
                       float* out, float* lse, int num_heads, int num_kv_heads, int head_dim,

@@ -106,6 +106,17 @@ hipError_t launch_rope_table(float* cs, int rows, int head_dim, double theta, hi
 
 hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t stream);
 
+// Fixed-size device scratch of the allocation-free decode (4 MiB per device):
+// a counter region of kNoallocCounterWords words (256 ticket slots of 64
+// words), then at most kNoallocScratchFloats - kNoallocCounterWords floats of
+// split partials.
+constexpr size_t kNoallocScratchFloats = (size_t)1 << 20;
+constexpr size_t kNoallocCounterWords = 256 * 64;
+// The current device's scratch (its device address, looked up once per
+// device; the first call also enqueues the zero fill of its counters on
+// `stream`).
+hipError_t noalloc_scratch(hipStream_t stream, float** ptr);
+
 // Dynamic LDS a paged decode launch needs for its page-table slice.
 size_t decode_table_lds_bytes(const DecodeShape& s, const DecodePlan& p, int page_size);
 
