@@ -152,6 +152,18 @@ def time_calls(fn, n, torch, clock=None):
     return float(np.mean(durs)), float(np.min(durs)), wall
 
 
+def warm_replays(graph, torch, seconds=0.15):
+    """Replay a captured graph back to back for about `seconds` of wall time
+    before a short timed region, so that the GPU runs at its steady clock
+    (a few milliseconds of timed work after an idle gap otherwise catch the
+    clock still rising; the long prefill steps do not need this)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            graph.replay()
+        torch.cuda.synchronize()
+
+
 def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None,
                   fused_qkv=False, clock=None):
     """Prefill timing. With graph_replays > 0 the call is captured once in a
@@ -212,7 +224,7 @@ def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None,
         with torch.cuda.graph(graph):
             for i in range(steps):
                 call(i)
-        graph.replay()
+        warm_replays(graph, torch)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -318,8 +330,7 @@ def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8, page_size=None,
     res = {}
     for kv_pos in kv_pos_values:
         pos.fill_(kv_pos)
-        for _ in range(3):
-            graph.replay()
+        warm_replays(graph, torch, 0.05)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -334,6 +345,73 @@ def bench_decode(w, kv_pos_values, replays, torch, ta, copies=8, page_size=None,
         res[str(kv_pos)] = {"us": round(per_call * 1e6, 2),
                             "GB/s": round(b / per_call / 1e9, 1),
                             "frac": round(b / per_call / 1e9 / HBM_PEAK_GBPS, 4)}
+    return res
+
+
+def bench_decode_read(w, kv_pos_values, replays, torch, copies=8, device_pos=False):
+    """Read ceiling of the decode's access pattern, measured the way the
+    decode is: the read-only probe kernel (libta03_probe.so: the decode's
+    grid, 64-key units, per-lane load shapes and two register sets, no math,
+    no merge) over the same 8 rotated caches, captured in one graph and
+    replayed. Same algorithmic bytes as the decode. The cache length is
+    passed from the host, or with device_pos read from device memory first,
+    as the decode reads kv_pos."""
+    import ctypes
+    from tiled_attention_03_amd import binding
+    binding.lib()  # torch's HIP runtime and libta03.so first
+    probe = ctypes.CDLL(os.path.join(ROOT, "tiled_attention_03_amd", "libta03_probe.so"))
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    probe.ta03_probe_decode_read_sink_floats.argtypes = [I, I, I, I]
+    probe.ta03_probe_decode_read_sink_floats.restype = S
+    probe.ta03_probe_decode_read.argtypes = [P, P, P, I, I, I, I, I, I, P, S, P]
+    probe.ta03_probe_decode_read.restype = I
+    dev = torch.device("cuda:0")
+    _, k, v = inputs.make_decode(w)
+    k0, v0 = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)
+    del k, v
+    caches = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    nsink = probe.ta03_probe_decode_read_sink_floats(w.num_heads, w.num_kv_heads, w.head_dim,
+                                                     w.max_seq)
+    sink = torch.empty(max(int(nsink), 1), device=dev)
+    res = {}
+    pos = torch.zeros(1, dtype=torch.int32, device=dev)
+    for kv_pos in kv_pos_values:
+        kv_len = min(kv_pos + 1, w.max_seq)
+        pos.fill_(kv_pos)
+
+        def call(i):
+            kc, vc = caches[i % copies]
+            st = probe.ta03_probe_decode_read(
+                kc.data_ptr(), vc.data_ptr(), pos.data_ptr() if device_pos else None, kv_len,
+                w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq, 0, sink.data_ptr(),
+                int(nsink), torch.cuda.current_stream().cuda_stream)
+            assert st == 0, f"read probe status {st}"
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(copies):
+                call(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(copies):
+                call(i)
+        warm_replays(graph, torch, 0.05)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(replays):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        per_call = start.elapsed_time(end) * 1e-3 / (replays * copies)
+        b = decode_bytes(w, kv_pos)
+        res[str(kv_pos)] = {"us": round(per_call * 1e6, 2),
+                            "GB/s": round(b / per_call / 1e9, 1)}
+        del graph
     return res
 
 
@@ -563,7 +641,14 @@ def main():
         clk_decode = ClockSampler(period=0.005)
         d = bench_decode(wd, wd.kv_pos_values, 25, torch, ta, clock=clk_decode)
         clocks["decode"] = clk_decode.summary()
+        rd = bench_decode_read(wd, wd.kv_pos_values, 25, torch)
+        rdp = bench_decode_read(wd, wd.kv_pos_values, 25, torch, device_pos=True)
+        for key, r in rd.items():
+            d[key]["read_probe_us"] = r["us"]
+            d[key]["vs_read_probe"] = round(d[key]["us"] / r["us"], 3)
+            d[key]["read_probe_device_pos_us"] = rdp[key]["us"]
         head = d[str(wd.kv_pos_values[-1])]
+        head_read = rd[str(wd.kv_pos_values[-1])]
         result["decode"] = {
             "workload": wd.name, "unit": "GB/s", "kv_pos": d,
             "roofline": {"bound": "hbm", "achieved": head["GB/s"], "peak": HBM_PEAK_GBPS,
@@ -571,6 +656,12 @@ def main():
                          "traffic": stored_traffic(DECODE_TRAFFIC),
                          "kernel": "decode_kernel<128>",
                          "kv_pos": wd.kv_pos_values[-1],
+                         "read_ceiling_GBps": head_read["GB/s"],
+                         "read_ceiling_us": head_read["us"],
+                         "read_ceiling_kernel": "decode_read_kernel<128> (libta03_probe.so), "
+                                                "cache length from the host",
+                         "read_ceiling_device_pos_us": rdp[str(wd.kv_pos_values[-1])]["us"],
+                         "vs_read_ceiling": round(head["us"] / head_read["us"], 3),
                          "measured_copy_GBps": copy_ceiling(torch)}}
         print(f"[bench] decode {d}", flush=True)
         if not args.no_reported:

@@ -286,9 +286,9 @@ int attn_decode(const float* q, const float* k_cache, const float* v_cache,
  * every call leaves the counters at zero.
  *
  * Limits: at most 256 (kv head, head block) groups, i.e. num_kv_heads *
- * ceil(group / 4) <= 256, and num_heads * n_splits * (head_dim + 2) floats of
+ * ceil(group / 4) <= 256, and num_heads * n_splits * (head_dim + 4) floats of
  * partials <= 1032192, n_splits being about the device's compute units per
- * group (on a 256-CU device at most 133120 floats for any head count);
+ * group (on a 256-CU device at most 135168 floats for any head count);
  * larger shapes return TA03_ERR_WORKSPACE before any HIP call.
  *
  * Every call on one GPU shares that GPU's array: calls that may overlap on

@@ -305,8 +305,9 @@ def test_workspace_bytes(lib):
     n = f(32, 8, 128, 8192)
     assert n > 0 and n % 16 == 0
     # one split for a one-row cache: one counter per KV head in a 256-byte
-    # slot, then per head a head_dim row plus (max, sum), rounded up to 256 bytes
-    assert f(32, 8, 128, 1) == 8 * 256 + (32 * 130 * 4 + 255) // 256 * 256
+    # slot, then per head a head_dim row plus (max, sum) and two pad floats,
+    # rounded up to 256 bytes
+    assert f(32, 8, 128, 1) == 8 * 256 + (32 * 132 * 4 + 255) // 256 * 256
     assert f(32, 7, 128, 8192) == 0
     assert f(32, 8, 96, 8192) == 0
     assert f(32, 8, 128, 0) == 0

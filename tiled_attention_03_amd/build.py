@@ -16,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libta03.so")
+PROBE_LIB = os.path.join(PKG, "libta03_probe.so")
 
 SOURCES = ["ta03_api.cpp", "prefill.hip", "prefill16.hip", "decode.hip", "rope.hip",
            "backward.hip"]
@@ -57,6 +58,22 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    # The benchmark's read-ceiling probe: a separate library on top of
+    # libta03.so (it uses the decode's launch plan), never loaded by the
+    # product path.
+    src = "probe_decode_read.hip"
+    obj = os.path.join(build_dir, "probe_decode_read.o")
+    cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", obj, "-L", PKG, "-lta03",
+           "-Wl,-rpath,$ORIGIN", "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -398,7 +398,7 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     __syncthreads();
 
     // Block partial per head: combine the 4 waves with log-sum-exp weights.
-    const size_t row = D + 2;
+    const size_t row = D + 4;
     if (n_active == 1) {
         // One split covers the cache: this block's partial is the result.
         for (int i = tid; i < nh * D; i += kBlock) {
@@ -421,8 +421,9 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
         }
         return;
     }
-    // Two columns per thread, published with 64-bit stores (rows are D + 2
-    // floats, so every pair starts 8-byte aligned).
+    // Two columns per thread, published with 64-bit stores. A partial row is
+    // D + 4 floats (the output row, then max and sum, then two pad floats), so
+    // rows start 16-byte aligned for the merge's 128-bit loads.
     for (int i = tid; i < nh * D / 2; i += kBlock) {
         const int h = 2 * i / D, d = 2 * i % D;
         float M = Mw[0][h];
@@ -464,38 +465,44 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
     __syncthreads();
     if (!last_flag) return;
 
-    // Merge: wave h serves head head0 + h, each lane D/64 columns. Splits go
-    // in batches of 32: lane j (and j + 32) loads the (max, sum) pair of
-    // split j of the batch, every lane loads its columns of all 32 partial
-    // rows (33 loads, one round trip), the batch max and the weights
-    // w_j = 2^(m_j - M) come from cross-lane steps, and each w_j reaches the
-    // column sums through a lane read. Across batches the running (M, L, o)
-    // is rescaled as in the online update. Indices past the last split are
-    // clamped to it (no load sits behind a branch) and their weight is 0.
+    // Merge: wave h serves head head0 + h. Splits go in batches of 32: lane
+    // j (and j + 32) loads the (max, sum) pair of split j of the batch; the
+    // partial rows come in 16-byte loads, lane l taking columns
+    // 4 (l % (D/4)) .. + 3 of split slot l / (D/4), so one instruction covers
+    // 64 / (D/4) splits (17 or 9 loads per lane per batch, one round trip;
+    // 64-bit loads of 2 columns per split took 33). The batch max and the
+    // weights w_j = 2^(m_j - M) come from cross-lane steps, each w_j reaches
+    // the lanes of its slot through lane reads, and the slots are summed at
+    // the end by half-row / half-wave swaps. Across batches the running
+    // (M, L, o) is rescaled as in the online update. Indices past the last
+    // split are clamped to it (no load sits behind a branch) and their
+    // weight is 0. The partial loads are buffer loads with the sc1 policy:
+    // coherent with the other blocks' agent-scope stores (a line this XCD's
+    // L2 kept from an earlier call is not used), like the agent-scope atomic
+    // loads of the (max, sum) pairs.
     if (wave < nh) {
-        constexpr int DPL = D / 64;
+        constexpr int LPS = D / 4;     // lanes per split row (one float4 each)
+        constexpr int SPI = 64 / LPS;  // splits per load instruction
         constexpr int NB = 32;
         const int head = head0 + wave;
         const float* hb = ws + a.part_offset + (size_t)head * a.n_splits * row;
         const int lj = lane & (NB - 1);
-        float M = kNegBig, L = 0.f, o[DPL];
-#pragma unroll
-        for (int c = 0; c < DPL; ++c) o[c] = 0.f;
+        const int sub = lane / LPS;
+        const int c4 = 4 * (lane % LPS);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(hb), 0, (int)(a.n_splits * row * 4), 0x00020000);
+        float M = kNegBig, L = 0.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s0 = 0; s0 < n_active; s0 += NB) {
             const bool live = s0 + lj < n_active;
             const float2 ml = load_pair(hb + (size_t)min(s0 + lj, n_active - 1) * row + D);
-            float ov[NB][DPL];
+            float4 ov[NB / SPI];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const float* p = hb + (size_t)min(s0 + j, n_active - 1) * row + lane * DPL;
-                if constexpr (DPL == 2) {
-                    const float2 x = load_pair(p);
-                    ov[j][0] = x.x;
-                    ov[j][1] = x.y;
-                } else {
-                    ov[j][0] = __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-                }
+            for (int i = 0; i < NB / SPI; ++i) {
+                const int s = min(s0 + i * SPI + sub, n_active - 1);
+                const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (s * (int)row + c4) * 4, 0, 16);
+                ov[i] = make_float4(__int_as_float(x[0]), __int_as_float(x[1]), __int_as_float(x[2]),
+                                    __int_as_float(x[3]));
             }
             const float mj = live ? ml.x : kNegBig;
             const float bm = fmaxf(M, max32(mj));
@@ -503,18 +510,30 @@ decode_kernel(const float* __restrict__ q, const float* __restrict__ k,
             M = bm;
             const float wj = live ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
             L = fmaf(L, r, sum32(ml.y * wj));
+            o.x *= r; o.y *= r; o.z *= r; o.w *= r;
 #pragma unroll
-            for (int c = 0; c < DPL; ++c) o[c] *= r;
+            for (int i = 0; i < NB / SPI; ++i) {
+                float w = 0.f;
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
-#pragma unroll
-                for (int c = 0; c < DPL; ++c) o[c] = fmaf(ov[j][c], w, o[c]);
+                for (int q2 = 0; q2 < SPI; ++q2) {
+                    const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), i * SPI + q2));
+                    w = sub == q2 ? wq : w;
+                }
+                o.x = fmaf(ov[i].x, w, o.x);
+                o.y = fmaf(ov[i].y, w, o.y);
+                o.z = fmaf(ov[i].z, w, o.z);
+                o.w = fmaf(ov[i].w, w, o.w);
             }
         }
+        // sum over the SPI split slots (lane groups LPS apart)
+        if constexpr (SPI == 4) {
+            o.x = pair_sum16(o.x); o.y = pair_sum16(o.y); o.z = pair_sum16(o.z); o.w = pair_sum16(o.w);
+        }
+        o.x = pair_sum32(o.x); o.y = pair_sum32(o.y); o.z = pair_sum32(o.z); o.w = pair_sum32(o.w);
         const float inv = 1.0f / L;
-#pragma unroll
-        for (int c = 0; c < DPL; ++c) out[(size_t)head * D + lane * DPL + c] = o[c] * inv;
+        if (lane < LPS)
+            *reinterpret_cast<float4*>(out + (size_t)head * D + c4) =
+                make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
         if (lse != nullptr && lane == 0) {
             lse[2 * head] = M * kLn2;
             lse[2 * head + 1] = __logf(L);
@@ -546,7 +565,7 @@ DecodePlan decode_plan(const DecodeShape& s, int target_blocks) {
     // a zero fill needs no split count), then the partials.
     p.n_counters = (size_t)rows * kCntStride;
     p.part_offset = p.n_counters;
-    const size_t part = (size_t)s.num_heads * (size_t)p.n_splits * (size_t)(s.head_dim + 2);
+    const size_t part = (size_t)s.num_heads * (size_t)p.n_splits * (size_t)(s.head_dim + 4);
     p.ws_floats = p.part_offset + (part + kCntStride - 1) / kCntStride * kCntStride;
     return p;
 }
