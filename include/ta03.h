@@ -188,19 +188,25 @@ int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStr
  *                 keys no row sees)
  *   mode, start_pos, scale  as the forward
  *   workspace     device scratch, 16-byte aligned, overwritten: at least
- *                 attn_bwd_workspace_bytes(q_seq, num_heads) bytes (D_i);
- *                 with attn_bwd_workspace_bytes_stored(q_seq, kv_len,
- *                 num_heads, mode, start_pos) bytes or more it also holds
- *                 every score gradient dS_ij of the call in 16 x 16 tiles
- *                 (4 bytes per (row, key) pair in the windows, per head,
- *                 rounded up to whole tiles), which lets dq be formed from
- *                 them instead of recomputing the scores
+ *                 attn_bwd_workspace_bytes(q_seq, num_heads) bytes (D_i).
+ *                 The bytes past that hold score gradients dS_ij in 16 x 16
+ *                 tiles (1 KiB per tile and head), which lets dq be formed
+ *                 from them instead of recomputing the scores:
+ *                 attn_bwd_workspace_bytes_stored(q_seq, kv_len, num_heads,
+ *                 mode, start_pos) bytes hold every tile of the call (4 bytes
+ *                 per (row, key) pair in the windows, per head, rounded up to
+ *                 whole tiles); any smaller workspace that holds the tiles of
+ *                 the call's longest 16-row query tile runs the stored path in
+ *                 windows of whole query tiles
  *
- * Stored path: three kernel launches (D_i; dk, dv and the dS tiles; dq from
- * the tiles). Otherwise two (dq with D_i, recomputing the scores; dk, dv).
- * The stored path is taken when the workspace holds the tiles and the call
- * is long enough for it to pay: the dq grid over the tiles has at least 256
- * blocks of 4 waves (one per compute unit); shorter calls recompute.
+ * Stored path: D_i, then per window of query tiles the dk/dv kernel over the
+ * window's rows, storing its dS tiles (dk, dv written by the first window,
+ * added to by the later ones), and dq of the window's rows from the tiles
+ * (three launches when every tile fits). Recompute path: two launches (dq
+ * with D_i, recomputing the scores; dk, dv). The stored path is taken when
+ * the call is long enough for it to pay (the dq grid over the tiles fills the
+ * device's compute units) and the workspace needs at most 64 windows;
+ * otherwise the call recomputes.
  * attn_set_kernel_override can force either path (testing). Both
  * paths run on stream with no allocation and no atomics (results are
  * run-to-run identical; the two paths agree to rounding). Errors: as attn_fwd for the sizes and mode;

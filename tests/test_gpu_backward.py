@@ -17,12 +17,26 @@ pytestmark = pytest.mark.gpu
 CAUSAL, FULL, CROSS = inputs.CAUSAL, inputs.FULL, inputs.CROSS
 
 
+def windowed_bytes(n, kv_len, H, mode, start_pos, parts=3):
+    """Workspace for the stored path in windows: the D_i scratch plus about
+    1/parts of the call's dS tiles, and at least the tiles of its longest
+    query tile (16 x 16 tiles of 1 KiB per head; query tile t of a causal call
+    spans the keys of its last row's window)."""
+    per_qt = []
+    for t in range((n + 15) // 16):
+        hi = min(16 * t + 16, n)
+        w = min(start_pos + hi, kv_len) if mode == CAUSAL else kv_len
+        per_qt.append((w + 15) // 16)
+    cap = max(max(per_qt), -(-sum(per_qt) // parts))
+    return ta.attn_bwd_workspace_bytes(n, H) + cap * H * 1024
+
+
 def gpu_fwd_bwd(q, k, v, g, *, num_heads, num_kv_heads, head_dim, mode, kv_len, start_pos,
-                scale, poison=True, stored=True, ws_short=0):
+                scale, poison=True, stored=True, ws_short=0, ws_bytes=None):
     """GPU forward (out, lse), then attn_bwd; outputs and workspace pre-filled
     with NaN so that an element the kernels skip (or a tile they never write)
     shows. stored: workspace for the stored-dS path, else the minimal one;
-    ws_short: bytes taken off the stored size."""
+    ws_short: bytes taken off the stored size; ws_bytes: this many bytes."""
     import torch
     dev = device()
     H, Hkv, d = num_heads, num_kv_heads, head_dim
@@ -38,6 +52,8 @@ def gpu_fwd_bwd(q, k, v, g, *, num_heads, num_kv_heads, head_dim, mode, kv_len, 
     if stored:
         nbytes = max(nbytes, ta.attn_bwd_workspace_bytes_stored(n, kv_len, H, mode, start_pos)
                      - ws_short)
+    if ws_bytes is not None:
+        nbytes = ws_bytes
     ws = torch.full((max(nbytes, 4) // 4,), fill, device=dev)
     ta.attn_bwd(qd, kd, vd, out, gd, lse, dq, dk, dv, n, kv_len, H, Hkv, d, mode, start_pos,
                 scale, ws, nbytes)
@@ -50,17 +66,24 @@ def _kw(w):
                 mode=w.mode, kv_len=w.kv_len, start_pos=w.start_pos, scale=w.scale)
 
 
-# Backward paths: "stored" (workspace for the dS tiles, the stored path
+# Backward paths: "stored" (workspace for every dS tile, the stored path
 # forced by the library's kernel-choice override even where its size rule
-# would recompute; dq from the tiles) and "recompute" (minimal workspace; dq
-# recomputes the scores, 16-key dk/dv kernel).
-PATHS = ["stored", "recompute"]
+# would recompute; dq from the tiles), "windows" (the same with a workspace
+# for about a third of the tiles: the stored path in windows of query tiles)
+# and "recompute" (minimal workspace; dq recomputes the scores, 16-key dk/dv
+# kernel).
+PATHS = ["stored", "windows", "recompute"]
 
 
 def _use_path(path, kernel_override):
-    if path == "stored":
+    if path in ("stored", "windows"):
         kernel_override(ta.OVERRIDE_BWD_PATH, 1)
-    return path == "stored"
+    return path != "recompute"
+
+
+def _ws_for(path, w):
+    return (windowed_bytes(w.q_seq, w.kv_len, w.num_heads, w.mode, w.start_pos)
+            if path == "windows" else None)
 
 
 def _check_all(got, ref, w, what):
@@ -79,7 +102,7 @@ def test_backward_pages_workloads(w, path, kernel_override):
     log(f"backward parity {w.name} path={path}")
     q, k, v = inputs.make_prefill(w)
     g = inputs.normal(q.shape, w.seed_base + 7)
-    got = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
+    got = gpu_fwd_bwd(q, k, v, g, stored=stored, ws_bytes=_ws_for(path, w), **_kw(w))
     ref = oracle.attention_backward(q, k, v, g, magnitudes=True, **_kw(w))
     e = _check_all(got, ref, w, w.name)
     log("  max|d| dq={:.2e} dk={:.2e} dv={:.2e}".format(*e))
@@ -115,7 +138,9 @@ def test_backward_long_causal_sampled(path, kernel_override):
     log(f"backward parity (sampled) {w.name} path={path}")
     q, k, v = inputs.make_prefill(w)
     g = inputs.normal(q.shape, w.seed_base + 7)
-    dq, dk, dv = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
+    # windows: the benchmark's bounded workspace (2 GB, about 9 windows)
+    ws = 2_000_000_000 if path == "windows" else None
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, g, stored=stored, ws_bytes=ws, **_kw(w))
     assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
     rows, keys, (rq, rk, rv, mq, mk, mv) = _long_causal_reference(w, q, k, v, g)
     n_rows = w.q_seq * w.group
@@ -156,21 +181,27 @@ def test_backward_ragged_sweep(case, path, kernel_override):
     k[kv:] = np.nan  # rows past kv_len must never be read into a result
     v[kv:] = np.nan
     g = inputs.normal(q.shape, 1101 + n)
-    got = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
+    got = gpu_fwd_bwd(q, k, v, g, stored=stored, ws_bytes=_ws_for(path, w), **_kw(w))
     ref = oracle.attention_backward(q, k, v, g, magnitudes=True, **_kw(w))
     _check_all(got, ref, w, str(case))
 
 
-def test_backward_workspace_short_of_stored_falls_back(kernel_override):
-    """A workspace one tile short of the stored size takes the recompute
-    path even when the stored path is asked for: same gradients as the
-    minimal workspace, bit for bit."""
+def test_backward_workspace_short_of_stored_runs_windows(kernel_override):
+    """A workspace one tile short of the stored size runs the stored path in
+    windows (checked against the checker); one too small for the tiles of the
+    longest query tile recomputes: same gradients as the minimal workspace,
+    bit for bit."""
     kernel_override(ta.OVERRIDE_BWD_PATH, 1)
     w, q, k, v = inputs.random_case(1120, CAUSAL, 90, 120, 4, 2, 64, start_pos=30)
     g = inputs.normal(q.shape, 1121)
     a = gpu_fwd_bwd(q, k, v, g, stored=True, ws_short=1024, **_kw(w))
-    b = gpu_fwd_bwd(q, k, v, g, stored=False, **_kw(w))
-    for x, y in zip(a, b):
+    ref = oracle.attention_backward(q, k, v, g, magnitudes=True, **_kw(w))
+    _check_all(a, ref, w, "one tile short")
+    base = ta.attn_bwd_workspace_bytes(w.q_seq, w.num_heads)
+    longest = (min(w.start_pos + w.q_seq, w.kv_len) + 15) // 16  # tiles of the last query tile
+    b = gpu_fwd_bwd(q, k, v, g, ws_bytes=base + (longest - 1) * w.num_heads * 1024, **_kw(w))
+    c = gpu_fwd_bwd(q, k, v, g, stored=False, **_kw(w))
+    for x, y in zip(b, c):
         assert np.array_equal(x, y)
 
 
@@ -213,24 +244,22 @@ def test_backward_zero_keys():
     assert np.array_equal(dq, np.zeros_like(dq)) and dk.size == 0 and dv.size == 0
 
 
-@pytest.mark.parametrize("stored", [True, False])
-def test_backward_deterministic(stored, kernel_override):
-    if stored:
-        kernel_override(ta.OVERRIDE_BWD_PATH, 1)
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_deterministic(path, kernel_override):
+    stored = _use_path(path, kernel_override)
     w, q, k, v = inputs.random_case(1180, CAUSAL, 300, 300, 8, 2, 128)
     g = inputs.normal(q.shape, 1181)
-    a = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
-    b = gpu_fwd_bwd(q, k, v, g, stored=stored, **_kw(w))
+    a = gpu_fwd_bwd(q, k, v, g, stored=stored, ws_bytes=_ws_for(path, w), **_kw(w))
+    b = gpu_fwd_bwd(q, k, v, g, stored=stored, ws_bytes=_ws_for(path, w), **_kw(w))
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("stored", [True, False])
-def test_backward_graph_replay(stored, kernel_override):
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_graph_replay(path, kernel_override):
     """Forward and backward captured in one graph, replayed with the
     program's own work in between: every replay matches the eager result."""
-    if stored:
-        kernel_override(ta.OVERRIDE_BWD_PATH, 1)
+    stored = _use_path(path, kernel_override)
     import torch
     H, Hkv, d, n = 8, 2, 64, 160
     w, q, k, v = inputs.random_case(1190, CAUSAL, n, n, H, Hkv, d)
@@ -244,6 +273,8 @@ def test_backward_graph_replay(stored, kernel_override):
     dv = torch.empty((n, Hkv * d), device=dev)
     nbytes = (ta.attn_bwd_workspace_bytes_stored(n, n, H, CAUSAL, 0) if stored
               else ta.attn_bwd_workspace_bytes(n, H))
+    if path == "windows":
+        nbytes = windowed_bytes(n, n, H, CAUSAL, 0)
     ws = torch.empty((nbytes // 4,), device=dev)
 
     def step():

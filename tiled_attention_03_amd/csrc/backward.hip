@@ -84,7 +84,14 @@ struct BwdArgs {
     float scale;
     int hg, rs, ks, n_head_blocks, n_row_blocks;  // dq kernel block shape (ks: key splits)
     DsLayout ds;                              // stored dS tiles (when kept)
-    long long ds_tph;                         // dS tiles per head
+    // Window of the stored-dS launches: query tiles [qt_lo, qt_hi) (the whole
+    // range in one window when every tile fits). The window's tiles are stored
+    // per head from ds: tile (h, qt, kt) at h * ds_tph + ds_tiles_before(qt) -
+    // ds_base + kt, ds_tph being the window's tiles per head.
+    int qt_lo, qt_hi;
+    long long ds_base;
+    long long ds_tph;
+    int accumulate;  // dk/dv kernel: add to dk, dv (windows after the first)
     int dq_hg, dq_rs, dq_rt, dq_n_head_blocks, dq_n_row_blocks;  // dq-from-dS block shape
 };
 
@@ -411,9 +418,12 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         dva[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // Query tiles of the window whose rows see some key of the block (causal:
+    // rows from blk_key0 - start_pos on).
     const int i_lo = a.causal ? max(0, blk_key0 - a.start_pos) : 0;
-    const int qt0 = i_lo / k16Rows;
-    const int n_qt = i_lo < a.q_seq ? (a.q_seq + k16Rows - 1) / k16Rows - qt0 : 0;
+    const int qt0 = max(i_lo / k16Rows, a.qt_lo);
+    const int qt_end = min((a.q_seq + k16Rows - 1) / k16Rows, a.qt_hi);
+    const int n_qt = i_lo < a.q_seq && qt0 < qt_end ? qt_end - qt0 : 0;
     const int total = a.group * n_qt;
 
     auto issue1 = [&](int it, int sub, float* tb, float* vb) __attribute__((always_inline)) {
@@ -540,8 +550,8 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                     // products so they complete under them.
                     const int h = kv_head * a.group + it / n_qt;
                     const int qt = qt0 + it % n_qt;
-                    float* tile = ds + ((size_t)h * a.ds_tph + ds_tiles_before(a.ds, qt) +
-                                        key0 / k16Keys) * (k16Rows * k16Keys);
+                    float* tile = ds + ((size_t)h * a.ds_tph + ds_tiles_before(a.ds, qt) -
+                                        a.ds_base + key0 / k16Keys) * (k16Rows * k16Keys);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) tile[(4 * g + r) * k16Keys + j] = dp[r];
                 }
@@ -582,12 +592,18 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
         for (int c = 0; c < NB / 4; ++c) {
             const int d0 = 64 * c + 4 * (4 * g + r);
-            *reinterpret_cast<float4*>(krow + d0) =
-                make_float4(dka[4 * c + 0][r] * a.scale, dka[4 * c + 1][r] * a.scale,
-                            dka[4 * c + 2][r] * a.scale, dka[4 * c + 3][r] * a.scale);
-            *reinterpret_cast<float4*>(vrow + d0) =
-                make_float4(dva[4 * c + 0][r], dva[4 * c + 1][r], dva[4 * c + 2][r],
-                            dva[4 * c + 3][r]);
+            float4 kx = make_float4(dka[4 * c + 0][r] * a.scale, dka[4 * c + 1][r] * a.scale,
+                                    dka[4 * c + 2][r] * a.scale, dka[4 * c + 3][r] * a.scale);
+            float4 vx = make_float4(dva[4 * c + 0][r], dva[4 * c + 1][r], dva[4 * c + 2][r],
+                                    dva[4 * c + 3][r]);
+            if (a.accumulate) {  // block-uniform: a later window adds to the earlier ones
+                const float4 k0 = *reinterpret_cast<const float4*>(krow + d0);
+                const float4 v0 = *reinterpret_cast<const float4*>(vrow + d0);
+                kx = make_float4(k0.x + kx.x, k0.y + kx.y, k0.z + kx.z, k0.w + kx.w);
+                vx = make_float4(v0.x + vx.x, v0.y + vx.y, v0.z + vx.z, v0.w + vx.w);
+            }
+            *reinterpret_cast<float4*>(krow + d0) = kx;
+            *reinterpret_cast<float4*>(vrow + d0) = vx;
         }
     }
 }
@@ -683,10 +699,10 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     const int strip = wave / a.dq_hg;
     const int kv_head = head / a.group;
     const int kvd = a.num_kv_heads * D;
-    const int n_qt = ds_query_tiles(a.ds);
-    const int qt_first = (rb * a.dq_rs + strip) * kDqRT;
-    const int blk_qt_last = min((rb + 1) * a.dq_rs * kDqRT, n_qt) - 1;
-    const int n_kt = blk_qt_last >= 0 ? ds_tiles_in(a.ds, blk_qt_last) : 0;
+    // Query tiles of the window [qt_lo, qt_hi).
+    const int qt_first = a.qt_lo + (rb * a.dq_rs + strip) * kDqRT;
+    const int blk_qt_last = min(a.qt_lo + (rb + 1) * a.dq_rs * kDqRT, a.qt_hi) - 1;
+    const int n_kt = blk_qt_last >= a.qt_lo ? ds_tiles_in(a.ds, blk_qt_last) : 0;
 
     // Per query tile: first tile index (clamped query tile) and tile count.
     long long tbase[kDqRT];
@@ -695,10 +711,10 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
 #pragma unroll
     for (int rt = 0; rt < kDqRT; ++rt) {
         const int qt = qt_first + rt;
-        const int qc = min(qt, n_qt - 1);
-        tlive[rt] = qt < n_qt;
+        const int qc = min(qt, a.qt_hi - 1);
+        tlive[rt] = qt < a.qt_hi;
         tcount[rt] = ds_tiles_in(a.ds, qc);
-        tbase[rt] = (long long)head * a.ds_tph + ds_tiles_before(a.ds, qc);
+        tbase[rt] = (long long)head * a.ds_tph + ds_tiles_before(a.ds, qc) - a.ds_base;
     }
 
     auto issue_k = [&](int kt, float* dst) __attribute__((always_inline)) {
@@ -780,6 +796,7 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
 #pragma unroll
     for (int rt = 0; rt < kDqRT; ++rt) {
         const int qt = qt_first + rt;
+        if (qt >= a.qt_hi) break;  // wave-uniform: past the window
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = qt * k16Rows + 4 * g + r;
@@ -834,26 +851,53 @@ hipError_t launch_dkdv16_any(size_t lds, hipStream_t stream, const float* q, con
                                       ds, a);
 }
 
+// The stored-dS path over windows of query tiles (one window when the
+// workspace holds every tile): D_i once; per window the dk/dv kernel over the
+// window's rows, storing the window's dS tiles (dk, dv written by the first
+// window, which covers every key, and added to by the later ones, which
+// cover the keys their rows see), then dq of the window's rows from them.
 template <int D>
 hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, const float* o,
                              const float* dout, const float* lse, float* dq, float* dk,
-                             float* dv, float* delta, float* ds, const BwdArgs& a,
-                             hipStream_t stream) {
-    const long long n_pairs = (long long)a.q_seq * a.num_heads;
+                             float* dv, float* delta, float* ds, const BwdArgs& a0,
+                             const int* win, int n_win, int cus, hipStream_t stream) {
+    const long long n_pairs = (long long)a0.q_seq * a0.num_heads;
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((n_pairs + 15) / 16)), dim3(256), 0,
                        stream, o, dout, delta, n_pairs);
-    const size_t lds16 = 0;  // static LDS
-    const hipError_t e = launch_dkdv16_any<D, true>(lds16, stream, q, k, v, dout, lse, delta, dk,
-                                                    dv, ds, a);
-    if (e != hipSuccess) return e;
-    const size_t lds_dq = 0;  // static LDS
-    const long long grid = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks;
-    if (a.dq_rt == 4) {
-        hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 4>), dim3((unsigned)grid), dim3(256), lds_dq,
-                           stream, k, ds, dq, a);
-    } else {
-        hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 1>), dim3((unsigned)grid), dim3(256), lds_dq,
-                           stream, k, ds, dq, a);
+    const int n_qt = ds_query_tiles(a0.ds);
+    for (int w = 0; w < n_win; ++w) {
+        BwdArgs a = a0;
+        a.qt_lo = win[w];
+        a.qt_hi = win[w + 1];
+        a.ds_base = ds_tiles_before(a.ds, a.qt_lo);
+        a.ds_tph = (a.qt_hi == n_qt ? ds_tiles_per_head(a.ds) : ds_tiles_before(a.ds, a.qt_hi)) -
+                   a.ds_base;
+        a.accumulate = w > 0 ? 1 : 0;
+        // Keys the window's rows see; the first window covers every key (it
+        // writes dk, dv, zero for keys no row sees).
+        int keys = a.kv_len;
+        if (w > 0 && a.causal) {
+            const long long hi = (long long)a.start_pos + min(a.qt_hi * k16Rows, a.q_seq);
+            keys = (int)(hi < a.kv_len ? hi : a.kv_len);
+        }
+        const long long blocks =
+            (long long)a.num_kv_heads * ((keys + 4 * k16Keys - 1) / (4 * k16Keys));
+        const hipError_t e = launch_dkdv16<D, 4, true>(blocks, 0, stream, q, k, v, dout, lse,
+                                                       delta, dk, dv, ds, a);
+        if (e != hipSuccess) return e;
+        // dq: 4 query tiles per wave while that still gives two blocks per CU.
+        const int tiles = a.qt_hi - a.qt_lo;
+        const auto rows = [&](int rt) { return (tiles + a.dq_rs * rt - 1) / (a.dq_rs * rt); };
+        a.dq_rt = (long long)a.dq_n_head_blocks * rows(4) >= 2 * cus ? 4 : 1;
+        a.dq_n_row_blocks = rows(a.dq_rt);
+        const long long grid = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks;
+        if (a.dq_rt == 4) {
+            hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 4>), dim3((unsigned)grid), dim3(256), 0,
+                               stream, k, ds, dq, a);
+        } else {
+            hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 1>), dim3((unsigned)grid), dim3(256), 0,
+                               stream, k, ds, dq, a);
+        }
     }
     return hipSuccess;
 }
@@ -881,9 +925,38 @@ hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, c
 
 }  // namespace
 
+int backward_windows(const DsLayout& l, long long capacity, int* win, int max_win) {
+    // Greedy windows of whole query tiles, each holding at most `capacity`
+    // tiles per head; 0 when one query tile alone exceeds it or more than
+    // max_win windows would be needed.
+    const int n = ds_query_tiles(l);
+    const auto upto = [&](int qt) {
+        return qt == n ? ds_tiles_per_head(l) : ds_tiles_before(l, qt);
+    };
+    int n_win = 0;
+    win[0] = 0;
+    int qa = 0;
+    while (qa < n) {
+        int qb = qa;
+        // widen while the window still fits (binary search on the monotone count)
+        int lo = qa + 1, hi = n;
+        if (upto(lo) - upto(qa) > capacity) return 0;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (upto(mid) - upto(qa) <= capacity) lo = mid; else hi = mid - 1;
+        }
+        qb = lo;
+        if (n_win == max_win) return 0;
+        win[++n_win] = qb;
+        qa = qb;
+    }
+    return n_win;
+}
+
 hipError_t launch_backward(const float* q, const float* k, const float* v, const float* o,
                            const float* dout, const float* lse, float* dq, float* dk, float* dv,
-                           float* delta, float* ds, const PrefillShape& s, hipStream_t stream) {
+                           float* delta, float* ds, long long ds_capacity, const PrefillShape& s,
+                           hipStream_t stream) {
     BwdArgs a;
     a.q_seq = s.q_seq;
     a.kv_len = s.kv_len;
@@ -912,31 +985,43 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
     a.n_head_blocks = s.num_heads / a.hg;
     a.n_row_blocks = (s.q_seq + a.rs * kBM - 1) / (a.rs * kBM);
     a.ds = DsLayout{s.causal, s.start_pos, s.q_seq, s.kv_len};
+    const int n_qt = ds_query_tiles(a.ds);
+    a.qt_lo = 0;
+    a.qt_hi = n_qt;
+    a.ds_base = 0;
     a.ds_tph = ds_tiles_per_head(a.ds);
+    a.accumulate = 0;
     a.dq_hg = gcd_int(a.group, kWaves);
     a.dq_rs = kWaves / a.dq_hg;
     a.dq_n_head_blocks = s.num_heads / a.dq_hg;
-    const auto dq_rows = [&](int rt) {
-        return (ds_query_tiles(a.ds) + a.dq_rs * rt - 1) / (a.dq_rs * rt);
-    };
-    // 4 query tiles per wave while that still gives two blocks per CU.
-    a.dq_rt = (long long)a.dq_n_head_blocks * dq_rows(4) >= 2 * cus ? 4 : 1;
-    a.dq_n_row_blocks = dq_rows(a.dq_rt);
+    a.dq_rt = 1;
+    a.dq_n_row_blocks = 0;
     // The stored path pays once the dq grid from the tiles fills the compute
-    // units; shorter calls recompute (a testing override forces either path,
-    // the stored one only with a workspace that holds the tiles).
+    // units (one block of 4 waves per CU with 4 query tiles per wave);
+    // shorter calls recompute. With fewer tiles than the call has, the stored
+    // path runs in windows (at most 64 when chosen by size). A testing
+    // override forces either path (the stored one whenever a window of one
+    // query tile fits).
     const int force = override_bwd_path();
-    const bool big = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks >= cus;
+    const auto dq_blocks = [&](int rt) {
+        return (long long)a.dq_n_head_blocks * ((n_qt + a.dq_rs * rt - 1) / (a.dq_rs * rt));
+    };
+    const bool big = dq_blocks(dq_blocks(4) >= 2 * cus ? 4 : 1) >= cus;
     const bool use_ds = force != 0 ? force == 1 : big;
     hipError_t e;
     if (ds != nullptr && use_ds && s.q_seq > 0 && s.kv_len > 0) {
-        if (s.head_dim == 128) {
-            e = launch_bwd_stored<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, stream);
-        } else {
-            e = launch_bwd_stored<64>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, stream);
+        constexpr int kMaxWin = 4096;
+        static thread_local int win[kMaxWin + 1];
+        const int n_win = backward_windows(a.ds, ds_capacity, win, force == 1 ? kMaxWin : 64);
+        if (n_win > 0) {
+            e = s.head_dim == 128
+                ? launch_bwd_stored<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, win,
+                                         n_win, cus, stream)
+                : launch_bwd_stored<64>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, win,
+                                        n_win, cus, stream);
+            if (e != hipSuccess) return e;
+            return hipGetLastError();
         }
-        if (e != hipSuccess) return e;
-        return hipGetLastError();
     }
     if (s.head_dim == 128) {
         e = launch_bwd_instance<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, a, stream);

@@ -14,9 +14,12 @@
 //     into the operand layouts, one tile ahead of its use (waves of a block
 //     that read the same keys meet in the L1 cache);
 //   * S^T = K Q^T: lane (j, g) of a 16x16x4 product supplies key/query j and
-//     k index g; k-step s with index g carries head-dim element g*D/4 + s, so
-//     each lane reads D/4 contiguous floats of its key (and holds D/4 of its
-//     query) -- the k order of a dot product is free;
+//     k index g; k-step 4c + e with index g carries head-dim element
+//     16c + 4g + e (the k order of a dot product is free), so each 16-byte
+//     load instruction c of a key tile reads 64 contiguous bytes of each of
+//     its 16 key rows (one half cache line per row; the order g*D/4 + s,
+//     64 bytes apart per lane, touched two lines per row and measured ~1%
+//     slower on the cross 512x2048 workload);
 //   * O^T += V^T P^T: k-step t with index g pairs key 4g + t, which is
 //     exactly register t of the score result in that lane, so P never leaves
 //     registers; O^T block b row m is head-dim (D/16)*m + b, so a lane reads
@@ -87,7 +90,7 @@ struct Args16 {
 
 template <int D>
 struct Tile {
-    float4 kx[D / 16];  // K[key j][g*D/4 .. +D/4)
+    float4 kx[D / 16];  // K[key j][16c + 4g .. +4) in kx[c]
     float4 vx[D / 16];  // V[key 4g + t][(D/16)*j .. +D/16), t-major
 };
 
@@ -129,13 +132,14 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int t_begin = kvs * nt;
     const int t_end = min(t_begin + nt, n_tiles);
 
-    // Q^T operand: lane (j, g) holds q[row][g*KS + s] * scale*log2(e).
+    // Q^T operand: lane (j, g) holds q[row][16c + 4g + e] * scale*log2(e)
+    // in register 4c + e (k-step 4c + e).
     float qr[KS];
     {
-        const float* qp = q + (size_t)(ok ? row : 0) * a.q_stride + head * D + g * KS;
+        const float* qp = q + (size_t)(ok ? row : 0) * a.q_stride + head * D + 4 * g;
 #pragma unroll
         for (int c = 0; c < KS / 4; ++c) {
-            const float4 x = ok ? *reinterpret_cast<const float4*>(qp + 4 * c)
+            const float4 x = ok ? *reinterpret_cast<const float4*>(qp + 16 * c)
                                 : make_float4(0.f, 0.f, 0.f, 0.f);
             qr[4 * c + 0] = x.x * a.qscale;
             qr[4 * c + 1] = x.y * a.qscale;
@@ -157,9 +161,9 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     auto load = [&](Tile<D>& T, int t) {
         const int kv0 = t * kKeys;
         const int key = min(kv0 + j, w_max - 1);
-        const float* kp = kbase + (size_t)key * a.k_stride + g * KS;
+        const float* kp = kbase + (size_t)key * a.k_stride + 4 * g;
 #pragma unroll
-        for (int c = 0; c < KS / 4; ++c) T.kx[c] = *reinterpret_cast<const float4*>(kp + 4 * c);
+        for (int c = 0; c < KS / 4; ++c) T.kx[c] = *reinterpret_cast<const float4*>(kp + 16 * c);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const int vkey = min(kv0 + 4 * g + tt, w_max - 1);
@@ -198,12 +202,16 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
             for (int b = 0; b < NB; ++b) o[b] *= corr;
         }
-        // O^T += V^T P^T: k-step tt pairs key 4g + tt with register tt.
+        __builtin_amdgcn_s_setprio(1);
+        // O^T += V^T P^T: k-step tt pairs key 4g + tt with register tt. At
+        // raised wave priority, so the SIMD's other wave fills the gaps with
+        // its softmax (as in the 32-row kernel; ~0.5% on the cross workload).
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 o[b] = mfma16(comp(T.vx[tt * (NB / 4) + b / 4], b % 4), s[tt], o[b]);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Two register tiles, the next one in flight while the current one is

@@ -181,14 +181,16 @@ int attn_bwd(const float* q, const float* k, const float* v, const float* out, c
     s.scale = scale;
     s.q_stride = s.out_stride = (long long)num_heads * head_dim;
     s.k_stride = s.v_stride = (long long)num_kv_heads * head_dim;
-    // With room for every dS tile the scores are formed once (stored path).
+    // Workspace past the D_i scratch holds dS tiles (stored path): every tile
+    // of the call, or a window of query tiles at a time.
     const size_t base = attn_bwd_workspace_bytes(q_seq, num_heads);
-    const size_t stored = attn_bwd_workspace_bytes_stored(q_seq, kv_len, num_heads, mode,
-                                                          start_pos);
-    float* ds = stored > base && workspace_bytes >= stored
-        ? static_cast<float*>(workspace) + base / sizeof(float) : nullptr;
+    const size_t tile_bytes = (size_t)ta03::kDsTile * ta03::kDsTile * sizeof(float);
+    const long long capacity = workspace_bytes > base && q_seq > 0
+        ? (long long)((workspace_bytes - base) / (tile_bytes * (size_t)num_heads)) : 0;
+    float* ds = capacity > 0 ? static_cast<float*>(workspace) + base / sizeof(float) : nullptr;
     const hipError_t e = ta03::launch_backward(q, k, v, out, dout, lse, dq, dk, dv,
-                                               static_cast<float*>(workspace), ds, s, stream);
+                                               static_cast<float*>(workspace), ds, capacity, s,
+                                               stream);
     return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
 }
 

@@ -95,11 +95,20 @@ __host__ __device__ inline long long ds_tiles_per_head(const DsLayout& l) {
     return n == 0 ? 0 : ds_tiles_before(l, n - 1) + ds_tiles_in(l, n - 1);
 }
 
-// ds == nullptr: dq recomputes the scores (two launches); otherwise the dk/dv
-// kernel stores dS in `ds` (DsLayout) and dq is computed from it.
+__host__ __device__ inline long long ds_tiles_upto(const DsLayout& l, int qt) {
+    return qt >= ds_query_tiles(l) ? ds_tiles_per_head(l) : ds_tiles_before(l, qt);
+}
+
+// ds == nullptr (or a capacity below the tiles of one query tile): dq
+// recomputes the scores (two launches). Otherwise the dk/dv kernel stores dS
+// tiles in `ds`, which holds ds_capacity tiles per head, and dq is computed
+// from them: in one window when every tile fits, else in windows of query
+// tiles, each window's tiles laid out as in DsLayout from the window's first
+// query tile on.
 hipError_t launch_backward(const float* q, const float* k, const float* v, const float* o,
                            const float* dout, const float* lse, float* dq, float* dk, float* dv,
-                           float* delta, float* ds, const PrefillShape& s, hipStream_t stream);
+                           float* delta, float* ds, long long ds_capacity, const PrefillShape& s,
+                           hipStream_t stream);
 
 // Rotary table: entry (p, e) = (cos, sin) of p * theta^(-2e/head_dim).
 hipError_t launch_rope_table(float* cs, int rows, int head_dim, double theta, hipStream_t stream);
