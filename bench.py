@@ -525,6 +525,34 @@ def copy_ceiling(torch, mib=64, copies=8, reps=48):
     return round(2 * n * 4 / per / 1e9, 1)
 
 
+def backward_legs(w, torch, ta):
+    """The backward on the 16K workload: stored-dS path with every tile, with
+    a 2 GB workspace (windows), and the recompute path."""
+    r = bench_backward(w, 3, 1, torch, ta)
+    rb = bench_backward(w, 3, 1, torch, ta, ws_bytes=BOUNDED_BWD_BYTES)
+    rr = bench_backward(w, 3, 1, torch, ta, stored=False)
+    return {
+        "workload": w.name, "ms": round(r["mean_s"] * 1e3, 3),
+        "flops_per_call": r["flops"], "TFLOP/s": round(r["tflops_kernel"], 3),
+        "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
+        "workspace_bytes": r["workspace_bytes"],
+        "kernels": "bwd_delta_kernel<128> + bwd_dkdv16_kernel<128, 4, true> + "
+                   "bwd_dq_ds_kernel<128, 4>",
+        "bounded": {"ms": round(rb["mean_s"] * 1e3, 3),
+                    "TFLOP/s": round(rb["tflops_kernel"], 3),
+                    "frac": round(rb["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
+                    "workspace_bytes": rb["workspace_bytes"],
+                    "kernels": "stored-dS path in windows of query tiles: "
+                               "bwd_delta_kernel<128>, then per window "
+                               "bwd_dkdv16_kernel<128, 4, true> + bwd_dq_ds_kernel<128, RT>"},
+        "recompute_path": {"ms": round(rr["mean_s"] * 1e3, 3),
+                           "TFLOP/s": round(rr["tflops_kernel"], 3),
+                           "frac": round(rr["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
+                           "workspace_bytes": rr["workspace_bytes"],
+                           "kernels": "bwd_dq_kernel<128> + "
+                                      "bwd_dkdv16_kernel<128, 4, false>"}}
+
+
 # ------------------------------------------------------------ main
 
 def main():
@@ -532,8 +560,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", choices=["prefill", "decode", "reported"], default=None,
-                    help="one part of the line; 'reported' = the smaller prefill workloads only")
+    ap.add_argument("--only", choices=["prefill", "decode", "reported", "backward"], default=None,
+                    help="one part of the line; 'reported' = the smaller prefill workloads only, "
+                         "'backward' = the backward legs only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reported", action="store_true",
                     help="skip the smaller prefill workloads")
@@ -561,6 +590,11 @@ def main():
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
               "dtype": "f32", "data": "synthetic"}
     clocks = {}
+
+    if args.only == "backward":
+        result["backward"] = backward_legs(w, torch, ta)
+        print(json.dumps(result), flush=True)
+        return
 
     if args.only == "reported":
         rep = {}
@@ -621,29 +655,7 @@ def main():
                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
                 "kernel": "prefill_kernel<128, true, 1>"}
             print(f"[bench] rotary {result['prefill_rope']}", flush=True)
-            r = bench_backward(w, 3, 1, torch, ta)
-            rb = bench_backward(w, 3, 1, torch, ta, ws_bytes=BOUNDED_BWD_BYTES)
-            rr = bench_backward(w, 3, 1, torch, ta, stored=False)
-            result["backward"] = {
-                "workload": w.name, "ms": round(r["mean_s"] * 1e3, 3),
-                "flops_per_call": r["flops"], "TFLOP/s": round(r["tflops_kernel"], 3),
-                "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                "workspace_bytes": r["workspace_bytes"],
-                "kernels": "bwd_delta_kernel<128> + bwd_dkdv16_kernel<128, 4, true> + "
-                           "bwd_dq_ds_kernel<128, 4>",
-                "bounded": {"ms": round(rb["mean_s"] * 1e3, 3),
-                            "TFLOP/s": round(rb["tflops_kernel"], 3),
-                            "frac": round(rb["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                            "workspace_bytes": rb["workspace_bytes"],
-                            "kernels": "stored-dS path in windows of query tiles: "
-                                       "bwd_delta_kernel<128>, then per window "
-                                       "bwd_dkdv16_kernel<128, 4, true> + bwd_dq_ds_kernel<128, RT>"},
-                "recompute_path": {"ms": round(rr["mean_s"] * 1e3, 3),
-                                   "TFLOP/s": round(rr["tflops_kernel"], 3),
-                                   "frac": round(rr["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                                   "workspace_bytes": rr["workspace_bytes"],
-                                   "kernels": "bwd_dq_kernel<128> + "
-                                              "bwd_dkdv16_kernel<128, 4, false>"}}
+            result["backward"] = backward_legs(w, torch, ta)
             print(f"[bench] backward {result['backward']}", flush=True)
 
     if args.only != "prefill":
