@@ -197,12 +197,13 @@ int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStr
  *                 per (row, key) pair in the windows, per head, rounded up to
  *                 whole tiles); any smaller workspace that holds the tiles of
  *                 the call's longest 16-row query tile runs the stored path in
- *                 windows of whole query tiles
+ *                 windows of whole query tiles (attn_bwd_windows)
  *
  * Stored path: D_i, then per window of query tiles the dk/dv kernel over the
  * window's rows, storing its dS tiles (dk, dv written by the first window,
  * added to by the later ones), and dq of the window's rows from the tiles
- * (three launches when every tile fits). Recompute path: two launches (dq
+ * (three launches when every tile fits). With n windows, window w holds the
+ * query tiles w, w + n, w + 2n, ... (every window spans the whole sequence). Recompute path: two launches (dq
  * with D_i, recomputing the scores; dk, dv). The stored path is taken when
  * the call is long enough for it to pay (the dq grid over the tiles fills the
  * device's compute units) and the workspace needs at most 64 windows;
@@ -222,6 +223,21 @@ size_t attn_bwd_workspace_bytes(int q_seq, int num_heads);
  * windows; 0 for sizes attn_bwd rejects. */
 size_t attn_bwd_workspace_bytes_stored(int q_seq, int kv_len, int num_heads, int mode,
                                        int start_pos);
+
+/*
+ * attn_bwd_windows -- host-only query: the number of windows of query tiles
+ * in which attn_bwd's stored path runs with a workspace of workspace_bytes
+ * for these sizes (the fewest n for which every window w < n, the 16-row
+ * query tiles w, w + n, w + 2n, ..., holds at most the dS tiles that fit past
+ * the D_i scratch). 1 when every tile fits. 0 when no count up to 64 fits
+ * (the workspace is below the tiles of the longest query tile, or more than
+ * 64 windows would be needed), for q_seq == 0 and for invalid sizes (as
+ * attn_bwd_workspace_bytes_stored); attn_bwd then recomputes. Whether a call
+ * with a count above 0 takes the stored path also depends on its size (see
+ * attn_bwd). Touches no device.
+ */
+int attn_bwd_windows(int q_seq, int kv_len, int num_heads, int mode, int start_pos,
+                     size_t workspace_bytes);
 int attn_bwd(const float* q, const float* k, const float* v, const float* out, const float* dout,
              const float* lse, float* dq, float* dk, float* dv, int q_seq, int kv_len,
              int num_heads, int num_kv_heads, int head_dim, int mode, int start_pos, float scale,

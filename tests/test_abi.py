@@ -38,7 +38,7 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_bytes",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_windows", "attn_bwd_workspace_bytes",
                                     "attn_bwd_workspace_bytes_stored", "attn_decode", "attn_decode_noalloc",
                                     "attn_decode_paged",
                                     "attn_decode_workspace_bytes",
@@ -239,6 +239,72 @@ def test_bwd_workspace_bytes_stored(lib):
     assert f(-1, 12, 4, CROSS, 0) == 0
     assert f(10, 12, 4, 7, 0) == 0
     assert f(0, 12, 4, CROSS, 0) == 0
+
+
+def _tiles_per_query_tile(q_seq, kv_len, mode, start_pos):
+    """dS tiles of each 16-row query tile: the keys of its last row's window,
+    in 16-key tiles."""
+    out = []
+    for qt in range((q_seq + 15) // 16):
+        rows_hi = min(16 * (qt + 1), q_seq)
+        w = min(start_pos + rows_hi, kv_len) if mode == CAUSAL else kv_len
+        out.append((w + 15) // 16)
+    return out
+
+
+def test_bwd_windows(lib):
+    """attn_bwd_windows returns the fewest n <= 64 for which each interleaved
+    window (query tiles w, w + n, ...) holds at most the tiles the workspace
+    fits past the D_i scratch, 1 when every tile fits, 0 when no n does;
+    tile counts by brute force over the query tiles."""
+    f = lib.attn_bwd_windows
+    rng = np.random.default_rng(78)
+    shapes = [(16384, 16384, 32, CAUSAL, 0), (512, 2048, 32, CAUSAL, 1536),
+              (1024, 1024, 8, FULL, 0), (512, 2048, 8, CROSS, 0), (90, 120, 4, CAUSAL, 30),
+              (3, 1000, 2, CAUSAL, 997), (7, 1, 1, CROSS, 0)]
+    for _ in range(60):
+        mode = int(rng.integers(0, 3))
+        q = int(rng.integers(1, 900))
+        if mode == CAUSAL:
+            sp = int(rng.integers(0, 200))
+            kv = q + sp + int(rng.integers(0, 40))
+        elif mode == FULL:
+            sp, kv = 0, q
+        else:
+            sp, kv = 0, int(rng.integers(1, 900))
+        shapes.append((q, kv, int(rng.integers(1, 9)), mode, sp))
+    checked = {0: 0, 1: 0, "many": 0}
+    for q, kv, H, mode, sp in shapes:
+        per_qt = _tiles_per_query_tile(q, kv, mode, sp)
+        total, longest = sum(per_qt), max(per_qt)
+        base = lib.attn_bwd_workspace_bytes(q, H)
+        caps = {longest - 1, longest, total - 1, total, total + 3, (total + 1) // 2,
+                (total + 8) // 9, max(longest, total // 70)}
+        caps |= {int(c) for c in rng.integers(longest, total + 2, size=6)}
+        for cap in sorted(c for c in caps if c >= 0):
+            ws = base + cap * H * 1024 + int(rng.integers(0, H * 1024))  # part of a tile is unused
+            n = f(q, kv, H, mode, sp, ws)
+
+            def fits(m):
+                return all(sum(per_qt[w::m]) <= cap for w in range(m))
+
+            if n == 0:
+                assert not any(fits(m) for m in range(1, min(64, len(per_qt)) + 1)), (q, kv, cap)
+                checked[0] += 1
+            else:
+                assert 1 <= n <= 64 and fits(n), (q, kv, H, mode, sp, cap, n)
+                assert n == 1 or not fits(n - 1), (q, kv, H, mode, sp, cap, n)
+                assert (n == 1) == (total <= cap)
+                checked[1 if n == 1 else "many"] += 1
+    assert min(checked.values()) > 10, checked
+    # the 16K causal workload: every tile; the bounded 2 GB workspace; sizes it rejects
+    stored = lib.attn_bwd_workspace_bytes_stored(16384, 16384, 32, CAUSAL, 0)
+    assert f(16384, 16384, 32, CAUSAL, 0, stored) == 1
+    assert f(16384, 16384, 32, CAUSAL, 0, stored - 1) == 2
+    assert f(16384, 16384, 32, CAUSAL, 0, 2_000_000_000) == 9
+    assert f(16384, 16384, 32, CAUSAL, 0, lib.attn_bwd_workspace_bytes(16384, 32)) == 0
+    assert f(10, 9, 4, CAUSAL, 0, 1 << 30) == 0
+    assert f(0, 12, 4, CROSS, 0, 1 << 30) == 0
 
 
 def test_validation_order_sizes_before_pointers(lib):

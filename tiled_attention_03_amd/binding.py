@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_workspace_bytes.restype = S
         L.attn_bwd_workspace_bytes_stored.argtypes = [I, I, I, I, I]
         L.attn_bwd_workspace_bytes_stored.restype = S
+        L.attn_bwd_windows.argtypes = [I, I, I, I, I, S]
+        L.attn_bwd_windows.restype = I
         L.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, S, P]
         L.attn_bwd.restype = I
         L.attn_decode_workspace_bytes.argtypes = [I, I, I, I]
@@ -227,6 +229,12 @@ def attn_bwd_workspace_bytes(q_seq: int, num_heads: int) -> int:
 def attn_bwd_workspace_bytes_stored(q_seq: int, kv_len: int, num_heads: int, mode: int,
                                     start_pos: int = 0) -> int:
     return int(lib().attn_bwd_workspace_bytes_stored(q_seq, kv_len, num_heads, mode, start_pos))
+
+
+def attn_bwd_windows(q_seq: int, kv_len: int, num_heads: int, mode: int, start_pos: int,
+                     workspace_bytes: int) -> int:
+    return int(lib().attn_bwd_windows(q_seq, kv_len, num_heads, mode, start_pos,
+                                      workspace_bytes))
 
 
 def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, q_seq: int, kv_len: int, num_heads: int,

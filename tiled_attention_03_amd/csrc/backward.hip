@@ -84,15 +84,18 @@ struct BwdArgs {
     float scale;
     int hg, rs, ks, n_head_blocks, n_row_blocks;  // dq kernel block shape (ks: key splits)
     DsLayout ds;                              // stored dS tiles (when kept)
-    // Window of the stored-dS launches: query tiles [qt_lo, qt_hi) (the whole
-    // range in one window when every tile fits). The window's tiles are stored
-    // per head from ds: tile (h, qt, kt) at h * ds_tph + ds_tiles_before(qt) -
-    // ds_base + kt, ds_tph being the window's tiles per head.
-    int qt_lo, qt_hi;
-    long long ds_base;
+    // Window of the stored-dS launches (every query tile in one window when
+    // every tile fits): query tiles win.off + j * win.stride, j < win.count.
+    // Tile (h, local j, kt) sits at h * ds_tph + ds_win_tiles_before(j) + kt,
+    // ds_tph being the window's tiles per head.
+    DsWindow win;
     long long ds_tph;
     int accumulate;  // dk/dv kernel: add to dk, dv (windows after the first)
     int dq_hg, dq_rs, dq_rt, dq_n_head_blocks, dq_n_row_blocks;  // dq-from-dS block shape
+    // dq from dS: 0, or the compute units of a grid that is resident all at
+    // once, whose blocks are then dealt in rounds of that many, heaviest
+    // first in even rounds and lightest first in odd ones.
+    int dq_round;
 };
 
 // Issue this wave's share (inst = first, first + step, ...) of a 32-row, D-wide
@@ -419,16 +422,19 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     }
 
     // Query tiles of the window whose rows see some key of the block (causal:
-    // rows from blk_key0 - start_pos on).
+    // rows from blk_key0 - start_pos on): local tiles j0 .. win.count - 1, query
+    // tile win.off + j * win.stride.
     const int i_lo = a.causal ? max(0, blk_key0 - a.start_pos) : 0;
-    const int qt0 = max(i_lo / k16Rows, a.qt_lo);
-    const int qt_end = min((a.q_seq + k16Rows - 1) / k16Rows, a.qt_hi);
-    const int n_qt = i_lo < a.q_seq && qt0 < qt_end ? qt_end - qt0 : 0;
+    const int qmin = i_lo / k16Rows;
+    const int j0 = qmin <= a.win.off ? 0 : (qmin - a.win.off + a.win.stride - 1) / a.win.stride;
+    const int n_qt = i_lo < a.q_seq && j0 < a.win.count ? a.win.count - j0 : 0;
     const int total = a.group * n_qt;
+    // query tile of the block's tile step it (head it / n_qt)
+    auto qt_of = [&](int it) { return a.win.off + (j0 + it % n_qt) * a.win.stride; };
 
     auto issue1 = [&](int it, int sub, float* tb, float* vb) __attribute__((always_inline)) {
         const int h = kv_head * a.group + it / n_qt;
-        const int row0 = (qt0 + it % n_qt) * k16Rows;
+        const int row0 = qt_of(it) * k16Rows;
         float* qdst = tb + (size_t)sub * 2 * TILE_F;
 #pragma unroll 1
         for (int inst = wave; inst < LOADS; inst += W) {
@@ -460,7 +466,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const int it = st * SUB + sub;
         if (it >= total) return;
         const int h = kv_head * a.group + it / n_qt;
-        const int row0 = (qt0 + it % n_qt) * k16Rows;
+        const int row0 = qt_of(it) * k16Rows;
         if (pc < 4) {
             const int inst = wave + W * (pc & 1);
             if (inst < LOADS) {
@@ -493,7 +499,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         __syncthreads();  // stage st landed for every wave; the other buffer is free
         // The next stage's copies go between the first sub-tile's score
         // products when this wave computes it, else here.
-        const int rows_hi0 = min((qt0 + (st * SUB) % n_qt) * k16Rows + k16Rows, a.q_seq);
+        const int rows_hi0 = min(qt_of(st * SUB) * k16Rows + k16Rows, a.q_seq);
         const int w_max0 = a.causal ? min(a.start_pos + rows_hi0, a.kv_len) : a.kv_len;
         const bool spread = st + 1 < n_st && strip_live && key0 < w_max0;
         if (st + 1 < n_st && !spread) issue(st + 1, wt, wv);
@@ -501,7 +507,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         for (int sub = 0; sub < SUB; ++sub) {
             const int it = st * SUB + sub;
             if (it >= total) break;
-            const int row0 = (qt0 + it % n_qt) * k16Rows;
+            const int row0 = qt_of(it) * k16Rows;
             const int rows_hi = min(row0 + k16Rows, a.q_seq);
             const int w_max = a.causal ? min(a.start_pos + rows_hi, a.kv_len) : a.kv_len;
             if (strip_live && key0 < w_max) {  // wave-uniform
@@ -549,9 +555,9 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                     // stores of 4 x 64 contiguous bytes, issued before the dv / dk
                     // products so they complete under them.
                     const int h = kv_head * a.group + it / n_qt;
-                    const int qt = qt0 + it % n_qt;
-                    float* tile = ds + ((size_t)h * a.ds_tph + ds_tiles_before(a.ds, qt) -
-                                        a.ds_base + key0 / k16Keys) * (k16Rows * k16Keys);
+                    const int jl = j0 + it % n_qt;
+                    float* tile = ds + ((size_t)h * a.ds_tph + ds_win_tiles_before(a.ds, a.win, jl) +
+                                        key0 / k16Keys) * (k16Rows * k16Keys);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) tile[(4 * g + r) * k16Keys + j] = dp[r];
                 }
@@ -691,7 +697,16 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     const int j = lane & 15;
     const int g = lane >> 4;
 
-    const int bid = blockIdx.x;
+    // Blocks in order of work, heaviest first; a grid resident all at once
+    // (round r: blocks r R .. r R + R - 1, one per compute unit as dispatched)
+    // takes them in snake order, so that every compute unit's blocks sum to
+    // about the same work.
+    int bid = blockIdx.x;
+    if (a.dq_round > 0) {
+        const int r = bid / a.dq_round, p = bid % a.dq_round;
+        const int cnt = min(a.dq_round, (int)gridDim.x - r * a.dq_round);
+        bid = r * a.dq_round + ((r & 1) ? cnt - 1 - p : p);
+    }
     const int head_block = bid % a.dq_n_head_blocks;
     const int seq = bid / a.dq_n_head_blocks;
     const int rb = a.causal ? (a.dq_n_row_blocks - 1 - seq) : seq;  // heaviest first
@@ -699,10 +714,10 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     const int strip = wave / a.dq_hg;
     const int kv_head = head / a.group;
     const int kvd = a.num_kv_heads * D;
-    // Query tiles of the window [qt_lo, qt_hi).
-    const int qt_first = a.qt_lo + (rb * a.dq_rs + strip) * kDqRT;
-    const int blk_qt_last = min(a.qt_lo + (rb + 1) * a.dq_rs * kDqRT, a.qt_hi) - 1;
-    const int n_kt = blk_qt_last >= a.qt_lo ? ds_tiles_in(a.ds, blk_qt_last) : 0;
+    // Local query tiles of the window (query tile win.off + j * win.stride).
+    const int j_first = (rb * a.dq_rs + strip) * kDqRT;
+    const int blk_j_last = min((rb + 1) * a.dq_rs * kDqRT, a.win.count) - 1;
+    const int n_kt = blk_j_last >= 0 ? ds_tiles_in(a.ds, a.win.off + blk_j_last * a.win.stride) : 0;
 
     // Per query tile: first tile index (clamped query tile) and tile count.
     long long tbase[kDqRT];
@@ -710,11 +725,11 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     bool tlive[kDqRT];
 #pragma unroll
     for (int rt = 0; rt < kDqRT; ++rt) {
-        const int qt = qt_first + rt;
-        const int qc = min(qt, a.qt_hi - 1);
-        tlive[rt] = qt < a.qt_hi;
-        tcount[rt] = ds_tiles_in(a.ds, qc);
-        tbase[rt] = (long long)head * a.ds_tph + ds_tiles_before(a.ds, qc) - a.ds_base;
+        const int jl = j_first + rt;
+        const int jc = min(jl, a.win.count - 1);
+        tlive[rt] = jl < a.win.count;
+        tcount[rt] = ds_tiles_in(a.ds, a.win.off + jc * a.win.stride);
+        tbase[rt] = (long long)head * a.ds_tph + ds_win_tiles_before(a.ds, a.win, jc);
     }
 
     auto issue_k = [&](int kt, float* dst) __attribute__((always_inline)) {
@@ -795,8 +810,9 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     const int qd = a.num_heads * D;
 #pragma unroll
     for (int rt = 0; rt < kDqRT; ++rt) {
-        const int qt = qt_first + rt;
-        if (qt >= a.qt_hi) break;  // wave-uniform: past the window
+        const int jl = j_first + rt;
+        if (jl >= a.win.count) break;  // wave-uniform: past the window
+        const int qt = a.win.off + jl * a.win.stride;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = qt * k16Rows + 4 * g + r;
@@ -851,33 +867,46 @@ hipError_t launch_dkdv16_any(size_t lds, hipStream_t stream, const float* q, con
                                       ds, a);
 }
 
+// Blocks of the dq-from-dS kernel that the device holds at once.
+template <int D>
+long long dq_resident_blocks(int rt, int cus) {
+    const auto occ = [](const void* f) {
+        int n = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) == hipSuccess ? n : 0;
+    };
+    static const int per_cu[2] = {occ(reinterpret_cast<const void*>(bwd_dq_ds_kernel<D, 1>)),
+                                  occ(reinterpret_cast<const void*>(bwd_dq_ds_kernel<D, 4>))};
+    return (long long)per_cu[rt == 4 ? 1 : 0] * cus;
+}
+
 // The stored-dS path over windows of query tiles (one window when the
-// workspace holds every tile): D_i once; per window the dk/dv kernel over the
-// window's rows, storing the window's dS tiles (dk, dv written by the first
-// window, which covers every key, and added to by the later ones, which
-// cover the keys their rows see), then dq of the window's rows from them.
+// workspace holds every tile; else n windows, window w taking the query tiles
+// w, w + n, w + 2n, ..., so that each spans every row and its dk/dv blocks
+// keep the single launch's spread of work): D_i once; per window the dk/dv
+// kernel over the window's rows, storing the window's dS tiles (dk, dv written
+// by the first window, whose grid covers every key, and added to by the later
+// ones, which cover the keys their rows see), then dq of the window's rows
+// from them.
 template <int D>
 hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, const float* o,
                              const float* dout, const float* lse, float* dq, float* dk,
                              float* dv, float* delta, float* ds, const BwdArgs& a0,
-                             const int* win, int n_win, int cus, hipStream_t stream) {
+                             int n_win, int cus, hipStream_t stream) {
     const long long n_pairs = (long long)a0.q_seq * a0.num_heads;
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((n_pairs + 15) / 16)), dim3(256), 0,
                        stream, o, dout, delta, n_pairs);
     const int n_qt = ds_query_tiles(a0.ds);
     for (int w = 0; w < n_win; ++w) {
         BwdArgs a = a0;
-        a.qt_lo = win[w];
-        a.qt_hi = win[w + 1];
-        a.ds_base = ds_tiles_before(a.ds, a.qt_lo);
-        a.ds_tph = (a.qt_hi == n_qt ? ds_tiles_per_head(a.ds) : ds_tiles_before(a.ds, a.qt_hi)) -
-                   a.ds_base;
+        a.win = ds_window(n_qt, n_win, w);
+        a.ds_tph = ds_win_tiles_per_head(a.ds, a.win);
         a.accumulate = w > 0 ? 1 : 0;
         // Keys the window's rows see; the first window covers every key (it
         // writes dk, dv, zero for keys no row sees).
         int keys = a.kv_len;
         if (w > 0 && a.causal) {
-            const long long hi = (long long)a.start_pos + min(a.qt_hi * k16Rows, a.q_seq);
+            const int qt_last = a.win.off + (a.win.count - 1) * a.win.stride;
+            const long long hi = (long long)a.start_pos + min((qt_last + 1) * k16Rows, a.q_seq);
             keys = (int)(hi < a.kv_len ? hi : a.kv_len);
         }
         const long long blocks =
@@ -885,12 +914,16 @@ hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, con
         const hipError_t e = launch_dkdv16<D, 4, true>(blocks, 0, stream, q, k, v, dout, lse,
                                                        delta, dk, dv, ds, a);
         if (e != hipSuccess) return e;
-        // dq: 4 query tiles per wave while that still gives two blocks per CU.
-        const int tiles = a.qt_hi - a.qt_lo;
+        // dq: 4 query tiles per wave while that still gives two blocks per
+        // CU, else one (then the device holds the whole grid at once and
+        // takes it in snake order; 2 per wave measured slower on the 16K
+        // causal pass in 9 windows).
+        const int tiles = a.win.count;
         const auto rows = [&](int rt) { return (tiles + a.dq_rs * rt - 1) / (a.dq_rs * rt); };
         a.dq_rt = (long long)a.dq_n_head_blocks * rows(4) >= 2 * cus ? 4 : 1;
         a.dq_n_row_blocks = rows(a.dq_rt);
         const long long grid = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks;
+        a.dq_round = grid <= dq_resident_blocks<D>(a.dq_rt, cus) ? cus : 0;
         if (a.dq_rt == 4) {
             hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 4>), dim3((unsigned)grid), dim3(256), 0,
                                stream, k, ds, dq, a);
@@ -925,32 +958,22 @@ hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, c
 
 }  // namespace
 
-int backward_windows(const DsLayout& l, long long capacity, int* win, int max_win) {
-    // Greedy windows of whole query tiles, each holding at most `capacity`
-    // tiles per head; 0 when one query tile alone exceeds it or more than
-    // max_win windows would be needed.
-    const int n = ds_query_tiles(l);
-    const auto upto = [&](int qt) {
-        return qt == n ? ds_tiles_per_head(l) : ds_tiles_before(l, qt);
-    };
-    int n_win = 0;
-    win[0] = 0;
-    int qa = 0;
-    while (qa < n) {
-        int qb = qa;
-        // widen while the window still fits (binary search on the monotone count)
-        int lo = qa + 1, hi = n;
-        if (upto(lo) - upto(qa) > capacity) return 0;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) / 2;
-            if (upto(mid) - upto(qa) <= capacity) lo = mid; else hi = mid - 1;
-        }
-        qb = lo;
-        if (n_win == max_win) return 0;
-        win[++n_win] = qb;
-        qa = qb;
+int backward_windows(const DsLayout& l, long long capacity, int max_win) {
+    // The fewest interleaved windows (window w of n: query tiles w + j n) each
+    // holding at most `capacity` tiles per head; 0 when more than max_win would
+    // be needed. No window count below total / capacity can fit.
+    const int n_qt = ds_query_tiles(l);
+    if (n_qt == 0 || capacity < ds_tiles_in(l, n_qt - 1)) return 0;  // the longest tile alone
+    const long long total = ds_tiles_per_head(l);
+    const long long lower = (total + capacity - 1) / capacity;
+    if (lower > max_win) return 0;
+    for (int n = (int)(lower < 1 ? 1 : lower); n <= max_win && n <= n_qt; ++n) {
+        bool fits = true;
+        for (int w = 0; w < n && fits; ++w)
+            fits = ds_win_tiles_per_head(l, ds_window(n_qt, n, w)) <= capacity;
+        if (fits) return n;
     }
-    return n_win;
+    return 0;
 }
 
 hipError_t launch_backward(const float* q, const float* k, const float* v, const float* o,
@@ -986,9 +1009,7 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
     a.n_row_blocks = (s.q_seq + a.rs * kBM - 1) / (a.rs * kBM);
     a.ds = DsLayout{s.causal, s.start_pos, s.q_seq, s.kv_len};
     const int n_qt = ds_query_tiles(a.ds);
-    a.qt_lo = 0;
-    a.qt_hi = n_qt;
-    a.ds_base = 0;
+    a.win = ds_window(n_qt, 1, 0);
     a.ds_tph = ds_tiles_per_head(a.ds);
     a.accumulate = 0;
     a.dq_hg = gcd_int(a.group, kWaves);
@@ -996,10 +1017,11 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
     a.dq_n_head_blocks = s.num_heads / a.dq_hg;
     a.dq_rt = 1;
     a.dq_n_row_blocks = 0;
+    a.dq_round = 0;
     // The stored path pays once the dq grid from the tiles fills the compute
     // units (one block of 4 waves per CU with 4 query tiles per wave);
     // shorter calls recompute. With fewer tiles than the call has, the stored
-    // path runs in windows (at most 64 when chosen by size). A testing
+    // path runs in windows (at most kMaxBwdWindows when chosen by size). A testing
     // override forces either path (the stored one whenever a window of one
     // query tile fits).
     const int force = override_bwd_path();
@@ -1010,15 +1032,13 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
     const bool use_ds = force != 0 ? force == 1 : big;
     hipError_t e;
     if (ds != nullptr && use_ds && s.q_seq > 0 && s.kv_len > 0) {
-        constexpr int kMaxWin = 4096;
-        static thread_local int win[kMaxWin + 1];
-        const int n_win = backward_windows(a.ds, ds_capacity, win, force == 1 ? kMaxWin : 64);
+        const int n_win = backward_windows(a.ds, ds_capacity, force == 1 ? 4096 : kMaxBwdWindows);
         if (n_win > 0) {
             e = s.head_dim == 128
-                ? launch_bwd_stored<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, win,
-                                         n_win, cus, stream)
-                : launch_bwd_stored<64>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, win,
-                                        n_win, cus, stream);
+                ? launch_bwd_stored<128>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, n_win,
+                                         cus, stream)
+                : launch_bwd_stored<64>(q, k, v, o, dout, lse, dq, dk, dv, delta, ds, a, n_win,
+                                        cus, stream);
             if (e != hipSuccess) return e;
             return hipGetLastError();
         }

@@ -144,6 +144,26 @@ size_t attn_bwd_workspace_bytes_stored(int q_seq, int kv_len, int num_heads, int
            (size_t)num_heads * (size_t)ta03::ds_tiles_per_head(l) * tile_bytes;
 }
 
+namespace {
+// dS tiles per head that a backward workspace holds past the D_i scratch.
+long long bwd_tile_capacity(int q_seq, int num_heads, size_t workspace_bytes) {
+    const size_t base = attn_bwd_workspace_bytes(q_seq, num_heads);
+    const size_t tile_bytes = (size_t)ta03::kDsTile * ta03::kDsTile * sizeof(float);
+    return workspace_bytes > base && q_seq > 0
+        ? (long long)((workspace_bytes - base) / (tile_bytes * (size_t)num_heads)) : 0;
+}
+}  // namespace
+
+int attn_bwd_windows(int q_seq, int kv_len, int num_heads, int mode, int start_pos,
+                     size_t workspace_bytes) {
+    if (attn_bwd_workspace_bytes_stored(q_seq, kv_len, num_heads, mode, start_pos) == 0 ||
+        q_seq == 0)
+        return 0;
+    const ta03::DsLayout l{mode == TA03_CAUSAL ? 1 : 0, start_pos, q_seq, kv_len};
+    return ta03::backward_windows(l, bwd_tile_capacity(q_seq, num_heads, workspace_bytes),
+                                  ta03::kMaxBwdWindows);
+}
+
 int attn_bwd(const float* q, const float* k, const float* v, const float* out, const float* dout,
              const float* lse, float* dq, float* dk, float* dv, int q_seq, int kv_len,
              int num_heads, int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
@@ -184,9 +204,7 @@ int attn_bwd(const float* q, const float* k, const float* v, const float* out, c
     // Workspace past the D_i scratch holds dS tiles (stored path): every tile
     // of the call, or a window of query tiles at a time.
     const size_t base = attn_bwd_workspace_bytes(q_seq, num_heads);
-    const size_t tile_bytes = (size_t)ta03::kDsTile * ta03::kDsTile * sizeof(float);
-    const long long capacity = workspace_bytes > base && q_seq > 0
-        ? (long long)((workspace_bytes - base) / (tile_bytes * (size_t)num_heads)) : 0;
+    const long long capacity = bwd_tile_capacity(q_seq, num_heads, workspace_bytes);
     float* ds = capacity > 0 ? static_cast<float*>(workspace) + base / sizeof(float) : nullptr;
     const hipError_t e = ta03::launch_backward(q, k, v, out, dout, lse, dq, dk, dv,
                                                static_cast<float*>(workspace), ds, capacity, s,

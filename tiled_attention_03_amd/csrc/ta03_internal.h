@@ -95,20 +95,47 @@ __host__ __device__ inline long long ds_tiles_per_head(const DsLayout& l) {
     return n == 0 ? 0 : ds_tiles_before(l, n - 1) + ds_tiles_in(l, n - 1);
 }
 
-__host__ __device__ inline long long ds_tiles_upto(const DsLayout& l, int qt) {
-    return qt >= ds_query_tiles(l) ? ds_tiles_per_head(l) : ds_tiles_before(l, qt);
+// A window of the stored path: query tiles off + j * stride, j < count (the
+// whole call: off 0, stride 1, count = all query tiles). Its tiles are laid
+// out per head as in DsLayout over the window's own query tiles: those of
+// local tile j after the tiles of local tiles 0 .. j - 1. Every local tile
+// but the window's last lies before the call's last query tile, so in a
+// causal call it holds qt + 1 + ceil(start_pos / 16) tiles and the sum has a
+// closed form.
+struct DsWindow {
+    int off, stride, count;
+};
+__host__ __device__ inline long long ds_win_tiles_before(const DsLayout& l, const DsWindow& w,
+                                                         int j) {  // j < count
+    if (!l.causal) return (long long)j * ((l.kv_len + kDsTile - 1) / kDsTile);
+    const long long c = (l.start_pos + kDsTile - 1) / kDsTile;
+    return (long long)j * (w.off + 1 + c) + (long long)w.stride * j * (j - 1) / 2;
+}
+__host__ __device__ inline long long ds_win_tiles_per_head(const DsLayout& l, const DsWindow& w) {
+    if (w.count == 0) return 0;
+    const int last = w.count - 1;  // the window's last tile counts its own keys
+    return ds_win_tiles_before(l, w, last) + ds_tiles_in(l, w.off + last * w.stride);
+}
+// Window w of n interleaved windows over n_qt query tiles (w < n <= n_qt).
+__host__ __device__ inline DsWindow ds_window(int n_qt, int n, int w) {
+    return DsWindow{w, n, (n_qt - w + n - 1) / n};
 }
 
 // ds == nullptr (or a capacity below the tiles of one query tile): dq
 // recomputes the scores (two launches). Otherwise the dk/dv kernel stores dS
 // tiles in `ds`, which holds ds_capacity tiles per head, and dq is computed
-// from them: in one window when every tile fits, else in windows of query
-// tiles, each window's tiles laid out as in DsLayout from the window's first
-// query tile on.
+// from them: in one window when every tile fits, else in n windows of
+// interleaved query tiles (window w: tiles w, w + n, w + 2n, ...), each laid
+// out as DsWindow says.
 hipError_t launch_backward(const float* q, const float* k, const float* v, const float* o,
                            const float* dout, const float* lse, float* dq, float* dk, float* dv,
                            float* delta, float* ds, long long ds_capacity, const PrefillShape& s,
                            hipStream_t stream);
+
+// The fewest interleaved windows whose tiles each fit `capacity` tiles per
+// head (1: every tile at once); 0 when none up to max_win do.
+int backward_windows(const DsLayout& l, long long capacity, int max_win);
+constexpr int kMaxBwdWindows = 64;  // windows chosen by size
 
 // Rotary table: entry (p, e) = (cos, sin) of p * theta^(-2e/head_dim).
 hipError_t launch_rope_table(float* cs, int rows, int head_dim, double theta, hipStream_t stream);
