@@ -47,6 +47,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ta03_internal.h"
 
 namespace ta03 {
@@ -162,6 +164,8 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         : (a.causal ? min(a.start_pos + min(row0 + kBM, a.q_seq), a.kv_len) : a.kv_len);
     const int row = row0 + j;
     const int w_row = a.causal ? min(a.start_pos + row + 1, a.kv_len) : a.kv_len;
+    // Smallest window of the wave's rows: tiles ending at or before it need no mask.
+    const int w_wave_min = a.causal ? min(a.start_pos + row0 + 1, a.kv_len) : a.kv_len;
 
     // Tiles of this wave's key split.
     const int n_tiles_all = (w_block + kBN - 1) / kBN;
@@ -347,7 +351,8 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
     // One tile: Ks is this split's K | V tiles of tile it, wb the buffer that
     // tile it + 1 is copied into.
-    auto step = [&](int it, const float* Ks, float* wb) __attribute__((always_inline)) {
+    auto step = [&](int it, const float* Ks, float* wb, auto masked_tag)
+        __attribute__((always_inline)) {
         const int t = t_begin + it;
         const bool have = t < t_end;
         wait_vmem();
@@ -366,6 +371,10 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             issue_tile(t + 1, wb);
             if constexpr (ROPE) load_k_rot(t + 1);
         }
+        // Tiles inside every row's window (the leading ones, most of them)
+        // run a version without mask code; the others apply the window as a
+        // select (see the loops below).
+        constexpr bool MASKED = decltype(masked_tag)::value;
         if (work) {  // wave-uniform
             const float* Vs = Ks + TILE_F;
 
@@ -385,12 +394,15 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 s = mfma32(kk.w, qr[4 * g + 3], s);
             }
 
-            // The window mask is a select on every tile: behind a branch it
-            // would put a basic-block edge between the last score product and
-            // the first vector read of its result, where the wait the matrix
-            // unit's result needs was once found missing in generated code.
+            // The window mask as a select (a branch here would put a block
+            // edge between the last score product and the first vector read
+            // of its result, where the wait the matrix unit's result needs was
+            // once found missing in generated code).
+            if constexpr (MASKED) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = kv0 + acc_row(r, hh) < w_row ? s[r] : -INFINITY;
+                for (int r = 0; r < 16; ++r)
+                    s[r] = kv0 + acc_row(r, hh) < w_row ? s[r] : -INFINITY;
+            }
 
             // Online softmax for query column j.
             float mx = s[0];
@@ -446,9 +458,21 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             }
         }
     };
-    for (int it = 0; it < nt; it += 2) {
-        step(it, my0, my1);
-        if (it + 1 < nt) step(it + 1, my1, my0);
+    // Two loops over the tiles (tile it in buffer it & 1): first the tiles
+    // that lie inside every row's window, without mask code, then the rest
+    // with the mask. Each loop body is straight-line from the score products
+    // to the softmax (no block edge between a product and the vector reads
+    // of its result), and the loops run one after the other, so the
+    // unmasked version adds no registers to the masked one.
+    const int n_int = max(0, min(nt, w_wave_min / kBN - t_begin));
+    int it = 0;
+    for (; it + 1 < n_int; it += 2) {
+        step(it, my0, my1, std::false_type{});
+        step(it + 1, my1, my0, std::false_type{});
+    }
+    for (; it < nt; it += 2) {
+        step(it, my0, my1, std::true_type{});
+        if (it + 1 < nt) step(it + 1, my1, my0, std::true_type{});
     }
 
     if constexpr (KS > 1) {
