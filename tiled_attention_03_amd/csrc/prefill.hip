@@ -630,9 +630,9 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     if (!rope) {
         // Fewer blocks than compute units: the 16-row kernel, which needs no
         // shared tiles, spreads the work over more waves (a testing override
-        // can force either kernel on any shape).
+        // can force either kernel on any shape the 16-row kernel takes).
         const int force = override_prefill_rows();
-        const bool use16 = force != 0 ? force == 16 : grid < cus;
+        const bool use16 = (force != 0 ? force == 16 : grid < cus) && prefill16_fits(s);
         if (use16) return launch_prefill16(q, k, v, out, lse, s, stream);
     }
     hipError_t e;

@@ -45,6 +45,8 @@ constexpr int kWavesPerCU = 8;  // two waves per SIMD
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Fourth word of a raw buffer resource: 32-bit data format (untyped loads).
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -156,21 +158,40 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
     const float* kbase = k + kv_head * D;
     const float* vbase = v + kv_head * D;
-    // Keys past the wave's last window are read as its last key (in bounds;
-    // their scores are masked and their weight is 0).
+    // Key tiles are read through buffer resources whose base is the tile's
+    // first row and whose size covers the rows before the wave's last window
+    // (scalar work per tile): each lane's byte offsets are the same for every
+    // tile, so a tile's loads cost no vector instructions for addresses, and
+    // rows past the window read as zero (their scores are masked and their
+    // weight is 0). K: row j, elements 16c + 4g (c in the instruction
+    // offset); V: row 4g + tt, elements NB j.
+    const unsigned kvo = (unsigned)(j * a.k_stride + 4 * g) * 4u;
+    unsigned vvo[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) vvo[tt] = (unsigned)((4 * g + tt) * a.v_stride + NB * j) * 4u;
     auto load = [&](Tile<D>& T, int t) {
         const int kv0 = t * kKeys;
-        const int key = min(kv0 + j, w_max - 1);
-        const float* kp = kbase + (size_t)key * a.k_stride + 4 * g;
+        const int rows = min(kKeys, w_max - kv0);
+        const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(kbase + (size_t)kv0 * a.k_stride), 0, rows * (int)a.k_stride * 4,
+            kBufferFlags);
+        const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(vbase + (size_t)kv0 * a.v_stride), 0, rows * (int)a.v_stride * 4,
+            kBufferFlags);
 #pragma unroll
-        for (int c = 0; c < KS / 4; ++c) T.kx[c] = *reinterpret_cast<const float4*>(kp + 16 * c);
+        for (int c = 0; c < KS / 4; ++c) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, kvo + 64u * c, 0, 0);
+            T.kx[c] = make_float4(__int_as_float(x[0]), __int_as_float(x[1]), __int_as_float(x[2]),
+                                  __int_as_float(x[3]));
+        }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const int vkey = min(kv0 + 4 * g + tt, w_max - 1);
-            const float* vp = vbase + (size_t)vkey * a.v_stride + NB * j;
 #pragma unroll
-            for (int c = 0; c < NB / 4; ++c)
-                T.vx[tt * (NB / 4) + c] = *reinterpret_cast<const float4*>(vp + 4 * c);
+            for (int c = 0; c < NB / 4; ++c) {
+                const auto x = __builtin_amdgcn_raw_buffer_load_b128(rv, vvo[tt] + 16u * c, 0, 0);
+                T.vx[tt * (NB / 4) + c] = make_float4(__int_as_float(x[0]), __int_as_float(x[1]),
+                                                      __int_as_float(x[2]), __int_as_float(x[3]));
+            }
         }
     };
 

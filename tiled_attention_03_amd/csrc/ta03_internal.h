@@ -59,6 +59,11 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
 // are compute units, or forced by override_prefill_rows().
 hipError_t launch_prefill16(const float* q, const float* k, const float* v, float* out,
                             float* lse, const PrefillShape& s, hipStream_t stream);
+// The 16-row kernel addresses a key tile's rows with 32-bit byte offsets:
+// K and V row strides below 2^25 floats.
+inline bool prefill16_fits(const PrefillShape& s) {
+    return s.k_stride < (1ll << 25) && s.v_stride < (1ll << 25);
+}
 
 // Attention backward (dense rows): dq [q_seq, H*d]; dk, dv [kv_len, Hkv*d];
 // delta: q_seq*H floats of scratch (D_i = <dout_i, out_i> per row and head).
