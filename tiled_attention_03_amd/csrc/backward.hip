@@ -359,7 +359,8 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     constexpr int CPR = D / 4;  // 16-byte chunks per row
     constexpr int TILE_F = k16Rows * D;
     constexpr int LOADS = TILE_F / 4 / 64;  // wave instructions per tile (<= 8)
-    // [2][SUB][Q tile | dout tile], then [2][SUB][64 floats: (m, log l) x 16 rows, D x 16 rows]
+    // [2][SUB][Q tile | dout tile], then [2][SUB][128 floats: (m, log l) x 16 rows
+    // (twice), D x 16 rows (four times)]
     constexpr int SUB = kDkdvSub;  // query tiles per stage (one barrier per stage)
     // Row r of a tile stores logical 16-byte chunk c at position c ^ swz(r).
     // A ds_read_b128 is served 16 lanes at a time over 64 four-byte banks (16
@@ -376,8 +377,8 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // copies to land (with offsets into one array it did).
     __shared__ __attribute__((aligned(16))) float tl0[SUB * 2 * TILE_F];
     __shared__ __attribute__((aligned(16))) float tl1[SUB * 2 * TILE_F];
-    __shared__ __attribute__((aligned(16))) float vc0[SUB * 64];
-    __shared__ __attribute__((aligned(16))) float vc1[SUB * 64];
+    __shared__ __attribute__((aligned(16))) float vc0[SUB * 128];
+    __shared__ __attribute__((aligned(16))) float vc1[SUB * 128];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -432,28 +433,59 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // query tile of the block's tile step it (head it / n_qt)
     auto qt_of = [&](int it) { return a.win.off + (j0 + it % n_qt) * a.win.stride; };
 
-    auto issue1 = [&](int it, int sub, float* tb, float* vb) __attribute__((always_inline)) {
+    // Copies go through buffer resources whose base is the tile's first row
+    // (of Q / dout at head h, of the (m, log l) pairs, of D_i) and whose size
+    // ends at q_seq: every lane's byte offsets are the same for every tile
+    // (computed once below), so a copy costs no vector instructions for its
+    // address, and rows past q_seq read as zero (those rows are masked).
+    // Tile load instruction inst = wave + W u: slot s = 64 inst + lane holds
+    // row s / CPR, position s % CPR = logical chunk ^ swz(row).
+    unsigned qoff[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int s_ = (wave + W * u) * 64 + lane;
+        const int r = s_ / CPR, p = s_ % CPR;
+        qoff[u] = (unsigned)(r * qd + 4 * (p ^ swz(r))) * 4u;
+    }
+    // (m, log l): lane l holds component l % 2 of row (l / 2) % 16; D_i: row l % 16.
+    const unsigned loff = (unsigned)(((lane >> 1) & 15) * a.num_heads * 2 + (lane & 1)) * 4u;
+    const unsigned doff = (unsigned)((lane & 15) * a.num_heads) * 4u;
+    auto issue_rows = [&](int it, int sub, float* tb, int u) __attribute__((always_inline)) {
+        const int inst = wave + W * u;
+        if (inst < LOADS) {
+            const int h = kv_head * a.group + it / n_qt;
+            const int row0 = qt_of(it) * k16Rows;
+            const int rows = min(k16Rows, a.q_seq - row0);
+            const size_t base = (size_t)row0 * qd + h * D;
+            const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(q + base), 0,
+                                                              rows * qd * 4, kBufferFlags);
+            const auto rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(dout + base), 0,
+                                                              rows * qd * 4, kBufferFlags);
+            float* qdst = tb + (size_t)sub * 2 * TILE_F;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(qdst + inst * 256), 16,
+                                                     qoff[u], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void*)(qdst + TILE_F + inst * 256),
+                                                     16, qoff[u], 0, 0, 0);
+        }
+    };
+    auto issue_vec = [&](int it, int sub, float* vb) __attribute__((always_inline)) {
         const int h = kv_head * a.group + it / n_qt;
         const int row0 = qt_of(it) * k16Rows;
-        float* qdst = tb + (size_t)sub * 2 * TILE_F;
-#pragma unroll 1
-        for (int inst = wave; inst < LOADS; inst += W) {
-            // slot s holds row s / CPR, position s % CPR = logical chunk ^ swz(tile row)
-            const int s_ = inst * 64 + lane;
-            const int r = s_ / CPR, p = s_ % CPR;
-            const int row = min(row0 + r, a.q_seq - 1);
-            const size_t src = (size_t)row * qd + h * D + 4 * (p ^ swz(r));
-            __builtin_amdgcn_global_load_lds(q + src, (lds_void*)(qdst + inst * 256), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(dout + src, (lds_void*)(qdst + TILE_F + inst * 256),
-                                             16, 0, 0);
-        }
-        if (wave == W - 1) {
-            // lanes 0..31: (m, log l) component l % 2 of row l / 2; 32..63: D of row l % 16
-            const float* src = lane < 32
-                ? lse + ((size_t)min(row0 + (lane >> 1), a.q_seq - 1) * a.num_heads + h) * 2 + (lane & 1)
-                : delta + (size_t)min(row0 + (lane & 15), a.q_seq - 1) * a.num_heads + h;
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(vb + sub * 64), 4, 0, 0);
-        }
+        const int rows = min(k16Rows, a.q_seq - row0);
+        const auto rl = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(lse + ((size_t)row0 * a.num_heads + h) * 2), 0,
+            rows * a.num_heads * 8, kBufferFlags);
+        const auto rd = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(delta + (size_t)row0 * a.num_heads + h), 0, rows * a.num_heads * 4,
+            kBufferFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(vb + sub * 128), 4, loff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(vb + sub * 128 + 64), 4, doff, 0, 0,
+                                                 0);
+    };
+    auto issue1 = [&](int it, int sub, float* tb, float* vb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) issue_rows(it, sub, tb, u);
+        if (wave == W - 1) issue_vec(it, sub, vb);
     };
     // One piece of stage st's copies (for spreading them between products):
     // pieces 0..3 = Q / dout rows of sub-tile p >> 1, instruction p & 1;
@@ -465,25 +497,10 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const int sub = pc < 4 ? pc >> 1 : pc - 4;
         const int it = st * SUB + sub;
         if (it >= total) return;
-        const int h = kv_head * a.group + it / n_qt;
-        const int row0 = qt_of(it) * k16Rows;
         if (pc < 4) {
-            const int inst = wave + W * (pc & 1);
-            if (inst < LOADS) {
-                float* qdst = tb + (size_t)sub * 2 * TILE_F;
-                const int s_ = inst * 64 + lane;
-                const int r = s_ / CPR, p = s_ % CPR;
-                const int row = min(row0 + r, a.q_seq - 1);
-                const size_t src = (size_t)row * qd + h * D + 4 * (p ^ swz(r));
-                __builtin_amdgcn_global_load_lds(q + src, (lds_void*)(qdst + inst * 256), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(dout + src, (lds_void*)(qdst + TILE_F + inst * 256),
-                                                 16, 0, 0);
-            }
+            issue_rows(it, sub, tb, pc & 1);
         } else if (wave == W - 1) {
-            const float* src = lane < 32
-                ? lse + ((size_t)min(row0 + (lane >> 1), a.q_seq - 1) * a.num_heads + h) * 2 + (lane & 1)
-                : delta + (size_t)min(row0 + (lane & 15), a.q_seq - 1) * a.num_heads + h;
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(vb + sub * 64), 4, 0, 0);
+            issue_vec(it, sub, vb);
         }
     };
     auto issue = [&](int st, float* tb, float* vb) __attribute__((always_inline)) {
@@ -513,7 +530,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
             if (strip_live && key0 < w_max) {  // wave-uniform
                 const float* Qs = rt + (size_t)sub * 2 * TILE_F;
                 const float* Gs = Qs + TILE_F;
-                const float* vd = rv + sub * 64;
+                const float* vd = rv + sub * 128;
                 // S = Q K^T, dP = dout V^T: register r of lane (j, g) is query
                 // row0 + 4g + r, key key0 + j.
                 f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -542,7 +559,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                     const int ir = 4 * g + r;
                     const int i = row0 + ir;
                     const float lse2 = (vd[2 * ir] + vd[2 * ir + 1]) * kLog2e;
-                    const float dl = vd[32 + ir];
+                    const float dl = vd[64 + ir];
                     const int w = a.causal ? min(a.start_pos + i + 1, a.kv_len) : a.kv_len;
                     const bool valid = i < a.q_seq && key < w;
                     const float p = valid ? __builtin_amdgcn_exp2f(s[r] - lse2) : 0.f;

@@ -45,8 +45,6 @@ constexpr int kWavesPerCU = 8;  // two waves per SIMD
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Fourth word of a raw buffer resource: 32-bit data format (untyped loads).
-constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

@@ -21,6 +21,10 @@ int device_cu_count();
 int override_prefill_rows();
 int override_bwd_path();
 
+// Fourth word of the raw buffer resources the kernels build
+// (__builtin_amdgcn_make_buffer_rsrc): 32-bit data format, for untyped loads.
+constexpr int kBufferFlags = 0x00020000;
+
 struct PrefillShape {
     int q_seq, kv_len, num_heads, num_kv_heads, head_dim;
     int causal, start_pos;  // start_pos: causal position of row 0 of q/out
