@@ -38,6 +38,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libta03.so)")
 
 
+def check_kernel_stubs(obj: str) -> None:
+    """Fail when the host pass left a kernel's launch stub undefined (it can
+    drop a kernel template's host side without a diagnostic); the library
+    would then fail to load or launch."""
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    out = subprocess.run([nm, obj], check=True, capture_output=True, text=True).stdout
+    missing = [line.split()[-1] for line in out.splitlines()
+               if "__device_stub__" in line and line.split()[0] == "U"]
+    if missing:
+        raise RuntimeError(f"{os.path.basename(obj)}: host pass dropped kernel stubs: {missing}")
+
+
 def build(verbose: bool = False) -> str:
     cc = hipcc()
     build_dir = os.path.join(PKG, "_build")
@@ -51,6 +63,7 @@ def build(verbose: bool = False) -> str:
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
+        check_kernel_stubs(obj)
         objs.append(obj)
     tmp = LIB + ".tmp"
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
@@ -67,6 +80,7 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    check_kernel_stubs(obj)
     tmp = PROBE_LIB + ".tmp"
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", obj, "-L", PKG, "-lta03",
            "-Wl,-rpath,$ORIGIN", "-o", tmp]

@@ -101,7 +101,7 @@ struct Args {
     int causal, start_pos;
     float qscale;  // scale * log2(e)
     long long q_stride, k_stride, v_stride, out_stride;  // row strides (floats)
-    int small_strides;  // 31 * max(k_stride, v_stride) + head_dim < 2^31: 32-bit tile offsets
+    int small_strides;  // 32 * 4 * max(k_stride, v_stride) < 2^31: 32-bit tile byte offsets
     int hg;        // heads per block
     int rs;        // 32-row strips per block
     int ks;        // key-range splits per block
@@ -227,53 +227,68 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // Issue this wave's share of tile t's K and V into buffer buf. LDS slot s
     // (16 bytes) of a tile holds row s/CPR; for K its chunk position p holds
     // logical chunk p ^ (row % 16), for V the natural chunk.
-    // Per-lane element offsets inside a tile (row s / CPR, chunk s % CPR of
-    // the wave's load slot s), the same for every tile. A tile that lies
-    // inside the block's window then costs one address add per load; the
-    // last tile of a window takes the clamped path below. At most LOADS / gw
-    // slots per wave: head_dim 128 runs at most 2 key splits (gw >= 2),
-    // head_dim 64 at most 4 (gw >= 1). The rotary instance keeps the general
-    // path (its registers are spoken for).
+    // Per-lane byte offsets inside a tile (row s / CPR, chunk s % CPR of the
+    // wave's load slot s), the same for every tile. With 32-bit tile offsets
+    // the copies go through buffer resources whose base is the tile's first
+    // row and whose size ends at the block's window: a copy then costs no
+    // vector instructions for its address, and rows past the window read as
+    // zero (their scores are masked and their weight is 0). At most
+    // LOADS / gw slots per wave: head_dim 128 runs at most 2 key splits
+    // (gw >= 2), head_dim 64 at most 4 (gw >= 1). The rotary instance and
+    // larger strides take the general path below.
     constexpr int MAXI = D == 128 ? LOADS / 2 : LOADS;
     unsigned koff[MAXI], voff[MAXI];
 #pragma unroll
     for (int u = 0; u < MAXI; ++u) {
         const unsigned s = (unsigned)((wg + u * gw) * 64 + lane);
         const unsigned r = s / CPR, c = s % CPR;
-        koff[u] = r * (unsigned)a.k_stride + 4u * (c ^ (r & 15u));
-        voff[u] = r * (unsigned)a.v_stride + 4u * c;
+        koff[u] = (r * (unsigned)a.k_stride + 4u * (c ^ (r & 15u))) * 4u;
+        voff[u] = (r * (unsigned)a.v_stride + 4u * c) * 4u;
     }
-    // Load u of this wave's share of tile t (fast path: the tile lies inside
-    // the block's window), issued between the score products of the
-    // current tile so the copies do not hold up the wave's issue.
+    // (Offsets reach the load builtins through named locals: an array
+    // element written as a builtin argument made the host pass of the
+    // compiler drop the kernel stubs without a diagnostic.)
+    // Load u of this wave's share of tile t (buffer path), issued between the
+    // score products of the current tile so the copies do not hold up the
+    // wave's issue.
     auto issue_u = [&](int t, float* kd, int u) __attribute__((always_inline)) {
         const int inst = wg + u * gw;
         if (inst < LOADS) {
-            const float* kt = kbase + (size_t)(t * kBN) * a.k_stride;
-            const float* vt = vbase + (size_t)(t * kBN) * a.v_stride;
-            const float* kg = kt + koff[u];
-            const float* vg = vt + voff[u];
-            __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kd + inst * 256), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vg, (lds_void*)(kd + TILE_F + inst * 256), 16, 0, 0);
+            const int kv0 = t * kBN;
+            const int rows = min(kBN, w_block - kv0);
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(kbase + (size_t)kv0 * a.k_stride), 0, rows * (int)a.k_stride * 4,
+                kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(vbase + (size_t)kv0 * a.v_stride), 0, rows * (int)a.v_stride * 4,
+                kBufferFlags);
+            const unsigned ko = koff[u], vo = voff[u];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + inst * 256), 16, ko, 0, 0,
+                                                     0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(kd + TILE_F + inst * 256), 16, vo,
+                                                     0, 0, 0);
         }
     };
     auto issue_tile = [&](int t, float* kd) __attribute__((always_inline)) {
         float* vd = kd + TILE_F;
         const int kv0 = t * kBN;
-        if (!ROPE && a.small_strides && kv0 + kBN <= w_block) {
-            const float* kt = kbase + (size_t)kv0 * a.k_stride;
-            const float* vt = vbase + (size_t)kv0 * a.v_stride;
+        if (!ROPE && a.small_strides) {
+            const int rows = min(kBN, w_block - kv0);
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(kbase + (size_t)kv0 * a.k_stride), 0, rows * (int)a.k_stride * 4,
+                kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(vbase + (size_t)kv0 * a.v_stride), 0, rows * (int)a.v_stride * 4,
+                kBufferFlags);
 #pragma unroll
             for (int u = 0; u < MAXI; ++u) {
                 const int inst = wg + u * gw;
                 if (inst < LOADS) {
-                    // (the addresses go through named locals: written inline
-                    // as builtin arguments, they made the host pass drop the
-                    // kernel stubs without a diagnostic)
-                    const float* kg = kt + koff[u];
-                    const float* vg = vt + voff[u];
-                    __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kd + inst * 256), 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds(vg, (lds_void*)(vd + inst * 256), 16, 0, 0);
+                    const unsigned ko = koff[u], vo = voff[u];
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + inst * 256), 16, ko,
+                                                             0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + inst * 256), 16, vo,
+                                                             0, 0, 0);
                 }
             }
             return;
@@ -366,7 +381,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const bool work = have && kv0 < w_wave_max;
         // the next tile's copies go between this tile's score products when
         // it lies inside the block's window (else, and without work, here)
-        const bool spread = !ROPE && next && work && a.small_strides && (t + 2) * kBN <= w_block;
+        const bool spread = !ROPE && next && work && a.small_strides;
         if (next && !spread) {
             issue_tile(t + 1, wb);
             if constexpr (ROPE) load_k_rot(t + 1);
@@ -602,7 +617,7 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     a.out_stride = s.out_stride;
     {
         const long long big = s.k_stride > s.v_stride ? s.k_stride : s.v_stride;
-        a.small_strides = 31 * big + s.head_dim < (1ll << 31) ? 1 : 0;
+        a.small_strides = 32 * 4 * big < (1ll << 31) ? 1 : 0;
     }
 
     // Block shape: heads of one GQA group x row strips x key splits = 4 waves.
