@@ -147,12 +147,12 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int rb = a.causal ? (a.n_row_blocks - 1 - seq) : seq;  // heaviest first
 
     // wave -> (key split, head, strip); waves sharing a key split share tiles
-    const int kvs = wave % a.ks;
-    const int rest = wave / a.ks;
+    const int kvs = wave % KS;
+    const int rest = wave / KS;
     const int head = head_block * a.hg + rest % a.hg;
     const int strip = rest / a.hg;
-    const int wg = wave / a.ks;              // index within its key split's group
-    const int gw = kWaves / a.ks;            // waves per key split
+    const int wg = wave / KS;              // index within its key split's group
+    const int gw = kWaves / KS;            // waves per key split
     const int row0 = (rb * a.rs + strip) * kBM;
     const int kv_head = head / a.group;
 
@@ -169,7 +169,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
     // Tiles of this wave's key split.
     const int n_tiles_all = (w_block + kBN - 1) / kBN;
-    const int nt = (n_tiles_all + a.ks - 1) / a.ks;
+    const int nt = (n_tiles_all + KS - 1) / KS;
     const int t_begin = kvs * nt;
     const int t_end = min(t_begin + nt, n_tiles_all);
 
@@ -364,6 +364,11 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         }
     }
 
+    // Byte offset in a K tile of the score operand's 16-byte read for
+    // k-steps g and g + 8: row j, chunk (2g + hh) ^ (j % 16).
+    unsigned kro[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) kro[g] = (unsigned)(j * D + 4 * ((2 * g + hh) ^ (j & 15))) * 4u;
     // One tile: Ks is this split's K | V tiles of tile it, wb the buffer that
     // tile it + 1 is copied into.
     auto step = [&](int it, const float* Ks, float* wb, auto masked_tag)
@@ -397,11 +402,13 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             f32x16 s;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = 0.f;
-            const float* kr = Ks + j * D;
+            const char* kb = reinterpret_cast<const char*>(Ks);
 #pragma unroll
             for (int g = 0; g < D / 8; ++g) {
-                const int c = (2 * g + hh) ^ (j & 15);
-                const float4 kk = *reinterpret_cast<const float4*>(kr + 4 * c);
+                // chunk (2g + hh) ^ (j % 16) of row j: k-steps 16 apart in g
+                // are 256 bytes apart, an instruction offset
+                const unsigned o = kro[g % 8];
+                const float4 kk = *reinterpret_cast<const float4*>(kb + o + 256 * (g / 8));
                 s = mfma32(kk.x, qr[4 * g + 0], s);
                 s = mfma32(kk.y, qr[4 * g + 1], s);
                 if (g < MAXI && spread) issue_u(t + 1, wb, g);
@@ -503,7 +510,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         static_assert((kWaves / KS) * (KS - 1) * PART * 64 <= (KS > 1 ? KS * 2 * TILE_F : 1 << 30),
                       "merge slots fit the first tile buffer");
         float4* part = reinterpret_cast<float4*>(lb0) +
-                       ((size_t)(rest * (a.ks - 1) + kvs - 1) * 64 + lane) * (PART / 4);
+                       ((size_t)(rest * (KS - 1) + kvs - 1) * 64 + lane) * (PART / 4);
         if (kvs > 0) {
             part[0] = make_float4(m_run, l_run, 0.f, 0.f);
 #pragma unroll
@@ -515,9 +522,9 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         }
         __syncthreads();
         if (kvs > 0) return;
-        for (int p = 1; p < a.ks; ++p) {
+        for (int p = 1; p < KS; ++p) {
             const float4* pp = reinterpret_cast<const float4*>(lb0) +
-                               ((size_t)(rest * (a.ks - 1) + p - 1) * 64 + lane) * (PART / 4);
+                               ((size_t)(rest * (KS - 1) + p - 1) * 64 + lane) * (PART / 4);
             const float4 ml = pp[0];
             const float M = fmaxf(m_run, ml.x);
             const float f0 = __builtin_amdgcn_exp2f(m_run - M);
