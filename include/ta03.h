@@ -214,7 +214,7 @@ int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStr
  * TA03_ERR_NULL for a NULL q, out, dout, lse, dq or workspace (q_seq > 0) or
  * k, v, dk, dv (kv_len > 0); TA03_ERR_WORKSPACE for a short workspace;
  * TA03_ERR_UNSUPPORTED for q_seq*num_heads*head_dim or
- * kv_len*num_kv_heads*head_dim >= 2^31, or num_heads*head_dim >= 2^25;
+ * kv_len*num_kv_heads*head_dim >= 2^31, or num_heads*head_dim >= 2^24;
  * TA03_ERR_ALIGN; TA03_ERR_HIP.
  * q_seq == 0 and kv_len == 0 is a no-op; q_seq == 0 alone writes zero dk, dv.
  */

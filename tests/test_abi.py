@@ -176,7 +176,7 @@ def bwd(lib, q=A, k=B, v=C, out=O, dout=O + 0x1000, lse=O + 0x2000, dq=O + 0x300
     (dict(scale=float("nan")), ERR_SHAPE),
     (dict(d=80), ERR_UNSUP),
     (dict(q_seq=1 << 20, kv_len=1 << 20, H=64, Hkv=64, d=64, ws_bytes=1 << 40), ERR_UNSUP),
-    (dict(q_seq=1, kv_len=1, H=1 << 19, Hkv=1, d=64, ws_bytes=1 << 40), ERR_UNSUP),  # row 2^25 floats
+    (dict(q_seq=1, kv_len=1, H=1 << 18, Hkv=1, d=64, ws_bytes=1 << 40), ERR_UNSUP),  # row 2^24 floats
     (dict(ws_bytes=8), ERR_WS),
     (dict(lse=None), ERR_NULL),
     (dict(dout=None), ERR_NULL),

@@ -99,20 +99,24 @@ struct BwdArgs {
 };
 
 // Issue this wave's share (inst = first, first + step, ...) of a 32-row, D-wide
-// tile starting at row row0 of a matrix with row stride ld into LDS,
-// XOR-swizzled; row indices are clamped to row_hi - 1.
+// tile starting at row row0 of a matrix with row stride ld (ld * 128 < 2^31)
+// into LDS, XOR-swizzled, through a buffer resource that ends at row row_hi:
+// rows past it read as zero.
 template <int D>
 __device__ __forceinline__ void issue_rows(const float* base, long long ld, int row0, int row_hi,
                                            float* dst, int first, int step, int lane) {
     constexpr int CPR = D / 4;
     constexpr int LOADS = kBN * D / 4 / 64;
+    const int rows = min(kBN, row_hi - row0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(base + (size_t)row0 * ld), 0, rows * (int)ld * 4, kBufferFlags);
 #pragma unroll 1
     for (int inst = first; inst < LOADS; inst += step) {
         const int s = inst * 64 + lane;
         const int r = s / CPR, p = s % CPR;
-        const int row = min(row0 + r, row_hi - 1);
-        const float* g = base + (size_t)row * ld + 4 * (p ^ (r & 15));
-        __builtin_amdgcn_global_load_lds(g, (lds_void*)(dst + inst * 256), 16, 0, 0);
+        const unsigned off = (unsigned)(r * (int)ld + 4 * (p ^ (r & 15))) * 4u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + inst * 256), 16, off, 0, 0,
+                                                 0);
     }
 }
 

@@ -179,8 +179,8 @@ int attn_bwd(const float* q, const float* k, const float* v, const float* out, c
     if ((long long)q_seq * num_heads * head_dim >= kMaxElems ||
         (long long)kv_len * num_kv_heads * head_dim >= kMaxElems)
         return TA03_ERR_UNSUPPORTED;
-    // The dk/dv kernel addresses 16 query rows with 32-bit byte offsets.
-    if ((long long)num_heads * head_dim >= (1ll << 25)) return TA03_ERR_UNSUPPORTED;
+    // The kernels address 16 query rows or 32 key rows with 32-bit byte offsets.
+    if ((long long)num_heads * head_dim >= (1ll << 24)) return TA03_ERR_UNSUPPORTED;
     if (q_seq == 0 && kv_len == 0) return TA03_OK;
     if (workspace_bytes < attn_bwd_workspace_bytes(q_seq, num_heads)) return TA03_ERR_WORKSPACE;
     if (q_seq > 0 && (q == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
