@@ -30,6 +30,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ta03_internal.h"
 
 namespace ta03 {
@@ -193,18 +195,22 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         }
     };
 
-    auto compute = [&](const Tile<D>& T, int t) {
+    auto compute = [&](const Tile<D>& T, int t, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         const int kv0 = t * kKeys;
         // S^T: row 4g + r is key kv0 + 4g + r, column j the query.
         f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < KS; ++st) s = mfma16(comp(T.kx[st / 4], st % 4), qr[st], s);
-        // The window mask is applied on every tile as a select: a branch
-        // here would put a block edge between the last product and the
-        // first vector read of its result, where the wait the matrix unit's
-        // result needs was found missing in the generated code.
+        // The window mask as a select (a branch here would put a block edge
+        // between the last product and the first vector read of its result,
+        // where the wait the matrix unit's result needs was found missing in
+        // the generated code); tiles inside every row's window run a version
+        // without it.
+        if constexpr (MASKED) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = kv0 + 4 * g + r < w_row ? s[r] : -INFINITY;
+            for (int r = 0; r < 4; ++r) s[r] = kv0 + 4 * g + r < w_row ? s[r] : -INFINITY;
+        }
         const float mx = pair_max32(pair_max16(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))));
         const float m_new = fmaxf(m_run, mx);
         const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -234,24 +240,37 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     };
 
     // Two register tiles, the next one in flight while the current one is
-    // consumed; loads never sit behind a branch inside the loop, so each
-    // wait covers exactly the tile it needs.
+    // consumed; loads never sit behind a branch inside a loop, so each wait
+    // covers exactly the tile it needs. The tiles inside every row's window
+    // (those before w_min) go first, in a loop without mask code; the rest
+    // follow with the mask. Each loop body is straight-line from the score
+    // products to the softmax.
+    const int w_min = a.causal ? min(a.start_pos + row0 + 1, a.kv_len) : a.kv_len;
+    const int t_int = w_min / kKeys;  // tiles before it need no mask
+    const std::false_type plain;
+    const std::true_type masked;
     if (t_begin < t_end) {
         Tile<D> A, B;
         load(A, t_begin);
         int t = t_begin;
+        for (; t + 2 < t_end && t + 1 < t_int; t += 2) {
+            load(B, t + 1);
+            compute(A, t, plain);
+            load(A, t + 2);
+            compute(B, t + 1, plain);
+        }
         for (; t + 2 < t_end; t += 2) {
             load(B, t + 1);
-            compute(A, t);
+            compute(A, t, masked);
             load(A, t + 2);
-            compute(B, t + 1);
+            compute(B, t + 1, masked);
         }
         if (t + 1 < t_end) {
             load(B, t + 1);
-            compute(A, t);
-            compute(B, t + 1);
+            compute(A, t, masked);
+            compute(B, t + 1, masked);
         } else {
-            compute(A, t);
+            compute(A, t, masked);
         }
     }
 
