@@ -28,6 +28,12 @@ HIP_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-product results and accumulators in vector registers: left to
+    # its heuristics, the compiler put some kernels' accumulators in the
+    # accumulator file and copied them to vector registers and back around
+    # every vector-ALU update (the online-softmax rescale, the decode's
+    # softmax), which costs vector-ALU time the f32 products share.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 
