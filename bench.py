@@ -12,7 +12,7 @@ and the decode over a paged cache (16- and 256-row pages).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--only prefill|decode] [--no-cpu-baseline]
-                    [--copy-calibration]
+                    [--copy-calibration] [--mfma-valu-probe]
 
 Timed region: barrier-free at one GPU; torch.cuda.synchronize() on both
 sides, wall clock around exactly K steps. Kernel durations come from HIP
@@ -418,6 +418,39 @@ def bench_decode_read(w, kv_pos_values, replays, torch, copies=8, device_pos=Fal
     return res
 
 
+def mfma_valu_probe(torch, iters=4000):
+    """Issue-rate probe (libta03_probe.so): one block per compute unit, one or
+    two waves per SIMD, f32 matrix instructions only, vector FMAs only, and
+    both in one loop; cycles per iteration per SIMD from the launch time at
+    2.4 GHz (the clock the 16K workload's busy-cycle counters show)."""
+    import ctypes
+    from tiled_attention_03_amd import binding
+    binding.lib()
+    probe = ctypes.CDLL(os.path.join(ROOT, "tiled_attention_03_amd", "libta03_probe.so"))
+    probe.ta03_probe_mfma_valu.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probe.ta03_probe_mfma_valu.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 512, device="cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for threads in (256, 512):
+        for mode, name in ((1, "matrix"), (2, "vector"), (3, "both")):
+            for _ in range(3):
+                assert probe.ta03_probe_mfma_valu(out.data_ptr(), cus, threads, iters, mode, st) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            assert probe.ta03_probe_mfma_valu(out.data_ptr(), cus, threads, iters, mode, st) == 0
+            e1.record()
+            torch.cuda.synchronize()
+            s = e0.elapsed_time(e1) * 1e-3
+            res[f"{threads // 256}_waves_per_simd_{name}"] = {
+                "ms": round(s * 1e3, 3), "cycles_per_iter_at_2.4GHz": round(s * 2.4e9 / iters)}
+    res["work_per_iter_per_wave"] = {"matrix": "32 v_mfma_f32_16x16x4_f32 (32 cycles each at "
+                                     "the f32 matrix peak)", "vector": "128 v_fma_f32"}
+    print(json.dumps({"mfma_valu_probe": res}), flush=True)
+
+
 def copy_calibration(torch, mib=1024, reps=3):
     """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
     dev = torch.device("cuda:0")
@@ -567,6 +600,8 @@ def main():
     ap.add_argument("--no-reported", action="store_true",
                     help="skip the smaller prefill workloads")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--mfma-valu-probe", action="store_true",
+                    help="only the matrix / vector-ALU issue-overlap probe")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -583,6 +618,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.mfma_valu_probe:
+        mfma_valu_probe(torch)
         return
 
     w = inputs.CAUSAL_16K

@@ -77,18 +77,20 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
-    # The benchmark's read-ceiling probe: a separate library on top of
-    # libta03.so (it uses the decode's launch plan), never loaded by the
-    # product path.
-    src = "probe_decode_read.hip"
-    obj = os.path.join(build_dir, "probe_decode_read.o")
-    cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    check_kernel_stubs(obj)
+    # The benchmark's probes (the decode's read ceiling, the matrix / vector
+    # ALU issue overlap): a separate library on top of libta03.so (the read
+    # probe uses the decode's launch plan), never loaded by the product path.
+    probe_objs = []
+    for src in ("probe_decode_read.hip", "probe_mfma_valu.hip"):
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        check_kernel_stubs(obj)
+        probe_objs.append(obj)
     tmp = PROBE_LIB + ".tmp"
-    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", obj, "-L", PKG, "-lta03",
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *probe_objs, "-L", PKG, "-lta03",
            "-Wl,-rpath,$ORIGIN", "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
