@@ -272,7 +272,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     auto issue_tile = [&](int t, float* kd) __attribute__((always_inline)) {
         float* vd = kd + TILE_F;
         const int kv0 = t * kBN;
-        if (!ROPE && a.small_strides) {
+        if (a.small_strides) {  // (the rotary instance copies V only: its K goes through registers)
             const int rows = min(kBN, w_block - kv0);
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<float*>(kbase + (size_t)kv0 * a.k_stride), 0, rows * (int)a.k_stride * 4,
@@ -285,8 +285,10 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 const int inst = wg + u * gw;
                 if (inst < LOADS) {
                     const unsigned ko = koff[u], vo = voff[u];
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + inst * 256), 16, ko,
-                                                             0, 0, 0);
+                    if constexpr (!ROPE) {
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + inst * 256), 16,
+                                                                 ko, 0, 0, 0);
+                    }
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + inst * 256), 16, vo,
                                                              0, 0, 0);
                 }
@@ -310,10 +312,51 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // Rotary keys: lane work item s of a tile is (row s / HC, chunk pair
     // (c, c + HC), c = s % HC), i.e. elements 4c..4c+3 and their partners
     // D/2 further on, with the (cos, sin) of pairs 4c..4c+3 at the row's
-    // position. Rows past the block's window are the last row, as above.
+    // position. With 32-bit tile offsets the rows come through buffer
+    // resources as the copies above do (rows past the window read as zero:
+    // their rotated keys are zero and masked); otherwise rows past the
+    // block's window are read as its last row.
     float4 rk[ROPE ? RMAX : 1][2], rc[ROPE ? RMAX : 1][2];
+    unsigned rko[ROPE ? RMAX : 1], rco[ROPE ? RMAX : 1];
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int u = 0; u < RMAX; ++u) {
+            const int s = (wg + u * gw) * 64 + lane;
+            const int r = s / HC, c = s % HC;
+            rko[u] = (unsigned)(r * (int)a.k_stride + 4 * c) * 4u;
+            rco[u] = (unsigned)(r * D + 8 * c) * 4u;
+        }
+    }
     auto load_k_rot = [&](int t) {
         const int kv0 = t * kBN;
+        if (a.small_strides) {
+            const int rows = min(kBN, w_block - kv0);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(kbase + (size_t)kv0 * a.k_stride), 0, rows * (int)a.k_stride * 4,
+                kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(a.rope_cs + (size_t)kv0 * D), 0, rows * D * 4, kBufferFlags);
+#pragma unroll
+            for (int u = 0; u < RMAX; ++u) {
+                const int inst = wg + u * gw;
+                if (inst < RP_INST) {
+                    const unsigned ko = rko[u], co = rco[u];
+                    const auto x0 = __builtin_amdgcn_raw_buffer_load_b128(rs, ko, 0, 0);
+                    const auto x1 = __builtin_amdgcn_raw_buffer_load_b128(rs, ko + 2u * D, 0, 0);
+                    const auto y0 = __builtin_amdgcn_raw_buffer_load_b128(rt, co, 0, 0);
+                    const auto y1 = __builtin_amdgcn_raw_buffer_load_b128(rt, co + 16u, 0, 0);
+                    rk[u][0] = make_float4(__int_as_float(x0[0]), __int_as_float(x0[1]),
+                                           __int_as_float(x0[2]), __int_as_float(x0[3]));
+                    rk[u][1] = make_float4(__int_as_float(x1[0]), __int_as_float(x1[1]),
+                                           __int_as_float(x1[2]), __int_as_float(x1[3]));
+                    rc[u][0] = make_float4(__int_as_float(y0[0]), __int_as_float(y0[1]),
+                                           __int_as_float(y0[2]), __int_as_float(y0[3]));
+                    rc[u][1] = make_float4(__int_as_float(y1[0]), __int_as_float(y1[1]),
+                                           __int_as_float(y1[2]), __int_as_float(y1[3]));
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < RMAX; ++u) {
             const int inst = wg + u * gw;
