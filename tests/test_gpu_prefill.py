@@ -330,3 +330,50 @@ def test_sub_batches_with_q_base(mode, sp):
                             kv_len=kv, start_pos=sp, scale=w.scale)
     check_out(out.cpu().numpy(), ro, f"sub-batches mode={mode}")
     check_lse(lse.cpu().numpy(), rl, f"sub-batches lse mode={mode}")
+
+
+@pytest.mark.parametrize("rope", [False, True], ids=["plain", "rotary"])
+@pytest.mark.parametrize("rows", ["auto", "16", "32"])
+@pytest.mark.parametrize("stride", [(1 << 24) + 64, (1 << 25) + 64], ids=["2^24", "2^25"])
+def test_row_strides_past_32bit_tile_offsets(stride, rows, rope, kernel_override):
+    """Q, K and V rows 2^24 + 64 or 2^25 + 64 floats apart (column slices of
+    one fused buffer of 40 such rows, 2.7 or 5.4 GB): the buffer-resource
+    tile copies need 32-bit tile offsets, so these launches take the general
+    copy path (and the 16-row kernel, which takes strides below 2^25, hands
+    the wider one to the 32-row kernel). Out and lse match the checker."""
+    import torch
+    import oracle
+    H, Hkv, d, n, sp = 4, 2, 64, 35, 5
+    kv = n + sp
+    if rows != "auto":
+        kernel_override(ta.OVERRIDE_PREFILL_ROWS, int(rows))
+    width = (H + 2 * Hkv) * d
+    qkv = inputs.normal((kv, width), 1300 + (stride >> 24))
+    q = np.ascontiguousarray(qkv[sp:, :H * d])
+    k = np.ascontiguousarray(qkv[:, H * d:(H + Hkv) * d])
+    v = np.ascontiguousarray(qkv[:, (H + Hkv) * d:])
+    dev = device()
+    log(f"row stride {stride} floats, {kv} rows: {kv * stride * 4 / 1e9:.1f} GB")
+    big = torch.empty((kv, stride), dtype=torch.float32, device=dev)
+    big[:, :width] = torch.from_numpy(qkv).to(dev)
+    out = torch.full((n, H * d), float("nan"), device=dev)
+    lse = torch.full((n, H, 2), float("nan"), device=dev)
+    scale = d ** -0.5
+    qv, kvv, vv = big[sp:, :H * d], big[:, H * d:(H + Hkv) * d], big[:, (H + Hkv) * d:]
+    table_ref = None
+    if rope:
+        table = torch.full((kv, d // 2, 2), float("nan"), dtype=torch.float32, device=dev)
+        ta.attn_rope_table(table, kv, d, 10000.0)
+        ta.attn_fwd_rope(qv, stride, kvv, stride, vv, stride, out, H * d, lse, 0, n, kv, H, Hkv,
+                         d, CAUSAL, sp, scale, table, kv)
+        table_ref = oracle.rope_table(kv, d, 10000.0)
+    else:
+        ta.attn_fwd_ex(qv, stride, kvv, stride, vv, stride, out, H * d, lse, 0, n, kv, H, Hkv, d,
+                       CAUSAL, sp, scale)
+    torch.cuda.synchronize()
+    del big
+    ro, rl = oracle.attention_forward(q, k, v, num_heads=H, num_kv_heads=Hkv, head_dim=d,
+                                      mode=CAUSAL, kv_len=kv, start_pos=sp, scale=scale,
+                                      rope=table_ref)
+    check_out(out.cpu().numpy(), ro, f"stride {stride} rows {rows} rope {rope}")
+    check_lse(lse.cpu().numpy(), rl, f"stride {stride} rows {rows} rope {rope} lse")
