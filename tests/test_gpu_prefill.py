@@ -377,3 +377,57 @@ def test_row_strides_past_32bit_tile_offsets(stride, rows, rope, kernel_override
                                       rope=table_ref)
     check_out(out.cpu().numpy(), ro, f"stride {stride} rows {rows} rope {rope}")
     check_lse(lse.cpu().numpy(), rl, f"stride {stride} rows {rows} rope {rope} lse")
+
+
+def _profile_case(profile, seed, mode, n, kv, H, Hkv, d, sp):
+    """Seeded inputs whose scores move a running max a lot: keys scaled up
+    (ramp_up) or down (ramp_down) along the sequence by up to 12x, a few
+    keys scaled 12x (spikes), or every score near -150 in log2 units
+    (far_below: queries along one direction, keys opposite to it). The
+    magnitudes stay where f32 dot products keep the scores within the lse
+    tolerance (|s| below ~110 in natural units)."""
+    w, q, k, v = inputs.random_case(seed, mode, n, kv, H, Hkv, d, start_pos=sp)
+    rows = k.shape[0]
+    ramp = (0.2 + 12.0 * np.arange(rows) / max(rows - 1, 1)).astype(np.float32)[:, None]
+    if profile == "ramp_up":
+        k = k * ramp
+    elif profile == "ramp_down":
+        k = k * ramp[::-1]
+    elif profile == "spikes":
+        idx = np.random.default_rng(seed).choice(rows, size=max(1, rows // 50), replace=False)
+        k = k.copy()
+        k[idx] *= np.float32(12.0)
+    elif profile == "far_below":
+        u = np.zeros(d, np.float32)
+        u[:: 3] = 1.0
+        u /= np.linalg.norm(u)
+        qh = q.reshape(q.shape[0], H, d)
+        kh = k.reshape(rows, Hkv, d)
+        q = (29.0 * u + 0.05 * qh).reshape(q.shape).astype(np.float32)
+        k = (-29.0 * u + 0.05 * kh).reshape(k.shape).astype(np.float32)
+    return w, np.ascontiguousarray(q), np.ascontiguousarray(k, dtype=np.float32), v
+
+
+@pytest.mark.parametrize("rows", ["auto", "16", "32"])
+@pytest.mark.parametrize("case", [(CAUSAL, 300, 300, 4, 2, 64, 0), (CAUSAL, 70, 400, 8, 2, 128, 330),
+                                  (CROSS, 70, 1500, 8, 8, 64, 0)],
+                         ids=["causal", "continuation", "cross_splits"])
+@pytest.mark.parametrize("profile", ["ramp_up", "ramp_down", "spikes", "far_below"])
+def test_score_profiles_that_move_the_running_max(profile, case, rows, kernel_override):
+    """Scores that climb by far more than 2^8 along the keys, fall, jump on a
+    few keys, or sit near -150 (log2 units) for every key: the 32-row
+    kernel's reference max moves many times, never, or from its first tile,
+    and out and lse (the true max and log-sum) still match the checker; the
+    cross case runs four key splits per block (their partial pairs are
+    merged after each is restored)."""
+    if rows != "auto":
+        kernel_override(ta.OVERRIDE_PREFILL_ROWS, int(rows))
+    mode, n, kv, H, Hkv, d, sp = case
+    w, q, k, v = _profile_case(profile, 1400 + 7 * ["ramp_up", "ramp_down", "spikes",
+                                                     "far_below"].index(profile),
+                               mode, n, kv, H, Hkv, d, sp)
+    go, gl, ro, rl = _run_both(w, q, k, v)
+    what = f"{profile} {case} rows={rows}"
+    log(f"{what}: lse max range {float(np.abs(rl[..., 0]).max()):.1f}")
+    check_out(go, ro, what)
+    check_lse(gl, rl, what)
