@@ -764,10 +764,15 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     if (grid <= 0) return hipSuccess;
     if (!rope) {
         // Fewer blocks than compute units: the 16-row kernel, which needs no
-        // shared tiles, spreads the work over more waves (a testing override
-        // can force either kernel on any shape the 16-row kernel takes).
+        // shared tiles, spreads the work over more waves. At one block per
+        // compute unit it still wins when the heads do not share K/V (group
+        // 1: full 1024^2 22.9 vs 24.2 us), and loses when a GQA group would
+        // share each tile through LDS (continuation 512 rows, group 4:
+        // 149.5 vs 138.6 us). A testing override can force either kernel on
+        // any shape the 16-row kernel takes.
         const int force = override_prefill_rows();
-        const bool use16 = (force != 0 ? force == 16 : grid < cus) && prefill16_fits(s);
+        const bool auto16 = grid < cus || (grid <= cus && a.group == 1);
+        const bool use16 = (force != 0 ? force == 16 : auto16) && prefill16_fits(s);
         if (use16) return launch_prefill16(q, k, v, out, lse, s, stream);
     }
     hipError_t e;
