@@ -206,7 +206,7 @@ int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStr
  * query tiles w, w + n, w + 2n, ... (every window spans the whole sequence). Recompute path: two launches (dq
  * with D_i, recomputing the scores; dk, dv). The stored path is taken when
  * the call is long enough for it to pay (the dq grid over the tiles fills the
- * device's compute units) and the workspace needs at most 16 windows;
+ * device's compute units) and the workspace needs at most 32 windows;
  * otherwise the call recomputes.
  * attn_set_kernel_override can force either path (testing). Both
  * paths run on stream with no allocation and no atomics (results are
@@ -230,9 +230,9 @@ size_t attn_bwd_workspace_bytes_stored(int q_seq, int kv_len, int num_heads, int
  * in which attn_bwd's stored path runs with a workspace of workspace_bytes
  * for these sizes (the fewest n for which every window w < n, the 16-row
  * query tiles w, w + n, w + 2n, ..., holds at most the dS tiles that fit past
- * the D_i scratch). 1 when every tile fits. 0 when no count up to 16 fits
+ * the D_i scratch). 1 when every tile fits. 0 when no count up to 32 fits
  * (the workspace is below the tiles of the longest query tile, or more than
- * 16 windows would be needed), for q_seq == 0 and for invalid sizes (as
+ * 32 windows would be needed), for q_seq == 0 and for invalid sizes (as
  * attn_bwd_workspace_bytes_stored); attn_bwd then recomputes. Whether a call
  * with a count above 0 takes the stored path also depends on its size (see
  * attn_bwd). Touches no device.

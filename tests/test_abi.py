@@ -254,7 +254,7 @@ def _tiles_per_query_tile(q_seq, kv_len, mode, start_pos):
 
 
 def test_bwd_windows(lib):
-    """attn_bwd_windows returns the fewest n <= 16 for which each interleaved
+    """attn_bwd_windows returns the fewest n <= 32 for which each interleaved
     window (query tiles w, w + n, ...) holds at most the tiles the workspace
     fits past the D_i scratch, 1 when every tile fits, 0 when no n does;
     tile counts by brute force over the query tiles."""
@@ -280,7 +280,8 @@ def test_bwd_windows(lib):
         total, longest = sum(per_qt), max(per_qt)
         base = lib.attn_bwd_workspace_bytes(q, H)
         caps = {longest - 1, longest, total - 1, total, total + 3, (total + 1) // 2,
-                (total + 8) // 9, max(longest, total // 20), max(longest, total // 14)}
+                (total + 8) // 9, max(longest, total // 20), max(longest, total // 14),
+                max(longest, total // 31), max(longest, total // 40)}
         caps |= {int(c) for c in rng.integers(longest, total + 2, size=6)}
         for cap in sorted(c for c in caps if c >= 0):
             ws = base + cap * H * 1024 + int(rng.integers(0, H * 1024))  # part of a tile is unused
@@ -290,10 +291,10 @@ def test_bwd_windows(lib):
                 return all(sum(per_qt[w::m]) <= cap for w in range(m))
 
             if n == 0:
-                assert not any(fits(m) for m in range(1, min(16, len(per_qt)) + 1)), (q, kv, cap)
+                assert not any(fits(m) for m in range(1, min(32, len(per_qt)) + 1)), (q, kv, cap)
                 checked[0] += 1
             else:
-                assert 1 <= n <= 16 and fits(n), (q, kv, H, mode, sp, cap, n)
+                assert 1 <= n <= 32 and fits(n), (q, kv, H, mode, sp, cap, n)
                 assert n == 1 or not fits(n - 1), (q, kv, H, mode, sp, cap, n)
                 assert (n == 1) == (total <= cap)
                 checked[1 if n == 1 else "many"] += 1

@@ -32,8 +32,7 @@
 // every head of its group that can see its keys (causal: rows from
 // key - start_pos on), Q and dout tiles streamed through LDS with their
 // (m, log l) and D. Per tile: S = Q K^T and dP = dout V^T (rows x keys), then
-// dv^T += dout^T P and dk^T += Q^T dS with P and dS in place. A first 32-key
-// version stays as an independent cross-check (TA03_BWD_KEYS=32).
+// dv^T += dout^T P and dk^T += Q^T dS with P and dS in place.
 
 #include <hip/hip_runtime.h>
 

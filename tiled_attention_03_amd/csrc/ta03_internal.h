@@ -145,9 +145,10 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
 // head (1: every tile at once); 0 when none up to max_win do.
 int backward_windows(const DsLayout& l, long long capacity, int max_win);
 // Windows chosen by size: each window past the first costs a dk/dv and a dq
-// launch (~0.6-0.95 ms on the 16K causal pass, where 24 windows already take
-// as long as recomputing the scores: 57.4 vs 59.4 ms).
-constexpr int kMaxBwdWindows = 16;
+// launch (on the 16K causal pass ~0.1-0.35 ms up to 16 windows, ~0.65 ms
+// beyond, where the launches hold fewer blocks than compute units; 32
+// windows take 54.7 ms against 57.7 ms recomputing the scores, 48 take 65.3).
+constexpr int kMaxBwdWindows = 32;
 
 // Rotary table: entry (p, e) = (cos, sin) of p * theta^(-2e/head_dim).
 hipError_t launch_rope_table(float* cs, int rows, int head_dim, double theta, hipStream_t stream);
