@@ -680,11 +680,10 @@ bwd_delta_kernel(const float* __restrict__ o, const float* __restrict__ dout,
 }
 
 // dq from stored dS. A block is 4 waves: dq_hg query heads of one GQA group
-// x dq_rs strips; a wave owns kDqRT query tiles of 16 rows of one head, and
-// the block streams the 16-key K tiles of its KV head through LDS (HBM ->
-// LDS directly, double-buffered), up to the window of its last query tile.
-// Per key tile and k-step t (keys 4g + t for lane group g), with
-// v_mfma_f32_16x16x4_f32:
+// x dq_rs strips; a wave owns RT query tiles of 16 rows of one head, and the
+// block streams the 16-key K tiles of its KV head through LDS (HBM -> LDS
+// directly), up to the window of its last query tile. Per key tile and k-step
+// t (keys 4g + t for lane group g), with v_mfma_f32_16x16x4_f32:
 //   A: lane (j, g) gives dS[row j][key 4g + t] -- one 16-byte load of the
 //      row-major tile per query tile covers all four k-steps;
 //   B: lane (j, g) gives K[key 4g + t][d] for d = 64 (b / 4) + 4 j + b % 4 in
@@ -694,183 +693,35 @@ bwd_delta_kernel(const float* __restrict__ o, const float* __restrict__ dout,
 //   result block b: register r of lane (j, g) is row 4g + r, column d, so a
 //      row's four column blocks store as one float4 per lane.
 // Tiles past a query tile's window (or query tiles past q_seq) are read
-// clamped to a valid tile and zeroed by a select. kDqRT query tiles per wave
-// (4: each K operand read serves 4 products); where that would leave the grid
-// short of blocks, bwd_dq_ds_ring_kernel takes one per wave.
-template <int D, int kDqRT>
-__global__ void __launch_bounds__(256, 2)
-bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
-                 float* __restrict__ dq, BwdArgs a) {
-    constexpr int NB = D / 16;
-    constexpr int CPR = D / 4;
-    constexpr int TILE_F = k16Keys * D;
-    constexpr int LOADS = TILE_F / 4 / 64;  // wave instructions per K tile (8 or 4)
-    constexpr int TF = k16Rows * k16Keys;   // floats per dS tile
-    // K tile double buffer as two LDS objects, named directly at every copy
-    // and read, so the reads of tile kt do not wait for tile kt+1's copies.
-    __shared__ __attribute__((aligned(16))) float kb0[TILE_F];
-    __shared__ __attribute__((aligned(16))) float kb1[TILE_F];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int j = lane & 15;
-    const int g = lane >> 4;
-
-    // Blocks in order of work, heaviest first; a grid resident all at once
-    // (round r: blocks r R .. r R + R - 1, one per compute unit as dispatched)
-    // takes them in snake order, so that every compute unit's blocks sum to
-    // about the same work.
-    int bid = blockIdx.x;
-    if (a.dq_round > 0) {
-        const int r = bid / a.dq_round, p = bid % a.dq_round;
-        const int cnt = min(a.dq_round, (int)gridDim.x - r * a.dq_round);
-        bid = r * a.dq_round + ((r & 1) ? cnt - 1 - p : p);
-    }
-    const int head_block = bid % a.dq_n_head_blocks;
-    const int seq = bid / a.dq_n_head_blocks;
-    const int rb = a.causal ? (a.dq_n_row_blocks - 1 - seq) : seq;  // heaviest first
-    const int head = head_block * a.dq_hg + wave % a.dq_hg;
-    const int strip = wave / a.dq_hg;
-    const int kv_head = head / a.group;
-    const int kvd = a.num_kv_heads * D;
-    // Local query tiles of the window (query tile win.off + j * win.stride).
-    const int j_first = (rb * a.dq_rs + strip) * kDqRT;
-    const int blk_j_last = min((rb + 1) * a.dq_rs * kDqRT, a.win.count) - 1;
-    const int n_kt = blk_j_last >= 0 ? ds_tiles_in(a.ds, a.win.off + blk_j_last * a.win.stride) : 0;
-
-    // Per query tile: first tile index (clamped query tile) and tile count.
-    long long tbase[kDqRT];
-    int tcount[kDqRT];
-    bool tlive[kDqRT];
-#pragma unroll
-    for (int rt = 0; rt < kDqRT; ++rt) {
-        const int jl = j_first + rt;
-        const int jc = min(jl, a.win.count - 1);
-        tlive[rt] = jl < a.win.count;
-        tcount[rt] = ds_tiles_in(a.ds, a.win.off + jc * a.win.stride);
-        tbase[rt] = (long long)head * a.ds_tph + ds_win_tiles_before(a.ds, a.win, jc);
-    }
-
-    auto issue_k = [&](int kt, float* dst) __attribute__((always_inline)) {
-#pragma unroll
-        for (int inst = wave; inst < LOADS; inst += 4) {
-            const int s_ = inst * 64 + lane;
-            const int r = s_ / CPR, c = s_ % CPR;
-            const int key = min(kt * k16Keys + r, a.kv_len - 1);
-            __builtin_amdgcn_global_load_lds(k + (size_t)key * kvd + kv_head * D + 4 * c,
-                                             (lds_void*)(dst + inst * 256), 16, 0, 0);
-        }
-    };
-    auto load_ds = [&](int kt, float4 (&x)[kDqRT]) {
-#pragma unroll
-        for (int rt = 0; rt < kDqRT; ++rt) {
-            const long long t = tbase[rt] + min(kt, max(tcount[rt] - 1, 0));
-            x[rt] = *reinterpret_cast<const float4*>(ds + (size_t)t * TF + 16 * j + 4 * g);
-        }
-    };
-
-    f32x4 acc[kDqRT][NB];
-#pragma unroll
-    for (int rt = 0; rt < kDqRT; ++rt)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto step = [&](int kt, const float4 (&cur)[kDqRT], float4 (&nxt)[kDqRT], const float* Ks,
-                    float* knext) __attribute__((always_inline)) {
-        wait_vmem();
-        __syncthreads();  // K tile kt landed for every wave; the other buffer is free
-        if (kt + 1 < n_kt) {  // block-uniform
-            issue_k(kt + 1, knext);
-            load_ds(kt + 1, nxt);
-        }
-        float av[kDqRT][4];
-#pragma unroll
-        for (int rt = 0; rt < kDqRT; ++rt) {
-            const bool live = tlive[rt] && kt < tcount[rt];
-            av[rt][0] = live ? cur[rt].x : 0.f;
-            av[rt][1] = live ? cur[rt].y : 0.f;
-            av[rt][2] = live ? cur[rt].z : 0.f;
-            av[rt][3] = live ? cur[rt].w : 0.f;
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float* kr = Ks + (4 * g + t) * D + 4 * j;
-            float kb[NB];
-#pragma unroll
-            for (int h2 = 0; h2 < NB / 4; ++h2) {
-                const float4 x = *reinterpret_cast<const float4*>(kr + 64 * h2);
-                kb[4 * h2 + 0] = x.x;
-                kb[4 * h2 + 1] = x.y;
-                kb[4 * h2 + 2] = x.z;
-                kb[4 * h2 + 3] = x.w;
-            }
-#pragma unroll
-            for (int rt = 0; rt < kDqRT; ++rt)
-#pragma unroll
-                for (int b = 0; b < NB; ++b) acc[rt][b] = mfma16(av[rt][t], kb[b], acc[rt][b]);
-        }
-    };
-
-    float4 da[kDqRT], db[kDqRT];
-    if (n_kt > 0) {
-        issue_k(0, kb0);
-        load_ds(0, da);
-    }
-    int kt = 0;
-    for (; kt + 1 < n_kt; kt += 2) {
-        step(kt, da, db, kb0, kb1);
-        step(kt + 1, db, da, kb1, kb0);
-    }
-    if (kt < n_kt) step(kt, da, db, kb0, kb1);
-    // The last products' results are read below by vector ALU instructions:
-    // keep the matrix-core result latency covered whatever path led here.
-    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-
-    const int qd = a.num_heads * D;
-#pragma unroll
-    for (int rt = 0; rt < kDqRT; ++rt) {
-        const int jl = j_first + rt;
-        if (jl >= a.win.count) break;  // wave-uniform: past the window
-        const int qt = a.win.off + jl * a.win.stride;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = qt * k16Rows + 4 * g + r;
-            if (row >= a.q_seq) continue;
-            float* dst = dq + (size_t)row * qd + head * D + 4 * j;
-#pragma unroll
-            for (int h2 = 0; h2 < NB / 4; ++h2) {
-                *reinterpret_cast<float4*>(dst + 64 * h2) = make_float4(
-                    acc[rt][4 * h2 + 0][r] * a.scale, acc[rt][4 * h2 + 1][r] * a.scale,
-                    acc[rt][4 * h2 + 2][r] * a.scale, acc[rt][4 * h2 + 3][r] * a.scale);
-            }
-        }
-    }
+// clamped to a valid tile and zeroed by a select. RT = 4 query tiles per wave
+// (each K operand read serves 4 products), 1 where that would leave the grid
+// short of blocks. K tiles stream through a ring of four LDS buffers and each
+// wave's dS tiles through a ring of four register sets, both issued three
+// steps ahead: with one query tile per wave a step is only 32 products per
+// wave, too short to cover a dS read from HBM issued one step ahead (with
+// four, one step ahead measured the same). Vector-memory counts complete in
+// issue order, so one wait for the current step's loads, with those of the
+// next two steps left in flight, covers K and dS.
+__host__ __device__ constexpr int waitcnt_vm(int n) {  // s_waitcnt vmcnt(n), other counters free
+    return 0x0F70 | (n & 15) | ((n >> 4) << 14);
 }
 
-// The same product with one query tile per wave, for grids the device holds
-// all at once (the stored path in windows). A step is then only 32 products
-// per wave, too short to cover a dS read from HBM issued one step ahead, so
-// K tiles stream through a ring of four LDS buffers and each wave's dS tiles
-// through a ring of four registers, both issued three steps ahead. Vector
-// memory counts complete in issue order, so one wait for the current step's
-// loads (those of the next two steps may stay in flight) covers K and dS.
-// Mapping, operands and epilogue as in bwd_dq_ds_kernel.
-template <int D>
+template <int D, int RT>
 __global__ void __launch_bounds__(256, 2)
-bwd_dq_ds_ring_kernel(const float* __restrict__ k, const float* __restrict__ ds,
+bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
                       float* __restrict__ dq, BwdArgs a) {
+    constexpr int NS = 4;  // ring slots: tiles issued NS - 1 steps ahead
     constexpr int NB = D / 16;
     constexpr int CPR = D / 4;
     constexpr int TILE_F = k16Keys * D;
     constexpr int LOADS = TILE_F / 4 / 64;  // wave instructions per K tile (8 or 4)
     constexpr int TF = k16Rows * k16Keys;   // floats per dS tile
     // Vector memory instructions a wave issues per step: its share of the K
-    // tile copy and one dS load.
-    constexpr int PER_STEP = LOADS / 4 + 1;
-    static_assert(PER_STEP <= 7, "vmcnt field of the waits below");
-    // Four LDS objects, named directly at every copy and read, so the reads of
-    // one tile do not wait for the copies of the others.
+    // tile copy and one dS load per query tile.
+    constexpr int PER_STEP = LOADS / 4 + RT;
+    static_assert((NS - 2) * PER_STEP < 64, "vmcnt range");
+    // One LDS object per slot, named directly at every copy and read, so the
+    // reads of one tile do not wait for the copies of the others.
     __shared__ __attribute__((aligned(16))) float kb0[TILE_F];
     __shared__ __attribute__((aligned(16))) float kb1[TILE_F];
     __shared__ __attribute__((aligned(16))) float kb2[TILE_F];
@@ -895,15 +746,23 @@ bwd_dq_ds_ring_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     const int strip = wave / a.dq_hg;
     const int kv_head = head / a.group;
     const int kvd = a.num_kv_heads * D;
-    const int jl = rb * a.dq_rs + strip;  // this wave's local query tile
-    const int blk_j_last = min((rb + 1) * a.dq_rs, a.win.count) - 1;
+    const int j_first = (rb * a.dq_rs + strip) * RT;  // this wave's first local query tile
+    const int blk_j_last = min((rb + 1) * a.dq_rs * RT, a.win.count) - 1;
     const int n_kt = blk_j_last >= 0 ? ds_tiles_in(a.ds, a.win.off + blk_j_last * a.win.stride) : 0;
-    const int jc = min(jl, a.win.count - 1);
-    const bool tlive = jl < a.win.count;
-    const int tcount = ds_tiles_in(a.ds, a.win.off + jc * a.win.stride);
-    const long long tbase = (long long)head * a.ds_tph + ds_win_tiles_before(a.ds, a.win, jc);
 
-    auto issue = [&](int kt, float* dst, float4& x) __attribute__((always_inline)) {
+    long long tbase[RT];
+    int tcount[RT];
+    bool tlive[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int jl = j_first + rt;
+        const int jc = min(jl, a.win.count - 1);
+        tlive[rt] = jl < a.win.count;
+        tcount[rt] = ds_tiles_in(a.ds, a.win.off + jc * a.win.stride);
+        tbase[rt] = (long long)head * a.ds_tph + ds_win_tiles_before(a.ds, a.win, jc);
+    }
+
+    auto issue = [&](int kt, float* dst, float4 (&x)[RT]) __attribute__((always_inline)) {
         // LOADS / 4 copies per wave (4 waves), a count the compiler sees, so
         // that it can count this wave's loads in flight at every wait.
 #pragma unroll
@@ -915,36 +774,44 @@ bwd_dq_ds_ring_kernel(const float* __restrict__ k, const float* __restrict__ ds,
             __builtin_amdgcn_global_load_lds(k + (size_t)key * kvd + kv_head * D + 4 * c,
                                              (lds_void*)(dst + inst * 256), 16, 0, 0);
         }
-        const long long t = tbase + min(kt, max(tcount - 1, 0));
-        x = *reinterpret_cast<const float4*>(ds + (size_t)t * TF + 16 * j + 4 * g);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const long long t = tbase[rt] + min(kt, max(tcount[rt] - 1, 0));
+            x[rt] = *reinterpret_cast<const float4*>(ds + (size_t)t * TF + 16 * j + 4 * g);
+        }
     };
 
-    f32x4 acc[NB];
+    f32x4 acc[RT][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Step kt reads K tile kt from Ks and dS tile kt from cur, and first
-    // issues tile kt + 3 into the buffers tile kt - 1 used.
-    auto step = [&](int kt, const float* Ks, float* kissue, const float4& cur, float4& nxt)
-        __attribute__((always_inline)) {
-        // Tile kt's loads complete while those of tiles kt + 1 and kt + 2 stay
+    // Step kt reads K tile kt from Ks and its dS tiles from cur, and first
+    // issues tile kt + NS - 1 into the buffers tile kt - 1 used.
+    auto step = [&](int kt, const float* Ks, float* kissue, const float4 (&cur)[RT],
+                    float4 (&nxt)[RT]) __attribute__((always_inline)) {
+        // Tile kt's loads complete while those of the next NS - 2 tiles stay
         // in flight (every step issues, past the last tile a clamped repeat,
         // so the count is fixed).
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PER_STEP));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * PER_STEP));
         // K tile kt landed for every wave; tile kt - 1's buffer is free. A
         // bare barrier: __syncthreads' fences would also wait for the copies
-        // of tiles kt + 1 and kt + 2, which write LDS. The wait above covers
-        // this wave's copies of tile kt, and every wave's reads of tile kt - 1
+        // of the tiles ahead, which write LDS. The wait above covers this
+        // wave's copies of tile kt, and every wave's reads of tile kt - 1
         // were consumed by its products before it arrived here; the clobber
         // keeps the compiler from moving memory accesses across.
         asm volatile("s_barrier" ::: "memory");
-        issue(kt + 3, kissue, nxt);
-        const bool live = tlive && kt < tcount;
-        float av[4];
-        av[0] = live ? cur.x : 0.f;
-        av[1] = live ? cur.y : 0.f;
-        av[2] = live ? cur.z : 0.f;
-        av[3] = live ? cur.w : 0.f;
+        issue(kt + NS - 1, kissue, nxt);
+        float av[RT][4];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const bool live = tlive[rt] && kt < tcount[rt];
+            av[rt][0] = live ? cur[rt].x : 0.f;
+            av[rt][1] = live ? cur[rt].y : 0.f;
+            av[rt][2] = live ? cur[rt].z : 0.f;
+            av[rt][3] = live ? cur[rt].w : 0.f;
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const float* kr = Ks + (4 * g + t) * D + 4 * j;
@@ -958,11 +825,14 @@ bwd_dq_ds_ring_kernel(const float* __restrict__ k, const float* __restrict__ ds,
                 kb[4 * h2 + 3] = x.w;
             }
 #pragma unroll
-            for (int b = 0; b < NB; ++b) acc[b] = mfma16(av[t], kb[b], acc[b]);
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[rt][b] = mfma16(av[rt][t], kb[b], acc[rt][b]);
         }
     };
 
-    float4 d0, d1, d2, d3;
+    float4 d0[RT], d1[RT], d2[RT], d3[RT];
+    int kt = 0;
     if (n_kt > 0) {  // block-uniform
         // Issued in tile order, as the steps do (the waits count on it).
         issue(0, kb0, d0);
@@ -971,7 +841,6 @@ bwd_dq_ds_ring_kernel(const float* __restrict__ k, const float* __restrict__ ds,
         asm volatile("" ::: "memory");
         issue(2, kb2, d2);
     }
-    int kt = 0;
     for (; kt + 4 <= n_kt; kt += 4) {
         step(kt, kb0, kb3, d0, d3);
         step(kt + 1, kb1, kb0, d1, d0);
@@ -983,24 +852,28 @@ bwd_dq_ds_ring_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     if (kt + 2 < n_kt) step(kt + 2, kb2, kb1, d2, d1);
     // The copies issued past the last tile land in LDS: wait for them before
     // the block can end and its LDS go to another block.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     // The last products' results are read below by vector ALU instructions:
     // keep the matrix-core result latency covered whatever path led here.
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
 
-    if (!tlive) return;  // wave-uniform: past the window
     const int qd = a.num_heads * D;
-    const int qt = a.win.off + jl * a.win.stride;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = qt * k16Rows + 4 * g + r;
-        if (row >= a.q_seq) continue;
-        float* dst = dq + (size_t)row * qd + head * D + 4 * j;
+    for (int rt = 0; rt < RT; ++rt) {
+        const int jl = j_first + rt;
+        if (jl >= a.win.count) break;  // wave-uniform: past the window
+        const int qt = a.win.off + jl * a.win.stride;
 #pragma unroll
-        for (int h2 = 0; h2 < NB / 4; ++h2) {
-            *reinterpret_cast<float4*>(dst + 64 * h2) =
-                make_float4(acc[4 * h2 + 0][r] * a.scale, acc[4 * h2 + 1][r] * a.scale,
-                            acc[4 * h2 + 2][r] * a.scale, acc[4 * h2 + 3][r] * a.scale);
+        for (int r = 0; r < 4; ++r) {
+            const int row = qt * k16Rows + 4 * g + r;
+            if (row >= a.q_seq) continue;
+            float* dst = dq + (size_t)row * qd + head * D + 4 * j;
+#pragma unroll
+            for (int h2 = 0; h2 < NB / 4; ++h2) {
+                *reinterpret_cast<float4*>(dst + 64 * h2) = make_float4(
+                    acc[rt][4 * h2 + 0][r] * a.scale, acc[rt][4 * h2 + 1][r] * a.scale,
+                    acc[rt][4 * h2 + 2][r] * a.scale, acc[rt][4 * h2 + 3][r] * a.scale);
+            }
         }
     }
 }
@@ -1051,7 +924,7 @@ long long dq_resident_blocks(int rt, int cus) {
         int n = 0;
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) == hipSuccess ? n : 0;
     };
-    static const int per_cu[2] = {occ(reinterpret_cast<const void*>(bwd_dq_ds_ring_kernel<D>)),
+    static const int per_cu[2] = {occ(reinterpret_cast<const void*>(bwd_dq_ds_kernel<D, 1>)),
                                   occ(reinterpret_cast<const void*>(bwd_dq_ds_kernel<D, 4>))};
     return (long long)per_cu[rt == 4 ? 1 : 0] * cus;
 }
@@ -1092,9 +965,9 @@ hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, con
                                                        delta, dk, dv, ds, a);
         if (e != hipSuccess) return e;
         // dq: 4 query tiles per wave while that still gives two blocks per
-        // CU, else one, through the ring kernel (then the device holds the
-        // whole grid at once and takes it in snake order; 2 per wave measured
-        // slower on the 16K causal pass in 9 windows).
+        // CU, else one (then the device holds the whole grid at once and
+        // takes it in snake order; 2 per wave measured slower on the 16K
+        // causal pass in 9 windows).
         const int tiles = a.win.count;
         const auto rows = [&](int rt) { return (tiles + a.dq_rs * rt - 1) / (a.dq_rs * rt); };
         a.dq_rt = (long long)a.dq_n_head_blocks * rows(4) >= 2 * cus ? 4 : 1;
@@ -1105,7 +978,7 @@ hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, con
             hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 4>), dim3((unsigned)grid), dim3(256), 0,
                                stream, k, ds, dq, a);
         } else {
-            hipLaunchKernelGGL((bwd_dq_ds_ring_kernel<D>), dim3((unsigned)grid), dim3(256), 0,
+            hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 1>), dim3((unsigned)grid), dim3(256), 0,
                                stream, k, ds, dq, a);
         }
     }
