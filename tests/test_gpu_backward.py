@@ -150,6 +150,38 @@ def test_backward_long_causal_sampled(path, kernel_override):
     log(f"  rows={len(rows)} keys={len(keys)} max|d| dq={e_q:.2e} dk={e_k:.2e} dv={e_v:.2e}")
 
 
+@pytest.mark.timeout(600)
+def test_backward_two_windows_four_tiles_per_wave():
+    """An 8192-row causal pass, 32 heads (MHA), head_dim 64, with the
+    smallest workspace that holds two interleaved windows: each window's dq
+    grid (32 head blocks x 16 row blocks of four 16-row query tiles per
+    wave) fills the compute units, so it takes four query tiles per wave, as
+    the single launch does; dq on sampled rows, dk, dv on sampled keys, of 8
+    of the 32 heads spread over the head blocks (the checker's cost)."""
+    n, H, d = 8192, 32, 64
+    w, q, k, v = inputs.random_case(1300, CAUSAL, n, n, H, H, d)
+    g = inputs.normal(q.shape, 1301)
+    per_qt = [-(-min(16 * t + 16, n) // 16) for t in range((n + 15) // 16)]  # causal
+    cap = max(sum(per_qt[0::2]), sum(per_qt[1::2]))
+    ws = ta.attn_bwd_workspace_bytes(n, H) + cap * H * 1024
+    assert ta.attn_bwd_windows(n, n, H, CAUSAL, 0, ws) == 2
+    log(f"backward two windows {n} rows H={H} d={d}, workspace {ws / 1e9:.2f} GB")
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, g, ws_bytes=ws, **_kw(w))
+    rng = np.random.default_rng(1302)
+    rows = np.unique(np.concatenate([[0, 15, 16, 17, 4095, 4096, n - 1],
+                                     rng.choice(n, 8, replace=False)]))
+    keys = np.unique(np.concatenate([[0, 1, 16, 4096, n - 17, n - 1],
+                                     rng.choice(n, 8, replace=False)]))
+    heads = [0, 5, 10, 15, 16, 21, 26, 31]  # MHA: KV head h is head h
+    rq, rk, rv, mq, mk, mv = oracle.attention_backward(q, k, v, g, rows=rows, keys=keys,
+                                                       kv_heads=heads, magnitudes=True, **_kw(w))
+    c = np.concatenate([np.arange(h * d, (h + 1) * d) for h in heads])
+    e_q = check_grad(dq[rows][:, c], rq[:, c], mq[:, c], n, "dq sampled")
+    e_k = check_grad(dk[keys][:, c], rk[:, c], mk[:, c], n, "dk sampled")
+    e_v = check_grad(dv[keys][:, c], rv[:, c], mv[:, c], n, "dv sampled")
+    log(f"  rows={len(rows)} keys={len(keys)} max|d| dq={e_q:.2e} dk={e_k:.2e} dv={e_v:.2e}")
+
+
 BWD_SWEEP = [
     # mode, q_seq, kv_len, H, Hkv, d, start_pos
     (CAUSAL, 1, 1, 1, 1, 64, 0),

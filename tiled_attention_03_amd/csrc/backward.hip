@@ -416,6 +416,10 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
             vr[4 * c + 2] = y.z;
             vr[4 * c + 3] = y.w;
         }
+        // Let K and V land here: a V register still in flight at the loop
+        // made the compiler wait for every load (the stage copies too) at its
+        // first use inside every stage.
+        wait_vmem();
     }
 
     f32x4 dka[NB], dva[NB];
@@ -513,10 +517,29 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     };
 
     const int n_st = (total + SUB - 1) / SUB;
+    // dS tiles this wave stored in the previous stage, after that stage's
+    // copies (four store instructions each).
+    int stored_prev = 0;
     auto stage = [&](int st, const float* rt, const float* rv, float* wt, float* wv)
         __attribute__((always_inline)) {
-        wait_vmem();
-        __syncthreads();  // stage st landed for every wave; the other buffer is free
+        if constexpr (STORE) {
+            // Vector-memory counts complete in issue order: this stage's
+            // copies are done once at most the previous stage's dS stores
+            // are in flight, which need not be complete here (nothing in this
+            // kernel reads them). A bare barrier: __syncthreads' fences would
+            // wait for every store too.
+            if (stored_prev == 0)
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+            else if (stored_prev == 1)
+                __builtin_amdgcn_s_waitcnt(0x0F74);
+            else
+                __builtin_amdgcn_s_waitcnt(0x0F78);
+            asm volatile("s_barrier" ::: "memory");
+            stored_prev = 0;
+        } else {
+            wait_vmem();
+            __syncthreads();  // stage st landed for every wave; the other buffer is free
+        }
         // The next stage's copies go between the first sub-tile's score
         // products when this wave computes it, else here.
         const int rows_hi0 = min(qt_of(st * SUB) * k16Rows + k16Rows, a.q_seq);
@@ -580,6 +603,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                         key0 / k16Keys) * (k16Rows * k16Keys);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) tile[(4 * g + r) * k16Keys + j] = dp[r];
+                    ++stored_prev;
                 }
                 // dv^T += dout^T P, dk^T += Q^T dS: k-step t of lane group g is
                 // query row 4g + t; lane (m, g) reads head-dims 4m .. 4m + 3 (and
