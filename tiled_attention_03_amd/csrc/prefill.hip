@@ -559,15 +559,19 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             // O^T += V^T P^T: k-step t pairs keys acc_row(t, 0) and acc_row(t, 1).
 #pragma unroll
             for (int tt = 0; tt < 16; ++tt) {
-                const float* vr = Vs + acc_row(tt, hh) * D + NB * j;
+                // (Indexed from the tile's base: with the address formed as
+                // a float pointer plus offsets, the compiler lost track of which
+                // LDS buffer these reads use and waited for the next tile's
+                // copies before them.)
+                const int vi = acc_row(tt, hh) * (D / NB) + j;  // in NB-float units
                 if constexpr (NB == 4) {
-                    const float4 vv = *reinterpret_cast<const float4*>(vr);
+                    const float4 vv = reinterpret_cast<const float4*>(Vs)[vi];
                     o[0] = mfma32(vv.x, s[tt], o[0]);
                     o[1] = mfma32(vv.y, s[tt], o[1]);
                     o[2] = mfma32(vv.z, s[tt], o[2]);
                     o[3] = mfma32(vv.w, s[tt], o[3]);
                 } else {
-                    const float2 vv = *reinterpret_cast<const float2*>(vr);
+                    const float2 vv = reinterpret_cast<const float2*>(Vs)[vi];
                     o[0] = mfma32(vv.x, s[tt], o[0]);
                     o[1] = mfma32(vv.y, s[tt], o[1]);
                 }
