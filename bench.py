@@ -570,14 +570,14 @@ def backward_legs(w, torch, ta):
         "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
         "workspace_bytes": r["workspace_bytes"],
         "kernels": "bwd_delta_kernel<128> + bwd_dkdv16_kernel<128, 4, true> + "
-                   "bwd_dq_ds_kernel<128, 4>",
+                   "bwd_dq_ds_kernel<128, 4, 1>",
         "bounded": {"ms": round(rb["mean_s"] * 1e3, 3),
                     "TFLOP/s": round(rb["tflops_kernel"], 3),
                     "frac": round(rb["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
                     "workspace_bytes": rb["workspace_bytes"],
                     "kernels": "stored-dS path in windows of query tiles: "
                                "bwd_delta_kernel<128>, then per window "
-                               "bwd_dkdv16_kernel<128, 4, true> + bwd_dq_ds_kernel<128, 1>"},
+                               "bwd_dkdv16_kernel<128, 4, true> + bwd_dq_ds_kernel<128, 1, 1>"},
         "recompute_path": {"ms": round(rr["mean_s"] * 1e3, 3),
                            "TFLOP/s": round(rr["tflops_kernel"], 3),
                            "frac": round(rr["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),

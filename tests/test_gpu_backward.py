@@ -182,6 +182,39 @@ def test_backward_two_windows_four_tiles_per_wave():
     log(f"  rows={len(rows)} keys={len(keys)} max|d| dq={e_q:.2e} dk={e_k:.2e} dv={e_v:.2e}")
 
 
+@pytest.mark.timeout(600)
+def test_backward_windows_mid_size_dq_grids():
+    """An 8192-row causal pass, 32 / 8 heads, head_dim 128, in eleven
+    interleaved windows: each window's dq grid (8 head blocks x 47 query
+    tiles, one per wave) is between one and two blocks per compute unit,
+    the range where the dq kernel splits each block's keys two ways; dq on
+    sampled rows, dk, dv on sampled keys, of two of the eight KV heads (the
+    checker's cost)."""
+    n, H, Hkv, d = 8192, 32, 8, 128
+    w, q, k, v = inputs.random_case(1310, CAUSAL, n, n, H, Hkv, d)
+    g = inputs.normal(q.shape, 1311)
+    ws = windowed_bytes(n, n, H, CAUSAL, 0, parts=10)
+    assert ta.attn_bwd_windows(n, n, H, CAUSAL, 0, ws) == 11
+    log(f"backward 11 windows {n} rows H={H}/{Hkv} d={d}, workspace {ws / 1e9:.2f} GB")
+    dq, dk, dv = gpu_fwd_bwd(q, k, v, g, ws_bytes=ws, **_kw(w))
+    rng = np.random.default_rng(1312)
+    rows = np.unique(np.concatenate([[0, 15, 16, 175, 176, 4095, n - 1],
+                                     rng.choice(n, 8, replace=False)]))
+    keys = np.unique(np.concatenate([[0, 1, 16, 4096, n - 17, n - 1],
+                                     rng.choice(n, 8, replace=False)]))
+    kvh = [2, 7]
+    rq, rk, rv, mq, mk, mv = oracle.attention_backward(q, k, v, g, rows=rows, keys=keys,
+                                                       kv_heads=kvh, magnitudes=True, **_kw(w))
+    cq = np.concatenate([np.arange(h * d, (h + 1) * d)
+                         for c in kvh for h in range(c * (H // Hkv), (c + 1) * (H // Hkv))])
+    ck = np.concatenate([np.arange(c * d, (c + 1) * d) for c in kvh])
+    n_rows = n * (H // Hkv)
+    e_q = check_grad(dq[rows][:, cq], rq[:, cq], mq[:, cq], n, "dq sampled")
+    e_k = check_grad(dk[keys][:, ck], rk[:, ck], mk[:, ck], n_rows, "dk sampled")
+    e_v = check_grad(dv[keys][:, ck], rv[:, ck], mv[:, ck], n_rows, "dv sampled")
+    log(f"  rows={len(rows)} keys={len(keys)} max|d| dq={e_q:.2e} dk={e_k:.2e} dv={e_v:.2e}")
+
+
 BWD_SWEEP = [
     # mode, q_seq, kv_len, H, Hkv, d, start_pos
     (CAUSAL, 1, 1, 1, 1, 64, 0),

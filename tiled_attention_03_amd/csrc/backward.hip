@@ -703,11 +703,12 @@ bwd_delta_kernel(const float* __restrict__ o, const float* __restrict__ dout,
     if (l16 == 0 && pair < n_pairs) delta[pair] = acc;
 }
 
-// dq from stored dS. A block is 4 waves: dq_hg query heads of one GQA group
-// x dq_rs strips; a wave owns RT query tiles of 16 rows of one head, and the
-// block streams the 16-key K tiles of its KV head through LDS (HBM -> LDS
-// directly), up to the window of its last query tile. Per key tile and k-step
-// t (keys 4g + t for lane group g), with v_mfma_f32_16x16x4_f32:
+// dq from stored dS. A block is 4 KS waves: KS key splits of 4 waves, the 4
+// waves being dq_hg query heads of one GQA group x dq_rs strips; a wave owns
+// RT query tiles of 16 rows of one head, and each split streams its share of
+// the 16-key K tiles of the block's KV head (up to the window of its last
+// query tile) through LDS (HBM -> LDS directly). Per key tile and k-step t
+// (keys 4g + t for lane group g), with v_mfma_f32_16x16x4_f32:
 //   A: lane (j, g) gives dS[row j][key 4g + t] -- one 16-byte load of the
 //      row-major tile per query tile covers all four k-steps;
 //   B: lane (j, g) gives K[key 4g + t][d] for d = 64 (b / 4) + 4 j + b % 4 in
@@ -719,21 +720,27 @@ bwd_delta_kernel(const float* __restrict__ o, const float* __restrict__ dout,
 // Tiles past a query tile's window (or query tiles past q_seq) are read
 // clamped to a valid tile and zeroed by a select. RT = 4 query tiles per wave
 // (each K operand read serves 4 products), 1 where that would leave the grid
-// short of blocks. K tiles stream through a ring of four LDS buffers and each
-// wave's dS tiles through a ring of four register sets, both issued three
-// steps ahead: with one query tile per wave a step is only 32 products per
-// wave, too short to cover a dS read from HBM issued one step ahead (with
-// four, one step ahead measured the same). Vector-memory counts complete in
-// issue order, so one wait for the current step's loads, with those of the
-// next two steps left in flight, covers K and dS.
+// short of blocks; then KS = 2 or 4 key splits where the grid is short even
+// so: a window's dq launch otherwise lasts as long as one wave's walk over
+// the keys of its last query tile, whatever the window's size. The splits'
+// partial dq meet in LDS and are added in split order (deterministic).
+// K tiles stream through a ring of four LDS buffers and each wave's dS tiles
+// through a ring of four register sets, both issued three steps ahead: with
+// one query tile per wave a step is only 32 products per wave, too short to
+// cover a dS read from HBM issued one step ahead (with four, one step ahead
+// measured the same). Vector-memory counts complete in issue order, so one
+// wait for the current step's loads, with those of the next two steps left
+// in flight, covers K and dS.
 __host__ __device__ constexpr int waitcnt_vm(int n) {  // s_waitcnt vmcnt(n), other counters free
     return 0x0F70 | (n & 15) | ((n >> 4) << 14);
 }
 
-template <int D, int RT>
-__global__ void __launch_bounds__(256, 2)
+template <int D, int RT, int KS>
+__global__ void __launch_bounds__(256 * KS, KS == 1 ? 2 : 1)
 bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
-                      float* __restrict__ dq, BwdArgs a) {
+                 float* __restrict__ dq, BwdArgs a) {
+    static_assert(KS == 1 || KS == 2 || KS == 4, "one, two or four key splits");
+    static_assert(KS == 1 || RT == 1, "key splits with one query tile per wave");
     constexpr int NS = 4;  // ring slots: tiles issued NS - 1 steps ahead
     constexpr int NB = D / 16;
     constexpr int CPR = D / 4;
@@ -744,16 +751,19 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     // tile copy and one dS load per query tile.
     constexpr int PER_STEP = LOADS / 4 + RT;
     static_assert((NS - 2) * PER_STEP < 64, "vmcnt range");
-    // One LDS object per slot, named directly at every copy and read, so the
-    // reads of one tile do not wait for the copies of the others.
-    __shared__ __attribute__((aligned(16))) float kb0[TILE_F];
-    __shared__ __attribute__((aligned(16))) float kb1[TILE_F];
-    __shared__ __attribute__((aligned(16))) float kb2[TILE_F];
-    __shared__ __attribute__((aligned(16))) float kb3[TILE_F];
+    // One LDS object per slot (each holding the slot of every split), named
+    // directly at every copy and read, so the reads of one tile do not wait
+    // for the copies of the others.
+    __shared__ __attribute__((aligned(16))) float kb0[KS * TILE_F];
+    __shared__ __attribute__((aligned(16))) float kb1[KS * TILE_F];
+    __shared__ __attribute__((aligned(16))) float kb2[KS * TILE_F];
+    __shared__ __attribute__((aligned(16))) float kb3[KS * TILE_F];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int split = KS == 1 ? 0 : wave >> 2;  // key split
+    const int wq = KS == 1 ? wave : wave & 3;     // wave of the split: (head, strip)
     const int j = lane & 15;
     const int g = lane >> 4;
 
@@ -766,13 +776,18 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     const int head_block = bid % a.dq_n_head_blocks;
     const int seq = bid / a.dq_n_head_blocks;
     const int rb = a.causal ? (a.dq_n_row_blocks - 1 - seq) : seq;  // heaviest first
-    const int head = head_block * a.dq_hg + wave % a.dq_hg;
-    const int strip = wave / a.dq_hg;
+    const int head = head_block * a.dq_hg + wq % a.dq_hg;
+    const int strip = wq / a.dq_hg;
     const int kv_head = head / a.group;
     const int kvd = a.num_kv_heads * D;
     const int j_first = (rb * a.dq_rs + strip) * RT;  // this wave's first local query tile
     const int blk_j_last = min((rb + 1) * a.dq_rs * RT, a.win.count) - 1;
-    const int n_kt = blk_j_last >= 0 ? ds_tiles_in(a.ds, a.win.off + blk_j_last * a.win.stride) : 0;
+    const int n_blk = blk_j_last >= 0 ? ds_tiles_in(a.ds, a.win.off + blk_j_last * a.win.stride) : 0;
+    // Split s walks key tiles s n_kt .. s n_kt + n_kt - 1 (every split the
+    // same step count: the barriers are block-wide).
+    const int n_kt = (n_blk + KS - 1) / KS;
+    const int kt0 = split * n_kt;
+    const int so = split * TILE_F;  // this split's slot in each buffer (floats)
 
     long long tbase[RT];
     int tcount[RT];
@@ -786,21 +801,22 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
         tbase[rt] = (long long)head * a.ds_tph + ds_win_tiles_before(a.ds, a.win, jc);
     }
 
+    // Step kt of this split: key tile kt0 + kt.
     auto issue = [&](int kt, float* dst, float4 (&x)[RT]) __attribute__((always_inline)) {
-        // LOADS / 4 copies per wave (4 waves), a count the compiler sees, so
-        // that it can count this wave's loads in flight at every wait.
+        // LOADS / 4 copies per wave (4 waves per split), a count the compiler
+        // sees, so that it can count this wave's loads in flight at every wait.
 #pragma unroll
         for (int i = 0; i < LOADS / 4; ++i) {
-            const int inst = wave + 4 * i;
+            const int inst = wq + 4 * i;
             const int s_ = inst * 64 + lane;
             const int r = s_ / CPR, c = s_ % CPR;
-            const int key = min(kt * k16Keys + r, a.kv_len - 1);
+            const int key = min((kt0 + kt) * k16Keys + r, a.kv_len - 1);
             __builtin_amdgcn_global_load_lds(k + (size_t)key * kvd + kv_head * D + 4 * c,
-                                             (lds_void*)(dst + inst * 256), 16, 0, 0);
+                                             (lds_void*)(dst + (so + inst * 256)), 16, 0, 0);
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const long long t = tbase[rt] + min(kt, max(tcount[rt] - 1, 0));
+            const long long t = tbase[rt] + min(kt0 + kt, max(tcount[rt] - 1, 0));
             x[rt] = *reinterpret_cast<const float4*>(ds + (size_t)t * TF + 16 * j + 4 * g);
         }
     };
@@ -811,8 +827,9 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[rt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Step kt reads K tile kt from Ks and its dS tiles from cur, and first
-    // issues tile kt + NS - 1 into the buffers tile kt - 1 used.
+    // Step kt reads K tile kt0 + kt from the split's slot of buffer Ks and its
+    // dS tiles from cur, and first issues tile kt + NS - 1 into the buffers
+    // tile kt - 1 used.
     auto step = [&](int kt, const float* Ks, float* kissue, const float4 (&cur)[RT],
                     float4 (&nxt)[RT]) __attribute__((always_inline)) {
         // Tile kt's loads complete while those of the next NS - 2 tiles stay
@@ -830,7 +847,7 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
         float av[RT][4];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const bool live = tlive[rt] && kt < tcount[rt];
+            const bool live = tlive[rt] && kt0 + kt < tcount[rt];
             av[rt][0] = live ? cur[rt].x : 0.f;
             av[rt][1] = live ? cur[rt].y : 0.f;
             av[rt][2] = live ? cur[rt].z : 0.f;
@@ -838,11 +855,14 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float* kr = Ks + (4 * g + t) * D + 4 * j;
+            // (Indexed from the buffer object itself: with the split's slot
+            // as a separate pointer the compiler lost track of which buffer
+            // these reads use and waited for every copy in flight.)
+            const int kr = (so + (4 * g + t) * D + 4 * j) / 4;  // in float4 units
             float kb[NB];
 #pragma unroll
             for (int h2 = 0; h2 < NB / 4; ++h2) {
-                const float4 x = *reinterpret_cast<const float4*>(kr + 64 * h2);
+                const float4 x = reinterpret_cast<const float4*>(Ks)[kr + 16 * h2];
                 kb[4 * h2 + 0] = x.x;
                 kb[4 * h2 + 1] = x.y;
                 kb[4 * h2 + 2] = x.z;
@@ -877,9 +897,42 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     // The copies issued past the last tile land in LDS: wait for them before
     // the block can end and its LDS go to another block.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    // The last products' results are read below by vector ALU instructions:
-    // keep the matrix-core result latency covered whatever path led here.
+    // The last products' results are read below by vector ALU and LDS
+    // instructions: keep the matrix-core result latency covered whatever
+    // path led here.
     asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+
+    if constexpr (KS > 1) {
+        // Splits 1 .. KS - 1 leave their partial dq in the tile buffers (one
+        // TILE_F region per wave: block b of lane l at float4 b 64 + l), and
+        // split 0 adds them in split order. Region r is slot r % KS of
+        // buffer r / KS (16 D floats = one K tile each).
+        asm volatile("s_barrier" ::: "memory");  // every wave is done with the tiles
+        auto region = [&](int r) -> float* {
+            const int o = (r % KS) * TILE_F;
+            return r < KS ? kb0 + o : r < 2 * KS ? kb1 + o : r < 3 * KS ? kb2 + o : kb3 + o;
+        };
+        if (split > 0) {
+            float4* p = reinterpret_cast<float4*>(region((split - 1) * 4 + wq));
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                p[b * 64 + lane] = make_float4(acc[0][b][0], acc[0][b][1], acc[0][b][2], acc[0][b][3]);
+        }
+        __syncthreads();
+        if (split > 0) return;
+#pragma unroll 1
+        for (int s = 1; s < KS; ++s) {
+            const float4* p = reinterpret_cast<const float4*>(region((s - 1) * 4 + wq));
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const float4 x = p[b * 64 + lane];
+                acc[0][b][0] += x.x;
+                acc[0][b][1] += x.y;
+                acc[0][b][2] += x.z;
+                acc[0][b][3] += x.w;
+            }
+        }
+    }
 
     const int qd = a.num_heads * D;
 #pragma unroll
@@ -941,16 +994,18 @@ hipError_t launch_dkdv16_any(size_t lds, hipStream_t stream, const float* q, con
                                       ds, a);
 }
 
-// Blocks of the dq-from-dS kernel that the device holds at once.
-template <int D>
-long long dq_resident_blocks(int rt, int cus) {
-    const auto occ = [](const void* f) {
+// Blocks of one dq-from-dS instance that the device holds at once.
+template <int D, int RT, int KS>
+long long dq_resident_blocks(int cus) {
+    static const int per_cu = [] {
         int n = 0;
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) == hipSuccess ? n : 0;
-    };
-    static const int per_cu[2] = {occ(reinterpret_cast<const void*>(bwd_dq_ds_kernel<D, 1>)),
-                                  occ(reinterpret_cast<const void*>(bwd_dq_ds_kernel<D, 4>))};
-    return (long long)per_cu[rt == 4 ? 1 : 0] * cus;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &n, reinterpret_cast<const void*>(bwd_dq_ds_kernel<D, RT, KS>), 256 * KS, 0) ==
+                       hipSuccess
+                   ? n
+                   : 0;
+    }();
+    return (long long)per_cu * cus;
 }
 
 // The stored-dS path over windows of query tiles (one window when the
@@ -989,21 +1044,28 @@ hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, con
                                                        delta, dk, dv, ds, a);
         if (e != hipSuccess) return e;
         // dq: 4 query tiles per wave while that still gives two blocks per
-        // CU, else one (then the device holds the whole grid at once and
-        // takes it in snake order; 2 per wave measured slower on the 16K
-        // causal pass in 9 windows).
+        // CU, else one (2 per wave measured slower on the 16K causal pass in 9
+        // windows), with the keys split 4 or 2 ways inside each block where
+        // the device then holds the whole grid at once. A grid the device
+        // holds at once takes its blocks in snake order.
         const int tiles = a.win.count;
         const auto rows = [&](int rt) { return (tiles + a.dq_rs * rt - 1) / (a.dq_rs * rt); };
         a.dq_rt = (long long)a.dq_n_head_blocks * rows(4) >= 2 * cus ? 4 : 1;
         a.dq_n_row_blocks = rows(a.dq_rt);
         const long long grid = (long long)a.dq_n_head_blocks * a.dq_n_row_blocks;
-        a.dq_round = grid <= dq_resident_blocks<D>(a.dq_rt, cus) ? cus : 0;
+        const dim3 g1((unsigned)grid);
         if (a.dq_rt == 4) {
-            hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 4>), dim3((unsigned)grid), dim3(256), 0,
-                               stream, k, ds, dq, a);
+            a.dq_round = grid <= dq_resident_blocks<D, 4, 1>(cus) ? cus : 0;
+            hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 4, 1>), g1, dim3(256), 0, stream, k, ds, dq, a);
+        } else if (grid <= dq_resident_blocks<D, 1, 4>(cus)) {
+            a.dq_round = cus;
+            hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 1, 4>), g1, dim3(1024), 0, stream, k, ds, dq, a);
+        } else if (grid <= dq_resident_blocks<D, 1, 2>(cus)) {
+            a.dq_round = cus;
+            hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 1, 2>), g1, dim3(512), 0, stream, k, ds, dq, a);
         } else {
-            hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 1>), dim3((unsigned)grid), dim3(256), 0,
-                               stream, k, ds, dq, a);
+            a.dq_round = grid <= dq_resident_blocks<D, 1, 1>(cus) ? cus : 0;
+            hipLaunchKernelGGL((bwd_dq_ds_kernel<D, 1, 1>), g1, dim3(256), 0, stream, k, ds, dq, a);
         }
     }
     return hipSuccess;

@@ -145,9 +145,9 @@ hipError_t launch_backward(const float* q, const float* k, const float* v, const
 // head (1: every tile at once); 0 when none up to max_win do.
 int backward_windows(const DsLayout& l, long long capacity, int max_win);
 // Windows chosen by size: each window past the first costs a dk/dv and a dq
-// launch (on the 16K causal pass ~0.1-0.35 ms up to 16 windows, ~0.65 ms
-// beyond, where the launches hold fewer blocks than compute units; 32
-// windows take 54.7 ms against 57.7 ms recomputing the scores, 48 take 65.3).
+// launch (on the 16K causal pass ~0.1-0.35 ms up to 16 windows, ~0.6 ms
+// beyond, where a window's dq lasts as long as its heaviest block; 32 windows
+// take 52.6 ms against 57.6 ms recomputing the scores).
 constexpr int kMaxBwdWindows = 32;
 
 // Rotary table: entry (p, e) = (cos, sin) of p * theta^(-2e/head_dim).
