@@ -166,7 +166,7 @@ def warm_replays(graph, torch, seconds=0.15):
 
 
 def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None,
-                  fused_qkv=False, clock=None):
+                  fused_qkv=False, clock=None, rope_keys_once=False):
     """Prefill timing. With graph_replays > 0 the call is captured once in a
     HIP graph and replayed back to back (for kernels shorter than a Python
     launch); otherwise each call is launched eagerly between events. With
@@ -174,7 +174,9 @@ def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None,
     timed calls; the rotation is not counted in the FLOPs). With fused_qkv,
     q, k and v are column slices of one [rows, (H + 2 Hkv) d] buffer and out
     is written into a buffer with 64 floats of padding per row
-    (attn_fwd_ex with row strides)."""
+    (attn_fwd_ex with row strides). With rope_keys_once each timed call
+    turns the keys once into a scratch copy (attn_rope_apply) and then runs
+    attn_fwd_rope_q, which turns only the queries (both in the time)."""
     dev = torch.device("cuda:0")
     q, k, v = inputs.make_prefill(w)
     qdim = w.num_heads * w.head_dim
@@ -207,10 +209,20 @@ def bench_prefill(w, steps, warmup, torch, ta, graph_replays=0, rope_theta=None,
         table = torch.empty((rows, w.head_dim // 2, 2), device=dev)
         ta.attn_rope_table(table, rows, w.head_dim, rope_theta)
 
-        def call(_i):
-            ta.attn_fwd_rope(qd, qdim, kd, kvdim, vd, kvdim, out, qdim, lse, 0, w.q_seq,
-                             w.kv_len, w.num_heads, w.num_kv_heads, w.head_dim, w.mode,
-                             w.start_pos, w.scale, table, rows)
+        if rope_keys_once:
+            k_rot = torch.empty_like(kd)
+
+            def call(_i):
+                ta.attn_rope_apply(kd, kvdim, k_rot, kvdim, w.kv_len, w.num_kv_heads,
+                                   w.head_dim, 0, table, rows)
+                ta.attn_fwd_rope_q(qd, qdim, k_rot, kvdim, vd, kvdim, out, qdim, lse, 0,
+                                   w.q_seq, w.kv_len, w.num_heads, w.num_kv_heads, w.head_dim,
+                                   w.mode, w.start_pos, w.scale, table, rows)
+        else:
+            def call(_i):
+                ta.attn_fwd_rope(qd, qdim, kd, kvdim, vd, kvdim, out, qdim, lse, 0, w.q_seq,
+                                 w.kv_len, w.num_heads, w.num_kv_heads, w.head_dim, w.mode,
+                                 w.start_pos, w.scale, table, rows)
 
     flops = prefill_flops(w)
     if graph_replays > 0:
@@ -663,7 +675,7 @@ def main():
                          "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(p["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
                          "traffic": stored_traffic(PREFILL_TRAFFIC),
-                         "kernel": "prefill_kernel<128, false, 1>",
+                         "kernel": "prefill_kernel<128, 0, 1>",
                          "kernel_ms_mean": round(p["mean_s"] * 1e3, 3),
                          "kernel_ms_min": round(p["min_s"] * 1e3, 3)},
         })
@@ -684,14 +696,20 @@ def main():
                 "layout": "q, k, v column slices of one [16384, 6144] buffer; out row stride 4160",
                 "ms": round(r["mean_s"] * 1e3, 3), "TFLOP/s": round(r["tflops_kernel"], 3),
                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                "kernel": "prefill_kernel<128, false, 1>"}
+                "kernel": "prefill_kernel<128, 0, 1>"}
             print(f"[bench] strided {result['prefill_strided']}", flush=True)
             r = bench_prefill(w, 3, 1, torch, ta, rope_theta=10000.0)
             result["prefill_rope"] = {
                 "workload": w.name + "_rope_theta10000",
                 "ms": round(r["mean_s"] * 1e3, 3), "TFLOP/s": round(r["tflops_kernel"], 3),
                 "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
-                "kernel": "prefill_kernel<128, true, 1>"}
+                "kernel": "prefill_kernel<128, 1, 1> (keys turned as loaded)"}
+            r = bench_prefill(w, 3, 1, torch, ta, rope_theta=10000.0, rope_keys_once=True)
+            result["prefill_rope"]["keys_turned_once"] = {
+                "ms": round(r["mean_s"] * 1e3, 3), "TFLOP/s": round(r["tflops_kernel"], 3),
+                "frac": round(r["tflops_kernel"] / MFMA_F32_PEAK_TFLOPS, 4),
+                "kernels": "rope_apply_kernel (keys, once per call) + prefill_kernel<128, 2, 1> "
+                           "(queries turned as loaded), both timed"}
             print(f"[bench] rotary {result['prefill_rope']}", flush=True)
             result["backward"] = backward_legs(w, torch, ta)
             print(f"[bench] backward {result['backward']}", flush=True)

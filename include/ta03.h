@@ -152,6 +152,48 @@ int attn_fwd_rope(const float* q, long long q_stride, const float* k, long long 
                   const float* rope_cs, int rope_rows, hipStream_t stream);
 
 /*
+ * attn_fwd_rope_q -- attn_fwd_rope for keys that are already turned (a cache
+ * that stores rotated keys, or keys passed once through attn_rope_apply): the
+ * queries are turned as the kernel loads them, exactly as in attn_fwd_rope,
+ * and k is used as given. The same rotation read into the pages' hooks
+ * (meganeura attention.wgsl, main), split so that each key is turned once
+ * per call instead of once per block of query rows that reads it. Arguments,
+ * layouts and errors as attn_fwd_rope, except that rope_rows must cover the
+ * query positions only: >= start_pos + q_base + q_seq.
+ */
+int attn_fwd_rope_q(const float* q, long long q_stride, const float* k, long long k_stride,
+                    const float* v, long long v_stride, float* out, long long out_stride,
+                    float* lse, int q_base, int q_seq, int kv_len, int num_heads,
+                    int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+                    const float* rope_cs, int rope_rows, hipStream_t stream);
+
+/*
+ * attn_rope_apply -- turn rows by the rotary table, the rotation
+ * attn_fwd_rope applies to keys as it loads them: for row r < rows, head
+ * h < heads and pair e < head_dim/2, at position pos0 + r with
+ * (cos, sin) = rope_cs[pos0 + r][e],
+ *     y[r][h*head_dim + e]              = x[..e] * cos - x[..e + head_dim/2] * sin
+ *     y[r][h*head_dim + e + head_dim/2] = x[..e + head_dim/2] * cos + x[..e] * sin
+ * Columns past heads * head_dim are not touched.
+ *
+ *   x, y      device, rows x heads * head_dim floats with row strides
+ *             x_stride, y_stride (floats, multiples of 4), 16-byte aligned;
+ *             y == x with y_stride == x_stride turns in place, any other
+ *             overlap is rejected
+ *   rope_cs   device, [rope_rows, head_dim/2, 2] floats, 16-byte aligned
+ *             (attn_rope_table), rope_rows >= pos0 + rows
+ *
+ * Errors: TA03_ERR_SHAPE for rows < 0, heads < 1, pos0 < 0, head_dim not a
+ * positive multiple of 8, a stride below heads * head_dim, too few rope_rows
+ * or overlapping x and y; TA03_ERR_UNSUPPORTED for a stride, heads *
+ * head_dim or rope_rows * head_dim >= 2^31; TA03_ERR_NULL; TA03_ERR_ALIGN;
+ * TA03_ERR_HIP. rows == 0 is a no-op.
+ */
+int attn_rope_apply(const float* x, long long x_stride, float* y, long long y_stride, int rows,
+                    int heads, int head_dim, int pos0, const float* rope_cs, int rope_rows,
+                    hipStream_t stream);
+
+/*
  * attn_rope_table -- fill the standard rotary table for attn_fwd_rope:
  * cos_sin[p][e] = (cos(a), sin(a)), a = p * theta^(-2e/head_dim), for
  * p < rows and e < head_dim/2 (the frequencies of the common rotary

@@ -43,7 +43,8 @@ def test_header_declares_the_entry_points():
                                     "attn_decode_paged",
                                     "attn_decode_workspace_bytes",
                                     "attn_decode_workspace_init", "attn_fwd", "attn_fwd_ex",
-                                    "attn_fwd_rope", "attn_rope_table",
+                                    "attn_fwd_rope", "attn_fwd_rope_q", "attn_rope_apply",
+                                    "attn_rope_table",
                                     "attn_set_kernel_override", "attn_strerror"]
 
 
@@ -139,6 +140,64 @@ def fwd_rope(lib, cs=O + 0x8000, rope_rows=64, q_base=0, q_seq=4, kv_len=8, H=4,
 ])
 def test_attn_fwd_rope_rejects_on_host(lib, kw, status):
     assert fwd_rope(lib, **kw) == status
+
+
+def fwd_rope_q(lib, cs=O + 0x8000, rope_rows=64, q_base=0, q_seq=4, kv_len=8, H=4, Hkv=2,
+               d=64, mode=0, sp=0):
+    return lib.attn_fwd_rope_q(A, H * d, B, Hkv * d, C, Hkv * d, O, H * d, None, q_base, q_seq,
+                               kv_len, H, Hkv, d, mode, sp, 0.125, cs, rope_rows, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cs=None), ERR_NULL),
+    (dict(cs=O + 0x8008), ERR_ALIGN),
+    (dict(sp=2, q_seq=4, kv_len=8, rope_rows=5), ERR_SHAPE),  # query positions 2..5
+    (dict(mode=2, q_base=10, q_seq=4, kv_len=3, rope_rows=13), ERR_SHAPE),  # rows up to 13
+    (dict(rope_rows=-1), ERR_SHAPE),
+    (dict(rope_rows=1 << 26, d=64), ERR_UNSUP),
+    (dict(d=96), ERR_UNSUP),
+    (dict(q_seq=0, cs=None), OK),
+])
+def test_attn_fwd_rope_q_rejects_on_host(lib, kw, status):
+    assert fwd_rope_q(lib, **kw) == status
+
+
+def test_attn_fwd_rope_q_needs_query_positions_only(lib):
+    """The keys are taken as given: a table that covers the queries' positions
+    (causal rows 2..5 of 8 keys: 6 rows) passes the size checks, which come
+    before the pointer checks (so the missing table is what is reported),
+    while attn_fwd_rope, which also turns the keys, needs 8 rows."""
+    assert fwd_rope(lib, sp=2, q_seq=4, kv_len=8, rope_rows=6, cs=None) == ERR_SHAPE
+    assert fwd_rope_q(lib, sp=2, q_seq=4, kv_len=8, rope_rows=6, cs=None) == ERR_NULL
+
+
+def rope_apply(lib, x=A, xs=256, y=B, ys=256, rows=4, heads=4, d=64, pos0=0, cs=O, rope_rows=8):
+    return lib.attn_rope_apply(x, xs, y, ys, rows, heads, d, pos0, cs, rope_rows, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), ERR_SHAPE),
+    (dict(heads=0), ERR_SHAPE),
+    (dict(pos0=-1), ERR_SHAPE),
+    (dict(d=60), ERR_SHAPE),                  # not a multiple of 8
+    (dict(d=0), ERR_SHAPE),
+    (dict(xs=255), ERR_SHAPE),                # stride below heads * head_dim
+    (dict(ys=128), ERR_SHAPE),
+    (dict(pos0=5, rope_rows=8), ERR_SHAPE),   # positions 5..8 need 9 rows
+    (dict(xs=1 << 31, ys=1 << 31), ERR_UNSUP),
+    (dict(rope_rows=1 << 26), ERR_UNSUP),
+    (dict(x=None), ERR_NULL),
+    (dict(y=None), ERR_NULL),
+    (dict(cs=None), ERR_NULL),
+    (dict(x=A + 8), ERR_ALIGN),
+    (dict(cs=O + 8), ERR_ALIGN),
+    (dict(xs=258, ys=258), ERR_ALIGN),
+    (dict(y=A + 1024), ERR_SHAPE),            # overlaps x's rows 1..3
+    (dict(y=A, ys=512), ERR_SHAPE),           # same start, another stride
+    (dict(rows=0, x=None, y=None, cs=None), OK),
+])
+def test_attn_rope_apply_rejects_on_host(lib, kw, status):
+    assert rope_apply(lib, **kw) == status
 
 
 @pytest.mark.parametrize("args,status", [

@@ -192,3 +192,125 @@ def test_rope_deterministic():
     a = gpu_rope(q, k, v, t, **_kw(w))
     b = gpu_rope(q, k, v, t, **_kw(w))
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# Keys turned once (attn_rope_apply), then attention that turns only the
+# queries (attn_fwd_rope_q): the same rotation, split in two calls.
+
+def gpu_rope_apply(x, heads, head_dim, pos0, table, pad=0, in_place=False):
+    """attn_rope_apply over the rows of x (a column slice of a wider buffer
+    when pad > 0: the pad columns hold NaN and must stay untouched).
+    Returns (turned rows, pad columns)."""
+    import torch
+    import tiled_attention_03_amd as ta
+    n, width = x.shape
+    buf = torch.full((n, width + pad), float("nan"), device=device())
+    buf[:, :width] = to_dev(x)
+    if in_place:
+        ta.attn_rope_apply(buf, width + pad, buf, width + pad, n, heads, head_dim, pos0, table,
+                           table.shape[0])
+        y = buf
+    else:
+        y = torch.full((n, width + pad), float("nan"), device=device())
+        ta.attn_rope_apply(buf[:, :width], width + pad, y[:, :width], width + pad, n, heads,
+                           head_dim, pos0, table, table.shape[0])
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    return y[:, :width], y[:, width:]
+
+
+@pytest.mark.parametrize("heads,d,pos0,pad", [(8, 128, 37, 64), (3, 64, 0, 0), (2, 8, 5, 4)])
+def test_rope_apply_matches_checker(heads, d, pos0, pad):
+    """Rows turned by an arbitrary seeded table (the same on both sides)
+    against the checker's rotation in float64, element by element: each
+    output is x_e cos -/+ x_e' sin, two float32 roundings at most, so the
+    error stays within 2^-22 (|x_e cos| + |x_e' sin|); columns past
+    heads * head_dim are left as they were."""
+    n = 300
+    x = inputs.normal((n, heads * d), 1400 + d)
+    table = 0.9 * inputs.normal((pos0 + n + 2, d // 2, 2), 1401 + d)
+    got, padcols = gpu_rope_apply(x, heads, d, pos0, to_dev(table), pad=pad)
+    ref = oracle.apply_rope(x, pos0 + np.arange(n), table, heads, d)
+    t = table[pos0 + np.arange(n)].astype(np.float64)
+    xh = x.astype(np.float64).reshape(n, heads, d)
+    half = d // 2
+    c, s = np.abs(t[:, None, :, 0]), np.abs(t[:, None, :, 1])
+    lo, hi = np.abs(xh[..., :half]), np.abs(xh[..., half:])
+    mag = np.concatenate([lo * c + hi * s, hi * c + lo * s], axis=-1).reshape(n, heads * d)
+    err = np.abs(got - ref)
+    assert np.all(err <= 2.0 ** -22 * mag + 1e-30), float((err / (mag + 1e-30)).max())
+    assert np.all(np.isnan(padcols))
+    log(f"rope apply heads={heads} d={d} pos0={pos0}: max err {err.max():.2e}")
+
+
+def test_rope_apply_in_place_equals_out_of_place():
+    x = inputs.normal((257, 4 * 128), 1410)
+    table = gpu_table(300, 128, THETA)
+    a, _ = gpu_rope_apply(x, 4, 128, 40, table, pad=32)
+    b, pad = gpu_rope_apply(x, 4, 128, 40, table, pad=32, in_place=True)
+    assert np.array_equal(a, b)
+    assert np.all(np.isnan(pad))
+
+
+def gpu_rope_q(q, k, v, table, *, num_heads, num_kv_heads, head_dim, mode, kv_len, start_pos,
+               scale):
+    """Keys turned once into a scratch copy (attn_rope_apply), then
+    attn_fwd_rope_q over dense rows."""
+    import torch
+    import tiled_attention_03_amd as ta
+    dev = device()
+    H, Hkv, d = num_heads, num_kv_heads, head_dim
+    n = q.shape[0]
+    kd = to_dev(k)
+    kr = torch.full_like(kd, float("nan"))
+    ta.attn_rope_apply(kd, Hkv * d, kr, Hkv * d, kv_len, Hkv, d, 0, table, table.shape[0])
+    out = torch.full((n, H * d), float("nan"), device=dev)
+    lse = torch.full((n, H, 2), float("nan"), device=dev)
+    ta.attn_fwd_rope_q(to_dev(q), H * d, kr, Hkv * d, to_dev(v), Hkv * d, out, H * d, lse, 0, n,
+                       kv_len, H, Hkv, d, mode, start_pos, scale, table, table.shape[0])
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "m{}_q{}_kv{}_h{}kv{}_d{}_s{}".format(*c))
+def test_rope_q_with_keys_turned_once(case):
+    """attn_rope_apply on the keys, then attn_fwd_rope_q, with a seeded
+    arbitrary table (the same on both sides) over the ragged shapes."""
+    mode, n, kv, H, Hkv, d, sp = case
+    w, q, k, v = inputs.random_case(1420 + n + kv, mode, n, kv, H, Hkv, d, start_pos=sp)
+    rows = max(sp + n, kv) + 3
+    table = 0.7 * inputs.normal((rows, d // 2, 2), 1421 + n)
+    go, gl = gpu_rope_q(q, k, v, to_dev(table), **_kw(w))
+    ro, rl = oracle_rope(q, k, v, table, **_kw(w))
+    check_out(go, ro, f"keys turned once {case}")
+    check_lse(gl, rl, f"keys turned once lse {case}")
+
+
+@pytest.mark.parametrize("w", [inputs.CAUSAL_SMALL, inputs.FULL_1K, inputs.CONTINUE_512],
+                         ids=lambda w: w.name)
+def test_rope_q_pages_workloads(w):
+    q, k, v = inputs.make_prefill(w)
+    rows = _table_rows(w)
+    go, gl = gpu_rope_q(q, k, v, gpu_table(rows, w.head_dim, THETA), **_kw(w))
+    ro, rl = oracle_rope(q, k, v, oracle.rope_table(rows, w.head_dim, THETA), **_kw(w))
+    check_out(go, ro, f"{w.name} keys turned once")
+    check_lse(gl, rl, f"{w.name} keys turned once")
+
+
+@pytest.mark.timeout(600)
+def test_rope_q_long_causal_sampled_rows():
+    """The 16384-row causal pass with heavy K rows, keys turned once then
+    attn_fwd_rope_q (the launch the benchmark times): 96 rows of every head,
+    the first and last row blocks and rows spread over the sequence, against
+    the checker."""
+    w = inputs.CAUSAL_16K
+    q, k, v = inputs.make_prefill(w)
+    go, gl = gpu_rope_q(q, k, v, gpu_table(w.kv_len, w.head_dim, THETA), **_kw(w))
+    rng = np.random.default_rng(1430)
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(w.q_seq - 32, w.q_seq),
+                                     rng.choice(w.q_seq, 32, replace=False)]))
+    ro, rl = oracle_rope(q, k, v, oracle.rope_table(w.kv_len, w.head_dim, THETA), rows=rows,
+                         **_kw(w))
+    e_o = check_out(go[rows], ro, f"{w.name} keys turned once, sampled rows")
+    e_l = check_lse(gl[rows], rl, f"{w.name} keys turned once, sampled rows")
+    log(f"  rows={len(rows)} max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")

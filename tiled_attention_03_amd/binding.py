@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_rope.argtypes = [P, LL, P, LL, P, LL, P, LL, P, I, I, I, I, I, I, I, I, F,
                                     P, I, P]
         L.attn_fwd_rope.restype = I
+        L.attn_fwd_rope_q.argtypes = L.attn_fwd_rope.argtypes
+        L.attn_fwd_rope_q.restype = I
+        L.attn_rope_apply.argtypes = [P, LL, P, LL, I, I, I, I, P, I, P]
+        L.attn_rope_apply.restype = I
         L.attn_rope_table.argtypes = [P, I, I, ctypes.c_double, P]
         L.attn_rope_table.restype = I
         L.attn_bwd_workspace_bytes.argtypes = [I, I]
@@ -193,19 +197,15 @@ def attn_fwd_ex(q, q_stride: int, k, k_stride: int, v, v_stride: int, out, out_s
     _check(status)
 
 
-def attn_fwd_rope(q, q_stride: int, k, k_stride: int, v, v_stride: int, out, out_stride: int,
-                  lse, q_base: int, q_seq: int, kv_len: int, num_heads: int, num_kv_heads: int,
-                  head_dim: int, mode: int, start_pos: int, scale: float, rope_cs,
-                  rope_rows: int, stream=None) -> None:
-    """Enqueue attn_fwd_ex with the rotary embedding turned into q and k at
-    load time (see include/ta03.h); rope_cs is a [rope_rows, head_dim/2, 2]
-    float32 GPU tensor of (cos, sin) pairs."""
+def _fwd_rope(fn, q, q_stride, k, k_stride, v, v_stride, out, out_stride, lse, q_base, q_seq,
+              kv_len, num_heads, num_kv_heads, head_dim, mode, start_pos, scale, rope_cs,
+              rope_rows, stream):
     qd, kvd = num_heads * head_dim, num_kv_heads * head_dim
     rows = q_base + q_seq
     kv_rows = kv_len if mode != CAUSAL else min(kv_len, start_pos + rows)
     def ext(n, stride, width):
         return (n - 1) * stride + width if n > 0 else 0
-    status = lib().attn_fwd_rope(
+    status = fn(
         _strided_ptr(q, ext(rows, q_stride, qd), "q"), int(q_stride),
         _strided_ptr(k, ext(kv_rows, k_stride, kvd), "k"), int(k_stride),
         _strided_ptr(v, ext(kv_rows, v_stride, kvd), "v"), int(v_stride),
@@ -214,6 +214,44 @@ def attn_fwd_rope(q, q_stride: int, k, k_stride: int, v, v_stride: int, out, out
         num_kv_heads, head_dim, mode, start_pos, float(scale),
         _ptr(rope_cs, max(rope_rows, 0) * head_dim, "rope_cs"), int(rope_rows), _stream(stream))
     _check(status)
+
+
+def attn_fwd_rope(q, q_stride: int, k, k_stride: int, v, v_stride: int, out, out_stride: int,
+                  lse, q_base: int, q_seq: int, kv_len: int, num_heads: int, num_kv_heads: int,
+                  head_dim: int, mode: int, start_pos: int, scale: float, rope_cs,
+                  rope_rows: int, stream=None) -> None:
+    """Enqueue attn_fwd_ex with the rotary embedding turned into q and k at
+    load time (see include/ta03.h); rope_cs is a [rope_rows, head_dim/2, 2]
+    float32 GPU tensor of (cos, sin) pairs."""
+    _fwd_rope(lib().attn_fwd_rope, q, q_stride, k, k_stride, v, v_stride, out, out_stride, lse,
+              q_base, q_seq, kv_len, num_heads, num_kv_heads, head_dim, mode, start_pos, scale,
+              rope_cs, rope_rows, stream)
+
+
+def attn_fwd_rope_q(q, q_stride: int, k, k_stride: int, v, v_stride: int, out, out_stride: int,
+                    lse, q_base: int, q_seq: int, kv_len: int, num_heads: int, num_kv_heads: int,
+                    head_dim: int, mode: int, start_pos: int, scale: float, rope_cs,
+                    rope_rows: int, stream=None) -> None:
+    """attn_fwd_rope for keys already turned (see include/ta03.h): only the
+    queries are turned at load time."""
+    _fwd_rope(lib().attn_fwd_rope_q, q, q_stride, k, k_stride, v, v_stride, out, out_stride,
+              lse, q_base, q_seq, kv_len, num_heads, num_kv_heads, head_dim, mode, start_pos,
+              scale, rope_cs, rope_rows, stream)
+
+
+def attn_rope_apply(x, x_stride: int, y, y_stride: int, rows: int, heads: int, head_dim: int,
+                    pos0: int, rope_cs, rope_rows: int, stream=None) -> None:
+    """Enqueue the rotation of rows [0, rows) of x into y at positions
+    pos0 + r (see include/ta03.h); x and y may be strided views, or the
+    same tensor (in place)."""
+    width = heads * head_dim
+    def ext(n, stride):
+        return (n - 1) * stride + width if n > 0 else 0
+    _check(lib().attn_rope_apply(
+        _strided_ptr(x, ext(rows, x_stride), "x"), int(x_stride),
+        _strided_ptr(y, ext(rows, y_stride), "y"), int(y_stride), int(rows), int(heads),
+        int(head_dim), int(pos0), _ptr(rope_cs, max(rope_rows, 0) * head_dim, "rope_cs"),
+        int(rope_rows), _stream(stream)))
 
 
 def attn_rope_table(cos_sin, rows: int, head_dim: int, theta: float, stream=None) -> None:

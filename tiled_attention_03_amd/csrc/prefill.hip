@@ -43,7 +43,9 @@
 //     turned in registers right after loading (element e and its partner
 //     e + d/2 sit in the same lane of the operand layout); keys go HBM ->
 //     registers -> turned -> LDS, one tile ahead of their use, while V keeps
-//     the direct path.
+//     the direct path. A third instance turns the queries only, for keys
+//     already turned in memory (a rotated cache, or attn_rope_apply once per
+//     call): its tile loop is the plain one.
 
 #include <hip/hip_runtime.h>
 
@@ -109,17 +111,24 @@ struct Args {
     int n_head_blocks, n_row_blocks;
 };
 
+// Rotary modes of the kernel: none, queries and keys rotated as they are
+// loaded, queries only (keys already rotated in memory).
+constexpr int kRopeNone = 0, kRopeQK = 1, kRopeQ = 2;
+
 // Rotary instance: most chunk-pair load instructions one wave issues per key
 // tile (the host keeps the key splits low enough for this).
 template <int D>
 constexpr int rope_rmax() { return D == 128 ? 2 : 4; }
 
 // Two blocks per CU while their LDS (KS * D * 512 bytes) allows it.
-template <int D, bool ROPE, int KS>
+template <int D, int ROPE, int KS>
 __global__ void __launch_bounds__(kBlock, KS * D <= 128 ? 2 : 1)
 prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                const float* __restrict__ v, float* __restrict__ out,
                float* __restrict__ lse, Args a) {
+    // Rotary modes: keys rotated as they are loaded (ROPE == kRopeQK), or
+    // queries only, the keys taken as given (kRopeQ).
+    constexpr bool ROT_K = ROPE == kRopeQK;
     constexpr int NB = D / 32;                // 32-row blocks of O^T
     constexpr int CPR = D / 4;                // 16-byte chunks per K/V row
     constexpr int TILE_F = kBN * D;           // floats per K (or V) tile
@@ -192,7 +201,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             qr[4 * g + 2] = x.z * a.qscale;
             qr[4 * g + 3] = x.w * a.qscale;
         }
-        if constexpr (ROPE) {
+        if constexpr (ROPE != kRopeNone) {
             // Element e = 8g + 4hh + c (register 4g + c) pairs with e + D/2
             // (register 4(g + D/16) + c); the row sits at start_pos + row.
             if (ok) {
@@ -226,11 +235,11 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // between): most tiles then need neither a subtraction per score nor a
     // rescale of O. rel = true running max - m_ref; before a row has seen a
     // key (has_ref false) m_ref is 0 and rel is -inf. The true (max, sum)
-    // pair is restored once at the end. The rotary instance, whose registers
-    // are spoken for (with the reference's registers it spilled 24 and took
-    // 17.5 instead of 16.2 ms on the 16K workload), keeps the plain running
-    // max m_run and rescales whenever it moves.
-    constexpr bool REF = !ROPE;
+    // pair is restored once at the end. The instance that turns the keys,
+    // whose registers are spoken for (with the reference's registers it
+    // spilled 24 and took 17.5 instead of 16.2 ms on the 16K workload), keeps
+    // the plain running max m_run and rescales whenever it moves.
+    constexpr bool REF = !ROT_K;
     float m_run = kNegBig;
     float m_ref = 0.f;
     float rel = -INFINITY;
@@ -253,8 +262,8 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // vector instructions for its address, and rows past the window read as
     // zero (their scores are masked and their weight is 0). At most
     // LOADS / gw slots per wave: head_dim 128 runs at most 2 key splits
-    // (gw >= 2), head_dim 64 at most 4 (gw >= 1). The rotary instance and
-    // larger strides take the general path below.
+    // (gw >= 2), head_dim 64 at most 4 (gw >= 1). The instance that turns
+    // the keys and larger strides take the general path below.
     constexpr int MAXI = D == 128 ? LOADS / 2 : LOADS;
     unsigned koff[MAXI], voff[MAXI];
 #pragma unroll
@@ -291,7 +300,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     auto issue_tile = [&](int t, float* kd) __attribute__((always_inline)) {
         float* vd = kd + TILE_F;
         const int kv0 = t * kBN;
-        if (a.small_strides) {  // (the rotary instance copies V only: its K goes through registers)
+        if (a.small_strides) {  // (turning the keys: V only, K goes through registers)
             const int rows = min(kBN, w_block - kv0);
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<float*>(kbase + (size_t)kv0 * a.k_stride), 0, rows * (int)a.k_stride * 4,
@@ -304,7 +313,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 const int inst = wg + u * gw;
                 if (inst < LOADS) {
                     const unsigned ko = koff[u], vo = voff[u];
-                    if constexpr (!ROPE) {
+                    if constexpr (!ROT_K) {
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + inst * 256), 16,
                                                                  ko, 0, 0, 0);
                     }
@@ -319,7 +328,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             const int s = inst * 64 + lane;
             const int r = s / CPR, p = s % CPR;
             const int key = min(kv0 + r, w_block - 1);
-            if constexpr (!ROPE) {
+            if constexpr (!ROT_K) {
                 const float* kg = kbase + (size_t)key * a.k_stride + 4 * (p ^ (r & 15));
                 __builtin_amdgcn_global_load_lds(kg, (lds_void*)(kd + inst * 256), 16, 0, 0);
             }
@@ -335,9 +344,9 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // resources as the copies above do (rows past the window read as zero:
     // their rotated keys are zero and masked); otherwise rows past the
     // block's window are read as its last row.
-    float4 rk[ROPE ? RMAX : 1][2], rc[ROPE ? RMAX : 1][2];
-    unsigned rko[ROPE ? RMAX : 1], rco[ROPE ? RMAX : 1];
-    if constexpr (ROPE) {
+    float4 rk[ROT_K ? RMAX : 1][2], rc[ROT_K ? RMAX : 1][2];
+    unsigned rko[ROT_K ? RMAX : 1], rco[ROT_K ? RMAX : 1];
+    if constexpr (ROT_K) {
 #pragma unroll
         for (int u = 0; u < RMAX; ++u) {
             const int s = (wg + u * gw) * 64 + lane;
@@ -419,7 +428,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
     if (t_begin < t_end) {
         issue_tile(t_begin, my0);
-        if constexpr (ROPE) {
+        if constexpr (ROT_K) {
             load_k_rot(t_begin);
             wait_vmem();
             store_k_rot(my0);
@@ -448,10 +457,10 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const bool work = have && kv0 < w_wave_max;
         // the next tile's copies go between this tile's score products when
         // it lies inside the block's window (else, and without work, here)
-        const bool spread = !ROPE && next && work && a.small_strides;
+        const bool spread = !ROT_K && next && work && a.small_strides;
         if (next && !spread) {
             issue_tile(t + 1, wb);
-            if constexpr (ROPE) load_k_rot(t + 1);
+            if constexpr (ROT_K) load_k_rot(t + 1);
         }
         // Tiles inside every row's window (the leading ones, most of them)
         // run a version without mask code; the others apply the window as a
@@ -461,7 +470,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             const float* Vs = Ks + TILE_F;
 
             // S^T - m_ref = K Q^T - m_ref for this tile (log2 units; the
-            // rotary instance: S^T).
+            // instance that turns the keys: S^T).
             f32x16 s;
             if constexpr (REF) {
                 s = negm;
@@ -578,7 +587,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             }
             __builtin_amdgcn_s_setprio(0);
         }
-        if constexpr (ROPE) {
+        if constexpr (ROT_K) {
             if (next) {  // next tile's keys: turned and written after this tile's math
                 wait_vmem();
                 store_k_rot(wb);
@@ -689,7 +698,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
 
 // One instance per key-split count (its LDS is static: KS x 2 buffers x
 // (K, V) tiles).
-template <int D, bool ROPE, int KS>
+template <int D, int ROPE, int KS>
 hipError_t launch_ks(long long grid, hipStream_t stream, const float* q, const float* k,
                      const float* v, float* out, float* lse, const Args& a) {
     hipLaunchKernelGGL((prefill_kernel<D, ROPE, KS>), dim3((unsigned)grid), dim3(kBlock), 0,
@@ -697,10 +706,10 @@ hipError_t launch_ks(long long grid, hipStream_t stream, const float* q, const f
     return hipSuccess;
 }
 
-template <int D, bool ROPE>
+template <int D, int ROPE>
 hipError_t launch_instance(long long grid, hipStream_t stream, const float* q, const float* k,
                            const float* v, float* out, float* lse, const Args& a) {
-    if constexpr (D == 128 && ROPE) {
+    if constexpr (D == 128 && ROPE == kRopeQK) {
         return launch_ks<D, ROPE, 1>(grid, stream, q, k, v, out, lse, a);
     } else if constexpr (D == 128) {
         return a.ks == 1 ? launch_ks<D, ROPE, 1>(grid, stream, q, k, v, out, lse, a)
@@ -751,10 +760,12 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     const long long base_waves = (long long)s.num_heads * strips;
     const int max_w = s.causal ? min(s.start_pos + s.q_seq, s.kv_len) : s.kv_len;
     const int key_tiles = (max_w + kBN - 1) / kBN;
-    // 2 buffers x (K, V) per split in 160 KB; the rotary instance also holds
-    // the next key tile in registers, at most rope_rmax instructions a wave.
+    // 2 buffers x (K, V) per split in 160 KB; the instance that turns the
+    // keys also holds the next key tile in registers, at most rope_rmax
+    // instructions a wave.
     const bool rope = s.rope_cs != nullptr;
-    const int max_ks = s.head_dim == 128 ? (rope ? 1 : 2) : 4;
+    const int rmode = !rope ? kRopeNone : s.rope_keys ? kRopeQK : kRopeQ;
+    const int max_ks = s.head_dim == 128 ? (rmode == kRopeQK ? 1 : 2) : 4;
     int ks = 1;
     const int cus = device_cu_count();
     const long long target_waves = (long long)kWavesPerCU * cus;
@@ -781,11 +792,13 @@ hipError_t launch_prefill(const float* q, const float* k, const float* v, float*
     }
     hipError_t e;
     if (s.head_dim == 128) {
-        e = rope ? launch_instance<128, true>(grid, stream, q, k, v, out, lse, a)
-                 : launch_instance<128, false>(grid, stream, q, k, v, out, lse, a);
+        e = rmode == kRopeQK ? launch_instance<128, kRopeQK>(grid, stream, q, k, v, out, lse, a)
+            : rmode == kRopeQ ? launch_instance<128, kRopeQ>(grid, stream, q, k, v, out, lse, a)
+                              : launch_instance<128, kRopeNone>(grid, stream, q, k, v, out, lse, a);
     } else {
-        e = rope ? launch_instance<64, true>(grid, stream, q, k, v, out, lse, a)
-                 : launch_instance<64, false>(grid, stream, q, k, v, out, lse, a);
+        e = rmode == kRopeQK ? launch_instance<64, kRopeQK>(grid, stream, q, k, v, out, lse, a)
+            : rmode == kRopeQ ? launch_instance<64, kRopeQ>(grid, stream, q, k, v, out, lse, a)
+                              : launch_instance<64, kRopeNone>(grid, stream, q, k, v, out, lse, a);
     }
     if (e != hipSuccess) return e;
     return hipGetLastError();

@@ -50,7 +50,8 @@ int fwd_common(const float* q, long long q_stride, const float* k, long long k_s
                const float* v, long long v_stride, float* out, long long out_stride,
                float* lse, int q_base, int q_seq, int kv_len, int num_heads,
                int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
-               bool rope, const float* rope_cs, int rope_rows, hipStream_t stream) {
+               bool rope, const float* rope_cs, int rope_rows, hipStream_t stream,
+               bool rope_keys = true) {
     if (num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0) return TA03_ERR_SHAPE;
     if (q_seq < 0 || kv_len < 0 || start_pos < 0 || q_base < 0) return TA03_ERR_SHAPE;
     if (mode != TA03_CAUSAL && mode != TA03_FULL && mode != TA03_CROSS) return TA03_ERR_SHAPE;
@@ -66,8 +67,10 @@ int fwd_common(const float* q, long long q_stride, const float* k, long long k_s
         v_stride >= kMaxElems)
         return TA03_ERR_UNSUPPORTED;
     if (rope) {
-        // Positions used: query rows start_pos + q_base .. + q_seq - 1, keys 0 .. kv_len - 1.
-        const long long need = std::max((long long)start_pos + q_base + q_seq, (long long)kv_len);
+        // Positions used: query rows start_pos + q_base .. + q_seq - 1, keys 0 .. kv_len - 1
+        // (when the keys are turned here).
+        const long long need = std::max((long long)start_pos + q_base + q_seq,
+                                        rope_keys ? (long long)kv_len : 0ll);
         if (rope_rows < 0 || (q_seq > 0 && rope_rows < need)) return TA03_ERR_SHAPE;
         if ((long long)rope_rows * head_dim >= kMaxElems) return TA03_ERR_UNSUPPORTED;
     }
@@ -93,6 +96,7 @@ int fwd_common(const float* q, long long q_stride, const float* k, long long k_s
     s.v_stride = v_stride;
     s.out_stride = out_stride;
     s.rope_cs = rope ? rope_cs : nullptr;
+    s.rope_keys = rope_keys;
     // Row q_base of the batch is row 0 of this launch.
     const float* qb = q + (size_t)q_base * (size_t)q_stride;
     float* ob = out + (size_t)q_base * (size_t)out_stride;
@@ -123,6 +127,43 @@ int attn_fwd_rope(const float* q, long long q_stride, const float* k, long long 
     return fwd_common(q, q_stride, k, k_stride, v, v_stride, out, out_stride, lse, q_base,
                       q_seq, kv_len, num_heads, num_kv_heads, head_dim, mode, start_pos, scale,
                       true, rope_cs, rope_rows, stream);
+}
+
+int attn_fwd_rope_q(const float* q, long long q_stride, const float* k, long long k_stride,
+                    const float* v, long long v_stride, float* out, long long out_stride,
+                    float* lse, int q_base, int q_seq, int kv_len, int num_heads,
+                    int num_kv_heads, int head_dim, int mode, int start_pos, float scale,
+                    const float* rope_cs, int rope_rows, hipStream_t stream) {
+    return fwd_common(q, q_stride, k, k_stride, v, v_stride, out, out_stride, lse, q_base,
+                      q_seq, kv_len, num_heads, num_kv_heads, head_dim, mode, start_pos, scale,
+                      true, rope_cs, rope_rows, stream, false);
+}
+
+int attn_rope_apply(const float* x, long long x_stride, float* y, long long y_stride, int rows,
+                    int heads, int head_dim, int pos0, const float* rope_cs, int rope_rows,
+                    hipStream_t stream) {
+    if (rows < 0 || heads < 1 || pos0 < 0 || head_dim < 8 || head_dim % 8 != 0)
+        return TA03_ERR_SHAPE;
+    const long long width = (long long)heads * head_dim;
+    if (x_stride < width || y_stride < width) return TA03_ERR_SHAPE;
+    if (rope_rows < 0 || (rows > 0 && (long long)rope_rows < (long long)pos0 + rows))
+        return TA03_ERR_SHAPE;
+    if (x_stride >= kMaxElems || y_stride >= kMaxElems || width >= kMaxElems ||
+        (long long)rope_rows * head_dim >= kMaxElems)
+        return TA03_ERR_UNSUPPORTED;
+    if (rows == 0) return TA03_OK;
+    if (x == nullptr || y == nullptr || rope_cs == nullptr) return TA03_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(rope_cs) || (x_stride | y_stride) % 4 != 0)
+        return TA03_ERR_ALIGN;
+    // In place (y == x, the same stride) or into memory that x does not cover.
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t x1 = x0 + (uintptr_t)(((long long)(rows - 1) * x_stride + width) * 4);
+    const uintptr_t y1 = y0 + (uintptr_t)(((long long)(rows - 1) * y_stride + width) * 4);
+    const bool same = x0 == y0 && x_stride == y_stride;
+    if (!same && x0 < y1 && y0 < x1) return TA03_ERR_SHAPE;
+    const hipError_t e = ta03::launch_rope_apply(x, x_stride, y, y_stride, rows, heads, head_dim,
+                                                 pos0, rope_cs, stream);
+    return e == hipSuccess ? TA03_OK : TA03_ERR_HIP;
 }
 
 size_t attn_bwd_workspace_bytes(int q_seq, int num_heads) {

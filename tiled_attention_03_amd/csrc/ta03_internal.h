@@ -32,6 +32,9 @@ struct PrefillShape {
     long long q_stride, k_stride, v_stride, out_stride;  // row strides in floats
     // Rotary (cos, sin) table [positions][head_dim/2][2]; nullptr: no rotation.
     const float* rope_cs = nullptr;
+    // With a table: rotate the keys as they are loaded (else they are taken
+    // as given, already rotated, and only the queries turn).
+    bool rope_keys = true;
 };
 
 struct DecodeShape {
@@ -152,6 +155,9 @@ constexpr int kMaxBwdWindows = 32;
 
 // Rotary table: entry (p, e) = (cos, sin) of p * theta^(-2e/head_dim).
 hipError_t launch_rope_table(float* cs, int rows, int head_dim, double theta, hipStream_t stream);
+hipError_t launch_rope_apply(const float* x, long long x_stride, float* y, long long y_stride,
+                             int rows, int heads, int head_dim, int pos0, const float* cs,
+                             hipStream_t stream);
 
 hipError_t launch_decode_ws_init(float* ws, const DecodePlan& p, hipStream_t stream);
 
