@@ -332,7 +332,8 @@ def test_sub_batches_with_q_base(mode, sp):
     check_lse(lse.cpu().numpy(), rl, f"sub-batches lse mode={mode}")
 
 
-@pytest.mark.parametrize("rope", [False, True], ids=["plain", "rotary"])
+@pytest.mark.parametrize("rope", [False, True, "keys_once"],
+                         ids=["plain", "rotary", "rotary_keys_once"])
 @pytest.mark.parametrize("rows", ["auto", "16", "32"])
 @pytest.mark.parametrize("stride", [(1 << 24) + 64, (1 << 25) + 64], ids=["2^24", "2^25"])
 def test_row_strides_past_32bit_tile_offsets(stride, rows, rope, kernel_override):
@@ -340,7 +341,9 @@ def test_row_strides_past_32bit_tile_offsets(stride, rows, rope, kernel_override
     one fused buffer of 40 such rows, 2.7 or 5.4 GB): the buffer-resource
     tile copies need 32-bit tile offsets, so these launches take the general
     copy path (and the 16-row kernel, which takes strides below 2^25, hands
-    the wider one to the 32-row kernel). Out and lse match the checker."""
+    the wider one to the 32-row kernel). Rotary: keys turned as loaded, or
+    turned once in place in the fused buffer (attn_rope_apply on the strided
+    K columns) before attn_fwd_rope_q. Out and lse match the checker."""
     import torch
     import oracle
     H, Hkv, d, n, sp = 4, 2, 64, 35, 5
@@ -364,8 +367,13 @@ def test_row_strides_past_32bit_tile_offsets(stride, rows, rope, kernel_override
     if rope:
         table = torch.full((kv, d // 2, 2), float("nan"), dtype=torch.float32, device=dev)
         ta.attn_rope_table(table, kv, d, 10000.0)
-        ta.attn_fwd_rope(qv, stride, kvv, stride, vv, stride, out, H * d, lse, 0, n, kv, H, Hkv,
-                         d, CAUSAL, sp, scale, table, kv)
+        if rope == "keys_once":
+            ta.attn_rope_apply(kvv, stride, kvv, stride, kv, Hkv, d, 0, table, kv)
+            ta.attn_fwd_rope_q(qv, stride, kvv, stride, vv, stride, out, H * d, lse, 0, n, kv, H,
+                               Hkv, d, CAUSAL, sp, scale, table, kv)
+        else:
+            ta.attn_fwd_rope(qv, stride, kvv, stride, vv, stride, out, H * d, lse, 0, n, kv, H,
+                             Hkv, d, CAUSAL, sp, scale, table, kv)
         table_ref = oracle.rope_table(kv, d, 10000.0)
     else:
         ta.attn_fwd_ex(qv, stride, kvv, stride, vv, stride, out, H * d, lse, 0, n, kv, H, Hkv, d,
