@@ -314,3 +314,26 @@ def test_rope_q_long_causal_sampled_rows():
     e_o = check_out(go[rows], ro, f"{w.name} keys turned once, sampled rows")
     e_l = check_lse(gl[rows], rl, f"{w.name} keys turned once, sampled rows")
     log(f"  rows={len(rows)} max|dout|={e_o:.2e} max|dlse|={e_l:.2e}")
+
+
+def test_rope_apply_strides_over_large_inputs():
+    """131072 rows of 16 heads x 128 (33.5 million four-pair items, past the
+    rotation kernel's capped grid, so its threads stride over the rows):
+    turned in place; sampled rows, the last among them, against the
+    checker."""
+    import torch
+    import tiled_attention_03_amd as ta
+    n, heads, d = 1 << 17, 16, 128
+    x = inputs.normal((n, heads * d), 1440)
+    table = gpu_table(n, d, THETA)
+    xd = to_dev(x)
+    ta.attn_rope_apply(xd, heads * d, xd, heads * d, n, heads, d, 0, table, n)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, n // 2, n - 2, n - 1],
+                                     np.random.default_rng(1441).choice(n, 40, replace=False)]))
+    got = xd[torch.from_numpy(rows).to(xd.device)].cpu().numpy()
+    del xd
+    ref = oracle.apply_rope(x[rows], rows, table.cpu().numpy(), heads, d)
+    err = np.abs(got - ref)
+    assert err.max() <= 2.0 ** -21 * (np.abs(x[rows]).max() + 1.0), err.max()
+    log(f"rope apply {n} rows in place: max err {err.max():.2e}")
