@@ -270,6 +270,31 @@ def test_backward_workspace_short_of_stored_runs_windows(kernel_override):
         assert np.array_equal(x, y)
 
 
+def test_attention_backward_capped_workspace(kernel_override):
+    """attention_backward with max_workspace_bytes runs attn_bwd with that
+    scratch (here a third of the tiles, the stored path forced: it runs in
+    windows): the gradients equal those of attn_bwd called with the same
+    workspace, bit for bit, and match the checker."""
+    import torch
+    kernel_override(ta.OVERRIDE_BWD_PATH, 1)
+    H, Hkv, d, n = 8, 2, 128, 300
+    w, q, k, v = inputs.random_case(1320, CAUSAL, n, n, H, Hkv, d)
+    g = inputs.normal(q.shape, 1321)
+    ws = windowed_bytes(n, n, H, CAUSAL, 0)
+    assert ta.attn_bwd_windows(n, n, H, CAUSAL, 0, ws) > 1
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    kw = dict(num_heads=H, num_kv_heads=Hkv, head_dim=d, mode=CAUSAL, scale=w.scale)
+    out, lse = ta.attention(qd, kd, vd, **kw)
+    got = [x.cpu().numpy() for x in ta.attention_backward(qd, kd, vd, out, gd, lse,
+                                                          max_workspace_bytes=ws, **kw)]
+    torch.cuda.synchronize()
+    want = gpu_fwd_bwd(q, k, v, g, ws_bytes=ws, **_kw(w))
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+    ref = oracle.attention_backward(q, k, v, g, magnitudes=True, **_kw(w))
+    _check_all(got, ref, w, "capped workspace")
+
+
 def test_backward_single_key_windows():
     """CROSS over one key: dq = dk = 0 and dv is the sum of dout over rows and
     the group's heads."""

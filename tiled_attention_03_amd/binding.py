@@ -293,11 +293,15 @@ def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, q_seq: int, kv_len: int, num_h
 def attention_backward(q, k, v, out, dout, lse, *, num_heads: int, num_kv_heads: int,
                        head_dim: int, mode: int, kv_len: Optional[int] = None,
                        start_pos: int = 0, scale: Optional[float] = None,
-                       store_scores: bool = True, stream=None):
+                       store_scores: bool = True, max_workspace_bytes: Optional[int] = None,
+                       stream=None):
     """Allocate dq, dk, dv and the scratch with torch and call attn_bwd;
     returns (dq, dk, dv) with dk, dv of kv_len rows. store_scores sizes the
     scratch for the stored-dS path (4 bytes per (row, key) pair per head);
-    False gives the minimal scratch (dq recomputes the scores)."""
+    False gives the minimal scratch (dq recomputes the scores).
+    max_workspace_bytes caps the stored path's scratch (never below the
+    minimal one): the library then runs it in windows of query rows, or
+    recomputes when the cap is too small for that (attn_bwd_windows)."""
     import torch
     q_seq = q.shape[0]
     if kv_len is None:
@@ -306,8 +310,11 @@ def attention_backward(q, k, v, out, dout, lse, *, num_heads: int, num_kv_heads:
         scale = head_dim ** -0.5
     dev = q.device
     s = _alloc_stream(stream)
+    minimal = attn_bwd_workspace_bytes(q_seq, num_heads)
     nbytes = (attn_bwd_workspace_bytes_stored(q_seq, kv_len, num_heads, mode, start_pos)
-              if store_scores else 0) or attn_bwd_workspace_bytes(q_seq, num_heads)
+              if store_scores else 0) or minimal
+    if max_workspace_bytes is not None:
+        nbytes = max(min(nbytes, int(max_workspace_bytes)), minimal)
     # Outputs and scratch belong to the stream the kernels run on: the scratch
     # is dropped on return while the kernels may still be running.
     with torch.cuda.stream(s):
