@@ -337,3 +337,46 @@ def test_rope_apply_strides_over_large_inputs():
     err = np.abs(got - ref)
     assert err.max() <= 2.0 ** -21 * (np.abs(x[rows]).max() + 1.0), err.max()
     log(f"rope apply {n} rows in place: max err {err.max():.2e}")
+
+
+def test_rope_q_graph_replay():
+    """Keys turned once and attention on them, captured in one HIP graph and
+    replayed after the keys change in place (eager work and synchronisation
+    between replays): every replay matches the checker on that replay's
+    inputs."""
+    import torch
+    import tiled_attention_03_amd as ta
+    H, Hkv, d, n = 8, 2, 128, 200
+    w, q, k0, v = inputs.random_case(1450, CAUSAL, n, n, H, Hkv, d)
+    dev = device()
+    table = gpu_table(n, d, THETA)
+    qd, kd, vd = to_dev(q), to_dev(k0), to_dev(v)
+    kr = torch.empty_like(kd)
+    out = torch.empty((n, H * d), device=dev)
+    lse = torch.empty((n, H, 2), device=dev)
+
+    def call():
+        ta.attn_rope_apply(kd, Hkv * d, kr, Hkv * d, n, Hkv, d, 0, table, n)
+        ta.attn_fwd_rope_q(qd, H * d, kr, Hkv * d, vd, Hkv * d, out, H * d, lse, 0, n, n, H, Hkv,
+                           d, CAUSAL, 0, w.scale, table, n)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    ref_table = oracle.rope_table(n, d, THETA)
+    for rep in range(3):
+        k = inputs.normal(k0.shape, 1460 + rep)
+        kd.copy_(torch.from_numpy(k).to(dev))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ro, rl = oracle_rope(q, k, v, ref_table, **_kw(w))
+        check_out(out.cpu().numpy(), ro, f"rope_q graph replay {rep}")
+        check_lse(lse.cpu().numpy(), rl, f"rope_q graph replay lse {rep}")
