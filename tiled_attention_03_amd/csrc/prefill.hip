@@ -440,9 +440,9 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     unsigned kro[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) kro[g] = (unsigned)(j * D + 4 * ((2 * g + hh) ^ (j & 15))) * 4u;
-    // One tile: Ks is this split's K | V tiles of tile it, wb the buffer that
-    // tile it + 1 is copied into.
-    auto step = [&](int it, const float* Ks, float* wb, auto masked_tag)
+    // One tile: Kb is the buffer holding tile it (this split's K | V tiles kvo
+    // floats in), wb this split's part of the buffer tile it + 1 is copied into.
+    auto step = [&](int it, const float* Kb, float* wb, auto masked_tag)
         __attribute__((always_inline)) {
         const int t = t_begin + it;
         const bool have = t < t_end;
@@ -467,7 +467,11 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         // select (see the loops below).
         constexpr bool MASKED = decltype(masked_tag)::value;
         if (work) {  // wave-uniform
-            const float* Vs = Ks + TILE_F;
+            // This split's K | V tiles start kvo floats into the buffer Kb;
+            // the reads index Kb itself (through a split pointer the compiler
+            // lost track of which buffer they read and waited for the next
+            // tile's copies before them).
+            const int kvo = kvs * 2 * TILE_F;
 
             // S^T - m_ref = K Q^T - m_ref for this tile (log2 units; the
             // instance that turns the keys: S^T).
@@ -478,13 +482,19 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[r] = 0.f;
             }
-            const char* kb = reinterpret_cast<const char*>(Ks);
+            const float4* kb4 = reinterpret_cast<const float4*>(Kb);
 #pragma unroll
             for (int g = 0; g < D / 8; ++g) {
                 // chunk (2g + hh) ^ (j % 16) of row j: k-steps 16 apart in g
                 // are 256 bytes apart, an instruction offset
                 const unsigned o = kro[g % 8];
-                const float4 kk = *reinterpret_cast<const float4*>(kb + o + 256 * (g / 8));
+                float4 kk;
+                if constexpr (ROT_K) {  // (this instance's registers prefer the pointer form)
+                    kk = *reinterpret_cast<const float4*>(
+                        reinterpret_cast<const char*>(Kb + kvo) + o + 256 * (g / 8));
+                } else {
+                    kk = kb4[(unsigned)(4 * kvo + o + 256 * (g / 8)) / 16u];
+                }
                 s = mfma32(kk.x, qr[4 * g + 0], s);
                 s = mfma32(kk.y, qr[4 * g + 1], s);
                 if (g < MAXI && spread) issue_u(t + 1, wb, g);
@@ -574,13 +584,17 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 // copies before them.)
                 const int vi = acc_row(tt, hh) * (D / NB) + j;  // in NB-float units
                 if constexpr (NB == 4) {
-                    const float4 vv = reinterpret_cast<const float4*>(Vs)[vi];
+                    const float4 vv = ROT_K
+                        ? *reinterpret_cast<const float4*>(Kb + kvo + TILE_F + 4 * vi)
+                        : reinterpret_cast<const float4*>(Kb)[(kvo + TILE_F) / 4 + vi];
                     o[0] = mfma32(vv.x, s[tt], o[0]);
                     o[1] = mfma32(vv.y, s[tt], o[1]);
                     o[2] = mfma32(vv.z, s[tt], o[2]);
                     o[3] = mfma32(vv.w, s[tt], o[3]);
                 } else {
-                    const float2 vv = reinterpret_cast<const float2*>(Vs)[vi];
+                    const float2 vv = ROT_K
+                        ? *reinterpret_cast<const float2*>(Kb + kvo + TILE_F + 2 * vi)
+                        : reinterpret_cast<const float2*>(Kb)[(kvo + TILE_F) / 2 + vi];
                     o[0] = mfma32(vv.x, s[tt], o[0]);
                     o[1] = mfma32(vv.y, s[tt], o[1]);
                 }
@@ -603,12 +617,12 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int n_int = max(0, min(nt, w_wave_min / kBN - t_begin));
     int it = 0;
     for (; it + 1 < n_int; it += 2) {
-        step(it, my0, my1, std::false_type{});
-        step(it + 1, my1, my0, std::false_type{});
+        step(it, lb0, my1, std::false_type{});
+        step(it + 1, lb1, my0, std::false_type{});
     }
     for (; it < nt; it += 2) {
-        step(it, my0, my1, std::true_type{});
-        if (it + 1 < nt) step(it + 1, my1, my0, std::true_type{});
+        step(it, lb0, my1, std::true_type{});
+        if (it + 1 < nt) step(it + 1, lb1, my0, std::true_type{});
     }
 
     // The true (max, sum) pair: max = m_ref + rel, sum and O scaled by
