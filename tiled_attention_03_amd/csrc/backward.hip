@@ -398,6 +398,12 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     const int key = key0 + j;
     const int qd = a.num_heads * D;
     const int kvd = a.num_kv_heads * D;
+    // Query row i weighs this lane's key iff i >= key - start_pos (causal),
+    // i < q_seq and key < kv_len. With i = row0 + 4g + r of a tile that is
+    // row0 + r + vbase in [0, vspan): one unsigned compare per score.
+    const int ilo = a.causal ? max(0, key - a.start_pos) : 0;
+    const unsigned vspan = (unsigned)max(0, (key < a.kv_len ? a.q_seq : 0) - ilo);
+    const int vbase = 4 * g - ilo;
 
     // K (log2 units) and V of key j: element g*KS + s in register s.
     float kr[KS], vr[KS];
@@ -557,9 +563,14 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 const float* Qs = rt + (size_t)sub * 2 * TILE_F;
                 const float* Gs = Qs + TILE_F;
                 const float* vd = rv + sub * 128;
-                // S = Q K^T, dP = dout V^T: register r of lane (j, g) is query
-                // row0 + 4g + r, key key0 + j.
-                f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+                // S = Q K^T - (m + log l) (log2 units), dP = dout V^T: register
+                // r of lane (j, g) is query row0 + 4g + r, key key0 + j. The
+                // score products start from the row's -(m + log l), so the
+                // exponent needs no subtraction.
+                f32x4 s;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    s[r] = (vd[2 * (4 * g + r)] + vd[2 * (4 * g + r) + 1]) * -kLog2e;
                 f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < KS / 4; ++c) {
@@ -582,13 +593,9 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 // the products and the first vector reads of their results).
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int ir = 4 * g + r;
-                    const int i = row0 + ir;
-                    const float lse2 = (vd[2 * ir] + vd[2 * ir + 1]) * kLog2e;
-                    const float dl = vd[64 + ir];
-                    const int w = a.causal ? min(a.start_pos + i + 1, a.kv_len) : a.kv_len;
-                    const bool valid = i < a.q_seq && key < w;
-                    const float p = valid ? __builtin_amdgcn_exp2f(s[r] - lse2) : 0.f;
+                    const float dl = vd[64 + 4 * g + r];
+                    const bool valid = (unsigned)(row0 + r + vbase) < vspan;
+                    const float p = valid ? __builtin_amdgcn_exp2f(s[r]) : 0.f;
                     s[r] = p;
                     dp[r] = p * (dp[r] - dl);
                 }
