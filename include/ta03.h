@@ -230,7 +230,8 @@ int attn_rope_table(float* cos_sin, int rows, int head_dim, double theta, hipStr
  *                 keys no row sees)
  *   mode, start_pos, scale  as the forward
  *   workspace     device scratch, 16-byte aligned, overwritten: at least
- *                 attn_bwd_workspace_bytes(q_seq, num_heads) bytes (D_i).
+ *                 attn_bwd_workspace_bytes(q_seq, num_heads) bytes (two
+ *                 floats per row and head: D_i and the row's exponent offset).
  *                 The bytes past that hold score gradients dS_ij in 16 x 16
  *                 tiles (1 KiB per tile and head), which lets dq be formed
  *                 from them instead of recomputing the scores:
@@ -272,7 +273,7 @@ size_t attn_bwd_workspace_bytes_stored(int q_seq, int kv_len, int num_heads, int
  * in which attn_bwd's stored path runs with a workspace of workspace_bytes
  * for these sizes (the fewest n for which every window w < n, the 16-row
  * query tiles w, w + n, w + 2n, ..., holds at most the dS tiles that fit past
- * the D_i scratch). 1 when every tile fits. 0 when no count up to 32 fits
+ * the row-vector scratch). 1 when every tile fits. 0 when no count up to 32 fits
  * (the workspace is below the tiles of the longest query tile, or more than
  * 32 windows would be needed), for q_seq == 0 and for invalid sizes (as
  * attn_bwd_workspace_bytes_stored); attn_bwd then recomputes. Whether a call

@@ -251,7 +251,7 @@ def test_attn_bwd_rejects_on_host(lib, kw, status):
 
 
 def test_bwd_workspace_bytes(lib):
-    assert lib.attn_bwd_workspace_bytes(16384, 32) == 16384 * 32 * 4
+    assert lib.attn_bwd_workspace_bytes(16384, 32) == 16384 * 32 * 8
     assert lib.attn_bwd_workspace_bytes(3, 5) == 256  # rounded up to 256 bytes
     assert lib.attn_bwd_workspace_bytes(0, 4) == 0
     assert lib.attn_bwd_workspace_bytes(-1, 4) == 0
@@ -290,7 +290,7 @@ def test_bwd_workspace_bytes_stored(lib):
         tiles = _stored_tiles_brute(q, kv, mode, sp)
         want = lib.attn_bwd_workspace_bytes(q, H) + H * tiles * 1024
         assert f(q, kv, H, mode, sp) == want, (q, kv, H, mode, sp)
-    assert f(16384, 16384, 32, CAUSAL, 0) == 16384 * 32 * 4 + 32 * (1024 * 1025 // 2) * 1024
+    assert f(16384, 16384, 32, CAUSAL, 0) == 16384 * 32 * 8 + 32 * (1024 * 1025 // 2) * 1024
     # sizes attn_bwd rejects
     assert f(10, 9, 4, CAUSAL, 0) == 0        # start_pos + q_seq > kv_len
     assert f(10, 12, 4, FULL, 0) == 0         # full needs kv_len == q_seq

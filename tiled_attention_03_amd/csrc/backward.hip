@@ -13,7 +13,8 @@
 // summed over the query heads of each KV head for dk, dv (GQA).
 //
 // No atomics anywhere (run-to-run bitwise deterministic). Two paths:
-//   * stored path (workspace for every 16 x 16 dS tile): D_i kernel; dk/dv
+//   * stored path (workspace for every 16 x 16 dS tile): row-vector kernel
+//     (D_i and the exponent offset of each row's pair); dk/dv
 //     kernel that also writes the dS tiles it forms; dq = scale * dS K as one
 //     product over the stored tiles. The matrix work is the algorithmic five
 //     products (S, dP, dV, dK, dQ);
@@ -25,13 +26,13 @@
 //     XOR-swizzled). Per tile: S^T = K Q^T and dP^T = V dout^T (keys x rows),
 //     P^T and dS^T elementwise in the accumulator registers, dq^T += K^T dS^T
 //     with dS^T reused in place as the B operand (the forward's P.V
-//     pairing); it also computes D_i for the second kernel. Then the dk/dv
+//     pairing); it also writes the row vectors for the second kernel. Then the dk/dv
 //     kernel. S and dP are formed in both kernels (seven products).
 // The dk/dv kernel (key-parallel) in both paths: a wave owns 16 keys of one
 // KV head, holds K and V as B operands, and walks the 16-row query tiles of
 // every head of its group that can see its keys (causal: rows from
 // key - start_pos on), Q and dout tiles streamed through LDS with their
-// (m, log l) and D. Per tile: S = Q K^T and dP = dout V^T (rows x keys), then
+// rows' exponent offsets and D. Per tile: S = Q K^T and dP = dout V^T (rows x keys), then
 // dv^T += dout^T P and dk^T += Q^T dS with P and dS in place.
 
 #include <hip/hip_runtime.h>
@@ -199,7 +200,11 @@ bwd_dq_kernel(const float* __restrict__ q, const float* __restrict__ k,
         if (ok) {
             const float2 ml = *reinterpret_cast<const float2*>(lse + ((size_t)row * a.num_heads + head) * 2);
             lse2 = (ml.x + ml.y) * kLog2e;
-            if (hh == 0 && kvs == 0) delta[(size_t)row * a.num_heads + head] = dlt;
+            if (hh == 0 && kvs == 0) {  // -D_i, then the exponent offset, for the dk/dv kernel
+                const size_t pr = (size_t)row * a.num_heads + head;
+                delta[pr] = -dlt;
+                delta[(size_t)a.q_seq * a.num_heads + pr] = -lse2;
+            }
         }
     }
 
@@ -354,16 +359,15 @@ template <int D, int W, bool STORE>
 __global__ void __launch_bounds__(64 * W, 8 / W)  // 8 waves per CU: two per SIMD
 bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                   const float* __restrict__ v, const float* __restrict__ dout,
-                  const float* __restrict__ lse, const float* __restrict__ delta,
-                  float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ ds,
-                  BwdArgs a) {
+                  const float* __restrict__ rowv, float* __restrict__ dk,
+                  float* __restrict__ dv, float* __restrict__ ds, BwdArgs a) {
     constexpr int KS = D / 4;   // k-steps of the score products
     constexpr int NB = D / 16;  // 16-row blocks of dk^T, dv^T
     constexpr int CPR = D / 4;  // 16-byte chunks per row
     constexpr int TILE_F = k16Rows * D;
     constexpr int LOADS = TILE_F / 4 / 64;  // wave instructions per tile (<= 8)
-    // [2][SUB][Q tile | dout tile], then [2][SUB][128 floats: (m, log l) x 16 rows
-    // (twice), D x 16 rows (four times)]
+    // [2][SUB][Q tile | dout tile], then [2][SUB][128 floats: the rows' exponent
+    // offsets -(m + log l) log2 e, then their -D_i, 16 rows four times each]
     constexpr int SUB = kDkdvSub;  // query tiles per stage (one barrier per stage)
     // Row r of a tile stores logical 16-byte chunk c at position c ^ swz(r).
     // A ds_read_b128 is served 16 lanes at a time over 64 four-byte banks (16
@@ -447,7 +451,7 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     auto qt_of = [&](int it) { return a.win.off + (j0 + it % n_qt) * a.win.stride; };
 
     // Copies go through buffer resources whose base is the tile's first row
-    // (of Q / dout at head h, of the (m, log l) pairs, of D_i) and whose size
+    // (of Q / dout at head h, of the row vectors) and whose size
     // ends at q_seq: every lane's byte offsets are the same for every tile
     // (computed once below), so a copy costs no vector instructions for its
     // address, and rows past q_seq read as zero (those rows are masked).
@@ -460,9 +464,10 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const int r = s_ / CPR, p = s_ % CPR;
         qoff[u] = (unsigned)(r * qd + 4 * (p ^ swz(r))) * 4u;
     }
-    // (m, log l): lane l holds component l % 2 of row (l / 2) % 16; D_i: row l % 16.
-    const unsigned loff = (unsigned)(((lane >> 1) & 15) * a.num_heads * 2 + (lane & 1)) * 4u;
+    // Row vectors (rowv: -D_i per (row, head), then the exponent offsets):
+    // lane l holds row l % 16.
     const unsigned doff = (unsigned)((lane & 15) * a.num_heads) * 4u;
+    const size_t n_pairs = (size_t)a.q_seq * a.num_heads;
     auto issue_rows = [&](int it, int sub, float* tb, int u) __attribute__((always_inline)) {
         const int inst = wave + W * u;
         if (inst < LOADS) {
@@ -486,12 +491,12 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         const int row0 = qt_of(it) * k16Rows;
         const int rows = min(k16Rows, a.q_seq - row0);
         const auto rl = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(lse + ((size_t)row0 * a.num_heads + h) * 2), 0,
-            rows * a.num_heads * 8, kBufferFlags);
+            const_cast<float*>(rowv + n_pairs + (size_t)row0 * a.num_heads + h), 0,
+            rows * a.num_heads * 4, kBufferFlags);
         const auto rd = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(delta + (size_t)row0 * a.num_heads + h), 0, rows * a.num_heads * 4,
+            const_cast<float*>(rowv + (size_t)row0 * a.num_heads + h), 0, rows * a.num_heads * 4,
             kBufferFlags);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(vb + sub * 128), 4, loff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(vb + sub * 128), 4, doff, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(vb + sub * 128 + 64), 4, doff, 0, 0,
                                                  0);
     };
@@ -563,15 +568,12 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 const float* Qs = rt + (size_t)sub * 2 * TILE_F;
                 const float* Gs = Qs + TILE_F;
                 const float* vd = rv + sub * 128;
-                // S = Q K^T - (m + log l) (log2 units), dP = dout V^T: register
-                // r of lane (j, g) is query row0 + 4g + r, key key0 + j. The
-                // score products start from the row's -(m + log l), so the
-                // exponent needs no subtraction.
-                f32x4 s;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    s[r] = (vd[2 * (4 * g + r)] + vd[2 * (4 * g + r) + 1]) * -kLog2e;
-                f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
+                // S = Q K^T - (m + log l) (log2 units), dP - D = dout V^T - D:
+                // register r of lane (j, g) is query row0 + 4g + r, key
+                // key0 + j. The products start from the rows' -(m + log l) and
+                // -D_i, so neither the exponent nor dS needs a subtraction.
+                f32x4 s = *reinterpret_cast<const f32x4*>(vd + 4 * g);
+                f32x4 dp = *reinterpret_cast<const f32x4*>(vd + 64 + 4 * g);
 #pragma unroll
                 for (int c = 0; c < KS / 4; ++c) {
                     const int pos = ((g * KS / 4 + c) ^ swz(j)) * 4;
@@ -593,11 +595,10 @@ bwd_dkdv16_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 // the products and the first vector reads of their results).
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float dl = vd[64 + 4 * g + r];
                     const bool valid = (unsigned)(row0 + r + vbase) < vspan;
                     const float p = valid ? __builtin_amdgcn_exp2f(s[r]) : 0.f;
                     s[r] = p;
-                    dp[r] = p * (dp[r] - dl);
+                    dp[r] = p * dp[r];
                 }
                 if constexpr (STORE) {
                     // The 16 x 16 dS tile (query rows x keys, row-major) of this
@@ -678,13 +679,15 @@ __device__ __forceinline__ float dpp_f(float x) {
                                                       0xF, 0xF, false));
 }
 
-// D_i = <dout_i, out_i> per (row, head): 16 lanes per pair, D/16 contiguous
-// floats each, summed over the 16 lanes with DPP (quad xor 1, quad xor 2,
-// half-row mirror, row mirror).
+// The dk/dv kernel's row vectors per (row, head): -D_i with D_i =
+// <dout_i, out_i> (16 lanes per pair, D/16 contiguous floats each, summed over
+// the 16 lanes with DPP: quad xor 1, quad xor 2, half-row mirror, row mirror),
+// and the exponent offset -(m + log l) log2 e of the row's stored pair. The
+// dk/dv kernel starts its products from them.
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_delta_kernel(const float* __restrict__ o, const float* __restrict__ dout,
-                 float* __restrict__ delta, long long n_pairs) {
+                 const float* __restrict__ lse, float* __restrict__ rowv, long long n_pairs) {
     constexpr int PER = D / 16;
     const int tid = threadIdx.x;
     const long long pair = (long long)blockIdx.x * 16 + (tid >> 4);
@@ -707,7 +710,11 @@ bwd_delta_kernel(const float* __restrict__ o, const float* __restrict__ dout,
     acc += dpp_f<0x4E>(acc);
     acc += dpp_f<0x141>(acc);
     acc += dpp_f<0x140>(acc);
-    if (l16 == 0 && pair < n_pairs) delta[pair] = acc;
+    const float2 ml = *reinterpret_cast<const float2*>(lse + 2 * pc);
+    if (l16 == 0 && pair < n_pairs) {
+        rowv[pair] = -acc;
+        rowv[n_pairs + pair] = (ml.x + ml.y) * -kLog2e;
+    }
 }
 
 // dq from stored dS. A block is 4 KS waves: KS key splits of 4 waves, the 4
@@ -973,32 +980,29 @@ int gcd_int(int x, int y) {
 
 template <int D, int W, bool STORE>
 hipError_t launch_dkdv16(long long grid, size_t lds, hipStream_t stream, const float* q,
-                         const float* k, const float* v, const float* dout, const float* lse,
-                         const float* delta, float* dk, float* dv, float* ds,
-                         const BwdArgs& a) {
+                         const float* k, const float* v, const float* dout, const float* rowv,
+                         float* dk, float* dv, float* ds, const BwdArgs& a) {
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(bwd_dkdv16_kernel<D, W, STORE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     if (grid > 0) {
         hipLaunchKernelGGL((bwd_dkdv16_kernel<D, W, STORE>), dim3((unsigned)grid), dim3(64 * W),
-                           lds, stream, q, k, v, dout, lse, delta, dk, dv, ds, a);
+                           lds, stream, q, k, v, dout, rowv, dk, dv, ds, a);
     }
     return hipSuccess;
 }
 
 template <int D, bool STORE>
 hipError_t launch_dkdv16_any(size_t lds, hipStream_t stream, const float* q, const float* k,
-                             const float* v, const float* dout, const float* lse,
-                             const float* delta, float* dk, float* dv, float* ds,
-                             const BwdArgs& a) {
+                             const float* v, const float* dout, const float* rowv, float* dk,
+                             float* dv, float* ds, const BwdArgs& a) {
     // Blocks of 4 waves (64 keys), two per compute unit: while one block's
     // waves wait at a barrier the other block's share each SIMD (8-wave
     // blocks, one per CU, measured ~1 ms slower on the 16K causal pass).
     const long long blocks =
         (long long)a.num_kv_heads * ((a.kv_len + 4 * k16Keys - 1) / (4 * k16Keys));
-    return launch_dkdv16<D, 4, STORE>(blocks, lds, stream, q, k, v, dout, lse, delta, dk, dv,
-                                      ds, a);
+    return launch_dkdv16<D, 4, STORE>(blocks, lds, stream, q, k, v, dout, rowv, dk, dv, ds, a);
 }
 
 // Blocks of one dq-from-dS instance that the device holds at once.
@@ -1030,7 +1034,7 @@ hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, con
                              int n_win, int cus, hipStream_t stream) {
     const long long n_pairs = (long long)a0.q_seq * a0.num_heads;
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((n_pairs + 15) / 16)), dim3(256), 0,
-                       stream, o, dout, delta, n_pairs);
+                       stream, o, dout, lse, delta, n_pairs);
     const int n_qt = ds_query_tiles(a0.ds);
     for (int w = 0; w < n_win; ++w) {
         BwdArgs a = a0;
@@ -1047,8 +1051,8 @@ hipError_t launch_bwd_stored(const float* q, const float* k, const float* v, con
         }
         const long long blocks =
             (long long)a.num_kv_heads * ((keys + 4 * k16Keys - 1) / (4 * k16Keys));
-        const hipError_t e = launch_dkdv16<D, 4, true>(blocks, 0, stream, q, k, v, dout, lse,
-                                                       delta, dk, dv, ds, a);
+        const hipError_t e =
+            launch_dkdv16<D, 4, true>(blocks, 0, stream, q, k, v, dout, delta, dk, dv, ds, a);
         if (e != hipSuccess) return e;
         // dq: 4 query tiles per wave while that still gives two blocks per
         // CU, else one (2 per wave measured slower on the 16K causal pass in 9
@@ -1095,8 +1099,7 @@ hipError_t launch_bwd_instance(const float* q, const float* k, const float* v, c
     }
     // With no query rows the dk/dv blocks walk no tiles and write zeros.
     const size_t lds16 = 0;  // static LDS
-    return launch_dkdv16_any<D, false>(lds16, stream, q, k, v, dout, lse, delta, dk, dv, nullptr,
-                                       a);
+    return launch_dkdv16_any<D, false>(lds16, stream, q, k, v, dout, delta, dk, dv, nullptr, a);
 }
 
 }  // namespace

@@ -168,7 +168,7 @@ int attn_rope_apply(const float* x, long long x_stride, float* y, long long y_st
 
 size_t attn_bwd_workspace_bytes(int q_seq, int num_heads) {
     if (q_seq < 0 || num_heads < 1) return 0;
-    const size_t n = (size_t)q_seq * (size_t)num_heads * sizeof(float);
+    const size_t n = 2 * (size_t)q_seq * (size_t)num_heads * sizeof(float);
     return (n + 255) / 256 * 256;
 }
 
@@ -186,7 +186,7 @@ size_t attn_bwd_workspace_bytes_stored(int q_seq, int kv_len, int num_heads, int
 }
 
 namespace {
-// dS tiles per head that a backward workspace holds past the D_i scratch.
+// dS tiles per head that a backward workspace holds past the row-vector scratch.
 long long bwd_tile_capacity(int q_seq, int num_heads, size_t workspace_bytes) {
     const size_t base = attn_bwd_workspace_bytes(q_seq, num_heads);
     const size_t tile_bytes = (size_t)ta03::kDsTile * ta03::kDsTile * sizeof(float);
@@ -244,7 +244,7 @@ int attn_bwd(const float* q, const float* k, const float* v, const float* out, c
     s.scale = scale;
     s.q_stride = s.out_stride = (long long)num_heads * head_dim;
     s.k_stride = s.v_stride = (long long)num_kv_heads * head_dim;
-    // Workspace past the D_i scratch holds dS tiles (stored path): every tile
+    // Workspace past the row-vector scratch holds dS tiles (stored path): every tile
     // of the call, or a window of query tiles at a time.
     const size_t base = attn_bwd_workspace_bytes(q_seq, num_heads);
     const long long capacity = bwd_tile_capacity(q_seq, num_heads, workspace_bytes);

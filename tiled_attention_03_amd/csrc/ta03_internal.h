@@ -73,7 +73,8 @@ inline bool prefill16_fits(const PrefillShape& s) {
 }
 
 // Attention backward (dense rows): dq [q_seq, H*d]; dk, dv [kv_len, Hkv*d];
-// delta: q_seq*H floats of scratch (D_i = <dout_i, out_i> per row and head).
+// delta: 2*q_seq*H floats of scratch (per row and head: -D_i with
+// D_i = <dout_i, out_i>, then the exponent offset -(m + log l) log2 e).
 // Stored score gradients of the backward: dS in 16 x 16 tiles (query rows x
 // keys, row-major, 1 KiB each), one run of tiles per head, and inside a head
 // the tiles of query tile qt (rows [16 qt, 16 qt + 16)) for key tiles
