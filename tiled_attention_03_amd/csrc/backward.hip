@@ -731,8 +731,8 @@ bwd_delta_kernel(const float* __restrict__ o, const float* __restrict__ dout,
 //      contiguous bytes (no bank conflicts);
 //   result block b: register r of lane (j, g) is row 4g + r, column d, so a
 //      row's four column blocks store as one float4 per lane.
-// Tiles past a query tile's window (or query tiles past q_seq) are read
-// clamped to a valid tile and zeroed by a select. RT = 4 query tiles per wave
+// Key tiles past a query tile's window (and query tiles past the window's
+// count) read as zero through the dS tiles' buffer resources. RT = 4 query tiles per wave
 // (each K operand read serves 4 products), 1 where that would leave the grid
 // short of blocks; then KS = 2 or 4 key splits where the grid is short even
 // so: a window's dq launch otherwise lasts as long as one wave's walk over
@@ -803,35 +803,55 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
     const int kt0 = split * n_kt;
     const int so = split * TILE_F;  // this split's slot in each buffer (floats)
 
-    long long tbase[RT];
-    int tcount[RT];
-    bool tlive[RT];
+    // The dS tiles of query tile rt go through a buffer resource whose base
+    // is its first tile and whose size is its tile count (0 for a tile past
+    // the window's count): key tiles past its window read as zero, so the
+    // products need no select and the loads no clamp.
+    __amdgpu_buffer_rsrc_t rds[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int jl = j_first + rt;
         const int jc = min(jl, a.win.count - 1);
-        tlive[rt] = jl < a.win.count;
-        tcount[rt] = ds_tiles_in(a.ds, a.win.off + jc * a.win.stride);
-        tbase[rt] = (long long)head * a.ds_tph + ds_win_tiles_before(a.ds, a.win, jc);
+        const int tcount = jl < a.win.count ? ds_tiles_in(a.ds, a.win.off + jc * a.win.stride) : 0;
+        const long long tbase = (long long)head * a.ds_tph + ds_win_tiles_before(a.ds, a.win, jc);
+        rds[rt] = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(ds + (size_t)tbase * TF), 0,
+                                                    tcount * TF * 4, kBufferFlags);
+    }
+    const unsigned dso = (unsigned)(16 * j + 4 * g) * 4u;  // the lane's float4 of a dS tile
+    // K copies through a buffer resource whose base is the key tile's first
+    // row of this KV head and whose size ends at kv_len (rows past it, and
+    // the repeats past the last tile, read as zero): each lane's byte offsets
+    // are fixed for the whole kernel. LOADS / 4 copies per wave (4 waves per
+    // split), a count the compiler sees, so that it can count this wave's
+    // loads in flight at every wait.
+    unsigned koff[LOADS / 4];
+#pragma unroll
+    for (int i = 0; i < LOADS / 4; ++i) {
+        const int s_ = (wq + 4 * i) * 64 + lane;
+        koff[i] = (unsigned)((s_ / CPR) * kvd + 4 * (s_ % CPR)) * 4u;
     }
 
     // Step kt of this split: key tile kt0 + kt.
     auto issue = [&](int kt, float* dst, float4 (&x)[RT]) __attribute__((always_inline)) {
-        // LOADS / 4 copies per wave (4 waves per split), a count the compiler
-        // sees, so that it can count this wave's loads in flight at every wait.
+        const int t = kt0 + kt;
+        // (Moved to a scalar register explicitly: the clamp otherwise became
+        // a vector min-max, and the resource a loop over its lanes.)
+        const int rows = __builtin_amdgcn_readfirstlane(min(k16Keys, max(a.kv_len - t * k16Keys, 0)));
+        const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(k + (size_t)t * k16Keys * kvd + kv_head * D), 0, rows * kvd * 4,
+            kBufferFlags);
 #pragma unroll
         for (int i = 0; i < LOADS / 4; ++i) {
-            const int inst = wq + 4 * i;
-            const int s_ = inst * 64 + lane;
-            const int r = s_ / CPR, c = s_ % CPR;
-            const int key = min((kt0 + kt) * k16Keys + r, a.kv_len - 1);
-            __builtin_amdgcn_global_load_lds(k + (size_t)key * kvd + kv_head * D + 4 * c,
-                                             (lds_void*)(dst + (so + inst * 256)), 16, 0, 0);
+            const unsigned ko = koff[i];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, (lds_void*)(dst + (so + (wq + 4 * i) * 256)), 16, ko, 0, 0, 0);
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const long long t = tbase[rt] + min(kt0 + kt, max(tcount[rt] - 1, 0));
-            x[rt] = *reinterpret_cast<const float4*>(ds + (size_t)t * TF + 16 * j + 4 * g);
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rds[rt], dso + (unsigned)t * (TF * 4),
+                                                                 0, 0);
+            x[rt] = make_float4(__int_as_float(v[0]), __int_as_float(v[1]), __int_as_float(v[2]),
+                                __int_as_float(v[3]));
         }
     };
 
@@ -861,11 +881,10 @@ bwd_dq_ds_kernel(const float* __restrict__ k, const float* __restrict__ ds,
         float av[RT][4];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const bool live = tlive[rt] && kt0 + kt < tcount[rt];
-            av[rt][0] = live ? cur[rt].x : 0.f;
-            av[rt][1] = live ? cur[rt].y : 0.f;
-            av[rt][2] = live ? cur[rt].z : 0.f;
-            av[rt][3] = live ? cur[rt].w : 0.f;
+            av[rt][0] = cur[rt].x;
+            av[rt][1] = cur[rt].y;
+            av[rt][2] = cur[rt].z;
+            av[rt][3] = cur[rt].w;
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
