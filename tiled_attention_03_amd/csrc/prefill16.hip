@@ -47,6 +47,7 @@ constexpr int kWavesPerCU = 8;  // two waves per SIMD
 constexpr float kNegBig = -1e30f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRefSlack = 8.0f;  // log2 units: weights stay <= 256 between reference moves
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -153,8 +154,21 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     f32x4 o[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = kNegBig;  // log2 units
-    float l_run = 0.f;
+    // Online softmax against a reference max (log2 units), as in the 32-row
+    // kernel: the score products start from -m_ref, so they give s - m_ref
+    // and p = exp2 of the result, and the reference (with O and the sum)
+    // moves only when some lane's score passes its row's reference by more
+    // than kRefSlack, or a row sees its first keys: one wave-wide vote per
+    // tile. A row's 16 keys of a tile sit in four lanes; each lane keeps its
+    // own running max above the reference (rel) and its own partial sum, and
+    // the row's are formed across the four lanes only when the reference
+    // moves and once after the last tile. Before a row has a reference,
+    // m_ref is 0, thr is -inf and rel is -inf.
+    float m_ref = 0.f;
+    float thr = -INFINITY;  // kRefSlack once the row has a reference
+    float rel = -INFINITY;
+    float l_part = 0.f;
+    f32x4 negm = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const float* kbase = k + kv_head * D;
     const float* vbase = v + kv_head * D;
@@ -198,8 +212,8 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
     auto compute = [&](const Tile<D>& T, int t, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int kv0 = t * kKeys;
-        // S^T: row 4g + r is key kv0 + 4g + r, column j the query.
-        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+        // S^T - m_ref: row 4g + r is key kv0 + 4g + r, column j the query.
+        f32x4 s = negm;
 #pragma unroll
         for (int st = 0; st < KS; ++st) s = mfma16(comp(T.kx[st / 4], st % 4), qr[st], s);
         // The window mask as a select (a branch here would put a block edge
@@ -211,21 +225,31 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
 #pragma unroll
             for (int r = 0; r < 4; ++r) s[r] = kv0 + 4 * g + r < w_row ? s[r] : -INFINITY;
         }
-        const float mx = pair_max32(pair_max16(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))));
-        const float m_new = fmaxf(m_run, mx);
-        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-        float ls = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
-            ls += s[r];
-        }
-        ls = pair_sum32(pair_sum16(ls));
-        l_run = l_run * corr + ls;
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0ull) {
+        const float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        rel = fmaxf(rel, mx);
+        if (__builtin_amdgcn_ballot_w64(mx > thr) != 0ull) {
+            // Every row takes its running max as the new reference. A row
+            // with a reference had one lane at rel = 0 after its last move, so
+            // its shift is >= 0 and the correction <= 1; a row without one
+            // has O and the sum still 0.
+            const float rrow = pair_max32(pair_max16(rel));
+            const bool seen = rrow > -INFINITY;
+            const float shift = seen ? rrow : 0.f;
+            const float corr = thr > -INFINITY ? __builtin_amdgcn_exp2f(-shift) : 0.f;
 #pragma unroll
             for (int b = 0; b < NB; ++b) o[b] *= corr;
+            l_part *= corr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[r] -= shift;
+            m_ref += shift;
+            rel -= shift;
+            thr = thr > -INFINITY || seen ? kRefSlack : -INFINITY;
+            negm = f32x4{-m_ref, -m_ref, -m_ref, -m_ref};
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = __builtin_amdgcn_exp2f(s[r]);
+            l_part += s[r];
         }
         __builtin_amdgcn_s_setprio(1);
         // O^T += V^T P^T: k-step tt pairs key 4g + tt with register tt. At
@@ -272,6 +296,22 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
         } else {
             compute(A, t, masked);
         }
+    }
+
+    // The row's (max, sum) pair from its four lanes' parts: max = m_ref +
+    // the lanes' max above the reference, the sum and O rescaled to it
+    // (selects, no branch: O holds matrix-core results).
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+    float m_run, l_run;
+    {
+        const float rrow = pair_max32(pair_max16(rel));
+        const float lrow = pair_sum32(pair_sum16(l_part));
+        const bool seen = rrow > -INFINITY;
+        const float f = seen ? __builtin_amdgcn_exp2f(-rrow) : 0.f;
+        m_run = seen ? m_ref + rrow : kNegBig;
+        l_run = lrow * f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) o[b] *= f;
     }
 
     if (a.ks > 1) {
