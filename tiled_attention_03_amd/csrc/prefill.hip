@@ -233,9 +233,12 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     // they produce s - m_ref directly, and the reference moves only when a
     // row's max exceeds it by more than kRefSlack (p <= 2^kRefSlack in
     // between): most tiles then need neither a subtraction per score nor a
-    // rescale of O. rel = true running max - m_ref; before a row has seen a
-    // key (has_ref false) m_ref is 0 and rel is -inf. The true (max, sum)
-    // pair is restored once at the end. The instance that turns the keys,
+    // rescale of O. A query column's 32 keys of a tile sit in two lanes (one
+    // per half-wave); each lane keeps its own running max above the reference
+    // (rel) and its own partial sum, and the column's are formed across the
+    // two lanes only when the reference moves and once at the end, where the
+    // true (max, sum) pair is restored. Before a row has seen a key m_ref is
+    // 0 and thr and rel are -inf. The instance that turns the keys,
     // whose registers are spoken for (with the reference's registers it
     // spilled 24 and took 17.5 instead of 16.2 ms on the 16K workload), keeps
     // the plain running max m_run and rescales whenever it moves.
@@ -243,8 +246,8 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     float m_run = kNegBig;
     float m_ref = 0.f;
     float rel = -INFINITY;
-    bool has_ref = false;
-    float l_run = 0.f;
+    float thr = -INFINITY;  // kRefSlack once the row has a reference
+    float l_run = 0.f;      // reference instance: this lane's partial sum
     f32x16 negm;
 #pragma unroll
     for (int r = 0; r < 16; ++r) negm[r] = 0.f;
@@ -516,18 +519,20 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
             float mx = s[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-            mx = pair_max32(mx);  // tile max - m_ref (-inf: no key of the tile in the window)
           if constexpr (REF) {
+            // This lane's tile max - m_ref (-inf: none of its keys in the window).
             rel = fmaxf(rel, mx);
-            // Move the reference (one wave-wide vote) when a row's max passed
-            // it by more than the slack, or a row sees its first keys: every
-            // row of the wave takes its true max as the new reference, and O,
-            // the sum and this tile's scores follow.
-            const bool move = mx > kRefSlack || (!has_ref && mx > -INFINITY);
-            if (__builtin_amdgcn_ballot_w64(move) != 0ull) {
-                const bool seen = rel > -INFINITY;
-                const float shift = seen ? rel : 0.f;
-                const float corr = has_ref ? __builtin_amdgcn_exp2f(-shift) : 0.f;
+            // Move the reference (one wave-wide vote) when a lane's max passed
+            // its row's by more than the slack, or a row sees its first keys:
+            // every row of the wave takes its true max as the new reference,
+            // and O, the sum and this tile's scores follow. A row with a
+            // reference had one lane at rel = 0 after its last move, so its
+            // shift is >= 0; a row without one has O and the sum still 0.
+            if (__builtin_amdgcn_ballot_w64(mx > thr) != 0ull) {
+                const float rrow = pair_max32(rel);
+                const bool seen = rrow > -INFINITY;
+                const float shift = seen ? rrow : 0.f;
+                const float corr = thr > -INFINITY ? __builtin_amdgcn_exp2f(-shift) : 0.f;
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -537,19 +542,22 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 for (int r = 0; r < 16; ++r) s[r] -= shift;
                 m_ref += shift;
                 rel -= shift;
-                has_ref = has_ref || seen;
+                thr = thr > -INFINITY || seen ? kRefSlack : -INFINITY;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) negm[r] = -m_ref;
             }
+            // The tile's sum first, then one add to the lane's running sum
+            // (thousands of single weights added to one running sum would
+            // round more).
             float ls = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 s[r] = __builtin_amdgcn_exp2f(s[r]);
                 ls += s[r];
             }
-            ls = pair_sum32(ls);
             l_run += ls;
           } else {
+            mx = pair_max32(mx);  // tile max (-inf: no key of the tile in the window)
             const float m_new = fmaxf(m_run, mx);
             const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
             float ls = 0.f;
@@ -625,12 +633,18 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         if (it + 1 < nt) step(it + 1, lb1, my0, std::true_type{});
     }
 
-    // The true (max, sum) pair: max = m_ref + rel, sum and O scaled by
-    // 2^-rel (rows that saw no key keep l = 0 and the sentinel max).
-    if (REF && has_ref) {
-        m_run = m_ref + rel;
-        const float f = __builtin_amdgcn_exp2f(-rel);
-        l_run *= f;
+    // The true (max, sum) pair from the two lanes' parts: max = m_ref + the
+    // lanes' max above the reference, sum and O scaled to it (rows that saw
+    // no key keep l = 0 and the sentinel max). Selects, no branch: O holds
+    // matrix-core results.
+    if constexpr (REF) {
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+        const float rrow = pair_max32(rel);
+        const float lrow = pair_sum32(l_run);
+        const bool seen = rrow > -INFINITY;
+        const float f = seen ? __builtin_amdgcn_exp2f(-rrow) : 0.f;
+        m_run = seen ? m_ref + rrow : kNegBig;
+        l_run = lrow * f;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll

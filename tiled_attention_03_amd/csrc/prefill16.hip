@@ -246,11 +246,10 @@ prefill16_kernel(const float* __restrict__ q, const float* __restrict__ k,
             thr = thr > -INFINITY || seen ? kRefSlack : -INFINITY;
             negm = f32x4{-m_ref, -m_ref, -m_ref, -m_ref};
         }
+        // The tile's sum first, then one add to the lane's running sum.
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            s[r] = __builtin_amdgcn_exp2f(s[r]);
-            l_part += s[r];
-        }
+        for (int r = 0; r < 4; ++r) s[r] = __builtin_amdgcn_exp2f(s[r]);
+        l_part += (s[0] + s[1]) + (s[2] + s[3]);
         __builtin_amdgcn_s_setprio(1);
         // O^T += V^T P^T: k-step tt pairs key 4g + tt with register tt. At
         // raised wave priority, so the SIMD's other wave fills the gaps with
