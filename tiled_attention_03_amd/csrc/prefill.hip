@@ -247,7 +247,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
     float m_ref = 0.f;
     float rel = -INFINITY;
     float thr = -INFINITY;  // kRefSlack once the row has a reference
-    float l_run = 0.f;      // reference instance: this lane's partial sum
+    float l_run = 0.f;      // this lane's partial sum until the end
     f32x16 negm;
 #pragma unroll
     for (int r = 0; r < 16; ++r) negm[r] = 0.f;
@@ -566,8 +566,7 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
                 s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
                 ls += s[r];
             }
-            ls = pair_sum32(ls);
-            l_run = l_run * corr + ls;
+            l_run = l_run * corr + ls;  // this lane's part; the pair's summed at the end
             m_run = m_new;
             // Rescale only if some row's max moved: one wave-wide vote
             // instead of 16*NB multiplies.
@@ -649,6 +648,8 @@ prefill_kernel(const float* __restrict__ q, const float* __restrict__ k,
         for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[b][r] *= f;
+    } else {
+        l_run = pair_sum32(l_run);
     }
 
     if constexpr (KS > 1) {
